@@ -1,0 +1,252 @@
+"""Benchmark: lightning-attention prefill at a million tokens, plus decode.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one prefill of the million-token workload (B=1, H=64,
+N=1,048,576, d=128, bf16 inputs and output, block 256, fp32 state), i.e. all
+of its kernels: decay-power table, chunk aggregates, chunk scan, chunk
+output.  Inputs are synthetic (seeded, generated on the device) and resident
+in HBM before timing starts.  Prints ONE JSON line:
+
+  value          whole-job prefill tokens/s (B*N / step time)
+  roofline       the output kernel (the dominant one): algorithmic bytes per
+                 launch (1024 B per head-token: q, k, v read + o written, bf16)
+                 over its mean duration from HIP events recorded around it on
+                 its own stream, against 8 TB/s
+  cpu_baseline   the fp64 oracle (plain-C recurrence) on a bounded sample of
+                 the same workload, on this host's cores
+  decode         256 sequences x 64 heads x d=128 decode step, 1000 in-place
+                 steps timed as a whole: GB/s of state + token traffic
+
+Only one GPU is used; --gpus > 1 exits with a message.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+_ROOT = os.path.dirname(os.path.abspath(__file__))
+if _ROOT not in sys.path:
+    sys.path.insert(0, _ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+BYTES_PER_HT = 1024            # q, k, v read + o written, bf16, d = 128
+FLOP_PER_HT = 131072           # causal half of 2*b*d (b = 256) + 4*d^2 (inter + state update)
+TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "chunk_output_traffic.json")
+PREFILL_SRC = os.path.join(_ROOT, "long_context_decayed_amd", "csrc", "la_prefill.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def _hip():
+    import torch
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def _src_hash():
+    h = hashlib.sha256()
+    for name in ("la_prefill.hip", "la_device.h"):
+        h.update(open(os.path.join(_ROOT, "long_context_decayed_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(launch_alg_bytes):
+    """HBM bytes per launch of the output kernel from the committed rocprofv3
+    counter summary, or None when it is absent or the kernel source changed."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != _src_hash():
+        log("traffic record is stale (kernel changed since the counters were taken): null")
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def bench_prefill(args, dev):
+    import torch
+    import long_context_decayed_amd as la
+    from long_context_decayed_amd.inputs import decay_lambdas, qkv_device
+
+    B, H, N, d, block = 1, 64, args.tokens, 128, 256
+    log("generating inputs B=%d H=%d N=%d d=%d bf16 (seed 3)" % (B, H, N, d))
+    q, k, v = qkv_device(B, H, N, d, seed=3, device=dev, slice_tokens=65536)
+    lam = torch.from_numpy(decay_lambdas(H)).to(dev)
+    out = torch.empty_like(q)
+    kv_out = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    chunk = la.chunk_for(B, H, N, block)
+    ws = torch.empty(la.workspace_bytes(B, H, N, d, block), device=dev, dtype=torch.uint8)
+    torch.cuda.synchronize()
+
+    hip = _hip()
+    evs = []
+    for _ in range(2 * args.steps):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e)
+
+    def step(i=None):
+        ev = None if i is None else (evs[2 * i].value, evs[2 * i + 1].value)
+        la.fwd(q, k, v, lam, kv_out=kv_out, block=block, out=out, workspace=ws, events=ev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("timing %d steps" % args.steps)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern = []
+    for i in range(args.steps):
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[2 * i], evs[2 * i + 1]) == 0
+        kern.append(ms.value)
+    for e in evs:
+        hip.hipEventDestroy(e)
+    kern_ms = sum(kern) / len(kern)
+    ht = B * H * N
+    alg_bytes = BYTES_PER_HT * ht
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = _traffic(alg_bytes)
+    res = dict(
+        B=B, H=H, N=N, d=d, block=block, chunk=chunk,
+        ms_per_step=ms_step,
+        tokens_per_s=B * N / (ms_step * 1e-3),
+        output_kernel_ms=kern_ms,
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS, traffic=traffic),
+        step_hbm_frac=alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        mfma_alg_frac=FLOP_PER_HT * ht / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+    )
+    sample = None
+    if args.cpu_baseline:
+        sample = (q, k, v, decay_lambdas(H))
+    else:
+        del q, k, v
+    del out, ws
+    return res, sample
+
+
+def bench_decode(args, dev):
+    import torch
+    import long_context_decayed_amd as la
+    from long_context_decayed_amd.inputs import decay_lambdas, qkv_device, state_device
+
+    B, H, d, steps = 256, 64, 128, args.decode_steps
+    log("decode: %d sequences x %d heads, d=%d, %d steps" % (B, H, d, steps))
+    q, k, v = (t[:, :, 0].contiguous() for t in qkv_device(B, H, 1, d, seed=4, device=dev))
+    s = state_device(B, H, d, seed=4, device=dev)
+    lam = torch.from_numpy(decay_lambdas(H)).to(dev)
+    o = torch.empty_like(q)
+    for _ in range(10):
+        la.decode_step(q, k, v, lam, kv_in=s, kv_out=s, out=o)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        la.decode_step(q, k, v, lam, kv_in=s, kv_out=s, out=o)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    per_step_bytes = 2 * B * H * d * d * 4 + 4 * B * H * d * 2
+    gbs = per_step_bytes * steps / (ms * 1e-3) / 1e9
+    return dict(workload="decode 256 seq x H=64 x d=128, fp32 state, bf16 q/k/v/o", steps=steps,
+                us_per_step=ms * 1e3 / steps, bytes_per_step=per_step_bytes, gb_per_s=gbs,
+                frac_hbm=gbs / HBM_PEAK_GBS)
+
+
+def cpu_baseline(sample, args):
+    """The fp64 oracle recurrence, untouched, on a bounded sample of the
+    workload: the first `heads` heads x first `tokens` tokens."""
+    import numpy as np
+    from oracle import crec
+
+    q, k, v, lam = sample
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(16, cores))
+    heads = threads
+    tokens = min(args.cpu_tokens, q.shape[2])
+    hs = lambda t: t[0, :heads, :tokens].float().cpu().numpy()
+    qs, ks, vs = hs(q), hs(k), hs(v)
+    log("cpu baseline: oracle on %d heads x %d tokens, %d threads" % (heads, tokens, threads))
+    t0 = time.perf_counter()
+    crec.recurrent(qs, ks, vs, lam[:heads].astype(np.float64), o_range=(tokens, tokens), threads=threads,
+                   want_state=False)
+    dt = time.perf_counter() - t0
+    ht_per_s = heads * tokens / dt
+    return dict(value=ht_per_s / q.shape[1], unit="tokens/s", cores=threads, kind="oracle",
+                sample="fp64 C recurrence over %d heads x %d tokens of the million-token workload "
+                       "(%.1f s wall); value = head-tokens/s divided by the workload's 64 heads" % (
+                           heads, tokens, dt))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tokens", type=int, default=1 << 20)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", dest="decode", action="store_false")
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--cpu-tokens", type=int, default=131072)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sequence, head and batch sharding are described in DESIGN.md but not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    prefill, sample = bench_prefill(args, dev)
+    dec = bench_decode(args, dev) if args.decode else None
+    cpu = cpu_baseline(sample, args) if args.cpu_baseline else None
+    line = {
+        "metric": "lightning-attn fwd tokens/s + % bf16 MFMA peak at N=1M; decode GB/s % HBM peak",
+        "value": prefill["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": prefill["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded device Gaussians / sqrt(d); per-head decays exp(-2^(-(8/H)(h+1))))",
+        "config": {"workload": "lightning-attention prefill, one million-token layer: B=1 H=64 N=%d d=128 "
+                               "bf16 in/out, block 256, chunk %d" % (prefill["N"], prefill["chunk"]),
+                   "batch": prefill["B"], "heads": prefill["H"], "seq_len": prefill["N"], "head_dim": 128,
+                   "block": 256, "chunk": prefill["chunk"]},
+        "roofline": prefill["roofline"],
+        "output_kernel_ms": prefill["output_kernel_ms"],
+        "step_hbm_frac": prefill["step_hbm_frac"],
+        "mfma_alg_frac": prefill["mfma_alg_frac"],
+        "cpu_baseline": cpu,
+        "decode": dec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

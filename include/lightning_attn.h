@@ -1,0 +1,149 @@
+/*
+ * lightning_attn.h -- C ABI of the MI355X (gfx950) lightning-attention library.
+ *
+ * What is computed.  The MiniMax-M1 fact sheet (archdb), "linear / SSM layer
+ * configuration" field, describes the lightning layer as linear attention
+ * with a fixed per-head exponential decay (ALiBi-style slopes) and a 128x128
+ * state per head; its "positional scheme" field says the layer has no RoPE.
+ * The CocoLoop explainer ("MiniMax-01 Lightning Attention", section "El
+ * enfoque de Lightning Attention") calls it a linear-attention variant that
+ * takes attention from O(n^2) to about O(n).  This library computes the
+ * causal decayed form of it, per (batch b, head h), with lam = decay[h]:
+ *
+ *     S_{-1} = kv_in[b,h] (zero if kv_in is NULL)
+ *     S_t    = lam * S_{t-1} + k_t^T v_t           (S is d x d, S[key][value])
+ *     o_t    = q_t S_t
+ *     kv_out[b,h] = S_{N-1}
+ *
+ * equivalently O = (Q K^T (.) M) V + diag(lam^(t+1)) Q S_{-1} with
+ * M[i][j] = lam^(i-j) for i >= j and 0 otherwise (lam^0 = 1, also at lam = 0).
+ * No 1/sqrt(d) scale and no normaliser are applied.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers, 16-byte aligned, contiguous.
+ *    Q, K, V, O are row-major [B][H][N][d]; states are float32 [B][H][d][d]
+ *    (row = key index, column = value index); decay is float32 [H], each
+ *    value in [0, 1], shared by every batch entry.
+ *  - bf16 means IEEE bfloat16 (1-8-7); results are rounded to nearest even.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls only enqueue work on it and return; there is no host
+ *    synchronisation.  A kernel fault surfaces at the caller's next sync.
+ *  - The caller owns every buffer.  The library never frees or retains
+ *    caller memory.
+ *  - kv_in may equal kv_out (in-place state update).  out must not overlap
+ *    q, k, v, kv_in or kv_out.
+ *  - Arguments are validated before any HIP call, so validation errors are
+ *    returned without touching the device.  Nothing is thrown across the ABI.
+ *
+ * Status codes: LA_OK, or one of the LA_ERR_* values below;
+ * lightning_attn_strerror() names them.
+ */
+#ifndef LIGHTNING_ATTN_H
+#define LIGHTNING_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_OK 0
+#define LA_ERR_INVALID 1      /* NULL pointer, size <= 0, bad block/chunk, misaligned pointer, overlap */
+#define LA_ERR_UNSUPPORTED 2  /* d not in {64, 128}; dtype/block combination not built; N*d >= 2^31 */
+#define LA_ERR_HIP 3          /* a HIP runtime call or kernel launch failed */
+#define LA_ERR_NOMEM 4        /* the library's own workspace allocation failed */
+#define LA_ERR_WORKSPACE 5    /* caller workspace too small */
+
+#define LA_DTYPE_BF16 0
+#define LA_DTYPE_F32 1
+
+/*
+ * Prefill, bf16 Q/K/V/O, fp32 accumulation and fp32 state.
+ *   q, k, v   : bf16 [B][H][N][d]            (read)
+ *   decay     : float [H]                    (read)
+ *   out       : bf16 [B][H][N][d]            (written)
+ *   kv_in     : float [B][H][d][d] or NULL   (read; NULL = zero initial state)
+ *   kv_out    : float [B][H][d][d] or NULL   (written; S after the last token)
+ *   B, H, N   : >= 1;  d in {64, 128}
+ *   block     : intra-block length of the blockwise algorithm, one of
+ *               {64, 128, 256}.  The result does not depend on it beyond
+ *               rounding.
+ * Scratch (decay-power table and per-chunk states, see
+ * lightning_attn_fwd_workspace_bytes) is allocated stream-ordered with
+ * hipMallocAsync/hipFreeAsync on `stream`.
+ */
+int lightning_attn_fwd(const void* q, const void* k, const void* v, const float* decay, void* out,
+                       const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
+                       int64_t block, void* stream);
+
+/* Same as lightning_attn_fwd with float32 q, k, v and out.  block 64 for d = 128;
+ * {64, 128, 256} for d = 64. */
+int lightning_attn_fwd_f32(const void* q, const void* k, const void* v, const float* decay, void* out,
+                           const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
+                           int64_t block, void* stream);
+
+/* Same as lightning_attn_fwd with bf16 q, k, v and a float32 out: the same
+ * kernels as the bf16 path, storing the fp32 accumulator instead of rounding
+ * it to bf16 (so bf16 out == RNE(fp32 out) for the same inputs). */
+int lightning_attn_fwd_bf16_f32out(const void* q, const void* k, const void* v, const float* decay,
+                                   void* out, const float* kv_in, float* kv_out, int64_t B, int64_t H,
+                                   int64_t N, int64_t d, int64_t block, void* stream);
+
+/*
+ * General prefill entry point behind the three above.
+ *   in_dtype, out_dtype : LA_DTYPE_BF16 / LA_DTYPE_F32 (f32 in requires f32 out)
+ *   chunk     : tokens per chunk of the chunk-parallel scan; 0 picks the
+ *               default (lightning_attn_fwd_chunk); otherwise a positive
+ *               multiple of block.  The result does not depend on it beyond
+ *               rounding.
+ *   workspace : device scratch of at least lightning_attn_fwd_workspace_bytes()
+ *               bytes, 256-byte aligned, owned by the caller and not used
+ *               after the enqueued work completes; NULL = allocate
+ *               stream-ordered as lightning_attn_fwd does.
+ *   evt_begin, evt_end : optional hipEvent_t (as void*), recorded on `stream`
+ *               immediately before and after the output kernel (the
+ *               dominant kernel), for timing; NULL = not recorded.
+ */
+int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const float* decay, void* out,
+                          const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
+                          int64_t block, int in_dtype, int out_dtype, int64_t chunk, void* workspace,
+                          size_t workspace_bytes, void* evt_begin, void* evt_end, void* stream);
+
+/* Chunk length the library uses for (B, H, N, block) when `chunk` is 0, or
+ * `chunk` itself when it is valid; -1 on invalid arguments. */
+int64_t lightning_attn_fwd_chunk(int64_t B, int64_t H, int64_t N, int64_t block, int64_t chunk);
+
+/* Bytes of scratch lightning_attn_fwd_ex needs for these sizes (0 on invalid
+ * arguments).  Layout: the decay-power table, then B*H*ceil(N/chunk) float32
+ * d x d chunk states. */
+size_t lightning_attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                                          int64_t chunk);
+
+/*
+ * One decode step for B sequences (N = 1 of the recurrence above):
+ *     S <- lam * S + k^T v ;   o = q S
+ *   q, k, v   : bf16 [B][H][d]              (read)
+ *   decay     : float [H]                   (read)
+ *   out       : bf16 [B][H][d]              (written)
+ *   kv_in     : float [B][H][d][d] or NULL  (read; NULL = zero state)
+ *   kv_out    : float [B][H][d][d] or NULL  (written; may equal kv_in)
+ *   B, H >= 1; d in {64, 128}
+ */
+int lightning_attn_decode_step(const void* q, const void* k, const void* v, const float* decay, void* out,
+                               const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t d,
+                               void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* lightning_attn_strerror(int status);
+
+/* HIP runtime version the library is running against (hipRuntimeGetVersion),
+ * written to *version; returns LA_OK or LA_ERR_HIP / LA_ERR_INVALID. */
+int lightning_attn_runtime_version(int* version);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIGHTNING_ATTN_H */

@@ -1,0 +1,184 @@
+"""MI355X (gfx950) lightning attention: causal decayed linear attention.
+
+Thin ctypes binding over liblightning_attn.so (C ABI in include/lightning_attn.h).
+This layer only checks and marshals arguments: every step of the computation
+runs in the library's HIP kernels.  torch supplies device memory and the
+current stream.  If the library has not been built the calls raise; there is
+no CPU fallback.
+
+    out = fwd(q, k, v, decay, kv_in=None, kv_out=None, block=256)
+    o   = decode_step(q, k, v, decay, kv_in, kv_out)
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LIB_PATH",
+    "LightningAttnError",
+    "load",
+    "fwd",
+    "decode_step",
+    "workspace_bytes",
+    "chunk_for",
+    "runtime_version",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblightning_attn.so")
+
+LA_DTYPE_BF16 = 0
+LA_DTYPE_F32 = 1
+_DT = {torch.bfloat16: LA_DTYPE_BF16, torch.float32: LA_DTYPE_F32}
+
+_lib = None
+
+
+class LightningAttnError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (what, _strerror(status), status))
+
+
+def load():
+    """Load the HIP library (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "liblightning_attn.so is not built (%s); run "
+            "`python -m long_context_decayed_amd.build`" % LIB_PATH
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    fwd_args = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64]
+    for name in ("lightning_attn_fwd", "lightning_attn_fwd_f32", "lightning_attn_fwd_bf16_f32out"):
+        fn = getattr(lib, name)
+        fn.restype = I
+        fn.argtypes = fwd_args + [P]
+    lib.lightning_attn_fwd_ex.restype = I
+    lib.lightning_attn_fwd_ex.argtypes = fwd_args + [I, I, I64, P, SZ, P, P, P]
+    lib.lightning_attn_fwd_chunk.restype = I64
+    lib.lightning_attn_fwd_chunk.argtypes = [I64, I64, I64, I64, I64]
+    lib.lightning_attn_fwd_workspace_bytes.restype = SZ
+    lib.lightning_attn_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64]
+    lib.lightning_attn_decode_step.restype = I
+    lib.lightning_attn_decode_step.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, P]
+    lib.lightning_attn_strerror.restype = ctypes.c_char_p
+    lib.lightning_attn_strerror.argtypes = [I]
+    lib.lightning_attn_runtime_version.restype = I
+    lib.lightning_attn_runtime_version.argtypes = [ctypes.POINTER(ctypes.c_int)]
+    _lib = lib
+    return lib
+
+
+def _strerror(status):
+    try:
+        return load().lightning_attn_strerror(int(status)).decode()
+    except Exception:  # pragma: no cover - only when the library is absent
+        return "status %d" % status
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_dev(name, t, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def chunk_for(B, H, N, block=256, chunk=0):
+    """Chunk length the library uses (chunk=0: its default)."""
+    return int(load().lightning_attn_fwd_chunk(B, H, N, block, chunk))
+
+
+def workspace_bytes(B, H, N, d, block=256, chunk=0):
+    return int(load().lightning_attn_fwd_workspace_bytes(B, H, N, d, block, chunk))
+
+
+def fwd(q, k, v, decay, kv_in=None, kv_out=None, block=256, out=None, out_dtype=None, chunk=0,
+        workspace=None, events=None, stream=None):
+    """Prefill.  q, k, v: [B, H, N, d] bf16 or fp32 device tensors; decay: fp32 [H];
+    kv_in / kv_out: fp32 [B, H, d, d] or None.  Returns out [B, H, N, d] in
+    out_dtype (default: the input dtype).
+
+    workspace: a uint8 device tensor of at least workspace_bytes(...) bytes;
+    None allocates one from torch's caching allocator.  events: optional pair
+    of hipEvent_t handles (ints) recorded around the output kernel."""
+    lib = load()
+    if q.dtype not in _DT:
+        raise TypeError("q must be bfloat16 or float32")
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype, (B, H, N, d))
+    _check_dev("decay", decay, torch.float32, (H,))
+    for name, t in (("kv_in", kv_in), ("kv_out", kv_out)):
+        if t is not None:
+            _check_dev(name, t, torch.float32, (B, H, d, d))
+    odt = out_dtype if out_dtype is not None else (out.dtype if out is not None else q.dtype)
+    if odt not in _DT:
+        raise TypeError("out dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((B, H, N, d), device=q.device, dtype=odt)
+    _check_dev("out", out, odt, (B, H, N, d))
+    need = int(lib.lightning_attn_fwd_workspace_bytes(B, H, N, d, block, chunk))
+    if need == 0:
+        raise LightningAttnError(1, "lightning_attn_fwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    _check_dev("workspace", workspace, torch.uint8)
+    e0, e1 = (None, None) if events is None else (ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
+    rc = lib.lightning_attn_fwd_ex(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(kv_in), _ptr(kv_out),
+        B, H, N, d, block, _DT[q.dtype], _DT[odt], chunk,
+        _ptr(workspace), workspace.numel(), e0, e1, _stream(stream),
+    )
+    if rc != 0:
+        raise LightningAttnError(rc, "lightning_attn_fwd_ex")
+    return out
+
+
+def decode_step(q, k, v, decay, kv_in=None, kv_out=None, out=None, stream=None):
+    """One decode step.  q, k, v: [B, H, d] bf16; decay fp32 [H]; kv_in / kv_out:
+    fp32 [B, H, d, d] (may be the same tensor).  Returns o [B, H, d] bf16."""
+    lib = load()
+    B, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, torch.bfloat16, (B, H, d))
+    _check_dev("decay", decay, torch.float32, (H,))
+    for name, t in (("kv_in", kv_in), ("kv_out", kv_out)):
+        if t is not None:
+            _check_dev(name, t, torch.float32, (B, H, d, d))
+    if out is None:
+        out = torch.empty((B, H, d), device=q.device, dtype=torch.bfloat16)
+    _check_dev("out", out, torch.bfloat16, (B, H, d))
+    rc = lib.lightning_attn_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(kv_in), _ptr(kv_out), B, H, d, _stream(stream)
+    )
+    if rc != 0:
+        raise LightningAttnError(rc, "lightning_attn_decode_step")
+    return out
+
+
+def runtime_version():
+    v = ctypes.c_int(0)
+    rc = load().lightning_attn_runtime_version(ctypes.byref(v))
+    if rc != 0:
+        raise LightningAttnError(rc, "lightning_attn_runtime_version")
+    return v.value

@@ -1,0 +1,218 @@
+// C ABI of the lightning-attention library: argument validation, chunk choice,
+// workspace layout and the calls into the kernel launchers.  Every check runs
+// before the first HIP call, so validation errors never touch the device.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lightning_attn.h"
+#include "la_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxTokens = int64_t(1) << 24;  // keeps N * d < 2^31 for per-head offsets
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  if (!a || !b) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool valid_block(int64_t block) { return block == 64 || block == 128 || block == 256; }
+
+// Default chunk: 4096 tokens, halved while the chunk-parallel passes would
+// launch fewer than 1024 workgroups, never below max(block, 256), and never
+// longer than the sequence rounded up to a whole block.
+int64_t pick_chunk(int64_t B, int64_t H, int64_t N, int64_t block) {
+  int64_t L = 4096;
+  const int64_t floor_l = block > 256 ? block : 256;
+  while (L > floor_l && B * H * ceil_div(N, L) < 1024) L /= 2;
+  const int64_t cap = ceil_div(N, block) * block;
+  if (L > cap) L = cap;
+  return L;
+}
+
+int resolve_chunk(int64_t B, int64_t H, int64_t N, int64_t block, int64_t chunk, int64_t* L) {
+  if (B < 1 || H < 1 || N < 1 || !valid_block(block)) return LA_ERR_INVALID;
+  if (chunk == 0) {
+    *L = pick_chunk(B, H, N, block);
+  } else {
+    if (chunk < 0 || chunk % block != 0 || chunk > kMaxTokens) return LA_ERR_INVALID;
+    *L = chunk;
+  }
+  return LA_OK;
+}
+
+int64_t tbl_stride_for(int64_t block) { return ((block + 1 + 63) / 64) * 64; }
+
+size_t workspace_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, int64_t L, size_t* tbl_bytes) {
+  const size_t tb = (size_t)H * (size_t)tbl_stride_for(block) * sizeof(float);
+  const size_t tb_al = (tb + 255) / 256 * 256;
+  const size_t nc = (size_t)ceil_div(N, L);
+  if (tbl_bytes) *tbl_bytes = tb_al;
+  return tb_al + (size_t)B * (size_t)H * nc * (size_t)d * (size_t)d * sizeof(float);
+}
+
+int from_hip(hipError_t e) {
+  if (e == hipSuccess) return LA_OK;
+  if (e == hipErrorOutOfMemory) return LA_ERR_NOMEM;
+  return LA_ERR_HIP;
+}
+
+int validate_prefill(const void* q, const void* k, const void* v, const float* decay, const void* out,
+                     const float* kv_in, const float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
+                     int64_t block, int in_dtype, int out_dtype, int64_t chunk, int64_t* L) {
+  if (!q || !k || !v || !decay || !out) return LA_ERR_INVALID;
+  if (B < 1 || H < 1 || N < 1 || d < 1) return LA_ERR_INVALID;
+  if (!valid_block(block)) return LA_ERR_INVALID;
+  if ((in_dtype != LA_DTYPE_BF16 && in_dtype != LA_DTYPE_F32) ||
+      (out_dtype != LA_DTYPE_BF16 && out_dtype != LA_DTYPE_F32))
+    return LA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(decay, 4) ||
+      !aligned(kv_in, 16) || !aligned(kv_out, 16))
+    return LA_ERR_INVALID;
+  if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+  if (!la::prefill_supported(in_dtype, out_dtype, d, block)) return LA_ERR_UNSUPPORTED;
+  if (N > kMaxTokens) return LA_ERR_UNSUPPORTED;
+  int rc = resolve_chunk(B, H, N, block, chunk, L);
+  if (rc != LA_OK) return rc;
+  if (B * H > kMaxGrid || B * H * ceil_div(N, *L) > kMaxGrid) return LA_ERR_UNSUPPORTED;
+  const int64_t in_es = in_dtype == LA_DTYPE_BF16 ? 2 : 4, out_es = out_dtype == LA_DTYPE_BF16 ? 2 : 4;
+  const int64_t in_bytes = B * H * N * d * in_es, out_bytes = B * H * N * d * out_es;
+  const int64_t st_bytes = B * H * d * d * 4;
+  if (overlap(out, out_bytes, q, in_bytes) || overlap(out, out_bytes, k, in_bytes) ||
+      overlap(out, out_bytes, v, in_bytes) || overlap(out, out_bytes, kv_in, st_bytes) ||
+      overlap(out, out_bytes, kv_out, st_bytes))
+    return LA_ERR_INVALID;
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const float* decay, void* out,
+                          const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
+                          int64_t block, int in_dtype, int out_dtype, int64_t chunk, void* workspace,
+                          size_t workspace_bytes, void* evt_begin, void* evt_end, void* stream) {
+  int64_t L = 0;
+  int rc = validate_prefill(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, in_dtype, out_dtype, chunk, &L);
+  if (rc != LA_OK) return rc;
+  size_t tbl_bytes = 0;
+  const size_t need = workspace_layout(B, H, N, d, block, L, &tbl_bytes);
+  if (workspace) {
+    if (workspace_bytes < need) return LA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return LA_ERR_INVALID;
+  }
+
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = workspace;
+  if (!ws) {
+    hipError_t e = hipMallocAsync(&ws, need, st);
+    if (e != hipSuccess) return e == hipErrorOutOfMemory ? LA_ERR_NOMEM : LA_ERR_HIP;
+  }
+  la::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.decay = decay;
+  a.out = out;
+  a.kv_in = kv_in;
+  a.kv_out = kv_out;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.block = block;
+  a.L = L;
+  a.nc = (int)ceil_div(N, L);
+  a.in_dtype = in_dtype == LA_DTYPE_BF16 ? la::kBF16 : la::kF32;
+  a.out_dtype = out_dtype == LA_DTYPE_BF16 ? la::kBF16 : la::kF32;
+  a.tbl = (float*)ws;
+  a.tbl_stride = (int)tbl_stride_for(block);
+  a.states = (float*)((char*)ws + tbl_bytes);
+  a.evt_begin = evt_begin;
+  a.evt_end = evt_end;
+  hipError_t e = la::launch_prefill(a, st);
+  if (!workspace) {
+    hipError_t f = hipFreeAsync(ws, st);
+    if (e == hipSuccess) e = f;
+  }
+  return from_hip(e);
+}
+
+int lightning_attn_fwd(const void* q, const void* k, const void* v, const float* decay, void* out,
+                       const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
+                       int64_t block, void* stream) {
+  return lightning_attn_fwd_ex(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, LA_DTYPE_BF16,
+                               LA_DTYPE_BF16, 0, nullptr, 0, nullptr, nullptr, stream);
+}
+
+int lightning_attn_fwd_f32(const void* q, const void* k, const void* v, const float* decay, void* out,
+                           const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
+                           int64_t block, void* stream) {
+  return lightning_attn_fwd_ex(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, LA_DTYPE_F32,
+                               LA_DTYPE_F32, 0, nullptr, 0, nullptr, nullptr, stream);
+}
+
+int lightning_attn_fwd_bf16_f32out(const void* q, const void* k, const void* v, const float* decay,
+                                   void* out, const float* kv_in, float* kv_out, int64_t B, int64_t H,
+                                   int64_t N, int64_t d, int64_t block, void* stream) {
+  return lightning_attn_fwd_ex(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, LA_DTYPE_BF16,
+                               LA_DTYPE_F32, 0, nullptr, 0, nullptr, nullptr, stream);
+}
+
+int64_t lightning_attn_fwd_chunk(int64_t B, int64_t H, int64_t N, int64_t block, int64_t chunk) {
+  int64_t L = 0;
+  if (resolve_chunk(B, H, N, block, chunk, &L) != LA_OK) return -1;
+  return L;
+}
+
+size_t lightning_attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                                          int64_t chunk) {
+  int64_t L = 0;
+  if (d < 1 || resolve_chunk(B, H, N, block, chunk, &L) != LA_OK) return 0;
+  return workspace_layout(B, H, N, d, block, L, nullptr);
+}
+
+int lightning_attn_decode_step(const void* q, const void* k, const void* v, const float* decay, void* out,
+                               const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t d,
+                               void* stream) {
+  if (!q || !k || !v || !decay || !out) return LA_ERR_INVALID;
+  if (B < 1 || H < 1 || d < 1) return LA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(decay, 4) ||
+      !aligned(kv_in, 16) || !aligned(kv_out, 16))
+    return LA_ERR_INVALID;
+  if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+  if (B * H > kMaxGrid) return LA_ERR_UNSUPPORTED;
+  const int64_t vec_bytes = B * H * d * 2, st_bytes = B * H * d * d * 4;
+  if (overlap(out, vec_bytes, q, vec_bytes) || overlap(out, vec_bytes, k, vec_bytes) ||
+      overlap(out, vec_bytes, v, vec_bytes) || overlap(out, vec_bytes, kv_in, st_bytes) ||
+      overlap(out, vec_bytes, kv_out, st_bytes))
+    return LA_ERR_INVALID;
+  return from_hip(la::launch_decode(q, k, v, decay, out, kv_in, kv_out, B, H, d, (hipStream_t)stream));
+}
+
+const char* lightning_attn_strerror(int status) {
+  switch (status) {
+    case LA_OK: return "ok";
+    case LA_ERR_INVALID: return "invalid argument";
+    case LA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case LA_ERR_HIP: return "HIP runtime error";
+    case LA_ERR_NOMEM: return "out of device memory";
+    case LA_ERR_WORKSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+int lightning_attn_runtime_version(int* version) {
+  if (!version) return LA_ERR_INVALID;
+  return hipRuntimeGetVersion(version) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+// Device-side building blocks shared by the gfx950 lightning-attention kernels:
+// MFMA operand traits, the 32x32 accumulator layout, LDS operand loaders and
+// the bf16 hi/lo split.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Accumulator layout of every 32x32 MFMA on CDNA: lane l, register j holds
+// row crow(j, l/32), column l%32.
+__device__ __forceinline__ int crow(int j, int hf) { return 8 * (j >> 2) + 4 * hf + (j & 3); }
+
+// lam^e in double by binary powering (lam^0 = 1, including lam = 0).
+__device__ __forceinline__ double pow_int(double x, int e) {
+  double r = 1.0, b = x;
+  while (e > 0) {
+    if (e & 1) r *= b;
+    b *= b;
+    e >>= 1;
+  }
+  return r;
+}
+
+// MFMA traits.  One instruction contracts KW elements; every lane contributes
+// EPL of them (lanes 0-31 and 32-63 split the contraction).  A and B use the
+// same (lane half, element) -> k correspondence, so any fixed permutation of
+// the contraction index is allowed as long as both operands follow it.
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<bf16> {
+  static constexpr int KW = 16;
+  static constexpr int EPL = 8;
+  static constexpr bool kSplit = true;  // fp32 operands are fed as bf16 hi + lo
+  typedef bf16x8 op_t;
+  static __device__ __forceinline__ f32x16 mma(op_t a, op_t b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // EPL contiguous elements.
+  static __device__ __forceinline__ op_t ld_nat(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  // Elements at columns crow(g*EPL + i, hf), i < EPL, of a row: two runs of 4.
+  static __device__ __forceinline__ op_t ld_cperm(const bf16* row, int g, int hf) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 16 * g + 4 * hf);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16 * g + 8 + 4 * hf);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // Elements p[r_i * stride] for rows r_i = crow(g*EPL + i, hf).
+  static __device__ __forceinline__ op_t ld_col_cperm(const bf16* p, int stride, int g, int hf) {
+    op_t r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = p[(16 * g + 8 * (i >> 2) + 4 * hf + (i & 3)) * stride];
+    return r;
+  }
+  // Elements p[(EPL*hf + i) * stride], i < EPL (natural contraction order).
+  static __device__ __forceinline__ op_t ld_col_nat(const bf16* p, int stride, int hf) {
+    op_t r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = p[(8 * hf + i) * stride];
+    return r;
+  }
+  static __device__ __forceinline__ op_t cvt(const float* x) {
+    op_t r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (bf16)x[i];
+    return r;
+  }
+  // x ~= hi + lo with hi = RNE(x), lo = RNE(x - hi); x - hi is exact in fp32.
+  static __device__ __forceinline__ void split(const float* x, op_t& hi, op_t& lo) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16 h = (bf16)x[i];
+      hi[i] = h;
+      lo[i] = (bf16)(x[i] - (float)h);
+    }
+  }
+  static __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+};
+
+template <>
+struct Mfma<float> {
+  static constexpr int KW = 2;
+  static constexpr int EPL = 1;
+  static constexpr bool kSplit = false;
+  typedef float op_t;
+  static __device__ __forceinline__ f32x16 mma(op_t a, op_t b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ op_t ld_nat(const float* p) { return *p; }
+  static __device__ __forceinline__ op_t ld_cperm(const float* row, int g, int hf) { return row[crow(g, hf)]; }
+  static __device__ __forceinline__ op_t ld_col_cperm(const float* p, int stride, int g, int hf) {
+    return p[crow(g, hf) * stride];
+  }
+  static __device__ __forceinline__ op_t ld_col_nat(const float* p, int stride, int hf) { return p[hf * stride]; }
+  static __device__ __forceinline__ op_t cvt(const float* x) { return x[0]; }
+  static __device__ __forceinline__ void split(const float* x, op_t& hi, op_t& lo) {
+    hi = x[0];
+    lo = 0.0f;
+  }
+  static __device__ __forceinline__ float to_f32(float x) { return x; }
+};
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+// Copy rows [t0, t0 + ROWS) of a [N][D] head into an LDS tile with row stride
+// LD elements; rows at or beyond t_end are zero-filled.  16-byte accesses.
+template <typename T, int D, int LD, int ROWS, int NT>
+__device__ __forceinline__ void stage_rows(T* __restrict__ dst, const T* __restrict__ src, int t0, int t_end,
+                                           int tid) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int CPR = D / VEC;
+  constexpr int TOTAL = ROWS * CPR;
+  static_assert(TOTAL % NT == 0, "tile must split evenly over the workgroup");
+  constexpr int PER = TOTAL / NT;
+  uint4 buf[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid + i * NT;
+    const int r = idx / CPR, cc = idx % CPR;
+    const int t = t0 + r;
+    if (t < t_end)
+      buf[i] = *reinterpret_cast<const uint4*>(src + (int64_t)t * D + cc * VEC);
+    else
+      buf[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid + i * NT;
+    const int r = idx / CPR, cc = idx % CPR;
+    *reinterpret_cast<uint4*>(dst + r * LD + cc * VEC) = buf[i];
+  }
+}
+
+}  // namespace la

@@ -1,0 +1,382 @@
+// Prefill kernels of causal decayed linear attention for gfx950.
+//
+// The MiniMax-M1 fact sheet (archdb), "linear / SSM layer configuration"
+// field: linear attention with a fixed per-head exponential decay and a d x d
+// (128 x 128) state per head.  Per (batch, head), with lam = decay[h]:
+//     S_t = lam S_{t-1} + k_t^T v_t,   o_t = q_t S_t.
+//
+// Blockwise form computed here.  Tokens are split into chunks of L tokens,
+// chunks into blocks of BLK tokens (L % BLK == 0, blocks aligned to chunk
+// starts).  For a block starting at token t_b with start state S_b, the rows
+// r of the block get
+//     o_r = lam^(r+1) q_r S_b  +  sum_{s <= r in block} lam^(r-s) (q_r . k_s) v_s
+// and the block hands on S_{b+1} = lam^BLK S_b + sum_s lam^(BLK-1-s) k_s^T v_s.
+// Only non-negative powers of lam appear (all from the table T[e] = lam^e,
+// 0 <= e <= BLK), so nothing overflows; powers that underflow are correctly 0.
+//
+// Three passes make long sequences fill the chip:
+//   A  la_chunk_state : per chunk, its aggregate U_c = sum_s lam^(L_c-1-s) k_s^T v_s,
+//                       all chunks in parallel (MFMA);
+//   B  la_chunk_scan  : per (batch, head), S <- kv_in; for c: Sstart_c = S,
+//                       S = lam^(L_c) S + U_c; kv_out = S (elementwise, fp32);
+//   C  la_chunk_output: per chunk, the block loop above from Sstart_c (MFMA).
+//
+// Precision recipe (bf16 inputs): products of two bf16 inputs are exact in the
+// fp32 MFMA accumulator.  Quantities formed in fp32 that feed an MFMA are
+// rounded: the masked, decayed scores P (one bf16), the state S used in q S
+// and the decayed values lam^(..) v used in the state update (both as a bf16
+// hi + lo pair, ~16 significant bits).  Accumulation is fp32 throughout and
+// the state stays fp32.
+
+#include <hip/hip_runtime.h>
+
+#include "la_device.h"
+#include "la_kernels.h"
+
+namespace la {
+
+constexpr int kSub = 64;  // rows per sub-tile (one LDS stage)
+
+// ---------------------------------------------------------------------------
+// Decay-power table: tbl[h][e] = lam_h^e, e in [0, stride), computed in double
+// and rounded once to float.
+__global__ void la_decay_table(const float* __restrict__ decay, float* __restrict__ tbl, int stride) {
+  const int h = blockIdx.x;
+  const double lam = (double)decay[h];
+  for (int e = threadIdx.x; e < stride; e += blockDim.x) tbl[(int64_t)h * stride + e] = (float)pow_int(lam, e);
+}
+
+// ---------------------------------------------------------------------------
+// Pass A.  One workgroup per (bh, chunk); D/32 waves, wave w owns columns
+// [32w, 32w + 32) of the chunk aggregate U (fp32 accumulators).  For each
+// sub-tile of n valid tokens: U = lam^n U + sum_{s<n} lam^(n-1-s) k_s^T v_s.
+template <typename TIn, int D>
+__global__ __launch_bounds__(D * 2) void la_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v,
+                                                        const float* __restrict__ tbl_all, float* __restrict__ ws,
+                                                        int H, int N, int L, int nc, int tbl_stride) {
+  typedef Mfma<TIn> M;
+  constexpr int NW = D / 32;
+  constexpr int NT = NW * 64;
+  constexpr int PAD = 16 / sizeof(TIn);
+  constexpr int LD = D + PAD;
+  constexpr int NRT = D / 32;
+  __shared__ __attribute__((aligned(16))) TIn Ks[kSub * LD];
+  __shared__ __attribute__((aligned(16))) TIn Vs[kSub * LD];
+  __shared__ float tbl[kSub + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
+  const int hh = bh % H;
+  const int64_t base = (int64_t)bh * N * D;
+  const TIn* kb = k + base;
+  const TIn* vb = v + base;
+  const int t_begin = c * L;
+  const int t_end = min(N, t_begin + L);
+
+  for (int e = tid; e <= kSub; e += NT) tbl[e] = tbl_all[(int64_t)hh * tbl_stride + e];
+
+  f32x16 U[NRT];
+#pragma unroll
+  for (int kt = 0; kt < NRT; ++kt) U[kt] = zero16();
+
+  for (int t0 = t_begin; t0 < t_end; t0 += kSub) {
+    const int n = min(kSub, t_end - t0);
+    stage_rows<TIn, D, LD, kSub, NT>(Ks, kb, t0, t_end, tid);
+    stage_rows<TIn, D, LD, kSub, NT>(Vs, vb, t0, t_end, tid);
+    __syncthreads();
+    const float dn = tbl[n];
+#pragma unroll
+    for (int kt = 0; kt < NRT; ++kt) U[kt] *= dn;
+#pragma unroll 2
+    for (int kk = 0; kk < kSub / M::KW; ++kk) {
+      // B operand: decayed values lam^(n-1-s) v[s][32w + l32], s = KW*kk + EPL*hf + i.
+      float x[M::EPL];
+#pragma unroll
+      for (int i = 0; i < M::EPL; ++i) {
+        const int s = M::KW * kk + M::EPL * hf + i;
+        const float dec = (s < n) ? tbl[n - 1 - s] : 0.0f;
+        x[i] = M::to_f32(Vs[s * LD + 32 * w + l32]) * dec;
+      }
+      typename M::op_t bhi, blo;
+      M::split(x, bhi, blo);
+#pragma unroll
+      for (int kt = 0; kt < NRT; ++kt) {
+        // A operand: K^T[dk = 32kt + l32][s]
+        const typename M::op_t a = M::ld_col_nat(Ks + (M::KW * kk) * LD + 32 * kt + l32, LD, hf);
+        U[kt] = M::mma(a, bhi, U[kt]);
+        if (M::kSplit) U[kt] = M::mma(a, blo, U[kt]);
+      }
+    }
+    __syncthreads();
+  }
+
+  float* dst = ws + ((int64_t)bh * nc + c) * D * D;
+#pragma unroll
+  for (int kt = 0; kt < NRT; ++kt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dst[(32 * kt + crow(j, hf)) * D + 32 * w + l32] = U[kt][j];
+}
+
+// ---------------------------------------------------------------------------
+// Pass B.  One thread per 4 consecutive state elements of one (bh); serial
+// over chunks.  ws holds U_c on entry and Sstart_c on exit.
+__global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ decay, float* __restrict__ ws,
+                                                     const float* __restrict__ kv_in, float* __restrict__ kv_out,
+                                                     int BH, int H, int N, int L, int nc, int D) {
+  const int per = D * D / 4;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)BH * per) return;
+  const int bh = (int)(gid / per), e4 = (int)(gid - (int64_t)bh * per);
+  const double lam = (double)decay[bh % H];
+  const float dl = (float)pow_int(lam, L);
+  const float dlast = (float)pow_int(lam, N - (nc - 1) * L);
+  f32x4 S = {0.f, 0.f, 0.f, 0.f};
+  if (kv_in) S = reinterpret_cast<const f32x4*>(kv_in)[(int64_t)bh * per + e4];
+  f32x4* U = reinterpret_cast<f32x4*>(ws) + (int64_t)bh * nc * per + e4;
+  int c = 0;
+  for (; c + 4 <= nc; c += 4) {
+    f32x4 u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = U[(int64_t)(c + i) * per];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      U[(int64_t)(c + i) * per] = S;
+      const float f = (c + i == nc - 1) ? dlast : dl;
+      S = f * S + u[i];
+    }
+  }
+  for (; c < nc; ++c) {
+    const f32x4 u = U[(int64_t)c * per];
+    U[(int64_t)c * per] = S;
+    const float f = (c == nc - 1) ? dlast : dl;
+    S = f * S + u;
+  }
+  if (kv_out) reinterpret_cast<f32x4*>(kv_out)[(int64_t)bh * per + e4] = S;
+}
+
+// ---------------------------------------------------------------------------
+// Pass C.  One workgroup per (bh, chunk); D/32 waves.  Wave w owns columns
+// [32w, 32w + 32) of the fp32 state S (NRT accumulator tiles) and of the
+// output.  LDS: Q of the current sub-tile, K and V of every sub-tile of the
+// current block (BLK/64 slots), the decay table.
+template <typename TIn, typename TOut, int D, int BLK>
+__global__ __launch_bounds__(D * 2) void la_chunk_output(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                                         const TIn* __restrict__ v, TOut* __restrict__ o,
+                                                         const float* __restrict__ tbl_all,
+                                                         const float* __restrict__ sstart, int H, int N, int L,
+                                                         int nc, int tbl_stride) {
+  typedef Mfma<TIn> M;
+  typedef typename M::op_t op_t;
+  constexpr int NW = D / 32;
+  constexpr int NT = NW * 64;
+  constexpr int PAD = 16 / sizeof(TIn);
+  constexpr int LD = D + PAD;
+  constexpr int NRT = D / 32;
+  constexpr int NS = BLK / kSub;
+  constexpr int G = 32 / M::KW;  // operand groups per 32-row accumulator tile
+  __shared__ __attribute__((aligned(16))) TIn Qs[kSub * LD];
+  __shared__ __attribute__((aligned(16))) TIn Ks[NS * kSub * LD];
+  __shared__ __attribute__((aligned(16))) TIn Vs[NS * kSub * LD];
+  __shared__ float tbl[BLK + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
+  const int hh = bh % H;
+  const int64_t base = (int64_t)bh * N * D;
+  const TIn* qb = q + base;
+  const TIn* kb = k + base;
+  const TIn* vb = v + base;
+  TOut* ob = o + base;
+  const int t_begin = c * L;
+  const int t_end = min(N, t_begin + L);
+  const int col = 32 * w + l32;  // this lane's value column
+
+  for (int e = tid; e <= BLK; e += NT) tbl[e] = tbl_all[(int64_t)hh * tbl_stride + e];
+
+  f32x16 S[NRT];
+  {
+    const float* src = sstart + ((int64_t)bh * nc + c) * D * D;
+#pragma unroll
+    for (int kt = 0; kt < NRT; ++kt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) S[kt][j] = src[(32 * kt + crow(j, hf)) * D + col];
+  }
+  op_t Shi[NRT][G], Slo[NRT][G];
+
+  int jb = 0;  // sub-tile index within the current block
+  for (int t0 = t_begin; t0 < t_end; t0 += kSub, jb = (jb + 1 == NS) ? 0 : jb + 1) {
+    TIn* Kj = Ks + jb * kSub * LD;
+    TIn* Vj = Vs + jb * kSub * LD;
+    stage_rows<TIn, D, LD, kSub, NT>(Qs, qb, t0, t_end, tid);
+    stage_rows<TIn, D, LD, kSub, NT>(Kj, kb, t0, t_end, tid);
+    stage_rows<TIn, D, LD, kSub, NT>(Vj, vb, t0, t_end, tid);
+    __syncthreads();
+
+    if (jb == 0) {
+      // Block start: snapshot S_b as MFMA B operands, then pre-decay S by lam^BLK.
+      const float dblk = tbl[BLK];
+#pragma unroll
+      for (int kt = 0; kt < NRT; ++kt) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float x[M::EPL];
+#pragma unroll
+          for (int i = 0; i < M::EPL; ++i) x[i] = S[kt][g * M::EPL + i];
+          M::split(x, Shi[kt][g], Slo[kt][g]);
+        }
+        S[kt] *= dblk;
+      }
+    }
+
+    // Inter-block: acc[rt] = diag(lam^(r+1)) Q S_b, r = position in the block.
+    f32x16 acc[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      acc[rt] = zero16();
+      const TIn* qrow = Qs + (32 * rt + l32) * LD;
+#pragma unroll
+      for (int kt = 0; kt < NRT; ++kt) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const op_t a = M::ld_cperm(qrow + 32 * kt, g, hf);
+          acc[rt] = M::mma(a, Shi[kt][g], acc[rt]);
+          if (M::kSplit) acc[rt] = M::mma(a, Slo[kt][g], acc[rt]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[rt][j] *= tbl[kSub * jb + 32 * rt + crow(j, hf) + 1];
+    }
+
+    // Intra-block: for every earlier-or-current sub-tile jk of the block,
+    // P^T = K_jk Q^T (32x32 tiles), masked and decayed by lam^(r-s), then acc += P V_jk.
+    for (int jk = 0; jk <= jb; ++jk) {
+      const TIn* Kk = Ks + jk * kSub * LD;
+      const TIn* Vk = Vs + jk * kSub * LD;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          if (jk == jb && st > rt) continue;
+          f32x16 p = zero16();
+          const TIn* krow = Kk + (32 * st + l32) * LD;
+          const TIn* qrow = Qs + (32 * rt + l32) * LD;
+#pragma unroll
+          for (int kk = 0; kk < D / M::KW; ++kk) {
+            const op_t a = M::ld_nat(krow + M::KW * kk + M::EPL * hf);
+            const op_t b = M::ld_nat(qrow + M::KW * kk + M::EPL * hf);
+            p = M::mma(a, b, p);
+          }
+          // p[j] = P^T[s][r] with s = 32st + crow(j, hf), r = 32rt + l32 (tile-local).
+          const int rdiff = kSub * (jb - jk) + 32 * (rt - st) + l32;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int dif = rdiff - crow(j, hf);
+            p[j] = (dif >= 0) ? p[j] * tbl[dif < 0 ? 0 : dif] : 0.0f;
+          }
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float x[M::EPL];
+#pragma unroll
+            for (int i = 0; i < M::EPL; ++i) x[i] = p[g * M::EPL + i];
+            const op_t pa = M::cvt(x);
+            const op_t vbop = M::ld_col_cperm(Vk + (32 * st) * LD + col, LD, g, hf);
+            acc[rt] = M::mma(pa, vbop, acc[rt]);
+          }
+        }
+      }
+    }
+
+    // State update: S += sum_s lam^(BLK-1-s) k_s^T v_s over this sub-tile
+    // (S was pre-decayed by lam^BLK at the block start).
+#pragma unroll 2
+    for (int kk = 0; kk < kSub / M::KW; ++kk) {
+      float x[M::EPL];
+#pragma unroll
+      for (int i = 0; i < M::EPL; ++i) {
+        const int s = M::KW * kk + M::EPL * hf + i;
+        x[i] = M::to_f32(Vj[s * LD + col]) * tbl[BLK - 1 - (kSub * jb + s)];
+      }
+      op_t bhi, blo;
+      M::split(x, bhi, blo);
+#pragma unroll
+      for (int kt = 0; kt < NRT; ++kt) {
+        const op_t a = M::ld_col_nat(Kj + (M::KW * kk) * LD + 32 * kt + l32, LD, hf);
+        S[kt] = M::mma(a, bhi, S[kt]);
+        if (M::kSplit) S[kt] = M::mma(a, blo, S[kt]);
+      }
+    }
+
+    // Store this sub-tile's rows.
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int t = t0 + 32 * rt + crow(j, hf);
+        if (t < t_end) ob[(int64_t)t * D + col] = from_f32<TOut>(acc[rt][j]);
+      }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers.
+
+template <typename TIn, typename TOut, int D, int BLK>
+static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
+  const int BH = (int)(a.B * a.H);
+  const int nc = a.nc;
+  hipLaunchKernelGGL(la_decay_table, dim3((unsigned)a.H), dim3(256), 0, st, a.decay, a.tbl, a.tbl_stride);
+  hipLaunchKernelGGL((la_chunk_state<TIn, D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+                     (const TIn*)a.k, (const TIn*)a.v, (const float*)a.tbl, a.states, (int)a.H, (int)a.N,
+                     (int)a.L, nc, a.tbl_stride);
+  {
+    const int64_t threads = (int64_t)BH * D * D / 4;
+    hipLaunchKernelGGL(la_chunk_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a.decay,
+                       a.states, a.kv_in, a.kv_out, BH, (int)a.H, (int)a.N, (int)a.L, nc, D);
+  }
+  if (a.evt_begin) {
+    hipError_t e = hipEventRecord((hipEvent_t)a.evt_begin, st);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((la_chunk_output<TIn, TOut, D, BLK>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+                     (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (TOut*)a.out, (const float*)a.tbl,
+                     (const float*)a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
+  if (a.evt_end) {
+    hipError_t e = hipEventRecord((hipEvent_t)a.evt_end, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipGetLastError();
+}
+
+template <typename TIn, typename TOut, int D>
+static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t st) {
+  switch (a.block) {
+    case 64: return launch_prefill_t<TIn, TOut, D, 64>(a, st);
+    case 128: return launch_prefill_t<TIn, TOut, D, 128>(a, st);
+    case 256: return launch_prefill_t<TIn, TOut, D, 256>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool prefill_supported(int in_dtype, int out_dtype, int64_t d, int64_t block) {
+  if (d != 64 && d != 128) return false;
+  if (block != 64 && block != 128 && block != 256) return false;
+  if (in_dtype == kBF16) return out_dtype == kBF16 || out_dtype == kF32;
+  if (in_dtype == kF32 && out_dtype == kF32) return d == 64 || block == 64;  // LDS limit for fp32 tiles
+  return false;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
+  if (a.in_dtype == kBF16 && a.out_dtype == kBF16) {
+    if (a.d == 128) return launch_prefill_d<bf16, bf16, 128>(a, st);
+    return launch_prefill_d<bf16, bf16, 64>(a, st);
+  }
+  if (a.in_dtype == kBF16 && a.out_dtype == kF32) {
+    if (a.d == 128) return launch_prefill_d<bf16, float, 128>(a, st);
+    return launch_prefill_d<bf16, float, 64>(a, st);
+  }
+  if (a.d == 128) return launch_prefill_t<float, float, 128, 64>(a, st);
+  return launch_prefill_d<float, float, 64>(a, st);
+}
+
+}  // namespace la

@@ -1,0 +1,145 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol that
+include/lightning_attn.h declares, and rejects bad arguments before any HIP
+call (every call here fails validation, so no device is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_decayed_amd as la
+from long_context_decayed_amd import build as la_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lightning_attn.h")
+
+LA_OK, LA_ERR_INVALID, LA_ERR_UNSUPPORTED, LA_ERR_HIP, LA_ERR_NOMEM, LA_ERR_WORKSPACE = range(6)
+
+# Fake, 256-byte-aligned, never-dereferenced device addresses.
+FAKE = [ctypes.c_void_p(0x7F0000000000 + i * (1 << 36)) for i in range(8)]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(la.LIB_PATH):
+        la_build.build()
+    return la.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|int64_t|const char\*)\s+(lightning_attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("lightning_attn_fwd", "lightning_attn_fwd_f32", "lightning_attn_fwd_bf16_f32out",
+                     "lightning_attn_fwd_ex", "lightning_attn_decode_step", "lightning_attn_fwd_workspace_bytes",
+                     "lightning_attn_fwd_chunk", "lightning_attn_strerror", "lightning_attn_runtime_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_library_is_gfx950_only(lib):
+    """Every device code object embedded in the library targets gfx950, and the
+    bundles are uncompressed (the runtime torch ships may predate the format)."""
+    blob = open(la.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa--(gfx[0-9a-z]+)", blob))
+    assert targets == {b"gfx950"}, targets
+    assert b"CCOB" not in blob
+
+
+def _fwd(lib, q=FAKE[0], k=FAKE[1], v=FAKE[2], decay=FAKE[3], out=FAKE[4], kv_in=None, kv_out=None,
+         B=1, H=2, N=128, d=64, block=64, ind=0, outd=0, chunk=0, ws=None, wsb=0):
+    return lib.lightning_attn_fwd_ex(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, ind, outd, chunk,
+                                     ws, wsb, None, None, None)
+
+
+def test_null_pointers_rejected(lib):
+    assert _fwd(lib, q=None) == LA_ERR_INVALID
+    assert _fwd(lib, k=None) == LA_ERR_INVALID
+    assert _fwd(lib, v=None) == LA_ERR_INVALID
+    assert _fwd(lib, decay=None) == LA_ERR_INVALID
+    assert _fwd(lib, out=None) == LA_ERR_INVALID
+    for fn in (lib.lightning_attn_fwd, lib.lightning_attn_fwd_f32, lib.lightning_attn_fwd_bf16_f32out):
+        assert fn(None, FAKE[1], FAKE[2], FAKE[3], FAKE[4], None, None, 1, 1, 64, 64, 64, None) == LA_ERR_INVALID
+
+
+def test_sizes_rejected(lib):
+    for kw in (dict(B=0), dict(H=0), dict(N=0), dict(d=0), dict(B=-1), dict(N=-5)):
+        assert _fwd(lib, **kw) == LA_ERR_INVALID, kw
+    for block in (0, 32, 100, 512):
+        assert _fwd(lib, block=block) == LA_ERR_INVALID, block
+    for d in (32, 96, 256):
+        assert _fwd(lib, d=d) == LA_ERR_UNSUPPORTED, d
+    assert _fwd(lib, N=(1 << 24) + 1) == LA_ERR_UNSUPPORTED
+
+
+def test_dtypes(lib):
+    assert _fwd(lib, ind=1, outd=0) == LA_ERR_UNSUPPORTED      # fp32 in, bf16 out
+    assert _fwd(lib, ind=2) == LA_ERR_INVALID
+    assert _fwd(lib, outd=7) == LA_ERR_INVALID
+    assert _fwd(lib, ind=1, outd=1, d=128, block=128) == LA_ERR_UNSUPPORTED  # fp32 d=128 needs block 64
+
+
+def test_chunk_rejected(lib):
+    assert _fwd(lib, chunk=100) == LA_ERR_INVALID
+    assert _fwd(lib, chunk=-64) == LA_ERR_INVALID
+    assert _fwd(lib, block=128, chunk=64) == LA_ERR_INVALID
+
+
+def test_alignment_and_overlap(lib):
+    assert _fwd(lib, q=ctypes.c_void_p(FAKE[0].value + 2)) == LA_ERR_INVALID
+    assert _fwd(lib, kv_in=ctypes.c_void_p(FAKE[5].value + 4)) == LA_ERR_INVALID
+    assert _fwd(lib, decay=ctypes.c_void_p(FAKE[3].value + 2)) == LA_ERR_INVALID
+    assert _fwd(lib, out=FAKE[0]) == LA_ERR_INVALID                                  # out == q
+    assert _fwd(lib, out=ctypes.c_void_p(FAKE[1].value + 64)) == LA_ERR_INVALID       # out inside k
+    assert _fwd(lib, out=FAKE[5], kv_out=ctypes.c_void_p(FAKE[5].value + 16)) == LA_ERR_INVALID
+
+
+def test_workspace_checks(lib):
+    need = lib.lightning_attn_fwd_workspace_bytes(1, 2, 128, 64, 64, 0)
+    assert need > 0
+    assert _fwd(lib, ws=FAKE[6], wsb=need - 1) == LA_ERR_WORKSPACE
+    assert _fwd(lib, ws=ctypes.c_void_p(FAKE[6].value + 16), wsb=need) == LA_ERR_INVALID
+
+
+def test_workspace_and_chunk_values(lib):
+    # million-token prefill: 64 heads, d=128, block 256 -> 4096-token chunks, 256 per head
+    assert lib.lightning_attn_fwd_chunk(1, 64, 1 << 20, 256, 0) == 4096
+    tbl = 64 * 320 * 4
+    assert lib.lightning_attn_fwd_workspace_bytes(1, 64, 1 << 20, 128, 256, 0) == tbl + 64 * 256 * 128 * 128 * 4
+    # 8192 tokens x 64 heads: chunks halve until >= 1024 workgroups
+    assert lib.lightning_attn_fwd_chunk(1, 64, 8192, 256, 0) == 512
+    # tiny: floor at 256 tokens, capped by the block-rounded length
+    assert lib.lightning_attn_fwd_chunk(1, 2, 1024, 64, 0) == 256
+    assert lib.lightning_attn_fwd_chunk(1, 1, 100, 64, 0) == 128
+    assert lib.lightning_attn_fwd_chunk(1, 1, 100, 64, 192) == 192
+    assert lib.lightning_attn_fwd_chunk(1, 1, 100, 64, 100) == -1
+    assert lib.lightning_attn_fwd_workspace_bytes(1, 1, 0, 64, 64, 0) == 0
+
+
+def test_decode_validation(lib):
+    f = lib.lightning_attn_decode_step
+    assert f(None, FAKE[1], FAKE[2], FAKE[3], FAKE[4], None, None, 1, 1, 128, None) == LA_ERR_INVALID
+    assert f(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], None, None, 0, 1, 128, None) == LA_ERR_INVALID
+    assert f(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], None, None, 1, 1, 96, None) == LA_ERR_UNSUPPORTED
+    assert f(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[0], None, None, 1, 1, 128, None) == LA_ERR_INVALID
+
+
+def test_strerror(lib):
+    for code in range(6):
+        s = lib.lightning_attn_strerror(code).decode()
+        assert s and s != "unknown status"
+    assert lib.lightning_attn_strerror(99).decode() == "unknown status"
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(la, "_lib", None)
+    monkeypatch.setattr(la, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        la.load()

@@ -1,0 +1,115 @@
+"""GPU parity of the decode step against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_decayed_amd as la
+import oracle as ora
+from long_context_decayed_amd.inputs import decay_lambdas, qkv_device, state_device
+import tolerances as tol
+from gpu_helpers import host, lam_for, oracle, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _tokens(b, h, d, seed, dev):
+    q, k, v = qkv_device(b, h, 1, d, seed=seed, device=dev)
+    return q[:, :, 0].contiguous(), k[:, :, 0].contiguous(), v[:, :, 0].contiguous()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_one_step(dev, d):
+    say("decode one step B256 H64 d", d)
+    B, H = 256, 64
+    q, k, v = _tokens(B, H, d, 4, dev)
+    lam = decay_lambdas(H)
+    s0 = state_device(B, H, d, seed=4, device=dev)
+    s_in = host(s0).astype(np.float64)
+    kv = torch.empty_like(s0)
+    o = la.decode_step(q, k, v, torch.from_numpy(lam).to(dev), kv_in=s0, kv_out=kv)
+    torch.cuda.synchronize()
+    o_ref, s_ref = ora.decode_step(host(q), host(k), host(v), lam.astype(np.float64), s_in)
+    tol.assert_state(host(kv), s_ref)
+    tol.assert_bf16_out(host(o), o_ref)
+    # k_i v_j of two bf16 values is exact in fp32: the only state rounding is
+    # lam*S + kv in fp32, so the state is far inside the tolerance
+    assert tol.state_error(host(kv), s_ref) < 1e-6
+
+
+def test_decode_1000_steps_closed_form(dev):
+    say("decode 1000 steps in place B256 H64 d128")
+    B, H, d = 256, 64, 128
+    q, k, v = _tokens(B, H, d, 5, dev)
+    lam = decay_lambdas(H)
+    s = state_device(B, H, d, seed=5, device=dev)
+    s_in = host(s).astype(np.float64)
+    lam_t = torch.from_numpy(lam).to(dev)
+    for _ in range(1000):
+        o = la.decode_step(q, k, v, lam_t, kv_in=s, kv_out=s)
+    torch.cuda.synchronize()
+    s_ref = ora.decode_repeated(s_in, host(k), host(v), lam.astype(np.float64), 1000)
+    tol.assert_state(host(s), s_ref)
+    o_ref = np.einsum("bhi,bhij->bhj", host(q).astype(np.float64), s_ref)
+    tol.assert_bf16_out(host(o), o_ref)
+
+
+@pytest.mark.parametrize("mode", ["one", "near_one"])
+def test_decode_many_steps_lam_one(dev, mode):
+    say("decode 300 steps lam", mode)
+    B, H, d = 4, 8, 128
+    q, k, v = _tokens(B, H, d, 6, dev)
+    lam = lam_for(H, mode)
+    s = state_device(B, H, d, seed=6, device=dev)
+    s_in = host(s).astype(np.float64)
+    lam_t = torch.from_numpy(lam).to(dev)
+    for _ in range(300):
+        la.decode_step(q, k, v, lam_t, kv_in=s, kv_out=s)
+    torch.cuda.synchronize()
+    tol.assert_state(host(s), ora.decode_repeated(s_in, host(k), host(v), lam.astype(np.float64), 300))
+
+
+def test_decode_zero_state_and_no_kv_out(dev):
+    say("decode kv_in=None kv_out=None")
+    B, H, d = 3, 5, 64
+    q, k, v = _tokens(B, H, d, 7, dev)
+    lam = decay_lambdas(H)
+    o = la.decode_step(q, k, v, torch.from_numpy(lam).to(dev))
+    torch.cuda.synchronize()
+    o_ref, _ = ora.decode_step(host(q), host(k), host(v), lam.astype(np.float64), np.zeros((B, H, d, d)))
+    tol.assert_bf16_out(host(o), o_ref)
+
+
+def test_prefill_then_decode_matches_longer_prefill(dev):
+    say("fwd(N) + decode == fwd(N+1) B2 H4 N513 d128")
+    B, H, d, n = 2, 4, 128, 513
+    q, k, v = qkv_device(B, H, n + 1, d, seed=8, device=dev)
+    lam = decay_lambdas(H)
+    lam_t = torch.from_numpy(lam).to(dev)
+    kv = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    la.fwd(q[:, :, :n].contiguous(), k[:, :, :n].contiguous(), v[:, :, :n].contiguous(), lam_t, kv_out=kv,
+           block=64)
+    o_dec = la.decode_step(q[:, :, n].contiguous(), k[:, :, n].contiguous(), v[:, :, n].contiguous(), lam_t,
+                           kv_in=kv, kv_out=kv)
+    kv_full = torch.empty_like(kv)
+    o_full = la.fwd(q, k, v, lam_t, kv_out=kv_full, block=64, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lam)
+    tol.assert_bf16_out(host(o_dec), o_ref[:, :, n], ref_rms=tol.rms(o_ref))
+    tol.assert_bf16_f32out(host(o_full), o_ref)
+    tol.assert_state(host(kv), s_ref)
+    tol.assert_state(host(kv_full), s_ref)
+    # decode == fwd with N = 1 (both against the oracle)
+    o1 = la.fwd(q[:, :, :1].contiguous(), k[:, :, :1].contiguous(), v[:, :, :1].contiguous(), lam_t,
+                kv_in=kv_full, block=64, out_dtype=torch.float32)
+    o2 = la.decode_step(q[:, :, 0].contiguous(), k[:, :, 0].contiguous(), v[:, :, 0].contiguous(), lam_t,
+                        kv_in=kv_full)
+    torch.cuda.synchronize()
+    r1, _ = ora.decode_step(host(q[:, :, 0]), host(k[:, :, 0]), host(v[:, :, 0]), lam.astype(np.float64),
+                            host(kv_full).astype(np.float64))
+    tol.assert_bf16_f32out(host(o1)[:, :, 0], r1)
+    tol.assert_bf16_out(host(o2), r1)

@@ -1,0 +1,191 @@
+"""GPU parity of the prefill path against the fp64 oracle, through the C ABI.
+
+Sizes run in seconds, span several tiles, blocks and chunks, and include
+ragged tails.  Each case prints its name before touching the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_decayed_amd as la
+from long_context_decayed_amd.inputs import decay_lambdas, qkv_cpu, qkv_device, state_device, ternary_device
+import tolerances as tol
+from gpu_helpers import host, lam_for, oracle, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _run(q, k, v, lam_np, dev, block, out_dtype=None, kv_in=None, chunk=0, want_kv=True):
+    lam = torch.from_numpy(lam_np).to(dev)
+    B, H, N, d = q.shape
+    kv_out = torch.empty((B, H, d, d), device=dev, dtype=torch.float32) if want_kv else None
+    out = la.fwd(q, k, v, lam, kv_in=kv_in, kv_out=kv_out, block=block, out_dtype=out_dtype, chunk=chunk)
+    torch.cuda.synchronize()
+    return out, kv_out
+
+
+# --- fp32 workload: B=1, H=2, N=1024, d=64, block 64, seed 0 ---------------
+
+@pytest.mark.parametrize("chunk", [0, 64, 1024])
+def test_fp32_tiny_workload(dev, chunk):
+    say("fp32 B1 H2 N1024 d64 block64 chunk", chunk)
+    q, k, v = (t.to(dev) for t in qkv_cpu(1, 2, 1024, 64, seed=0))
+    lam = decay_lambdas(2)
+    out, kv = _run(q, k, v, lam, dev, 64, chunk=chunk)
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lam)
+    tol.assert_fp32(host(out), o_ref)
+    tol.assert_fp32(host(kv), s_ref, "kv_out")
+
+
+@pytest.mark.parametrize("block", [64, 128, 256])
+def test_fp32_d64_blocks_with_state(dev, block):
+    say("fp32 B2 H3 N777 d64 block", block)
+    q, k, v = (t.to(dev) for t in qkv_cpu(2, 3, 777, 64, seed=5))
+    lam = np.array([0.5, 0.9, 0.999], dtype=np.float32)
+    s0 = state_device(2, 3, 64, seed=5, device=dev)
+    out, kv = _run(q, k, v, lam, dev, block, kv_in=s0, chunk=2 * block)
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lam, host(s0).astype(np.float64))
+    tol.assert_fp32(host(out), o_ref)
+    tol.assert_fp32(host(kv), s_ref, "kv_out")
+
+
+def test_fp32_d128(dev):
+    say("fp32 B1 H2 N600 d128 block64")
+    q, k, v = (t.to(dev) for t in qkv_cpu(1, 2, 600, 128, seed=6))
+    lam = np.array([0.7, 0.99], dtype=np.float32)
+    out, kv = _run(q, k, v, lam, dev, 64, chunk=128)
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lam)
+    tol.assert_fp32(host(out), o_ref)
+    tol.assert_fp32(host(kv), s_ref, "kv_out")
+
+
+# --- integer-exact check: lam = 1, entries in {-1, 0, 1} ---------------------
+# Every partial sum is an integer below 2^24 in magnitude, so fp32 arithmetic
+# (and the bf16 hi/lo splits of integers below 2^16) is exact.
+
+def test_ternary_exact_fp32(dev):
+    say("ternary fp32 lam=1 B1 H2 N1024 d64")
+    q, k, v = ternary_device(1, 2, 1024, 64, seed=1, device=dev, dtype=torch.float32)
+    lam = lam_for(2, "one")
+    out, kv = _run(q, k, v, lam, dev, 64, chunk=256)
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lam)
+    assert np.array_equal(host(out).astype(np.float64), o_ref)
+    assert np.array_equal(host(kv).astype(np.float64), s_ref)
+
+
+@pytest.mark.parametrize("block", [64, 128, 256])
+def test_ternary_exact_bf16_f32out(dev, block):
+    say("ternary bf16->f32 lam=1 B1 H2 N1024 d128 block", block)
+    q, k, v = ternary_device(1, 2, 1024, 128, seed=2, device=dev, dtype=torch.bfloat16)
+    lam = lam_for(2, "one")
+    out, kv = _run(q, k, v, lam, dev, block, out_dtype=torch.float32, chunk=256 if block < 256 else 512)
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lam)
+    assert np.array_equal(host(out).astype(np.float64), o_ref)
+    assert np.array_equal(host(kv).astype(np.float64), s_ref)
+
+
+# --- bf16: one layer shaped like the 64-head model, N = 8192 ---------------
+
+@pytest.fixture(scope="module")
+def layer_8k(dev):
+    say("bf16 B1 H64 N8192 d128 block256 (inputs + oracle)")
+    q, k, v = qkv_device(1, 64, 8192, 128, seed=1, device=dev)
+    lam = decay_lambdas(64)
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lam)
+    return q, k, v, lam, o_ref, s_ref
+
+
+def test_bf16_layer_8k(dev, layer_8k):
+    q, k, v, lam, o_ref, s_ref = layer_8k
+    say("bf16 B1 H64 N8192 block256: fp32-out and bf16-out")
+    o32, kv32 = _run(q, k, v, lam, dev, 256, out_dtype=torch.float32)
+    o16, kv16 = _run(q, k, v, lam, dev, 256, out_dtype=torch.bfloat16)
+    e = tol.assert_bf16_f32out(host(o32), o_ref)
+    tol.assert_bf16_out(host(o16), o_ref)
+    assert torch.equal(o32.to(torch.bfloat16), o16), "bf16 out must be RNE(fp32 out)"
+    es = tol.assert_state(host(kv32), s_ref, "kv_out")
+    assert torch.equal(kv32, kv16)
+    print("max|err|/RMS = %.4e  (bf16 out: %.4e)  state rel = %.3e" % (
+        e, tol.bf16_rms_error(host(o16), o_ref), es))
+
+
+@pytest.mark.parametrize("block,chunk", [(64, 64), (64, 1024), (128, 512), (256, 256), (256, 2048)])
+def test_bf16_layer_8k_block_chunk_invariance(dev, layer_8k, block, chunk):
+    q, k, v, lam, o_ref, s_ref = layer_8k
+    say("bf16 B1 H64 N8192 block", block, "chunk", chunk)
+    o32, kv = _run(q, k, v, lam, dev, block, out_dtype=torch.float32, chunk=chunk)
+    tol.assert_bf16_f32out(host(o32), o_ref)
+    tol.assert_state(host(kv), s_ref, "kv_out")
+
+
+def test_bf16_deterministic(dev, layer_8k):
+    q, k, v, lam, _, _ = layer_8k
+    say("bf16 determinism")
+    a, ka = _run(q, k, v, lam, dev, 256)
+    b, kb = _run(q, k, v, lam, dev, 256)
+    assert torch.equal(a, b) and torch.equal(ka, kb)
+
+
+# --- ragged tails, initial state, state carry, in-place state ----------------
+
+@pytest.mark.parametrize("n", [1, 63, 65, 1000, 4097 + 13])
+def test_bf16_tails_with_state(dev, n):
+    say("bf16 tails B2 H4 N", n)
+    q, k, v = qkv_device(2, 4, n, 128, seed=10 + n, device=dev)
+    lam = decay_lambdas(4)
+    s0 = state_device(2, 4, 128, seed=10 + n, device=dev)
+    o32, kv = _run(q, k, v, lam, dev, 128, out_dtype=torch.float32, kv_in=s0, chunk=256)
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lam, host(s0).astype(np.float64))
+    tol.assert_bf16_f32out(host(o32), o_ref)
+    tol.assert_state(host(kv), s_ref, "kv_out")
+
+
+@pytest.mark.parametrize("t0", [512, 700])
+def test_bf16_state_carry(dev, t0):
+    say("bf16 state carry B1 H4 N2048 split", t0)
+    n = 2048
+    q, k, v = qkv_device(1, 4, n, 128, seed=20, device=dev)
+    lam = lam_for(4, "near_one")
+    s0 = state_device(1, 4, 128, seed=20, device=dev)
+    full, kv_full = _run(q, k, v, lam, dev, 64, out_dtype=torch.float32, kv_in=s0)
+    a, kv_a = _run(q[:, :, :t0].contiguous(), k[:, :, :t0].contiguous(), v[:, :, :t0].contiguous(), lam, dev, 64,
+                   out_dtype=torch.float32, kv_in=s0)
+    b, kv_b = _run(q[:, :, t0:].contiguous(), k[:, :, t0:].contiguous(), v[:, :, t0:].contiguous(), lam, dev, 64,
+                   out_dtype=torch.float32, kv_in=kv_a)
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lam, host(s0).astype(np.float64))
+    split = np.concatenate([host(a), host(b)], axis=2)
+    tol.assert_bf16_f32out(split, o_ref)
+    tol.assert_bf16_f32out(host(full), o_ref)
+    tol.assert_state(host(kv_b), s_ref)
+    tol.assert_state(host(kv_full), s_ref)
+
+
+def test_bf16_state_in_place(dev):
+    say("bf16 kv_in is kv_out")
+    q, k, v = qkv_device(1, 4, 1500, 64, seed=30, device=dev)
+    lam = decay_lambdas(4)
+    s0 = state_device(1, 4, 64, seed=30, device=dev)
+    s_host = host(s0).astype(np.float64)
+    out = la.fwd(q, k, v, torch.from_numpy(lam).to(dev), kv_in=s0, kv_out=s0, block=64, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lam, s_host)
+    tol.assert_bf16_f32out(host(out), o_ref)
+    tol.assert_state(host(s0), s_ref)
+
+
+# --- long-range carries: lam = 1 and just below 1 -----------------------------
+
+@pytest.mark.parametrize("mode", ["one", "near_one"])
+def test_bf16_long_range_carry(dev, mode):
+    say("bf16 long range lam", mode, "B1 H2 N65536+100")
+    n = 65536 + 100
+    q, k, v = qkv_device(1, 2, n, 128, seed=40, device=dev)
+    lam = lam_for(2, mode)
+    o32, kv = _run(q, k, v, lam, dev, 256, out_dtype=torch.float32, chunk=4096)
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lam)
+    tol.assert_bf16_f32out(host(o32), o_ref)
+    tol.assert_state(host(kv), s_ref)
