@@ -79,7 +79,7 @@ def bench_prefill(args, dev):
     import long_context_decayed_amd as la
     from long_context_decayed_amd.inputs import decay_lambdas, qkv_device
 
-    B, H, N, d, block = 1, 64, args.tokens, 128, 256
+    B, H, N, d, block = 1, 64, args.tokens, 128, args.block
     log("generating inputs B=%d H=%d N=%d d=%d bf16 (seed 3)" % (B, H, N, d))
     q, k, v = qkv_device(B, H, N, d, seed=3, device=dev, slice_tokens=65536)
     lam = torch.from_numpy(decay_lambdas(H)).to(dev)
@@ -203,6 +203,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--tokens", type=int, default=1 << 20)
+    ap.add_argument("--block", type=int, default=256, choices=[64, 128, 256])
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", dest="decode", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
@@ -235,9 +236,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded device Gaussians / sqrt(d); per-head decays exp(-2^(-(8/H)(h+1))))",
         "config": {"workload": "lightning-attention prefill, one million-token layer: B=1 H=64 N=%d d=128 "
-                               "bf16 in/out, block 256, chunk %d" % (prefill["N"], prefill["chunk"]),
+                               "bf16 in/out, block %d, chunk %d" % (prefill["N"], prefill["block"], prefill["chunk"]),
                    "batch": prefill["B"], "heads": prefill["H"], "seq_len": prefill["N"], "head_dim": 128,
-                   "block": 256, "chunk": prefill["chunk"]},
+                   "block": prefill["block"], "chunk": prefill["chunk"]},
         "roofline": prefill["roofline"],
         "output_kernel_ms": prefill["output_kernel_ms"],
         "step_hbm_frac": prefill["step_hbm_frac"],

@@ -36,6 +36,19 @@ __device__ __forceinline__ double pow_int(double x, int e) {
 template <typename T>
 struct Mfma;
 
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, output lane l receives, as element j (j < 4), the 16-bit value at
+// (address given by lane 4j + l/4 of the group) + 2 * (l % 4) bytes.  If lane
+// 4j + q of a group points at row (r + j), column (c + 4q) of a row-major
+// tile, output lane l of the group holds rows r..r+3 of column c + l.
+__device__ __forceinline__ bf16x4 ds_tr4(const bf16* p) {
+  const shortx4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
 template <>
 struct Mfma<bf16> {
   static constexpr int KW = 16;
@@ -53,19 +66,21 @@ struct Mfma<bf16> {
     const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16 * g + 8 + 4 * hf);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
-  // Elements p[r_i * stride] for rows r_i = crow(g*EPL + i, hf).
-  static __device__ __forceinline__ op_t ld_col_cperm(const bf16* p, int stride, int g, int hf) {
-    op_t r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = p[(16 * g + 8 * (i >> 2) + 4 * hf + (i & 3)) * stride];
-    return r;
+  // Operand with lane L = 32h + n holding X[row0 + 8h + i][col0 + n], i < 8,
+  // from a row-major LDS tile X with row stride ld (two transpose reads).
+  static __device__ __forceinline__ op_t ld_tr_nat(const bf16* X, int ld, int row0, int col0, int lane) {
+    const int h = lane >> 5, j = (lane & 15) >> 2;
+    const bf16* p = X + (row0 + 8 * h + j) * ld + col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const bf16x4 lo = ds_tr4(p), hi = ds_tr4(p + 4 * ld);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
-  // Elements p[(EPL*hf + i) * stride], i < EPL (natural contraction order).
-  static __device__ __forceinline__ op_t ld_col_nat(const bf16* p, int stride, int hf) {
-    op_t r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = p[(8 * hf + i) * stride];
-    return r;
+  // Same, with element i taken from row row0 + crow(8g + i, h) (the row order
+  // of an accumulator tile used as an operand).
+  static __device__ __forceinline__ op_t ld_tr_cperm(const bf16* X, int ld, int row0, int g, int col0, int lane) {
+    const int h = lane >> 5, j = (lane & 15) >> 2;
+    const bf16* p = X + (row0 + 16 * g + 4 * h + j) * ld + col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const bf16x4 lo = ds_tr4(p), hi = ds_tr4(p + 8 * ld);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
   static __device__ __forceinline__ op_t cvt(const float* x) {
     op_t r;
@@ -83,6 +98,7 @@ struct Mfma<bf16> {
     }
   }
   static __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+  static __device__ __forceinline__ bf16 elem(op_t x, int i) { return x[i]; }
 };
 
 template <>
@@ -96,16 +112,19 @@ struct Mfma<float> {
   }
   static __device__ __forceinline__ op_t ld_nat(const float* p) { return *p; }
   static __device__ __forceinline__ op_t ld_cperm(const float* row, int g, int hf) { return row[crow(g, hf)]; }
-  static __device__ __forceinline__ op_t ld_col_cperm(const float* p, int stride, int g, int hf) {
-    return p[crow(g, hf) * stride];
+  static __device__ __forceinline__ op_t ld_tr_nat(const float* X, int ld, int row0, int col0, int lane) {
+    return X[(row0 + (lane >> 5)) * ld + col0 + (lane & 31)];
   }
-  static __device__ __forceinline__ op_t ld_col_nat(const float* p, int stride, int hf) { return p[hf * stride]; }
+  static __device__ __forceinline__ op_t ld_tr_cperm(const float* X, int ld, int row0, int g, int col0, int lane) {
+    return X[(row0 + crow(g, lane >> 5)) * ld + col0 + (lane & 31)];
+  }
   static __device__ __forceinline__ op_t cvt(const float* x) { return x[0]; }
   static __device__ __forceinline__ void split(const float* x, op_t& hi, op_t& lo) {
     hi = x[0];
     lo = 0.0f;
   }
   static __device__ __forceinline__ float to_f32(float x) { return x; }
+  static __device__ __forceinline__ float elem(op_t x, int) { return x; }
 };
 
 template <typename T>
@@ -122,33 +141,40 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// Copy rows [t0, t0 + ROWS) of a [N][D] head into an LDS tile with row stride
-// LD elements; rows at or beyond t_end are zero-filled.  16-byte accesses.
-template <typename T, int D, int LD, int ROWS, int NT>
-__device__ __forceinline__ void stage_rows(T* __restrict__ dst, const T* __restrict__ src, int t0, int t_end,
-                                           int tid) {
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int CPR = D / VEC;
-  constexpr int TOTAL = ROWS * CPR;
+// 64 rows of a [N][D] head held in registers between a global load and an
+// LDS store (so the next tile's loads overlap the current tile's compute).
+// Rows at or beyond t_end read as zero.  16-byte accesses; a wave covers
+// whole contiguous rows.
+template <typename T, int D, int NT>
+struct RowTile {
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int CPR = D / VEC;
+  static constexpr int TOTAL = 64 * CPR;
   static_assert(TOTAL % NT == 0, "tile must split evenly over the workgroup");
-  constexpr int PER = TOTAL / NT;
-  uint4 buf[PER];
+  static constexpr int PER = TOTAL / NT;
+  uint4 r[PER];
+
+  __device__ __forceinline__ void load(const T* __restrict__ src, int t0, int t_end, int tid) {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int idx = tid + i * NT;
-    const int r = idx / CPR, cc = idx % CPR;
-    const int t = t0 + r;
-    if (t < t_end)
-      buf[i] = *reinterpret_cast<const uint4*>(src + (int64_t)t * D + cc * VEC);
-    else
-      buf[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NT;
+      const int row = idx / CPR, cc = idx % CPR;
+      const int t = t0 + row;
+      if (t < t_end)
+        r[i] = *reinterpret_cast<const uint4*>(src + (int64_t)t * D + cc * VEC);
+      else
+        r[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
   }
+  template <int LD>
+  __device__ __forceinline__ void store(T* __restrict__ dst, int tid) const {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int idx = tid + i * NT;
-    const int r = idx / CPR, cc = idx % CPR;
-    *reinterpret_cast<uint4*>(dst + r * LD + cc * VEC) = buf[i];
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NT;
+      const int row = idx / CPR, cc = idx % CPR;
+      *reinterpret_cast<uint4*>(dst + row * LD + cc * VEC) = r[i];
+    }
   }
-}
+};
 
 }  // namespace la

@@ -50,11 +50,15 @@ __global__ void la_decay_table(const float* __restrict__ decay, float* __restric
 // Pass A.  One workgroup per (bh, chunk); D/32 waves, wave w owns columns
 // [32w, 32w + 32) of the chunk aggregate U (fp32 accumulators).  For each
 // sub-tile of n valid tokens: U = lam^n U + sum_{s<n} lam^(n-1-s) k_s^T v_s.
+// The next sub-tile's K and V are loaded into registers while the current
+// one is contracted; operands with the token index along the contraction are
+// read from the row-major LDS tiles with transpose reads.
 template <typename TIn, int D>
 __global__ __launch_bounds__(D * 2) void la_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v,
                                                         const float* __restrict__ tbl_all, float* __restrict__ ws,
                                                         int H, int N, int L, int nc, int tbl_stride) {
   typedef Mfma<TIn> M;
+  typedef typename M::op_t op_t;
   constexpr int NW = D / 32;
   constexpr int NT = NW * 64;
   constexpr int PAD = 16 / sizeof(TIn);
@@ -64,7 +68,7 @@ __global__ __launch_bounds__(D * 2) void la_chunk_state(const TIn* __restrict__ 
   __shared__ __attribute__((aligned(16))) TIn Vs[kSub * LD];
   __shared__ float tbl[kSub + 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
   const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
   const int hh = bh % H;
   const int64_t base = (int64_t)bh * N * D;
@@ -79,30 +83,38 @@ __global__ __launch_bounds__(D * 2) void la_chunk_state(const TIn* __restrict__ 
 #pragma unroll
   for (int kt = 0; kt < NRT; ++kt) U[kt] = zero16();
 
+  RowTile<TIn, D, NT> pk, pv;
+  pk.load(kb, t_begin, t_end, tid);
+  pv.load(vb, t_begin, t_end, tid);
   for (int t0 = t_begin; t0 < t_end; t0 += kSub) {
     const int n = min(kSub, t_end - t0);
-    stage_rows<TIn, D, LD, kSub, NT>(Ks, kb, t0, t_end, tid);
-    stage_rows<TIn, D, LD, kSub, NT>(Vs, vb, t0, t_end, tid);
+    pk.template store<LD>(Ks, tid);
+    pv.template store<LD>(Vs, tid);
     __syncthreads();
+    if (t0 + kSub < t_end) {
+      pk.load(kb, t0 + kSub, t_end, tid);
+      pv.load(vb, t0 + kSub, t_end, tid);
+    }
     const float dn = tbl[n];
 #pragma unroll
     for (int kt = 0; kt < NRT; ++kt) U[kt] *= dn;
-#pragma unroll 2
+#pragma unroll
     for (int kk = 0; kk < kSub / M::KW; ++kk) {
-      // B operand: decayed values lam^(n-1-s) v[s][32w + l32], s = KW*kk + EPL*hf + i.
+      // B operand: lam^(n-1-s) v[s][32w + n'] for s = KW*kk + EPL*hf + i.
+      const op_t vraw = M::ld_tr_nat(Vs, LD, M::KW * kk, 32 * w, lane);
       float x[M::EPL];
 #pragma unroll
       for (int i = 0; i < M::EPL; ++i) {
         const int s = M::KW * kk + M::EPL * hf + i;
-        const float dec = (s < n) ? tbl[n - 1 - s] : 0.0f;
-        x[i] = M::to_f32(Vs[s * LD + 32 * w + l32]) * dec;
+        const float dec = (s < n) ? tbl[max(n - 1 - s, 0)] : 0.0f;
+        x[i] = M::to_f32(M::elem(vraw, i)) * dec;
       }
-      typename M::op_t bhi, blo;
+      op_t bhi, blo;
       M::split(x, bhi, blo);
 #pragma unroll
       for (int kt = 0; kt < NRT; ++kt) {
-        // A operand: K^T[dk = 32kt + l32][s]
-        const typename M::op_t a = M::ld_col_nat(Ks + (M::KW * kk) * LD + 32 * kt + l32, LD, hf);
+        // A operand: K^T[dk = 32kt + n'][s]
+        const op_t a = M::ld_tr_nat(Ks, LD, M::KW * kk, 32 * kt, lane);
         U[kt] = M::mma(a, bhi, U[kt]);
         if (M::kSplit) U[kt] = M::mma(a, blo, U[kt]);
       }
@@ -114,7 +126,7 @@ __global__ __launch_bounds__(D * 2) void la_chunk_state(const TIn* __restrict__ 
 #pragma unroll
   for (int kt = 0; kt < NRT; ++kt)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) dst[(32 * kt + crow(j, hf)) * D + 32 * w + l32] = U[kt][j];
+    for (int j = 0; j < 16; ++j) dst[(32 * kt + crow(j, hf)) * D + 32 * w + (lane & 31)] = U[kt][j];
 }
 
 // ---------------------------------------------------------------------------
@@ -158,9 +170,18 @@ __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ d
 // Pass C.  One workgroup per (bh, chunk); D/32 waves.  Wave w owns columns
 // [32w, 32w + 32) of the fp32 state S (NRT accumulator tiles) and of the
 // output.  LDS: Q of the current sub-tile, K and V of every sub-tile of the
-// current block (BLK/64 slots), the decay table.
+// current block (BLK/64 slots), the decay table.  The next sub-tile's Q, K, V
+// are loaded into registers while the current one is computed.
+//
+// Per 64-row sub-tile (row r, position p = 64*jb + r in its block):
+//   inter  acc = diag(lam^(p+1)) Q S_b                    (S_b as bf16 hi + lo)
+//   intra  acc += (P^T)^T V, P^T = K Q^T masked by lam^(p-s) for s <= p
+//   update S += sum_s lam^(BLK-1-s) k_s^T v_s               (decayed v as hi + lo)
+// with S pre-decayed by lam^BLK once per block.  With BLK = 64 the state is
+// split into hi/lo on the fly; with longer blocks the block-start split is
+// kept in registers for the block's later sub-tiles.
 template <typename TIn, typename TOut, int D, int BLK>
-__global__ __launch_bounds__(D * 2) void la_chunk_output(const TIn* __restrict__ q, const TIn* __restrict__ k,
+__global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) void la_chunk_output(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                                          const TIn* __restrict__ v, TOut* __restrict__ o,
                                                          const float* __restrict__ tbl_all,
                                                          const float* __restrict__ sstart, int H, int N, int L,
@@ -174,6 +195,7 @@ __global__ __launch_bounds__(D * 2) void la_chunk_output(const TIn* __restrict__
   constexpr int NRT = D / 32;
   constexpr int NS = BLK / kSub;
   constexpr int G = 32 / M::KW;  // operand groups per 32-row accumulator tile
+  constexpr int SNAP = (NS > 1) ? NRT : 1;
   __shared__ __attribute__((aligned(16))) TIn Qs[kSub * LD];
   __shared__ __attribute__((aligned(16))) TIn Ks[NS * kSub * LD];
   __shared__ __attribute__((aligned(16))) TIn Vs[NS * kSub * LD];
@@ -201,20 +223,40 @@ __global__ __launch_bounds__(D * 2) void la_chunk_output(const TIn* __restrict__
 #pragma unroll
       for (int j = 0; j < 16; ++j) S[kt][j] = src[(32 * kt + crow(j, hf)) * D + col];
   }
-  op_t Shi[NRT][G], Slo[NRT][G];
+  op_t Shi[SNAP][G], Slo[SNAP][G];
+
+  constexpr bool kPrefetch = !(BLK == 64 && sizeof(TIn) == 2);
+  RowTile<TIn, D, NT> pq, pk, pv;
+  if (kPrefetch) {
+    pq.load(qb, t_begin, t_end, tid);
+    pk.load(kb, t_begin, t_end, tid);
+    pv.load(vb, t_begin, t_end, tid);
+  }
 
   int jb = 0;  // sub-tile index within the current block
   for (int t0 = t_begin; t0 < t_end; t0 += kSub, jb = (jb + 1 == NS) ? 0 : jb + 1) {
     TIn* Kj = Ks + jb * kSub * LD;
     TIn* Vj = Vs + jb * kSub * LD;
-    stage_rows<TIn, D, LD, kSub, NT>(Qs, qb, t0, t_end, tid);
-    stage_rows<TIn, D, LD, kSub, NT>(Kj, kb, t0, t_end, tid);
-    stage_rows<TIn, D, LD, kSub, NT>(Vj, vb, t0, t_end, tid);
+    if (!kPrefetch) {
+      pq.load(qb, t0, t_end, tid);
+      pk.load(kb, t0, t_end, tid);
+      pv.load(vb, t0, t_end, tid);
+    }
+    pq.template store<LD>(Qs, tid);
+    pk.template store<LD>(Kj, tid);
+    pv.template store<LD>(Vj, tid);
     __syncthreads();
+    if (kPrefetch && t0 + kSub < t_end) {
+      pq.load(qb, t0 + kSub, t_end, tid);
+      pk.load(kb, t0 + kSub, t_end, tid);
+      pv.load(vb, t0 + kSub, t_end, tid);
+    }
 
-    if (jb == 0) {
-      // Block start: snapshot S_b as MFMA B operands, then pre-decay S by lam^BLK.
-      const float dblk = tbl[BLK];
+    // Inter-block: acc[rt] = diag(lam^(p+1)) Q S_b.
+    f32x16 acc[2];
+    acc[0] = zero16();
+    acc[1] = zero16();
+    if constexpr (NS == 1) {
 #pragma unroll
       for (int kt = 0; kt < NRT; ++kt) {
 #pragma unroll
@@ -222,33 +264,54 @@ __global__ __launch_bounds__(D * 2) void la_chunk_output(const TIn* __restrict__
           float x[M::EPL];
 #pragma unroll
           for (int i = 0; i < M::EPL; ++i) x[i] = S[kt][g * M::EPL + i];
-          M::split(x, Shi[kt][g], Slo[kt][g]);
+          op_t hi, lo;
+          M::split(x, hi, lo);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            const op_t a = M::ld_cperm(Qs + (32 * rt + l32) * LD + 32 * kt, g, hf);
+            acc[rt] = M::mma(a, hi, acc[rt]);
+            if (M::kSplit) acc[rt] = M::mma(a, lo, acc[rt]);
+          }
         }
-        S[kt] *= dblk;
+        S[kt] *= tbl[BLK];
+      }
+    } else {
+      if (jb == 0) {
+        // Block start: keep S_b as MFMA B operands, then pre-decay S by lam^BLK.
+        const float dblk = tbl[BLK];
+#pragma unroll
+        for (int kt = 0; kt < SNAP; ++kt) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float x[M::EPL];
+#pragma unroll
+            for (int i = 0; i < M::EPL; ++i) x[i] = S[kt][g * M::EPL + i];
+            M::split(x, Shi[kt][g], Slo[kt][g]);
+          }
+          S[kt] *= dblk;
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const TIn* qrow = Qs + (32 * rt + l32) * LD;
+#pragma unroll
+        for (int kt = 0; kt < SNAP; ++kt) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const op_t a = M::ld_cperm(qrow + 32 * kt, g, hf);
+            acc[rt] = M::mma(a, Shi[kt][g], acc[rt]);
+            if (M::kSplit) acc[rt] = M::mma(a, Slo[kt][g], acc[rt]);
+          }
+        }
       }
     }
-
-    // Inter-block: acc[rt] = diag(lam^(r+1)) Q S_b, r = position in the block.
-    f32x16 acc[2];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      acc[rt] = zero16();
-      const TIn* qrow = Qs + (32 * rt + l32) * LD;
-#pragma unroll
-      for (int kt = 0; kt < NRT; ++kt) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const op_t a = M::ld_cperm(qrow + 32 * kt, g, hf);
-          acc[rt] = M::mma(a, Shi[kt][g], acc[rt]);
-          if (M::kSplit) acc[rt] = M::mma(a, Slo[kt][g], acc[rt]);
-        }
-      }
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[rt][j] *= tbl[kSub * jb + 32 * rt + crow(j, hf) + 1];
-    }
 
     // Intra-block: for every earlier-or-current sub-tile jk of the block,
-    // P^T = K_jk Q^T (32x32 tiles), masked and decayed by lam^(r-s), then acc += P V_jk.
+    // P^T = K_jk Q^T (32x32 tiles), masked and decayed by lam^(p-s), then acc += P V_jk.
     for (int jk = 0; jk <= jb; ++jk) {
       const TIn* Kk = Ks + jk * kSub * LD;
       const TIn* Vk = Vs + jk * kSub * LD;
@@ -279,8 +342,8 @@ __global__ __launch_bounds__(D * 2) void la_chunk_output(const TIn* __restrict__
 #pragma unroll
             for (int i = 0; i < M::EPL; ++i) x[i] = p[g * M::EPL + i];
             const op_t pa = M::cvt(x);
-            const op_t vbop = M::ld_col_cperm(Vk + (32 * st) * LD + col, LD, g, hf);
-            acc[rt] = M::mma(pa, vbop, acc[rt]);
+            const op_t vop = M::ld_tr_cperm(Vk, LD, 32 * st, g, 32 * w, lane);
+            acc[rt] = M::mma(pa, vop, acc[rt]);
           }
         }
       }
@@ -288,19 +351,20 @@ __global__ __launch_bounds__(D * 2) void la_chunk_output(const TIn* __restrict__
 
     // State update: S += sum_s lam^(BLK-1-s) k_s^T v_s over this sub-tile
     // (S was pre-decayed by lam^BLK at the block start).
-#pragma unroll 2
+#pragma unroll
     for (int kk = 0; kk < kSub / M::KW; ++kk) {
+      const op_t vraw = M::ld_tr_nat(Vj, LD, M::KW * kk, 32 * w, lane);
       float x[M::EPL];
 #pragma unroll
       for (int i = 0; i < M::EPL; ++i) {
         const int s = M::KW * kk + M::EPL * hf + i;
-        x[i] = M::to_f32(Vj[s * LD + col]) * tbl[BLK - 1 - (kSub * jb + s)];
+        x[i] = M::to_f32(M::elem(vraw, i)) * tbl[BLK - 1 - (kSub * jb + s)];
       }
       op_t bhi, blo;
       M::split(x, bhi, blo);
 #pragma unroll
       for (int kt = 0; kt < NRT; ++kt) {
-        const op_t a = M::ld_col_nat(Kj + (M::KW * kk) * LD + 32 * kt + l32, LD, hf);
+        const op_t a = M::ld_tr_nat(Kj, LD, M::KW * kk, 32 * kt, lane);
         S[kt] = M::mma(a, bhi, S[kt]);
         if (M::kSplit) S[kt] = M::mma(a, blo, S[kt]);
       }
