@@ -208,6 +208,9 @@ def main():
     ap.add_argument("--no-decode", dest="decode", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-tokens", type=int, default=131072)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB (a known-size "
+                         "reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -219,6 +222,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: %d bytes read, %d bytes written" % (n, n))
+        del src, dst
     prefill, sample = bench_prefill(args, dev)
     dec = bench_decode(args, dev) if args.decode else None
     cpu = cpu_baseline(sample, args) if args.cpu_baseline else None

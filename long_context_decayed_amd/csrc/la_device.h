@@ -36,6 +36,14 @@ __device__ __forceinline__ double pow_int(double x, int e) {
 template <typename T>
 struct Mfma;
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// RNE of two floats into one dword of two bf16 (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
@@ -83,19 +91,23 @@ struct Mfma<bf16> {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
   static __device__ __forceinline__ op_t cvt(const float* x) {
-    op_t r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = (bf16)x[i];
-    return r;
+    return __builtin_bit_cast(op_t, uint4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                          pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])});
   }
-  // x ~= hi + lo with hi = RNE(x), lo = RNE(x - hi); x - hi is exact in fp32.
+  // x ~= hi + lo: hi = x truncated to bf16 (its top 16 bits), lo = RNE(x - hi).
+  // x - hi is exact in fp32 and |x - hi| < 2^-7 |x|, so |x - hi - lo| < 2^-16 |x|.
   static __device__ __forceinline__ void split(const float* x, op_t& hi, op_t& lo) {
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bf16 h = (bf16)x[i];
-      hi[i] = h;
-      lo[i] = (bf16)(x[i] - (float)h);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t b0 = __float_as_uint(x[2 * i]), b1 = __float_as_uint(x[2 * i + 1]);
+      const float r0 = x[2 * i] - __uint_as_float(b0 & 0xffff0000u);
+      const float r1 = x[2 * i + 1] - __uint_as_float(b1 & 0xffff0000u);
+      h[i] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // {hi16(b0), hi16(b1)}
+      l[i] = pack_bf16x2(r0, r1);
     }
+    hi = __builtin_bit_cast(op_t, uint4{h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(op_t, uint4{l[0], l[1], l[2], l[3]});
   }
   static __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
   static __device__ __forceinline__ bf16 elem(op_t x, int i) { return x[i]; }
@@ -155,15 +167,23 @@ struct RowTile {
   uint4 r[PER];
 
   __device__ __forceinline__ void load(const T* __restrict__ src, int t0, int t_end, int tid) {
+    const T* base = src + (int64_t)t0 * D;
+    if (t0 + 64 <= t_end) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = tid + i * NT;
-      const int row = idx / CPR, cc = idx % CPR;
-      const int t = t0 + row;
-      if (t < t_end)
-        r[i] = *reinterpret_cast<const uint4*>(src + (int64_t)t * D + cc * VEC);
-      else
-        r[i] = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = 0; i < PER; ++i) {
+        const int idx = tid + i * NT;
+        r[i] = *reinterpret_cast<const uint4*>(base + (idx / CPR) * D + (idx % CPR) * VEC);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int idx = tid + i * NT;
+        const int row = idx / CPR;
+        if (t0 + row < t_end)
+          r[i] = *reinterpret_cast<const uint4*>(base + row * D + (idx % CPR) * VEC);
+        else
+          r[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
   }
   template <int LD>

@@ -383,6 +383,183 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 }
 
 // ---------------------------------------------------------------------------
+// Pass C, block = 64, bf16 inputs: the fast path.  Same arithmetic as
+// la_chunk_output with BLK = 64, organised to cut per-element VALU work:
+//   * the 3 masked, decayed score tiles P^T (32x32) of a sub-tile are each
+//     computed by one wave and shared through LDS as ready-made bf16 MFMA A
+//     operands (instead of every wave recomputing all three);
+//   * the mask/decay factors of the score tiles and the row factors
+//     lam^(r+1) of the inter term are per-lane tables built once in LDS;
+//   * the decays lam^(63-s) of the state update are a wave-uniform power
+//     times a per-half-wave power (no per-element lookups);
+//   * full sub-tiles store without per-element bounds checks.
+template <typename TOut, int D>
+__global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                              const bf16* __restrict__ v, TOut* __restrict__ o,
+                                                              const float* __restrict__ tbl_all,
+                                                              const float* __restrict__ sstart, int H, int N, int L,
+                                                              int nc, int tbl_stride) {
+  typedef Mfma<bf16> M;
+  typedef M::op_t op_t;
+  constexpr int NW = D / 32;
+  constexpr int NT = NW * 64;
+  constexpr int LD = D + 8;
+  constexpr int NRT = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16 Qs[kSub * LD];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kSub * LD];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[kSub * LD];
+  __shared__ __attribute__((aligned(16))) op_t Pbuf[3][2][64];     // score tiles as A operands
+  __shared__ __attribute__((aligned(16))) f32x4 dP[2][4][64];      // [diag/off][j/4][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 dRow[2][4][64];    // [rt][j/4][lane]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
+  const int hh = bh % H;
+  const int64_t base = (int64_t)bh * N * D;
+  const bf16* qb = q + base;
+  const bf16* kb = k + base;
+  const bf16* vb = v + base;
+  TOut* ob = o + base;
+  const int t_begin = c * L;
+  const int t_end = min(N, t_begin + L);
+  const int col = 32 * w + l32;
+  const float* tb = tbl_all + (int64_t)hh * tbl_stride;  // lam^e, e <= 64
+
+  // Per-lane decay tables.
+  for (int e = tid; e < 2 * 16 * 64; e += NT) {
+    const int t = e >> 10, j = (e >> 6) & 15, ln = e & 63;
+    const int dif = 32 * t + (ln & 31) - crow(j, ln >> 5);
+    dP[t][j >> 2][ln][j & 3] = dif >= 0 ? tb[dif] : 0.0f;
+    const int rt = t;
+    dRow[rt][j >> 2][ln][j & 3] = tb[32 * rt + crow(j, ln >> 5) + 1];
+  }
+  const float lane_f = tb[8 * (1 - hf)];  // lam^(8(1-hf)): the half-wave part of lam^(63-s)
+  const float d64 = tb[64];
+
+  f32x16 S[NRT];
+  {
+    const float* src = sstart + ((int64_t)bh * nc + c) * D * D;
+#pragma unroll
+    for (int kt = 0; kt < NRT; ++kt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) S[kt][j] = src[(32 * kt + crow(j, hf)) * D + col];
+  }
+
+  RowTile<bf16, D, NT> pq, pk, pv;
+  for (int t0 = t_begin; t0 < t_end; t0 += kSub) {
+    pq.load(qb, t0, t_end, tid);
+    pk.load(kb, t0, t_end, tid);
+    pv.load(vb, t0, t_end, tid);
+    pq.template store<LD>(Qs, tid);
+    pk.template store<LD>(Ks, tid);
+    pv.template store<LD>(Vs, tid);
+    __syncthreads();
+
+    // Score tiles: tile i = (st, rt) in {(0,0), (0,1), (1,1)}, computed by wave i % NW.
+    for (int ti = w; ti < 3; ti += NW) {
+      const int st = ti == 2 ? 1 : 0, rt = ti == 0 ? 0 : 1;
+      f32x16 p = zero16();
+      const bf16* krow = Ks + (32 * st + l32) * LD + 8 * hf;
+      const bf16* qrow = Qs + (32 * rt + l32) * LD + 8 * hf;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) p = M::mma(M::ld_nat(krow + 16 * kk), M::ld_nat(qrow + 16 * kk), p);
+      const int t = rt - st;
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const f32x4 f = dP[t][jq][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[4 * jq + e] *= f[e];
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = p[8 * g + i];
+        Pbuf[ti][g][lane] = M::cvt(x);
+      }
+    }
+
+    // Inter-block term with S split into bf16 hi + lo on the fly; then S *= lam^64.
+    f32x16 acc[2];
+    acc[0] = zero16();
+    acc[1] = zero16();
+#pragma unroll
+    for (int kt = 0; kt < NRT; ++kt) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = S[kt][8 * g + i];
+        op_t hi, lo;
+        M::split(x, hi, lo);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const op_t a = M::ld_cperm(Qs + (32 * rt + l32) * LD + 32 * kt, g, hf);
+          acc[rt] = M::mma(a, hi, acc[rt]);
+          acc[rt] = M::mma(a, lo, acc[rt]);
+        }
+      }
+      S[kt] *= d64;
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const f32x4 f = dRow[rt][jq][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[rt][4 * jq + e] *= f[e];
+      }
+    __syncthreads();  // score tiles visible
+
+    // Intra-block term: acc[rt] += P V over the shared score tiles.
+#pragma unroll
+    for (int ti = 0; ti < 3; ++ti) {
+      const int st = ti == 2 ? 1 : 0, rt = ti == 0 ? 0 : 1;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const op_t vop = M::ld_tr_cperm(Vs, LD, 32 * st, g, 32 * w, lane);
+        acc[rt] = M::mma(Pbuf[ti][g][lane], vop, acc[rt]);
+      }
+    }
+
+    // State update: S += sum_s lam^(63-s) k_s^T v_s.
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const op_t vraw = M::ld_tr_nat(Vs, LD, 16 * kk, 32 * w, lane);
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * (tb[55 - 16 * kk - i] * lane_f);
+      op_t bhi, blo;
+      M::split(x, bhi, blo);
+#pragma unroll
+      for (int kt = 0; kt < NRT; ++kt) {
+        const op_t a = M::ld_tr_nat(Ks, LD, 16 * kk, 32 * kt, lane);
+        S[kt] = M::mma(a, bhi, S[kt]);
+        S[kt] = M::mma(a, blo, S[kt]);
+      }
+    }
+
+    // Store this sub-tile's rows.
+    TOut* orow = ob + (int64_t)t0 * D + col;
+    if (t0 + kSub <= t_end) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) orow[(32 * rt + crow(j, hf)) * D] = from_f32<TOut>(acc[rt][j]);
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = 32 * rt + crow(j, hf);
+          if (t0 + r < t_end) orow[r * D] = from_f32<TOut>(acc[rt][j]);
+        }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launchers.
 
 template <typename TIn, typename TOut, int D, int BLK>
@@ -402,9 +579,14 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     hipError_t e = hipEventRecord((hipEvent_t)a.evt_begin, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((la_chunk_output<TIn, TOut, D, BLK>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
-                     (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (TOut*)a.out, (const float*)a.tbl,
-                     (const float*)a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
+  if constexpr (BLK == 64 && sizeof(TIn) == 2)
+    hipLaunchKernelGGL((la_chunk_output64<TOut, D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, (const float*)a.tbl,
+                       (const float*)a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
+  else
+    hipLaunchKernelGGL((la_chunk_output<TIn, TOut, D, BLK>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (TOut*)a.out, (const float*)a.tbl,
+                       (const float*)a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
   if (a.evt_end) {
     hipError_t e = hipEventRecord((hipEvent_t)a.evt_end, st);
     if (e != hipSuccess) return e;
