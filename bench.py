@@ -38,7 +38,6 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096
 BYTES_PER_HT = 1024            # q, k, v read + o written, bf16, d = 128
 FLOP_PER_HT = 131072           # causal half of 2*b*d (b = 256) + 4*d^2 (inter + state update)
 TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "chunk_output_traffic.json")
-PREFILL_SRC = os.path.join(_ROOT, "long_context_decayed_amd", "csrc", "la_prefill.hip")
 
 
 def log(*a):
@@ -56,7 +55,7 @@ def _hip():
 
 def _src_hash():
     h = hashlib.sha256()
-    for name in ("la_prefill.hip", "la_device.h"):
+    for name in ("la_output.hip", "la_device.h"):
         h.update(open(os.path.join(_ROOT, "long_context_decayed_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 

@@ -13,6 +13,17 @@ namespace {
 constexpr int64_t kMaxTokens = int64_t(1) << 24;  // keeps N * d < 2^31 for per-head offsets
 constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 
+// dtype / head-dim / block combinations the kernels are built for.  fp32
+// tiles are twice as large, so fp32 with d = 128 is limited to block 64 by
+// the 160 KiB of LDS per CU.
+bool prefill_supported(int in_dtype, int out_dtype, int64_t d, int64_t block) {
+  if (d != 64 && d != 128) return false;
+  if (block != 64 && block != 128 && block != 256) return false;
+  if (in_dtype == LA_DTYPE_BF16) return out_dtype == LA_DTYPE_BF16 || out_dtype == LA_DTYPE_F32;
+  if (in_dtype == LA_DTYPE_F32 && out_dtype == LA_DTYPE_F32) return d == 64 || block == 64;
+  return false;
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
@@ -77,7 +88,7 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* d
       !aligned(kv_in, 16) || !aligned(kv_out, 16))
     return LA_ERR_INVALID;
   if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
-  if (!la::prefill_supported(in_dtype, out_dtype, d, block)) return LA_ERR_UNSUPPORTED;
+  if (!prefill_supported(in_dtype, out_dtype, d, block)) return LA_ERR_UNSUPPORTED;
   if (N > kMaxTokens) return LA_ERR_UNSUPPORTED;
   int rc = resolve_chunk(B, H, N, block, chunk, L);
   if (rc != LA_OK) return rc;
@@ -138,7 +149,8 @@ int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const flo
   a.states = (float*)((char*)ws + tbl_bytes);
   a.evt_begin = evt_begin;
   a.evt_end = evt_end;
-  hipError_t e = la::launch_prefill(a, st);
+  hipError_t e = la::launch_state_passes(a, st);
+  if (e == hipSuccess) e = la::launch_output_pass(a, st);
   if (!workspace) {
     hipError_t f = hipFreeAsync(ws, st);
     if (e == hipSuccess) e = f;

@@ -8,6 +8,8 @@
 
 namespace la {
 
+constexpr int kSub = 64;  // token rows per LDS stage of the prefill kernels
+
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -184,6 +186,24 @@ struct RowTile {
         else
           r[i] = make_uint4(0u, 0u, 0u, 0u);
       }
+    }
+  }
+  // Store with 8-byte writes into a tile whose row stride is an odd number
+  // of 8-byte units: lane c of a row writes the even or the odd half of its
+  // 16 bytes first depending on bit 3 of c, so the 16 lanes of each write
+  // instruction cover 16 distinct half-rows of banks.
+  template <int LD>
+  __device__ __forceinline__ void store_halves(T* __restrict__ dst, int tid) const {
+    static_assert((LD * sizeof(T)) % 8 == 0, "8-byte aligned rows");
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NT;
+      const int row = idx / CPR, cc = idx % CPR;
+      const bool odd_first = (cc >> 3) & 1;
+      const uint2 lo = make_uint2(r[i].x, r[i].y), hi = make_uint2(r[i].z, r[i].w);
+      T* p = dst + row * LD + cc * VEC;
+      *reinterpret_cast<uint2*>(p + (odd_first ? VEC / 2 : 0)) = odd_first ? hi : lo;
+      *reinterpret_cast<uint2*>(p + (odd_first ? 0 : VEC / 2)) = odd_first ? lo : hi;
     }
   }
   template <int LD>

@@ -26,8 +26,10 @@ struct PrefillArgs {
   void* evt_end;
 };
 
-bool prefill_supported(int in_dtype, int out_dtype, int64_t d, int64_t block);
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+// Passes A and B (decay table, chunk aggregates, chunk scan): la_state.hip.
+hipError_t launch_state_passes(const PrefillArgs& a, hipStream_t st);
+// Pass C (outputs), with the optional timing events around it: la_output.hip.
+hipError_t launch_output_pass(const PrefillArgs& a, hipStream_t st);
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* decay, void* out,
                          const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t d, hipStream_t st);

@@ -1,0 +1,178 @@
+// Chunk-parallel state passes of the gfx950 lightning-attention prefill:
+// the decay-power table, pass A (per-chunk aggregates, MFMA) and pass B (the
+// scan over chunks).  The blockwise scheme is described in la_output.hip.
+//
+// The MiniMax-M1 fact sheet (archdb), "linear / SSM layer configuration"
+// field: linear attention with a fixed per-head exponential decay and a d x d
+// (128 x 128) state per head.  Per (batch, head), with lam = decay[h]:
+//     S_t = lam S_{t-1} + k_t^T v_t,   o_t = q_t S_t.
+// A chunk c of L_c tokens hands on S_end = lam^(L_c) S_start + U_c with
+// U_c = sum_s lam^(L_c-1-s) k_s^T v_s, so the chunk start states follow from
+// the aggregates by a short serial scan.
+
+#include <hip/hip_runtime.h>
+
+#include "la_device.h"
+#include "la_kernels.h"
+
+namespace la {
+
+// ---------------------------------------------------------------------------
+// Decay-power table: tbl[h][e] = lam_h^e, e in [0, stride), computed in double
+// and rounded once to float.
+__global__ void la_decay_table(const float* __restrict__ decay, float* __restrict__ tbl, int stride) {
+  const int h = blockIdx.x;
+  const double lam = (double)decay[h];
+  for (int e = threadIdx.x; e < stride; e += blockDim.x) tbl[(int64_t)h * stride + e] = (float)pow_int(lam, e);
+}
+
+// ---------------------------------------------------------------------------
+// Pass A.  One workgroup per (bh, chunk); D/32 waves, wave w owns columns
+// [32w, 32w + 32) of the chunk aggregate U (fp32 accumulators).  For each
+// sub-tile of n valid tokens: U = lam^n U + sum_{s<n} lam^(n-1-s) k_s^T v_s.
+// Operands with the token index along the contraction are read from the
+// row-major LDS tiles with transpose reads.  For full sub-tiles the decay
+// lam^(63-s) of token s = 16kk + 8h + i is the wave-uniform power
+// lam^(55-16kk-i) times the per-half-wave power lam^(8(1-h)).
+template <typename TIn, int D>
+__global__ __launch_bounds__(D * 2, sizeof(TIn) == 2 ? 3 : 1) void la_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v,
+                                                           const float* __restrict__ tbl_all,
+                                                           float* __restrict__ ws, int H, int N, int L, int nc,
+                                                           int tbl_stride) {
+  typedef Mfma<TIn> M;
+  typedef typename M::op_t op_t;
+  constexpr int NW = D / 32;
+  constexpr int NT = NW * 64;
+  // Row stride: 32 bytes past a multiple of 128 (bf16), so the 16 lanes of a
+  // transpose read (4 rows x 32 contiguous bytes) and the 8 lanes of a 16-byte
+  // row store each touch 32 distinct banks.
+  constexpr int PAD = sizeof(TIn) == 2 ? 16 : 4;
+  constexpr int LD = D + PAD;
+  constexpr int NRT = D / 32;
+  __shared__ __attribute__((aligned(16))) TIn Ks[kSub * LD];
+  __shared__ __attribute__((aligned(16))) TIn Vs[kSub * LD];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
+  const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
+  const int hh = bh % H;
+  const int64_t base = (int64_t)bh * N * D;
+  const TIn* kb = k + base;
+  const TIn* vb = v + base;
+  const int t_begin = c * L;
+  const int t_end = min(N, t_begin + L);
+  const float* tb = tbl_all + (int64_t)hh * tbl_stride;  // lam^e, e <= 64
+  const float lane_f = tb[8 * (1 - hf)];
+
+  f32x16 U[NRT];
+#pragma unroll
+  for (int kt = 0; kt < NRT; ++kt) U[kt] = zero16();
+
+  RowTile<TIn, D, NT> pk, pv;
+  pk.load(kb, t_begin, t_end, tid);
+  pv.load(vb, t_begin, t_end, tid);
+  for (int t0 = t_begin; t0 < t_end; t0 += kSub) {
+    const int n = min(kSub, t_end - t0);
+    pk.template store<LD>(Ks, tid);
+    pv.template store<LD>(Vs, tid);
+    __syncthreads();
+    if (t0 + kSub < t_end) {  // next sub-tile's loads overlap this one's MFMAs
+      pk.load(kb, t0 + kSub, t_end, tid);
+      pv.load(vb, t0 + kSub, t_end, tid);
+    }
+    const float dn = tb[n];
+#pragma unroll
+    for (int kt = 0; kt < NRT; ++kt) U[kt] *= dn;
+    const bool full = n == kSub;
+#pragma unroll
+    for (int kk = 0; kk < kSub / M::KW; ++kk) {
+      const op_t vraw = M::ld_tr_nat(Vs, LD, M::KW * kk, 32 * w, lane);
+      float x[M::EPL];
+#pragma unroll
+      for (int i = 0; i < M::EPL; ++i) {
+        float dec;
+        if (M::EPL == 8 && full) {
+          dec = tb[55 - 16 * kk - i] * lane_f;
+        } else {
+          const int s = M::KW * kk + M::EPL * hf + i;
+          dec = (s < n) ? tb[max(n - 1 - s, 0)] : 0.0f;
+        }
+        x[i] = M::to_f32(M::elem(vraw, i)) * dec;
+      }
+      op_t bhi, blo;
+      M::split(x, bhi, blo);
+#pragma unroll
+      for (int kt = 0; kt < NRT; ++kt) {
+        const op_t a = M::ld_tr_nat(Ks, LD, M::KW * kk, 32 * kt, lane);
+        U[kt] = M::mma(a, bhi, U[kt]);
+        if (M::kSplit) U[kt] = M::mma(a, blo, U[kt]);
+      }
+    }
+    __syncthreads();
+  }
+
+  float* dst = ws + ((int64_t)bh * nc + c) * D * D + 32 * w + (lane & 31);
+#pragma unroll
+  for (int kt = 0; kt < NRT; ++kt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dst[(32 * kt + crow(j, hf)) * D] = U[kt][j];
+}
+
+// ---------------------------------------------------------------------------
+// Pass B.  One thread per 4 consecutive state elements of one (bh); serial
+// over chunks.  ws holds U_c on entry and Sstart_c on exit.
+__global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ decay, float* __restrict__ ws,
+                                                     const float* __restrict__ kv_in, float* __restrict__ kv_out,
+                                                     int BH, int H, int N, int L, int nc, int D) {
+  const int per = D * D / 4;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)BH * per) return;
+  const int bh = (int)(gid / per), e4 = (int)(gid - (int64_t)bh * per);
+  const double lam = (double)decay[bh % H];
+  const float dl = (float)pow_int(lam, L);
+  const float dlast = (float)pow_int(lam, N - (nc - 1) * L);
+  f32x4 S = {0.f, 0.f, 0.f, 0.f};
+  if (kv_in) S = reinterpret_cast<const f32x4*>(kv_in)[(int64_t)bh * per + e4];
+  f32x4* U = reinterpret_cast<f32x4*>(ws) + (int64_t)bh * nc * per + e4;
+  int c = 0;
+  for (; c + 4 <= nc; c += 4) {
+    f32x4 u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = U[(int64_t)(c + i) * per];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      U[(int64_t)(c + i) * per] = S;
+      const float f = (c + i == nc - 1) ? dlast : dl;
+      S = f * S + u[i];
+    }
+  }
+  for (; c < nc; ++c) {
+    const f32x4 u = U[(int64_t)c * per];
+    U[(int64_t)c * per] = S;
+    const float f = (c == nc - 1) ? dlast : dl;
+    S = f * S + u;
+  }
+  if (kv_out) reinterpret_cast<f32x4*>(kv_out)[(int64_t)bh * per + e4] = S;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launcher: table, pass A, pass B on `st`.
+
+template <typename TIn, int D>
+static hipError_t launch_state_t(const PrefillArgs& a, hipStream_t st) {
+  const int BH = (int)(a.B * a.H);
+  const int nc = a.nc;
+  hipLaunchKernelGGL(la_decay_table, dim3((unsigned)a.H), dim3(256), 0, st, a.decay, a.tbl, a.tbl_stride);
+  hipLaunchKernelGGL((la_chunk_state<TIn, D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st, (const TIn*)a.k,
+                     (const TIn*)a.v, (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
+  const int64_t threads = (int64_t)BH * D * D / 4;
+  hipLaunchKernelGGL(la_chunk_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a.decay, a.states,
+                     a.kv_in, a.kv_out, BH, (int)a.H, (int)a.N, (int)a.L, nc, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_passes(const PrefillArgs& a, hipStream_t st) {
+  if (a.in_dtype == kBF16) return a.d == 128 ? launch_state_t<bf16, 128>(a, st) : launch_state_t<bf16, 64>(a, st);
+  return a.d == 128 ? launch_state_t<float, 128>(a, st) : launch_state_t<float, 64>(a, st);
+}
+
+}  // namespace la
