@@ -92,6 +92,29 @@ struct Mfma<bf16> {
     const bf16x4 lo = ds_tr4(p), hi = ds_tr4(p + 8 * ld);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
+  // Transpose reads from an unpadded D-column tile swizzled as in
+  // RowTile::store_swz (chunk c of row r stored at chunk c ^ 2(r & 3)).  The
+  // 16 lanes of a read touch 4 rows r0..r0+3 (r0 % 4 == 0) x 2 adjacent
+  // chunks; the swizzle sends them to 8 distinct bank groups.
+  template <int D>
+  static __device__ __forceinline__ const bf16* tr_swz_addr(const bf16* X, int row, int col, int j) {
+    return X + row * D + ((((col >> 3) ^ (2 * j)) << 3) | (col & 7));
+  }
+  template <int D>
+  static __device__ __forceinline__ op_t ld_tr_nat_swz(const bf16* X, int row0, int col0, int lane) {
+    const int h = lane >> 5, j = (lane & 15) >> 2;
+    const bf16* p = tr_swz_addr<D>(X, row0 + 8 * h + j, col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3), j);
+    const bf16x4 lo = ds_tr4(p), hi = ds_tr4(p + 4 * D);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  template <int D>
+  static __device__ __forceinline__ op_t ld_tr_cperm_swz(const bf16* X, int row0, int g, int col0, int lane) {
+    const int h = lane >> 5, j = (lane & 15) >> 2;
+    const bf16* p =
+        tr_swz_addr<D>(X, row0 + 16 * g + 4 * h + j, col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3), j);
+    const bf16x4 lo = ds_tr4(p), hi = ds_tr4(p + 8 * D);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
   static __device__ __forceinline__ op_t cvt(const float* x) {
     return __builtin_bit_cast(op_t, uint4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
                                           pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])});
@@ -204,6 +227,18 @@ struct RowTile {
       T* p = dst + row * LD + cc * VEC;
       *reinterpret_cast<uint2*>(p + (odd_first ? VEC / 2 : 0)) = odd_first ? hi : lo;
       *reinterpret_cast<uint2*>(p + (odd_first ? 0 : VEC / 2)) = odd_first ? lo : hi;
+    }
+  }
+  // Store into an unpadded tile (row stride D) whose 16-byte chunks are
+  // XOR-swizzled by 2 * (row % 4): chunk c of row r lands at chunk
+  // c ^ (2 * (r & 3)).  8 lanes writing 8 aligned chunks of a row still cover
+  // 8 distinct bank groups.
+  __device__ __forceinline__ void store_swz(T* __restrict__ dst, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NT;
+      const int row = idx / CPR, cc = idx % CPR;
+      *reinterpret_cast<uint4*>(dst + row * D + ((cc ^ (2 * (row & 3))) * VEC)) = r[i];
     }
   }
   template <int LD>

@@ -23,10 +23,11 @@
 //
 // Precision recipe (bf16 inputs): products of two bf16 inputs are exact in the
 // fp32 MFMA accumulator.  Quantities formed in fp32 that feed an MFMA are
-// rounded: the masked, decayed scores P (one bf16), the state S used in q S
-// and the decayed values lam^(..) v used in the state update (both as a bf16
-// hi + lo pair, ~16 significant bits).  Accumulation is fp32 throughout and
-// the state stays fp32.
+// rounded: the state S used in q S and the decayed values lam^(..) v used in
+// the state update go in as a bf16 hi + lo pair (~16 significant bits); the
+// masked, decayed scores P go in as one bf16 with block 64 and as a hi + lo
+// pair with longer blocks (their rounding error grows with the window).
+// Accumulation is fp32 throughout and the state stays fp32.
 
 #include <hip/hip_runtime.h>
 
@@ -205,14 +206,18 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
             const int dif = rdiff - crow(j, hf);
             p[j] = (dif >= 0) ? p[j] * tbl[dif < 0 ? 0 : dif] : 0.0f;
           }
+          // Scores are fed as bf16 hi + lo: over windows longer than 64
+          // tokens a single bf16 rounding of P is the dominant error.
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             float x[M::EPL];
 #pragma unroll
             for (int i = 0; i < M::EPL; ++i) x[i] = p[g * M::EPL + i];
-            const op_t pa = M::cvt(x);
+            op_t pa, pl;
+            M::split(x, pa, pl);
             const op_t vop = M::ld_tr_cperm(Vk, LD, 32 * st, g, 32 * w, lane);
             acc[rt] = M::mma(pa, vop, acc[rt]);
+            if (M::kSplit) acc[rt] = M::mma(pl, vop, acc[rt]);
           }
         }
       }
@@ -254,39 +259,39 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 // ---------------------------------------------------------------------------
 // Pass C, block = 64, bf16 inputs: the fast path.  Same arithmetic as
 // la_chunk_output with BLK = 64, organised around the MI355X limits that
-// bind it (LDS bandwidth and VALU issue, next to HBM):
+// bind it (LDS capacity and bandwidth and VALU issue, next to HBM):
 //   * the score tiles P^T = K Q^T contract over the key dimension in the row
 //     order of the state's accumulator tiles, so the Q operands loaded for
 //     the inter term q S are reused as the B operands of the score tiles;
 //   * each of the 3 causal 32x32 score tiles of a sub-tile is computed by one
-//     wave, masked, decayed and shared through LDS as bf16 MFMA A operands;
+//     wave, masked, decayed and shared through LDS as bf16 hi + lo MFMA A
+//     operands (P V then costs two MFMAs per step but keeps ~16 bits of P);
 //   * LDS tiles use per-reader layouts: Q and one copy of K have a row stride
 //     of an odd number of 8-byte units (16 rows x 8 bytes at one column hit
-//     16 distinct bank pairs), V and a second copy of K have a stride of 32
-//     bytes past a multiple of 128 (conflict-free transpose reads);
-//   * decay factors are per-lane powers times wave-uniform powers, except
-//     the masked diagonal score tile, whose factors come from an LDS table.
+//     16 distinct bank pairs); V and a second copy of K are unpadded with
+//     16-byte chunks XOR-swizzled by row (conflict-free transpose reads);
+//   * decay factors are per-lane powers times wave-uniform powers; the masked
+//     diagonal score tile uses lam^d = exp2(d log2 lam) for d > 0.
 // With two workgroups per CU the LDS footprint stays under 80 KiB.
 template <typename TOut, int D>
 __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                               const bf16* __restrict__ v, TOut* __restrict__ o,
                                                               const float* __restrict__ tbl_all,
+                                                              const float* __restrict__ decay,
                                                               const float* __restrict__ sstart, int H, int N, int L,
                                                               int nc, int tbl_stride) {
   typedef Mfma<bf16> M;
   typedef M::op_t op_t;
   constexpr int NW = D / 32;
   constexpr int NT = NW * 64;
-  constexpr int LDC = D + 4;   // odd number of 8-byte units per row
-  constexpr int LDT = D + 16;  // 32 bytes past a multiple of 128 per row
+  constexpr int LDC = D + 4;  // odd number of 8-byte units per row
   constexpr int NRT = D / 32;
   constexpr int MAXT = (3 + NW - 1) / NW;  // score tiles per wave
   __shared__ __attribute__((aligned(16))) bf16 Qs[kSub * LDC];
   __shared__ __attribute__((aligned(16))) bf16 Kc[kSub * LDC];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[kSub * LDT];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[kSub * LDT];
-  __shared__ __attribute__((aligned(16))) op_t Pbuf[3][2][64];  // score tiles as A operands
-  __shared__ __attribute__((aligned(16))) f32x4 dDiag[4][64];   // diagonal tile factors [j/4][lane]
+  __shared__ __attribute__((aligned(16))) bf16 Kt[kSub * D];  // swizzled
+  __shared__ __attribute__((aligned(16))) bf16 Vt[kSub * D];  // swizzled
+  __shared__ __attribute__((aligned(16))) op_t Pbuf[3][2][2][64];  // [tile][g][hi/lo][lane]
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -302,28 +307,23 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   const int col = 32 * w + l32;
   const float* tb = tbl_all + (int64_t)hh * tbl_stride;  // lam^e, e <= 64
 
-  // Diagonal score tile: lam^(r-s) for r >= s, else 0 (r = l32, s = crow(j, hf)).
-  for (int e = tid; e < 16 * 64; e += NT) {
-    const int j = e >> 6, ln = e & 63;
-    const int dif = (ln & 31) - crow(j, ln >> 5);
-    dDiag[j >> 2][ln][j & 3] = dif >= 0 ? tb[dif] : 0.0f;
-  }
   // Decay factors as per-lane powers times wave-uniform powers (exponents all
   // non-negative):
   //   update,  s = 16kk + 8h + i:      lam^(63-s) = lam^(48-16kk) * ul[i],   ul[i] = lam^(8(1-h)+7-i)
   //   inter,   p = 32rt + crow(j, h):  lam^(p+1)  = lam^(32rt+8jq) * rl[jj], rl[jj] = lam^(4h+jj+1)
   //   off-diagonal score tile (r = 32 + l, s = crow(j, h)):
   //            lam^(r-s) = lam^(24-8jq) * ol[jj],  ol[jj] = lam^(l+4-4h+4-jj)
-  // with j = 4jq + jj.
-  float ul[8], rl[4], ol[4];
+  // with j = 4jq + jj.  Diagonal tile (r = l, s = crow(j, h)): d = r - s,
+  // factor 1 at d = 0, exp2(d log2 lam) at d > 0, 0 (masked) at d < 0.
+  // ul and rl take one of two wave-uniform values per lane half, selected at
+  // each use (cheaper than keeping 12 more registers live across the loop).
+  float ol[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ul[i] = tb[8 * (1 - hf) + 7 - i];
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    rl[jj] = tb[4 * hf + jj + 1];
-    ol[jj] = tb[l32 + 8 - 4 * hf - jj];
-  }
+  for (int jj = 0; jj < 4; ++jj) ol[jj] = tb[l32 + 8 - 4 * hf - jj];
+  const bool h1 = hf != 0;
   const float d64 = tb[64];
+  const float log2lam = __builtin_amdgcn_logf(decay[hh]);  // -inf at lam = 0
+  const float dbase = (float)(l32 - 4 * hf);
 
   // Accumulator element (tile row 32a + crow(j, h), column col) sits at
   // (32a + 8(j>>2) + (j&3)) * D + lane_off from a wave-uniform base.
@@ -344,8 +344,8 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
     pv.load(vb, t0, t_end, tid);
     pq.template store_halves<LDC>(Qs, tid);
     pk.template store_halves<LDC>(Kc, tid);
-    pk.template store<LDT>(Kt, tid);
-    pv.template store<LDT>(Vt, tid);
+    pk.store_swz(Kt, tid);
+    pv.store_swz(Vt, tid);
     __syncthreads();
 
     // Inter term acc = Q S_b (S split into bf16 hi + lo on the fly) and this
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
       // (the register file is shared by two workgroups per CU).
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Mask, decay and publish the score tiles.
+    // Mask, decay and publish the score tiles as hi + lo operands.
 #pragma unroll
     for (int m = 0; m < MAXT; ++m) {
       const int ti = w + m * NW;
@@ -398,11 +398,15 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
             for (int jj = 0; jj < 4; ++jj) pt[m][4 * jq + jj] *= ol[jj] * u;
           }
         } else {
+          // Opaque copies: recomputing 16 factors here is cheaper than the
+          // compiler's choice of hoisting them out of the loop and spilling.
+          float db = dbase, lg = log2lam;
+          asm volatile("" : "+v"(db), "+v"(lg));
 #pragma unroll
-          for (int jq = 0; jq < 4; ++jq) {
-            const f32x4 f = dDiag[jq][lane];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pt[m][4 * jq + e] *= f[e];
+          for (int j = 0; j < 16; ++j) {
+            const float dd = db - (float)(8 * (j >> 2) + (j & 3));
+            const float f = dd > 0.0f ? __builtin_amdgcn_exp2f(dd * lg) : (dd == 0.0f ? 1.0f : 0.0f);
+            pt[m][j] *= f;
           }
         }
 #pragma unroll
@@ -410,7 +414,10 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
           float x[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) x[i] = pt[m][8 * g + i];
-          Pbuf[ti][g][lane] = M::cvt(x);
+          op_t hi, lo;
+          M::split(x, hi, lo);
+          Pbuf[ti][g][0][lane] = hi;
+          Pbuf[ti][g][1][lane] = lo;
         }
       }
     }
@@ -421,7 +428,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
       for (int jq = 0; jq < 4; ++jq) {
         const float u = tb[32 * rt + 8 * jq];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[rt][4 * jq + jj] *= rl[jj] * u;
+        for (int jj = 0; jj < 4; ++jj) acc[rt][4 * jq + jj] *= (h1 ? tb[jj + 5] : tb[jj + 1]) * u;
       }
     __syncthreads();  // score tiles visible
 
@@ -431,23 +438,24 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
       const int st = ti == 2 ? 1 : 0, rt = ti == 0 ? 0 : 1;
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const op_t vop = M::ld_tr_cperm(Vt, LDT, 32 * st, g, 32 * w, lane);
-        acc[rt] = M::mma(Pbuf[ti][g][lane], vop, acc[rt]);
+        const op_t vop = M::ld_tr_cperm_swz<D>(Vt, 32 * st, g, 32 * w, lane);
+        acc[rt] = M::mma(Pbuf[ti][g][0][lane], vop, acc[rt]);
+        acc[rt] = M::mma(Pbuf[ti][g][1][lane], vop, acc[rt]);
       }
     }
 
     // State update: S += sum_s lam^(63-s) k_s^T v_s.
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const op_t vraw = M::ld_tr_nat(Vt, LDT, 16 * kk, 32 * w, lane);
+      const op_t vraw = M::ld_tr_nat_swz<D>(Vt, 16 * kk, 32 * w, lane);
       float x[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * (ul[i] * tb[48 - 16 * kk]);
+      for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * ((h1 ? tb[7 - i] : tb[15 - i]) * tb[48 - 16 * kk]);
       op_t bhi, blo;
       M::split(x, bhi, blo);
 #pragma unroll
       for (int kt = 0; kt < NRT; ++kt) {
-        const op_t a = M::ld_tr_nat(Kt, LDT, 16 * kk, 32 * kt, lane);
+        const op_t a = M::ld_tr_nat_swz<D>(Kt, 16 * kk, 32 * kt, lane);
         S[kt] = M::mma(a, bhi, S[kt]);
         S[kt] = M::mma(a, blo, S[kt]);
       }
@@ -489,7 +497,7 @@ static hipError_t launch_output_t(const PrefillArgs& a, hipStream_t st) {
   if constexpr (BLK == 64 && sizeof(TIn) == 2)
     hipLaunchKernelGGL((la_chunk_output64<TOut, D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, (const float*)a.tbl,
-                       (const float*)a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
+                       a.decay, (const float*)a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
   else
     hipLaunchKernelGGL((la_chunk_output<TIn, TOut, D, BLK>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                        (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (TOut*)a.out, (const float*)a.tbl,
