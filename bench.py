@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 One step = one prefill of the million-token workload (B=1, H=64,
-N=1,048,576, d=128, bf16 inputs and output, block 256, fp32 state), i.e. all
+N=1,048,576, d=128, bf16 inputs and output, block 64, fp32 state), i.e. all
 of its kernels: decay-power table, chunk aggregates, chunk scan, chunk
 output.  Inputs are synthetic (seeded, generated on the device) and resident
 in HBM before timing starts.  Prints ONE JSON line:
@@ -202,7 +202,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--tokens", type=int, default=1 << 20)
-    ap.add_argument("--block", type=int, default=256, choices=[64, 128, 256])
+    ap.add_argument("--block", type=int, default=64, choices=[64, 128, 256])
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", dest="decode", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
