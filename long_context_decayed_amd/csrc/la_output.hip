@@ -257,22 +257,130 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 }
 
 // ---------------------------------------------------------------------------
+// Fast-path LDS tiles: 64 rows x D bf16, unpadded, 16-byte chunk c of row r
+// stored at chunk c ^ swz(r) with swz(r) = 2(r & 3) | ((r >> 2) & 1).
+//   * 16-byte row reads (8 lanes = 8 consecutive rows at one chunk) see swz
+//     take all 8 values on r % 8, so the 8 lanes cover all 32 banks;
+//   * transpose reads (16 lanes = rows r0..r0+3, r0 % 4 == 0, x two adjacent
+//     chunks) see 2(r & 3) move the chunk pair to 4 distinct pairs while bit
+//     (r >> 2) & 1, equal for the 4 rows, only swaps within a pair.
+__device__ __forceinline__ int swz(int r) { return (2 * (r & 3)) | ((r >> 2) & 1); }
+// Element offset of (row, col) within the tile (row stride D).
+template <int D>
+__device__ __forceinline__ int swz_at(int row, int col) {
+  return row * D + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
+}
+
+// LDS DMA.  The tiles reach LDS without passing through registers: with
+// global_load_lds_dwordx4 lane i of a wave moves 16 bytes from its own global
+// address to LDS byte address m0 + 16 i (m0 is wave-uniform), so one
+// instruction fills 1 KiB of a tile, and each lane fetches the global chunk
+// that belongs at its swizzled slot.  A tile with rows past the end of the
+// sequence is moved row by row with 4-byte transfers, the missing rows being
+// zero-filled with ordinary LDS stores.
+// Completion is tracked by the wave's vector-memory counter, which counts
+// loads, LDS DMA and stores in issue order: each wave waits for its own
+// transfers (vmcnt(n), n = vector-memory instructions it issued after them)
+// and then the barrier publishes them to the other waves.  The transfers are
+// issued from inline assembly so that the compiler, which cannot tell which
+// tile a transpose read touches, does not make every LDS read wait for them;
+// the waits are explicit, in sync_lds_after_vmem.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+__device__ __forceinline__ void dma_dword(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_dwordx4(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m0) : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory instructions are in
+// flight and its LDS operations are done, then barrier.  Also a compiler
+// barrier for memory accesses.
+template <int N>
+__device__ __forceinline__ void sync_lds_after_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+// Rows [0, nvalid) of a 64-row tile (src: its row 0, wave-uniform) into the
+// swizzled LDS tile dst; rows >= nvalid become zero.  The NW waves split the
+// instructions.  Full tile: NI / NW 16-byte instructions per wave.
+template <int D, int NW>
+__device__ __forceinline__ void dma_tile(const bf16* __restrict__ src, bf16* dst, int nvalid, int w, int lane) {
+  const uint32_t t0 = lds_addr(dst);
+  if (nvalid >= kSub) {
+    constexpr int CPR = D / 8, RPI = 64 / CPR, NI = kSub / RPI;
+    const int rr = lane / CPR, pc = lane % CPR;
+#pragma unroll
+    for (int m = 0; m < NI / NW; ++m) {
+      const int qi = w + NW * m;
+      const int row = RPI * qi + rr;
+      dma_dwordx4(src + row * D + ((pc ^ swz(row)) << 3), t0 + 1024 * qi);
+    }
+  } else if (lane < D / 2) {
+    for (int r = w; r < kSub; r += NW) {
+      if (r < nvalid)
+        dma_dword(src + r * D + (((lane >> 2) ^ swz(r)) << 3) + 2 * (lane & 3), t0 + 2 * r * D);
+      else
+        *reinterpret_cast<uint32_t*>(dst + r * D + 2 * lane) = 0u;
+    }
+  }
+}
+
+// 16-byte row operand: elements col .. col + 7 (col % 8 == 0) of a row.
+template <int D>
+__device__ __forceinline__ bf16x8 ld_row8(const bf16* X, int row, int col) {
+  return *reinterpret_cast<const bf16x8*>(X + swz_at<D>(row, col));
+}
+
+// Transpose-read operand: lane L = 32h + n gets, as element i < 8, X[row0 +
+// crow(i, h)][col0 + cn(n)] with cn(n) = n, or, with PI, n with bits 2 and 3
+// swapped (the feature order of the state's accumulator rows).  Within a
+// group of 16 lanes, lane 4j + q points at row row0 + 4h + j and the 4
+// columns of piece q (piece ((q & 1) << 1 | q >> 1) with PI); the second read
+// is 8 rows further down (same swizzle).
+template <int D, bool PI>
+__device__ __forceinline__ bf16x8 ld_tr8(const bf16* X, int row0, int col0, int lane) {
+  const int h = lane >> 5, j = (lane & 15) >> 2, q = lane & 3;
+  const int qq = PI ? (((q & 1) << 1) | (q >> 1)) : q;
+  const int row = row0 + 4 * h + j;
+  const bf16* p = X + swz_at<D>(row, col0 + 16 * ((lane >> 4) & 1) + 4 * qq);
+  const bf16x4 lo = ds_tr4(p), hi = ds_tr4(p + 8 * D);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ---------------------------------------------------------------------------
 // Pass C, block = 64, bf16 inputs: the fast path.  Same arithmetic as
-// la_chunk_output with BLK = 64, organised around the MI355X limits that
-// bind it (LDS capacity and bandwidth and VALU issue, next to HBM):
-//   * the score tiles P^T = K Q^T contract over the key dimension in the row
-//     order of the state's accumulator tiles, so the Q operands loaded for
-//     the inter term q S are reused as the B operands of the score tiles;
-//   * each of the 3 causal 32x32 score tiles of a sub-tile is computed by one
-//     wave, masked, decayed and shared through LDS as bf16 hi + lo MFMA A
-//     operands (P V then costs two MFMAs per step but keeps ~16 bits of P);
-//   * LDS tiles use per-reader layouts: Q and one copy of K have a row stride
-//     of an odd number of 8-byte units (16 rows x 8 bytes at one column hit
-//     16 distinct bank pairs); V and a second copy of K are unpadded with
-//     16-byte chunks XOR-swizzled by row (conflict-free transpose reads);
+// la_chunk_output with BLK = 64, organised around what binds it on MI355X
+// (HBM, and the issue of vector-memory instructions, next to LDS and VALU):
+//   * the output is computed transposed, O^T = S^T diag Q^T + V^T P^T: with
+//     the accumulator holding O^T, each lane owns one token row and 4
+//     consecutive columns per register quad, so a 64 x 32 block of O leaves
+//     in 8 stores of 8 bytes per lane, and the inter-term decay lam^(p+1) is
+//     one per-lane factor;
+//   * the state's accumulator rows hold the features in an order with bits 2
+//     and 3 of the row index swapped, so the 8 features a lane contributes to
+//     one MFMA step are contiguous in Q and K: one 16-byte LDS read;
+//   * Q, K and V tiles arrive by 16-byte LDS DMA; K is brought in twice (the
+//     second read is served by L2), as the row-read operand of the score
+//     tiles and as the transpose-read operand of the state update, so that
+//     each copy is needed in one phase only;
+//   * the 3 causal 32x32 score tiles P^T = K Q^T of a sub-tile are computed
+//     by one wave each, masked, decayed and shared through LDS as bf16 hi + lo
+//     MFMA operands (~16 bits of P);
 //   * decay factors are per-lane powers times wave-uniform powers; the masked
-//     diagonal score tile uses lam^d = exp2(d log2 lam) for d > 0.
-// With two workgroups per CU the LDS footprint stays under 80 KiB.
+//     diagonal score tile uses lam^d = exp2(d log2 lam) for d > 0;
+//   * software pipeline over the two compute phases of a sub-tile: Q and the
+//     score copy of K are only read in phase 1 (inter term and scores), so
+//     the next ones are requested at the barrier that ends phase 1 and waited
+//     for at the one that ends phase 2; V and the update copy of K are only
+//     read in phase 2 (P V and the state update), so the next ones are
+//     requested after that barrier, ahead of this sub-tile's output stores,
+//     and waited for at the end of the next phase 1.
+// Two workgroups per CU (76 KiB of LDS each).
 template <typename TOut, int D>
 __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                               const bf16* __restrict__ v, TOut* __restrict__ o,
@@ -283,14 +391,13 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   typedef Mfma<bf16> M;
   typedef M::op_t op_t;
   constexpr int NW = D / 32;
-  constexpr int NT = NW * 64;
-  constexpr int LDC = D + 4;  // odd number of 8-byte units per row
   constexpr int NRT = D / 32;
   constexpr int MAXT = (3 + NW - 1) / NW;  // score tiles per wave
-  __shared__ __attribute__((aligned(16))) bf16 Qs[kSub * LDC];
-  __shared__ __attribute__((aligned(16))) bf16 Kc[kSub * LDC];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[kSub * D];  // swizzled
-  __shared__ __attribute__((aligned(16))) bf16 Vt[kSub * D];  // swizzled
+  constexpr int kStores = sizeof(TOut) == 2 ? 2 * 2 : 2 * 4;  // output store instructions per sub-tile
+  __shared__ __attribute__((aligned(16))) bf16 Qs[kSub * D];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kSub * D];  // score operands (phase 1)
+  __shared__ __attribute__((aligned(16))) bf16 Kt[kSub * D];  // update operands (phase 2)
+  __shared__ __attribute__((aligned(16))) bf16 Vs[kSub * D];
   __shared__ __attribute__((aligned(16))) op_t Pbuf[3][2][2][64];  // [tile][g][hi/lo][lane]
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
@@ -307,49 +414,57 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   const int col = 32 * w + l32;
   const float* tb = tbl_all + (int64_t)hh * tbl_stride;  // lam^e, e <= 64
 
-  // Decay factors as per-lane powers times wave-uniform powers (exponents all
-  // non-negative):
-  //   update,  s = 16kk + 8h + i:      lam^(63-s) = lam^(48-16kk) * ul[i],   ul[i] = lam^(8(1-h)+7-i)
-  //   inter,   p = 32rt + crow(j, h):  lam^(p+1)  = lam^(32rt+8jq) * rl[jj], rl[jj] = lam^(4h+jj+1)
+  // Decay factors (all exponents non-negative), j = 4jq + jj:
+  //   update, s = 16kk + crow(i, h):   lam^(63-s) = lam^(48-16kk) * ul[i],  ul[i] = lam^(15-crow(i,h))
+  //   inter,  token p = 32rt + l:      lam^(p+1)  = rf[rt]
   //   off-diagonal score tile (r = 32 + l, s = crow(j, h)):
-  //            lam^(r-s) = lam^(24-8jq) * ol[jj],  ol[jj] = lam^(l+4-4h+4-jj)
-  // with j = 4jq + jj.  Diagonal tile (r = l, s = crow(j, h)): d = r - s,
-  // factor 1 at d = 0, exp2(d log2 lam) at d > 0, 0 (masked) at d < 0.
-  // ul and rl take one of two wave-uniform values per lane half, selected at
-  // each use (cheaper than keeping 12 more registers live across the loop).
-  float ol[4];
+  //           lam^(r-s) = lam^(24-8jq) * ol[jj],  ol[jj] = lam^(l+4-4h+4-jj)
+  //   diagonal tile (r = l, s = crow(j, h)), d = r - s: 1 at d = 0,
+  //           exp2(d log2 lam) at d > 0, 0 (masked) at d < 0.
+  // They are loaded here, before the tile loop, so that the loop issues no
+  // vector-memory loads of its own.
+  float ol[4], ul[8], rf[2];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) ol[jj] = tb[l32 + 8 - 4 * hf - jj];
-  const bool h1 = hf != 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ul[i] = tb[15 - crow(i, hf)];
+  rf[0] = tb[l32 + 1];
+  rf[1] = tb[l32 + 33];
   const float d64 = tb[64];
   const float log2lam = __builtin_amdgcn_logf(decay[hh]);  // -inf at lam = 0
   const float dbase = (float)(l32 - 4 * hf);
 
-  // Accumulator element (tile row 32a + crow(j, h), column col) sits at
-  // (32a + 8(j>>2) + (j&3)) * D + lane_off from a wave-uniform base.
-  const int lane_off = 4 * hf * D + col;
+  // State tile kt, register j of lane (h, n): feature 32kt + pf(crow(j, h)),
+  // value column col, where pf swaps bits 2 and 3:
+  //   pf(crow(j, h)) = 16(j >> 3) + 8h + 4((j >> 2) & 1) + (j & 3).
   f32x16 S[NRT];
   {
-    const float* src = sstart + ((int64_t)bh * nc + c) * D * D;
+    const float* src = sstart + ((int64_t)bh * nc + c) * D * D + col;
 #pragma unroll
     for (int kt = 0; kt < NRT; ++kt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) S[kt][j] = src[lane_off + (32 * kt + 8 * (j >> 2) + (j & 3)) * D];
+      for (int j = 0; j < 16; ++j)
+        S[kt][j] = src[(32 * kt + 16 * (j >> 3) + 8 * hf + 4 * ((j >> 2) & 1) + (j & 3)) * D];
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the state and the factors are in registers
 
-  RowTile<bf16, D, NT> pq, pk, pv;
+  {
+    const int nv = min(kSub, t_end - t_begin);
+    const int64_t off = (int64_t)t_begin * D;
+    dma_tile<D, NW>(qb + off, Qs, nv, w, lane);
+    dma_tile<D, NW>(kb + off, Ks, nv, w, lane);
+    dma_tile<D, NW>(kb + off, Kt, nv, w, lane);
+    dma_tile<D, NW>(vb + off, Vs, nv, w, lane);
+    sync_lds_after_vmem<0>();
+  }
   for (int t0 = t_begin; t0 < t_end; t0 += kSub) {
-    pq.load(qb, t0, t_end, tid);
-    pk.load(kb, t0, t_end, tid);
-    pv.load(vb, t0, t_end, tid);
-    pq.template store_halves<LDC>(Qs, tid);
-    pk.template store_halves<LDC>(Kc, tid);
-    pk.store_swz(Kt, tid);
-    pv.store_swz(Vt, tid);
-    __syncthreads();
+    const bool more = t0 + kSub < t_end;
+    const int nv_next = min(kSub, t_end - t0 - kSub);
+    const int64_t off_next = (int64_t)(t0 + kSub) * D;
 
-    // Inter term acc = Q S_b (S split into bf16 hi + lo on the fly) and this
-    // wave's score tiles P^T = K Q^T, sharing the Q operands; then S *= lam^64.
+    // Phase 1.  Inter term acc[rt] = S_b^T Q^T for tokens 32rt + l (S split
+    // into bf16 hi + lo on the fly) and this wave's score tiles P^T = K Q^T,
+    // sharing the Q operands; then S *= lam^64.
     f32x16 acc[2], pt[MAXT];
     acc[0] = zero16();
     acc[1] = zero16();
@@ -359,23 +474,24 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
     for (int kt = 0; kt < NRT; ++kt) {
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const op_t qa0 = M::ld_cperm(Qs + l32 * LDC + 32 * kt, g, hf);
-        const op_t qa1 = M::ld_cperm(Qs + (32 + l32) * LDC + 32 * kt, g, hf);
+        const int f0 = 32 * kt + 16 * g + 8 * hf;
+        const op_t qa0 = ld_row8<D>(Qs, l32, f0);
+        const op_t qa1 = ld_row8<D>(Qs, 32 + l32, f0);
         float x[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = S[kt][8 * g + i];
         op_t hi, lo;
         M::split(x, hi, lo);
-        acc[0] = M::mma(qa0, hi, acc[0]);
-        acc[1] = M::mma(qa1, hi, acc[1]);
-        acc[0] = M::mma(qa0, lo, acc[0]);
-        acc[1] = M::mma(qa1, lo, acc[1]);
+        acc[0] = M::mma(hi, qa0, acc[0]);
+        acc[1] = M::mma(hi, qa1, acc[1]);
+        acc[0] = M::mma(lo, qa0, acc[0]);
+        acc[1] = M::mma(lo, qa1, acc[1]);
 #pragma unroll
         for (int m = 0; m < MAXT; ++m) {
           const int ti = w + m * NW;
           if (ti < 3) {
             const int st = ti == 2 ? 1 : 0, rt = ti == 0 ? 0 : 1;
-            const op_t ka = M::ld_cperm(Kc + (32 * st + l32) * LDC + 32 * kt, g, hf);
+            const op_t ka = ld_row8<D>(Ks, 32 * st + l32, f0);
             pt[m] = M::mma(ka, rt ? qa1 : qa0, pt[m]);
           }
         }
@@ -399,7 +515,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
           }
         } else {
           // Opaque copies: recomputing 16 factors here is cheaper than the
-          // compiler's choice of hoisting them out of the loop and spilling.
+          // compiler's choice of hoisting them out of the loop.
           float db = dbase, lg = log2lam;
           asm volatile("" : "+v"(db), "+v"(lg));
 #pragma unroll
@@ -421,64 +537,91 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
         }
       }
     }
-    // Row factors lam^(p+1) of the inter term.
+    // Inter-term decay lam^(p+1), one factor per lane and token tile.
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const float u = tb[32 * rt + 8 * jq];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[rt][4 * jq + jj] *= (h1 ? tb[jj + 5] : tb[jj + 1]) * u;
-      }
-    __syncthreads();  // score tiles visible
+    for (int rt = 0; rt < 2; ++rt) acc[rt] *= rf[rt];
 
-    // Intra-block term: acc[rt] += P V over the shared score tiles.
+    // This sub-tile's V and K^T copy (requested before the previous
+    // sub-tile's kStores output stores, which may still be in flight) and
+    // the score tiles become visible; Q and the score copy of K are free.
+    sync_lds_after_vmem<kStores>();
+    if (more) {
+      dma_tile<D, NW>(qb + off_next, Qs, nv_next, w, lane);
+      dma_tile<D, NW>(kb + off_next, Ks, nv_next, w, lane);
+    }
+
+    // Phase 2.  Intra-block term acc[rt] += V^T P^T over the shared score tiles.
 #pragma unroll
     for (int ti = 0; ti < 3; ++ti) {
       const int st = ti == 2 ? 1 : 0, rt = ti == 0 ? 0 : 1;
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const op_t vop = M::ld_tr_cperm_swz<D>(Vt, 32 * st, g, 32 * w, lane);
-        acc[rt] = M::mma(Pbuf[ti][g][0][lane], vop, acc[rt]);
-        acc[rt] = M::mma(Pbuf[ti][g][1][lane], vop, acc[rt]);
+        const op_t vop = ld_tr8<D, false>(Vs, 32 * st + 16 * g, 32 * w, lane);
+        acc[rt] = M::mma(vop, Pbuf[ti][g][0][lane], acc[rt]);
+        acc[rt] = M::mma(vop, Pbuf[ti][g][1][lane], acc[rt]);
       }
     }
 
-    // State update: S += sum_s lam^(63-s) k_s^T v_s.
+    // State update: S += sum_s lam^(63-s) k_s^T v_s, tokens s = 16kk + crow(i, h).
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const op_t vraw = M::ld_tr_nat_swz<D>(Vt, 16 * kk, 32 * w, lane);
+      const op_t vraw = ld_tr8<D, false>(Vs, 16 * kk, 32 * w, lane);
+      const float u = tb[48 - 16 * kk];
       float x[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * ((h1 ? tb[7 - i] : tb[15 - i]) * tb[48 - 16 * kk]);
+      for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * (ul[i] * u);
       op_t bhi, blo;
       M::split(x, bhi, blo);
 #pragma unroll
       for (int kt = 0; kt < NRT; ++kt) {
-        const op_t a = M::ld_tr_nat_swz<D>(Kt, 16 * kk, 32 * kt, lane);
+        const op_t a = ld_tr8<D, true>(Kt, 16 * kk, 32 * kt, lane);
         S[kt] = M::mma(a, bhi, S[kt]);
         S[kt] = M::mma(a, blo, S[kt]);
       }
     }
 
-    // Store this sub-tile's rows.
-    TOut* orow = ob + (int64_t)t0 * D;
-    if (t0 + kSub <= t_end) {
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          orow[lane_off + (32 * rt + 8 * (j >> 2) + (j & 3)) * D] = from_f32<TOut>(acc[rt][j]);
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int r = 32 * rt + crow(j, hf);
-          if (t0 + r < t_end) orow[lane_off + (32 * rt + 8 * (j >> 2) + (j & 3)) * D] = from_f32<TOut>(acc[rt][j]);
-        }
+    // The next sub-tile's Q and K (and this wave's older stores) are done
+    // and visible; V, K^T and the score tiles are free from here on.
+    sync_lds_after_vmem<0>();
+    if (more) {
+      dma_tile<D, NW>(kb + off_next, Kt, nv_next, w, lane);
+      dma_tile<D, NW>(vb + off_next, Vs, nv_next, w, lane);
     }
-    __syncthreads();
+
+    // Store O.  Lane (h, l) holds token t0 + 32rt + l, columns 32w + 8jq +
+    // 4h + jj.  bf16: the two lane halves trade quads (v_permlane32_swap) so
+    // that each lane owns 8 consecutive columns 32w + 16p + 8h .. + 7 of
+    // column pair p and stores them as 16 bytes (the two halves then write
+    // 32 contiguous bytes of each row).
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int t = t0 + 32 * rt + l32;
+      if constexpr (sizeof(TOut) == 2) {
+        uint4 pk[2];
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int ja = 8 * pp, jb = 8 * pp + 4;  // quads jq = 2pp (kept by h = 0), 2pp + 1 (kept by h = 1)
+          const uint32_t a0 = pack_bf16x2(acc[rt][ja], acc[rt][ja + 1]), a1 = pack_bf16x2(acc[rt][ja + 2], acc[rt][ja + 3]);
+          const uint32_t b0 = pack_bf16x2(acc[rt][jb], acc[rt][jb + 1]), b1 = pack_bf16x2(acc[rt][jb + 2], acc[rt][jb + 3]);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+          pk[pp] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+        }
+        if (t < t_end) {
+          bf16* orow = reinterpret_cast<bf16*>(ob) + (int64_t)t * D + 32 * w + 8 * hf;
+          *reinterpret_cast<uint4*>(orow) = pk[0];
+          *reinterpret_cast<uint4*>(orow + 16) = pk[1];
+        }
+      } else {
+        if (t < t_end) {
+          TOut* orow = ob + (int64_t)t * D + 32 * w + 4 * hf;
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq)
+            *reinterpret_cast<f32x4*>(orow + 8 * jq) =
+                f32x4{acc[rt][4 * jq], acc[rt][4 * jq + 1], acc[rt][4 * jq + 2], acc[rt][4 * jq + 3]};
+        }
+      }
+    }
   }
 }
 

@@ -132,16 +132,20 @@ def test_bf16_deterministic(dev, layer_8k):
 
 # --- ragged tails, initial state, state carry, in-place state ----------------
 
+@pytest.mark.parametrize("block,d", [(128, 128), (64, 128), (64, 64)])
 @pytest.mark.parametrize("n", [1, 63, 65, 1000, 4097 + 13])
-def test_bf16_tails_with_state(dev, n):
-    say("bf16 tails B2 H4 N", n)
-    q, k, v = qkv_device(2, 4, n, 128, seed=10 + n, device=dev)
+def test_bf16_tails_with_state(dev, n, block, d):
+    say("bf16 tails B2 H4 N", n, "d", d, "block", block)
+    q, k, v = qkv_device(2, 4, n, d, seed=10 + n, device=dev)
     lam = decay_lambdas(4)
-    s0 = state_device(2, 4, 128, seed=10 + n, device=dev)
-    o32, kv = _run(q, k, v, lam, dev, 128, out_dtype=torch.float32, kv_in=s0, chunk=256)
+    s0 = state_device(2, 4, d, seed=10 + n, device=dev)
+    o32, kv = _run(q, k, v, lam, dev, block, out_dtype=torch.float32, kv_in=s0, chunk=256)
+    o16, kv16 = _run(q, k, v, lam, dev, block, out_dtype=torch.bfloat16, kv_in=s0, chunk=256)
     o_ref, s_ref = oracle(host(q), host(k), host(v), lam, host(s0).astype(np.float64))
     tol.assert_bf16_f32out(host(o32), o_ref)
     tol.assert_state(host(kv), s_ref, "kv_out")
+    assert torch.equal(o32.to(torch.bfloat16), o16), "bf16 out must be RNE(fp32 out)"
+    assert torch.equal(kv, kv16)
 
 
 @pytest.mark.parametrize("t0", [512, 700])
