@@ -290,11 +290,22 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void_t*)p;
 }
+// m0 (the LDS base of the transfer) is saved and restored around it.
 __device__ __forceinline__ void dma_dword(const void* g, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(m0) : "memory", "m0");
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(g), "s"(m0)
+      : "memory");
 }
 __device__ __forceinline__ void dma_dwordx4(const void* g, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m0) : "memory", "m0");
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(g), "s"(m0)
+      : "memory");
 }
 
 // Wait until at most N of this wave's vector-memory instructions are in
@@ -354,13 +365,13 @@ __device__ __forceinline__ bf16x8 ld_tr8(const bf16* X, int row0, int col0, int 
 
 // ---------------------------------------------------------------------------
 // Pass C, block = 64, bf16 inputs: the fast path.  Same arithmetic as
-// la_chunk_output with BLK = 64, organised around what binds it on MI355X
-// (HBM, and the issue of vector-memory instructions, next to LDS and VALU):
+// la_chunk_output with BLK = 64, organised around what binds it on MI355X:
+// VALU + MFMA issue per SIMD, vector-memory instruction issue, HBM, LDS.
 //   * the output is computed transposed, O^T = S^T diag Q^T + V^T P^T: with
 //     the accumulator holding O^T, each lane owns one token row and 4
-//     consecutive columns per register quad, so a 64 x 32 block of O leaves
-//     in 8 stores of 8 bytes per lane, and the inter-term decay lam^(p+1) is
-//     one per-lane factor;
+//     consecutive columns per register quad, so after a lane-half swap a
+//     64 x 32 block of bf16 O leaves in 4 stores of 16 bytes per lane, and
+//     the inter-term decay lam^(p+1) is one per-lane factor;
 //   * the state's accumulator rows hold the features in an order with bits 2
 //     and 3 of the row index swapped, so the 8 features a lane contributes to
 //     one MFMA step are contiguous in Q and K: one 16-byte LDS read;
@@ -372,7 +383,8 @@ __device__ __forceinline__ bf16x8 ld_tr8(const bf16* X, int row0, int col0, int 
 //     by one wave each, masked, decayed and shared through LDS as bf16 hi + lo
 //     MFMA operands (~16 bits of P);
 //   * decay factors are per-lane powers times wave-uniform powers; the masked
-//     diagonal score tile uses lam^d = exp2(d log2 lam) for d > 0;
+//     factors of the two diagonal score tiles come from a per-lane LDS table
+//     built once per workgroup;
 //   * software pipeline over the two compute phases of a sub-tile: Q and the
 //     score copy of K are only read in phase 1 (inter term and scores), so
 //     the next ones are requested at the barrier that ends phase 1 and waited
@@ -380,12 +392,11 @@ __device__ __forceinline__ bf16x8 ld_tr8(const bf16* X, int row0, int col0, int 
 //     read in phase 2 (P V and the state update), so the next ones are
 //     requested after that barrier, ahead of this sub-tile's output stores,
 //     and waited for at the end of the next phase 1.
-// Two workgroups per CU (76 KiB of LDS each).
+// Two workgroups per CU (80 KiB of LDS each).
 template <typename TOut, int D>
 __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                               const bf16* __restrict__ v, TOut* __restrict__ o,
                                                               const float* __restrict__ tbl_all,
-                                                              const float* __restrict__ decay,
                                                               const float* __restrict__ sstart, int H, int N, int L,
                                                               int nc, int tbl_stride) {
   typedef Mfma<bf16> M;
@@ -399,6 +410,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   __shared__ __attribute__((aligned(16))) bf16 Kt[kSub * D];  // update operands (phase 2)
   __shared__ __attribute__((aligned(16))) bf16 Vs[kSub * D];
   __shared__ __attribute__((aligned(16))) op_t Pbuf[3][2][2][64];  // [tile][g][hi/lo][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 Dtab[4][64];        // diagonal-tile factors [jq][lane]
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -419,8 +431,8 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   //   inter,  token p = 32rt + l:      lam^(p+1)  = rf[rt]
   //   off-diagonal score tile (r = 32 + l, s = crow(j, h)):
   //           lam^(r-s) = lam^(24-8jq) * ol[jj],  ol[jj] = lam^(l+4-4h+4-jj)
-  //   diagonal tile (r = l, s = crow(j, h)), d = r - s: 1 at d = 0,
-  //           exp2(d log2 lam) at d > 0, 0 (masked) at d < 0.
+  //   diagonal tile (r = l, s = crow(j, h)), d = r - s: lam^d for d >= 0,
+  //           0 (masked) for d < 0, kept in Dtab[jq][lane][jj].
   // They are loaded here, before the tile loop, so that the loop issues no
   // vector-memory loads of its own.
   float ol[4], ul[8], rf[2];
@@ -431,8 +443,12 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   rf[0] = tb[l32 + 1];
   rf[1] = tb[l32 + 33];
   const float d64 = tb[64];
-  const float log2lam = __builtin_amdgcn_logf(decay[hh]);  // -inf at lam = 0
-  const float dbase = (float)(l32 - 4 * hf);
+  for (int e = tid; e < 4 * 64; e += NW * 64) {
+    const int jq = e >> 6, ln = e & 63;
+    const int dd = (ln & 31) - 4 * (ln >> 5) - 8 * jq;
+    Dtab[jq][ln] = f32x4{dd >= 0 ? tb[dd] : 0.0f, dd >= 1 ? tb[dd - 1] : 0.0f, dd >= 2 ? tb[dd - 2] : 0.0f,
+                         dd >= 3 ? tb[dd - 3] : 0.0f};
+  }
 
   // State tile kt, register j of lane (h, n): feature 32kt + pf(crow(j, h)),
   // value column col, where pf swaps bits 2 and 3:
@@ -514,15 +530,11 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
             for (int jj = 0; jj < 4; ++jj) pt[m][4 * jq + jj] *= ol[jj] * u;
           }
         } else {
-          // Opaque copies: recomputing 16 factors here is cheaper than the
-          // compiler's choice of hoisting them out of the loop.
-          float db = dbase, lg = log2lam;
-          asm volatile("" : "+v"(db), "+v"(lg));
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const float dd = db - (float)(8 * (j >> 2) + (j & 3));
-            const float f = dd > 0.0f ? __builtin_amdgcn_exp2f(dd * lg) : (dd == 0.0f ? 1.0f : 0.0f);
-            pt[m][j] *= f;
+          for (int jq = 0; jq < 4; ++jq) {
+            const f32x4 f = Dtab[jq][lane];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) pt[m][4 * jq + jj] *= f[jj];
           }
         }
 #pragma unroll
@@ -640,7 +652,7 @@ static hipError_t launch_output_t(const PrefillArgs& a, hipStream_t st) {
   if constexpr (BLK == 64 && sizeof(TIn) == 2)
     hipLaunchKernelGGL((la_chunk_output64<TOut, D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, (const float*)a.tbl,
-                       a.decay, (const float*)a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
+                       (const float*)a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
   else
     hipLaunchKernelGGL((la_chunk_output<TIn, TOut, D, BLK>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                        (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (TOut*)a.out, (const float*)a.tbl,
