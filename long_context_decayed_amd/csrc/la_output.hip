@@ -257,113 +257,6 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 }
 
 // ---------------------------------------------------------------------------
-// Fast-path LDS tiles: 64 rows x D bf16, unpadded, 16-byte chunk c of row r
-// stored at chunk c ^ swz(r) with swz(r) = 2(r & 3) | ((r >> 2) & 1).
-//   * 16-byte row reads (8 lanes = 8 consecutive rows at one chunk) see swz
-//     take all 8 values on r % 8, so the 8 lanes cover all 32 banks;
-//   * transpose reads (16 lanes = rows r0..r0+3, r0 % 4 == 0, x two adjacent
-//     chunks) see 2(r & 3) move the chunk pair to 4 distinct pairs while bit
-//     (r >> 2) & 1, equal for the 4 rows, only swaps within a pair.
-__device__ __forceinline__ int swz(int r) { return (2 * (r & 3)) | ((r >> 2) & 1); }
-// Element offset of (row, col) within the tile (row stride D).
-template <int D>
-__device__ __forceinline__ int swz_at(int row, int col) {
-  return row * D + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
-}
-
-// LDS DMA.  The tiles reach LDS without passing through registers: with
-// global_load_lds_dwordx4 lane i of a wave moves 16 bytes from its own global
-// address to LDS byte address m0 + 16 i (m0 is wave-uniform), so one
-// instruction fills 1 KiB of a tile, and each lane fetches the global chunk
-// that belongs at its swizzled slot.  A tile with rows past the end of the
-// sequence is moved row by row with 4-byte transfers, the missing rows being
-// zero-filled with ordinary LDS stores.
-// Completion is tracked by the wave's vector-memory counter, which counts
-// loads, LDS DMA and stores in issue order: each wave waits for its own
-// transfers (vmcnt(n), n = vector-memory instructions it issued after them)
-// and then the barrier publishes them to the other waves.  The transfers are
-// issued from inline assembly so that the compiler, which cannot tell which
-// tile a transpose read touches, does not make every LDS read wait for them;
-// the waits are explicit, in sync_lds_after_vmem.
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
-}
-// m0 (the LDS base of the transfer) is saved and restored around it.
-__device__ __forceinline__ void dma_dword(const void* g, uint32_t m0) {
-  uint32_t keep;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "v"(g), "s"(m0)
-      : "memory");
-}
-__device__ __forceinline__ void dma_dwordx4(const void* g, uint32_t m0) {
-  uint32_t keep;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "v"(g), "s"(m0)
-      : "memory");
-}
-
-// Wait until at most N of this wave's vector-memory instructions are in
-// flight and its LDS operations are done, then barrier.  Also a compiler
-// barrier for memory accesses.
-template <int N>
-__device__ __forceinline__ void sync_lds_after_vmem() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
-}
-
-// Rows [0, nvalid) of a 64-row tile (src: its row 0, wave-uniform) into the
-// swizzled LDS tile dst; rows >= nvalid become zero.  The NW waves split the
-// instructions.  Full tile: NI / NW 16-byte instructions per wave.
-template <int D, int NW>
-__device__ __forceinline__ void dma_tile(const bf16* __restrict__ src, bf16* dst, int nvalid, int w, int lane) {
-  const uint32_t t0 = lds_addr(dst);
-  if (nvalid >= kSub) {
-    constexpr int CPR = D / 8, RPI = 64 / CPR, NI = kSub / RPI;
-    const int rr = lane / CPR, pc = lane % CPR;
-#pragma unroll
-    for (int m = 0; m < NI / NW; ++m) {
-      const int qi = w + NW * m;
-      const int row = RPI * qi + rr;
-      dma_dwordx4(src + row * D + ((pc ^ swz(row)) << 3), t0 + 1024 * qi);
-    }
-  } else if (lane < D / 2) {
-    for (int r = w; r < kSub; r += NW) {
-      if (r < nvalid)
-        dma_dword(src + r * D + (((lane >> 2) ^ swz(r)) << 3) + 2 * (lane & 3), t0 + 2 * r * D);
-      else
-        *reinterpret_cast<uint32_t*>(dst + r * D + 2 * lane) = 0u;
-    }
-  }
-}
-
-// 16-byte row operand: elements col .. col + 7 (col % 8 == 0) of a row.
-template <int D>
-__device__ __forceinline__ bf16x8 ld_row8(const bf16* X, int row, int col) {
-  return *reinterpret_cast<const bf16x8*>(X + swz_at<D>(row, col));
-}
-
-// Transpose-read operand: lane L = 32h + n gets, as element i < 8, X[row0 +
-// crow(i, h)][col0 + cn(n)] with cn(n) = n, or, with PI, n with bits 2 and 3
-// swapped (the feature order of the state's accumulator rows).  Within a
-// group of 16 lanes, lane 4j + q points at row row0 + 4h + j and the 4
-// columns of piece q (piece ((q & 1) << 1 | q >> 1) with PI); the second read
-// is 8 rows further down (same swizzle).
-template <int D, bool PI>
-__device__ __forceinline__ bf16x8 ld_tr8(const bf16* X, int row0, int col0, int lane) {
-  const int h = lane >> 5, j = (lane & 15) >> 2, q = lane & 3;
-  const int qq = PI ? (((q & 1) << 1) | (q >> 1)) : q;
-  const int row = row0 + 4 * h + j;
-  const bf16* p = X + swz_at<D>(row, col0 + 16 * ((lane >> 4) & 1) + 4 * qq);
-  const bf16x4 lo = ds_tr4(p), hi = ds_tr4(p + 8 * D);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// ---------------------------------------------------------------------------
 // Pass C, block = 64, bf16 inputs: the fast path.  Same arithmetic as
 // la_chunk_output with BLK = 64, organised around what binds it on MI355X:
 // VALU + MFMA issue per SIMD, vector-memory instruction issue, HBM, LDS.

@@ -118,6 +118,134 @@ __global__ __launch_bounds__(D * 2, sizeof(TIn) == 2 ? 3 : 1) void la_chunk_stat
 }
 
 // ---------------------------------------------------------------------------
+// Pass A, bf16 inputs: the fast path.  Same aggregate, organised like the
+// block-64 output kernel: wave w owns columns [32w, 32w + 32) of U, the K and
+// V sub-tiles arrive by 16-byte LDS DMA into swizzled tiles, double-buffered
+// so that the next sub-tile's transfer overlaps this one's MFMAs (one
+// barrier per sub-tile), and the sub-tiles are taken from the last to the
+// first.  In that order the decay of token s of a full sub-tile b,
+// lam^(L_c - 1 - (64b + s)) = lam^(L_c - 64(b+1)) lam^(63 - s), is a
+// sub-tile scalar u_b (kept in double, u_(b-1) = u_b lam^64) times the
+// per-token power, so U is never rescaled.  Only the last sub-tile of the
+// sequence can be partial (n < 64 tokens, factors lam^(n-1-s)); it comes
+// first and then sets u to lam^n.
+//   Token s = 16kk + crow(i, h) of a full sub-tile (the row order of the
+// transpose-read operands): lam^(63-s) u = ul[i] * (lam^(48-16kk) u) with the
+// per-lane ul[i] = lam^(15 - crow(i, h)).
+template <int D>
+__global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                                             const float* __restrict__ decay,
+                                                             const float* __restrict__ tbl_all, float* __restrict__ ws,
+                                                             int H, int N, int L, int nc, int tbl_stride) {
+  typedef Mfma<bf16> M;
+  typedef M::op_t op_t;
+  constexpr int NW = D / 32;
+  constexpr int NRT = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kSub * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][kSub * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
+  const int hh = bh % H;
+  const int64_t base = (int64_t)bh * N * D;
+  const bf16* kb = k + base;
+  const bf16* vb = v + base;
+  const int t_begin = c * L;
+  const int lc = min(N, t_begin + L) - t_begin;  // tokens in this chunk, >= 1
+  const float* tb = tbl_all + (int64_t)hh * tbl_stride;  // lam^e, e <= 64
+
+  float ul[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ul[i] = tb[15 - crow(i, hf)];
+  const double lam = (double)decay[hh];
+  const double lam64 = pow_int(lam, kSub);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the factors are in registers before any transfer
+
+  f32x16 U[NRT];
+#pragma unroll
+  for (int kt = 0; kt < NRT; ++kt) U[kt] = zero16();
+
+  const int nsub = (lc + kSub - 1) / kSub;
+  const int n_last = lc - (nsub - 1) * kSub;  // 1..64
+  {
+    const int64_t off = (int64_t)(t_begin + (nsub - 1) * kSub) * D;
+    dma_tile<D, NW>(kb + off, Ks[0], n_last, w, lane);
+    dma_tile<D, NW>(vb + off, Vs[0], n_last, w, lane);
+  }
+  double ud = 1.0;  // u_b of the next full sub-tile
+  int b = nsub - 1, cur = 0;
+  if (n_last < kSub) {
+    // The partial last sub-tile (peeled, so the main loop has one path):
+    // tokens s < n_last get lam^(n_last-1-s), the rest 0.
+    sync_lds_after_vmem<0>();
+    if (b > 0) {
+      const int64_t off = (int64_t)(t_begin + (b - 1) * kSub) * D;
+      dma_tile<D, NW>(kb + off, Ks[1], kSub, w, lane);
+      dma_tile<D, NW>(vb + off, Vs[1], kSub, w, lane);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const op_t vraw = ld_tr8<D, false>(Vs[0], 16 * kk, 32 * w, lane);
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int s = 16 * kk + crow(i, hf);
+        x[i] = s < n_last ? (float)vraw[i] * tb[max(n_last - 1 - s, 0)] : 0.0f;
+      }
+      op_t bhi, blo;
+      M::split(x, bhi, blo);
+#pragma unroll
+      for (int kt = 0; kt < NRT; ++kt) {
+        const op_t a = ld_tr8<D, false>(Ks[0], 16 * kk, 32 * kt, lane);
+        U[kt] = M::mma(a, bhi, U[kt]);
+        U[kt] = M::mma(a, blo, U[kt]);
+      }
+    }
+    ud = pow_int(lam, n_last);
+    --b;
+    cur = 1;
+  }
+  for (; b >= 0; --b, cur ^= 1) {
+    // Sub-tile b (full) is in buffer cur and visible; every wave is done
+    // with the other buffer, which now receives sub-tile b - 1.
+    sync_lds_after_vmem<0>();
+    if (b > 0) {
+      const int64_t off = (int64_t)(t_begin + (b - 1) * kSub) * D;
+      dma_tile<D, NW>(kb + off, Ks[cur ^ 1], kSub, w, lane);
+      dma_tile<D, NW>(vb + off, Vs[cur ^ 1], kSub, w, lane);
+    }
+    const bf16* Kc = Ks[cur];
+    const bf16* Vc = Vs[cur];
+    const float u = (float)ud;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const op_t vraw = ld_tr8<D, false>(Vc, 16 * kk, 32 * w, lane);
+      const float wk = tb[48 - 16 * kk] * u;
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * ul[i] * wk;
+      op_t bhi, blo;
+      M::split(x, bhi, blo);
+#pragma unroll
+      for (int kt = 0; kt < NRT; ++kt) {
+        const op_t a = ld_tr8<D, false>(Kc, 16 * kk, 32 * kt, lane);
+        U[kt] = M::mma(a, bhi, U[kt]);
+        U[kt] = M::mma(a, blo, U[kt]);
+      }
+    }
+    ud *= lam64;
+  }
+
+  // U tile kt, register j of lane (h, l): row 32kt + crow(j, h), column 32w + l.
+  float* dst = ws + ((int64_t)bh * nc + c) * D * D + 32 * w + l32;
+#pragma unroll
+  for (int kt = 0; kt < NRT; ++kt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dst[(32 * kt + crow(j, hf)) * D] = U[kt][j];
+}
+
+// ---------------------------------------------------------------------------
 // Pass B.  One thread per 4 consecutive state elements of one (bh); serial
 // over chunks.  ws holds U_c on entry and Sstart_c on exit.
 __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ decay, float* __restrict__ ws,
@@ -162,8 +290,14 @@ static hipError_t launch_state_t(const PrefillArgs& a, hipStream_t st) {
   const int BH = (int)(a.B * a.H);
   const int nc = a.nc;
   hipLaunchKernelGGL(la_decay_table, dim3((unsigned)a.H), dim3(256), 0, st, a.decay, a.tbl, a.tbl_stride);
-  hipLaunchKernelGGL((la_chunk_state<TIn, D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st, (const TIn*)a.k,
-                     (const TIn*)a.v, (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
+  if constexpr (sizeof(TIn) == 2)
+    hipLaunchKernelGGL((la_chunk_state64<D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st, (const bf16*)a.k,
+                       (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc,
+                       a.tbl_stride);
+  else
+    hipLaunchKernelGGL((la_chunk_state<TIn, D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st, (const TIn*)a.k,
+                       (const TIn*)a.v, (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc,
+                       a.tbl_stride);
   const int64_t threads = (int64_t)BH * D * D / 4;
   hipLaunchKernelGGL(la_chunk_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a.decay, a.states,
                      a.kv_in, a.kv_out, BH, (int)a.H, (int)a.N, (int)a.L, nc, D);
