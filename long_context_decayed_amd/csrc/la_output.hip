@@ -298,6 +298,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   constexpr int NRT = D / 32;
   constexpr int MAXT = (3 + NW - 1) / NW;  // score tiles per wave
   constexpr int kStores = sizeof(TOut) == 2 ? 2 * 2 : 2 * 4;  // output store instructions per sub-tile
+  constexpr bool kDefer = sizeof(TOut) == 2;  // bf16 rows are stored during the next sub-tile's phase 1
   __shared__ __attribute__((aligned(16))) bf16 Qs[kSub * D];
   __shared__ __attribute__((aligned(16))) bf16 Ks[kSub * D];  // score operands (phase 1)
   __shared__ __attribute__((aligned(16))) bf16 Kt[kSub * D];  // update operands (phase 2)
@@ -366,6 +367,12 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
     dma_tile<D, NW>(vb + off, Vs, nv, w, lane);
     sync_lds_after_vmem<0>();
   }
+  // bf16 output of the previous sub-tile, packed and lane-swapped, stored
+  // one instruction per step of the next inter loop so that the stores
+  // trickle out instead of queueing all at once behind the CU's store path.
+  uint4 pend[2][2];
+  bool have_pend = false;
+  int t_pend = 0;
   for (int t0 = t_begin; t0 < t_end; t0 += kSub) {
     const bool more = t0 + kSub < t_end;
     const int nv_next = min(kSub, t_end - t0 - kSub);
@@ -406,6 +413,18 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
         }
       }
       S[kt] *= d64;
+      if constexpr (kDefer) {
+        // The pending sub-tile is a full one (only the last can be partial).
+        static_assert(4 % NRT == 0, "whole stores per step");
+        if (have_pend) {
+#pragma unroll
+          for (int q = 0; q < 4 / NRT; ++q) {
+            const int e = kt * (4 / NRT) + q, rt = e >> 1, pp = e & 1;
+            bf16* orow = reinterpret_cast<bf16*>(ob) + (int64_t)(t_pend + 32 * rt + l32) * D + 32 * w + 16 * pp + 8 * hf;
+            *reinterpret_cast<uint4*>(orow) = pend[rt][pp];
+          }
+        }
+      }
       // Keep the scheduler from hoisting every kt step's LDS operands at once
       // (the register file is shared by two workgroups per CU).
       __builtin_amdgcn_sched_barrier(0);
@@ -493,16 +512,15 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
       dma_tile<D, NW>(vb + off_next, Vs, nv_next, w, lane);
     }
 
-    // Store O.  Lane (h, l) holds token t0 + 32rt + l, columns 32w + 8jq +
-    // 4h + jj.  bf16: the two lane halves trade quads (v_permlane32_swap) so
-    // that each lane owns 8 consecutive columns 32w + 16p + 8h .. + 7 of
-    // column pair p and stores them as 16 bytes (the two halves then write
-    // 32 contiguous bytes of each row).
+    // Output rows.  Lane (h, l) holds token t0 + 32rt + l, columns 32w + 8jq
+    // + 4h + jj.  bf16: the two lane halves trade quads (v_permlane32_swap)
+    // so that each lane owns 8 consecutive columns 32w + 16p + 8h .. + 7 of
+    // column pair p, stored as 16 bytes (the two halves then write 32
+    // contiguous bytes of each row) during the next sub-tile, or below after
+    // the last one.  fp32: four 16-byte stores per token tile, here.
+    if constexpr (kDefer) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int t = t0 + 32 * rt + l32;
-      if constexpr (sizeof(TOut) == 2) {
-        uint4 pk[2];
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           const int ja = 8 * pp, jb = 8 * pp + 4;  // quads jq = 2pp (kept by h = 0), 2pp + 1 (kept by h = 1)
@@ -510,14 +528,14 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
           const uint32_t b0 = pack_bf16x2(acc[rt][jb], acc[rt][jb + 1]), b1 = pack_bf16x2(acc[rt][jb + 2], acc[rt][jb + 3]);
           const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
           const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-          pk[pp] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+          pend[rt][pp] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
         }
-        if (t < t_end) {
-          bf16* orow = reinterpret_cast<bf16*>(ob) + (int64_t)t * D + 32 * w + 8 * hf;
-          *reinterpret_cast<uint4*>(orow) = pk[0];
-          *reinterpret_cast<uint4*>(orow + 16) = pk[1];
-        }
-      } else {
+      have_pend = true;
+      t_pend = t0;
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int t = t0 + 32 * rt + l32;
         if (t < t_end) {
           TOut* orow = ob + (int64_t)t * D + 32 * w + 4 * hf;
 #pragma unroll
@@ -525,6 +543,18 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
             *reinterpret_cast<f32x4*>(orow + 8 * jq) =
                 f32x4{acc[rt][4 * jq], acc[rt][4 * jq + 1], acc[rt][4 * jq + 2], acc[rt][4 * jq + 3]};
         }
+      }
+    }
+  }
+  if constexpr (kDefer) {
+    // The last sub-tile (possibly partial).
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int t = t_pend + 32 * rt + l32;
+      if (t < t_end) {
+        bf16* orow = reinterpret_cast<bf16*>(ob) + (int64_t)t * D + 32 * w + 8 * hf;
+        *reinterpret_cast<uint4*>(orow) = pend[rt][0];
+        *reinterpret_cast<uint4*>(orow + 16) = pend[rt][1];
       }
     }
   }
