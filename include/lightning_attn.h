@@ -112,7 +112,9 @@ int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const flo
                           size_t workspace_bytes, void* evt_begin, void* evt_end, void* stream);
 
 /* Chunk length the library uses for (B, H, N, block) when `chunk` is 0, or
- * `chunk` itself when it is valid; -1 on invalid arguments. */
+ * `chunk` itself when it is valid; -1 on invalid arguments.  The default
+ * starts at 16384 tokens and halves while B*H*ceil(N/chunk) < 2048, down to
+ * max(block, 256), then is capped at N rounded up to a whole block. */
 int64_t lightning_attn_fwd_chunk(int64_t B, int64_t H, int64_t N, int64_t block, int64_t chunk);
 
 /* Bytes of scratch lightning_attn_fwd_ex needs for these sizes (0 on invalid

@@ -40,9 +40,12 @@ bool valid_block(int64_t block) { return block == 64 || block == 128 || block ==
 // launch fewer than 1024 workgroups, never below max(block, 256), and never
 // longer than the sequence rounded up to a whole block.
 int64_t pick_chunk(int64_t B, int64_t H, int64_t N, int64_t block) {
-  int64_t L = 4096;
+  // Long chunks keep the chunk-state traffic small (each chunk moves four
+  // d x d fp32 states through HBM across the three passes); enough of them
+  // keep four rounds of resident workgroups (2 per CU) busy.
+  int64_t L = 16384;
   const int64_t floor_l = block > 256 ? block : 256;
-  while (L > floor_l && B * H * ceil_div(N, L) < 1024) L /= 2;
+  while (L > floor_l && B * H * ceil_div(N, L) < 2048) L /= 2;
   const int64_t cap = ceil_div(N, block) * block;
   if (L > cap) L = cap;
   return L;

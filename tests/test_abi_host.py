@@ -109,12 +109,14 @@ def test_workspace_checks(lib):
 
 
 def test_workspace_and_chunk_values(lib):
-    # million-token prefill: 64 heads, d=128, block 256 -> 4096-token chunks, 256 per head
-    assert lib.lightning_attn_fwd_chunk(1, 64, 1 << 20, 256, 0) == 4096
+    # million-token prefill: 64 heads, d=128, block 256 -> 16384-token chunks, 64 per head (4096 workgroups)
+    assert lib.lightning_attn_fwd_chunk(1, 64, 1 << 20, 256, 0) == 16384
     tbl = 64 * 320 * 4
-    assert lib.lightning_attn_fwd_workspace_bytes(1, 64, 1 << 20, 128, 256, 0) == tbl + 64 * 256 * 128 * 128 * 4
-    # 8192 tokens x 64 heads: chunks halve until >= 1024 workgroups
-    assert lib.lightning_attn_fwd_chunk(1, 64, 8192, 256, 0) == 512
+    assert lib.lightning_attn_fwd_workspace_bytes(1, 64, 1 << 20, 128, 256, 0) == tbl + 64 * 64 * 128 * 128 * 4
+    # batched: 4 x 64 heads x 65536 tokens -> halve once to reach 2048 workgroups
+    assert lib.lightning_attn_fwd_chunk(4, 64, 65536, 64, 0) == 8192
+    # 8192 tokens x 64 heads: chunks halve until >= 2048 workgroups (floor 256)
+    assert lib.lightning_attn_fwd_chunk(1, 64, 8192, 256, 0) == 256
     # tiny: floor at 256 tokens, capped by the block-rounded length
     assert lib.lightning_attn_fwd_chunk(1, 2, 1024, 64, 0) == 256
     assert lib.lightning_attn_fwd_chunk(1, 1, 100, 64, 0) == 128
