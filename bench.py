@@ -4,15 +4,20 @@
 
 One step = one prefill of the million-token workload (B=1, H=64,
 N=1,048,576, d=128, bf16 inputs and output, block 64, fp32 state), i.e. all
-of its kernels: decay-power table, chunk aggregates, chunk scan, chunk
-output.  Inputs are synthetic (seeded, generated on the device) and resident
-in HBM before timing starts.  Prints ONE JSON line:
+of its kernels: decay-power table, chunk aggregates of the heads that do not
+decay within a chunk, zero-start output pass of those that do (with their
+chunk aggregates), chunk scan, output pass from the chunk start states (the
+leading rows of each chunk for the decaying heads).  Inputs are synthetic
+(seeded, generated on the device) and resident in HBM before timing starts.
+Prints ONE JSON line:
 
   value          whole-job prefill tokens/s (B*N / step time)
-  roofline       the output kernel (the dominant one): algorithmic bytes per
-                 launch (1024 B per head-token: q, k, v read + o written, bf16)
-                 over its mean duration from HIP events recorded around it on
-                 its own stream, against 8 TB/s
+  roofline       the kernel that writes every output row (the dominant one:
+                 the zero-start output pass here, all 64 heads decay within a
+                 chunk): algorithmic bytes per launch (1024 B per head-token:
+                 q, k, v read + o written, bf16; plus the 4 d^2 bytes of each
+                 chunk aggregate it writes) over its mean duration from HIP
+                 events recorded around it on its own stream, against 8 TB/s
   cpu_baseline   the fp64 oracle (plain-C recurrence) on a bounded sample of
                  the same workload, on this host's cores
   decode         256 sequences x 64 heads x d=128 decode step, 1000 in-place
@@ -51,6 +56,26 @@ def _hip():
     lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
     lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
     return lib
+
+
+def decaying_heads(lam, chunk):
+    """Which heads the library puts through its zero-start pass (bf16 inputs,
+    block 64): those whose chunk-start state weighs at most 2^-30 of itself
+    (lam^(r+1)) from row r = carry span on, with the span rounded up to whole
+    64-token sub-tiles and at most a third of the chunk.  The kernels' rule,
+    restated here for the byte count only."""
+    out = []
+    for x in lam:
+        x = float(x)
+        if x == 0.0:
+            span = 0
+        elif not (0.0 < x < 1.0):
+            span = None
+        else:
+            t = 20.79441541679836 / -math.log(x)  # 30 ln 2 / -ln lam
+            span = None if not t < 1e9 else ((math.ceil(t) + 63) // 64) * 64
+        out.append(span is not None and 3 * span <= chunk)
+    return out
 
 
 def _src_hash():
@@ -118,17 +143,22 @@ def bench_prefill(args, dev):
         hip.hipEventDestroy(e)
     kern_ms = sum(kern) / len(kern)
     ht = B * H * N
-    alg_bytes = BYTES_PER_HT * ht
+    fast = sum(decaying_heads(decay_lambdas(H), chunk)) if block == 64 else H
+    nc = -(-N // chunk)
+    if block == 64:  # zero-start pass: its heads' q, k, v, o and chunk aggregates
+        alg_bytes = BYTES_PER_HT * B * fast * N + 4 * d * d * B * fast * nc
+    else:            # output pass over every head
+        alg_bytes = BYTES_PER_HT * ht
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    traffic = _traffic(alg_bytes)
+    traffic = _traffic(alg_bytes) if block == 64 else None  # the counters were taken at block 64
     res = dict(
-        B=B, H=H, N=N, d=d, block=block, chunk=chunk,
+        B=B, H=H, N=N, d=d, block=block, chunk=chunk, zero_start_heads=fast,
         ms_per_step=ms_step,
         tokens_per_s=B * N / (ms_step * 1e-3),
         output_kernel_ms=kern_ms,
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS, traffic=traffic),
-        step_hbm_frac=alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        step_hbm_frac=BYTES_PER_HT * ht / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         mfma_alg_frac=FLOP_PER_HT * ht / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
     )
     sample = None
@@ -180,7 +210,7 @@ def cpu_baseline(sample, args):
     except AttributeError:
         cores = os.cpu_count() or 1
     threads = max(1, min(16, cores))
-    heads = threads
+    heads = min(q.shape[1], 2 * threads)
     tokens = min(args.cpu_tokens, q.shape[2])
     hs = lambda t: t[0, :heads, :tokens].float().cpu().numpy()
     qs, ks, vs = hs(q), hs(k), hs(v)
@@ -206,7 +236,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", dest="decode", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
-    ap.add_argument("--cpu-tokens", type=int, default=131072)
+    ap.add_argument("--cpu-tokens", type=int, default=1 << 20)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a known-size "
                          "reference for the HBM byte counters)")
@@ -252,6 +282,7 @@ def main():
                    "block": prefill["block"], "chunk": prefill["chunk"]},
         "roofline": prefill["roofline"],
         "output_kernel_ms": prefill["output_kernel_ms"],
+        "zero_start_heads": prefill["zero_start_heads"],
         "step_hbm_frac": prefill["step_hbm_frac"],
         "mfma_alg_frac": prefill["mfma_alg_frac"],
         "cpu_baseline": cpu,

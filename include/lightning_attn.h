@@ -70,6 +70,14 @@ extern "C" {
  *   block     : intra-block length of the blockwise algorithm, one of
  *               {64, 128, 256}.  The result does not depend on it beyond
  *               rounding.
+ * Decays are meant to lie in [0, 1].  With bf16 inputs and block 64, a head
+ * whose chunk-start state weighs at most 2^-30 of itself (lam^(r+1)) from
+ * row r = span on, span = ceil(30 ln 2 / -ln lam) rounded up to a multiple
+ * of 64 and at most a third of the chunk, is computed per chunk from a zero
+ * start state, and only rows r < span of each chunk are computed again from
+ * the true start state: in the other rows the start state's term
+ * lam^(r+1) q_r S_start, at most 2^-30 of q_r S_start, is left out.  Every
+ * other head, and every other dtype and block, is computed without omission.
  * Scratch (decay-power table and per-chunk states, see
  * lightning_attn_fwd_workspace_bytes) is allocated stream-ordered with
  * hipMallocAsync/hipFreeAsync on `stream`.
@@ -103,8 +111,10 @@ int lightning_attn_fwd_bf16_f32out(const void* q, const void* k, const void* v, 
  *               after the enqueued work completes; NULL = allocate
  *               stream-ordered as lightning_attn_fwd does.
  *   evt_begin, evt_end : optional hipEvent_t (as void*), recorded on `stream`
- *               immediately before and after the output kernel (the
- *               dominant kernel), for timing; NULL = not recorded.
+ *               immediately before and after the kernel that writes every
+ *               output row (the dominant kernel): the zero-start pass with
+ *               bf16 inputs and block 64, the output pass otherwise; for
+ *               timing; NULL = not recorded.
  */
 int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const float* decay, void* out,
                           const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,

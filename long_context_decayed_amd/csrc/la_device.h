@@ -31,6 +31,26 @@ __device__ __forceinline__ double pow_int(double x, int e) {
   return r;
 }
 
+// Rows after a chunk start whose outputs still feel the chunk's start state
+// by more than 2^-30 of its own weight: the state enters row r scaled by
+// lam^(r+1), and lam^(r+1) <= 2^-30 once r + 1 >= 30 ln 2 / -ln lam.  Rounded
+// up to whole 64-token sub-tiles; 0 for lam = 0; INT32_MAX for lam >= 1 (no
+// decay).  Computed in double so that every kernel classifies a head alike.
+__device__ __forceinline__ int carry_span(float lam) {
+  if (lam == 0.0f) return 0;
+  if (!(lam > 0.0f && lam < 1.0f)) return 0x7fffffff;  // negative, >= 1 or NaN: never dropped
+  const double t = 20.79441541679836 / -log((double)lam);  // 30 ln 2 / -ln lam
+  if (!(t < 1.0e9)) return 0x7fffffff;
+  const int64_t r = (int64_t)ceil(t);
+  return (int)(((r + 63) / 64) * 64);
+}
+
+// A head decays within its chunk of L tokens when 3 carry_span <= L.  Such a
+// head's chunk outputs are computed from a zero start state in one pass that
+// also yields the chunk aggregates, and only the first carry_span rows of
+// each chunk are then redone from the true start state.
+__device__ __forceinline__ bool decays_within_chunk(int span, int L) { return 3ll * (long long)span <= (long long)L; }
+
 // MFMA traits.  One instruction contracts KW elements; every lane contributes
 // EPL of them (lanes 0-31 and 32-63 split the contraction).  A and B use the
 // same (lane half, element) -> k correspondence, so any fixed permutation of

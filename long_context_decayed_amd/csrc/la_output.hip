@@ -20,6 +20,12 @@
 //   B  la_chunk_scan  : per (batch, head), S <- kv_in; for c: Sstart_c = S,
 //                       S = lam^(L_c) S + U_c; kv_out = S (fp32)         [la_state.hip]
 //   C  la_chunk_output: per chunk, the block loop above from Sstart_c (MFMA) [here]
+// With bf16 inputs and block 64, a head that decays within its chunk skips
+// pass A: before pass B, la_chunk_output64 in zero-start mode computes its
+// chunks from a zero start state, writing every output row and, as the state
+// reached at the chunk end, U_c; pass C then redoes only the leading rows of
+// its chunks (those on which the start state still weighs more than 2^-30 of
+// itself) from Sstart_c.  Q, K and V of such a head are read about once.
 //
 // Precision recipe (bf16 inputs): products of two bf16 inputs are exact in the
 // fp32 MFMA accumulator.  Quantities formed in fp32 that feed an MFMA are
@@ -286,12 +292,30 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 //     requested after that barrier, ahead of this sub-tile's output stores,
 //     and waited for at the end of the next phase 1.
 // Two workgroups per CU (80 KiB of LDS each).
-template <typename TOut, int D>
+//
+// Two modes, by how the chunk's start state enters:
+//   kZeroStart  heads that decay within their chunk (decays_within_chunk):
+//               every row of the chunk from a zero start state, and the
+//               state reached at the chunk end, which is then the chunk
+//               aggregate U_c, stored to `states` for the scan.  Other heads
+//               return at once.
+//   kFromStart  the chunk from its true start state Sstart_c (read from
+//               `states`): every row for the other heads; for decaying heads
+//               only the first carry_span rows, the only ones on which the
+//               start state weighs more than 2^-30 of itself, and nothing for
+//               chunk 0 when there is no initial state (its start state is
+//               zero).  Workgroups run in reverse order so that the longest
+//               ones (heads of slowest decay, last in the head order of the
+//               usual slope schedules) start first.
+enum { kZeroStart = 0, kFromStart = 1 };
+
+template <typename TOut, int D, int MODE>
 __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                               const bf16* __restrict__ v, TOut* __restrict__ o,
+                                                              const float* __restrict__ decay,
                                                               const float* __restrict__ tbl_all,
-                                                              const float* __restrict__ sstart, int H, int N, int L,
-                                                              int nc, int tbl_stride) {
+                                                              float* __restrict__ states, int H, int N, int L,
+                                                              int nc, int tbl_stride, int has_kv_in) {
   typedef Mfma<bf16> M;
   typedef M::op_t op_t;
   constexpr int NW = D / 32;
@@ -308,15 +332,27 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
+  const int blk = MODE == kFromStart ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+  const int bh = blk / nc, c = blk - (blk / nc) * nc;
   const int hh = bh % H;
+  const int span = carry_span(decay[hh]);
+  const bool decaying = decays_within_chunk(span, L);
+  const int t_begin = c * L;
+  int t_end = min(N, t_begin + L);
+  if constexpr (MODE == kZeroStart) {
+    if (!decaying) return;
+  } else {
+    if (decaying) {
+      if (c == 0 && !has_kv_in) return;
+      t_end = min(t_end, t_begin + span);
+      if (t_end <= t_begin) return;
+    }
+  }
   const int64_t base = (int64_t)bh * N * D;
   const bf16* qb = q + base;
   const bf16* kb = k + base;
   const bf16* vb = v + base;
   TOut* ob = o + base;
-  const int t_begin = c * L;
-  const int t_end = min(N, t_begin + L);
   const int col = 32 * w + l32;
   const float* tb = tbl_all + (int64_t)hh * tbl_stride;  // lam^e, e <= 64
 
@@ -337,6 +373,15 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   rf[0] = tb[l32 + 1];
   rf[1] = tb[l32 + 33];
   const float d64 = tb[64];
+  // Zero-start mode hands on the exact chunk-end state, so its last sub-tile,
+  // when partial (n < 64 tokens, only at the end of the sequence), decays the
+  // state by lam^n and weights token s by lam^(n-1-s): lam^e for e < 64 is
+  // kept one per lane and fetched by lane shuffle.
+  float tlane = 0.0f, d_last = 0.0f;
+  if constexpr (MODE == kZeroStart) {
+    tlane = tb[lane];
+    d_last = tb[(t_end - t_begin) - kSub * ((t_end - t_begin - 1) / kSub)];
+  }
   for (int e = tid; e < 4 * 64; e += NW * 64) {
     const int jq = e >> 6, ln = e & 63;
     const int dd = (ln & 31) - 4 * (ln >> 5) - 8 * jq;
@@ -348,8 +393,11 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   // value column col, where pf swaps bits 2 and 3:
   //   pf(crow(j, h)) = 16(j >> 3) + 8h + 4((j >> 2) & 1) + (j & 3).
   f32x16 S[NRT];
-  {
-    const float* src = sstart + ((int64_t)bh * nc + c) * D * D + col;
+  if constexpr (MODE == kZeroStart) {
+#pragma unroll
+    for (int kt = 0; kt < NRT; ++kt) S[kt] = zero16();
+  } else {
+    const float* src = states + ((int64_t)bh * nc + c) * D * D + col;
 #pragma unroll
     for (int kt = 0; kt < NRT; ++kt)
 #pragma unroll
@@ -412,7 +460,10 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
           }
         }
       }
-      S[kt] *= d64;
+      if constexpr (MODE == kZeroStart)
+        S[kt] *= more ? d64 : d_last;
+      else
+        S[kt] *= d64;
       if constexpr (kDefer) {
         // The pending sub-tile is a full one (only the last can be partial).
         static_assert(4 % NRT == 0, "whole stores per step");
@@ -487,20 +538,23 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
     }
 
     // State update: S += sum_s lam^(63-s) k_s^T v_s, tokens s = 16kk + crow(i, h).
+    // A partial last sub-tile of zero-start mode is added after the loop.
+    if (!(MODE == kZeroStart && !more && t_end - t0 < kSub)) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const op_t vraw = ld_tr8<D, false>(Vs, 16 * kk, 32 * w, lane);
-      const float u = tb[48 - 16 * kk];
-      float x[8];
+      for (int kk = 0; kk < 4; ++kk) {
+        const op_t vraw = ld_tr8<D, false>(Vs, 16 * kk, 32 * w, lane);
+        const float u = tb[48 - 16 * kk];
+        float x[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * (ul[i] * u);
-      op_t bhi, blo;
-      M::split(x, bhi, blo);
+        for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * (ul[i] * u);
+        op_t bhi, blo;
+        M::split(x, bhi, blo);
 #pragma unroll
-      for (int kt = 0; kt < NRT; ++kt) {
-        const op_t a = ld_tr8<D, true>(Kt, 16 * kk, 32 * kt, lane);
-        S[kt] = M::mma(a, bhi, S[kt]);
-        S[kt] = M::mma(a, blo, S[kt]);
+        for (int kt = 0; kt < NRT; ++kt) {
+          const op_t a = ld_tr8<D, true>(Kt, 16 * kk, 32 * kt, lane);
+          S[kt] = M::mma(a, bhi, S[kt]);
+          S[kt] = M::mma(a, blo, S[kt]);
+        }
       }
     }
 
@@ -548,15 +602,50 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   }
   if constexpr (kDefer) {
     // The last sub-tile (possibly partial).
+    if (have_pend) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int t = t_pend + 32 * rt + l32;
-      if (t < t_end) {
-        bf16* orow = reinterpret_cast<bf16*>(ob) + (int64_t)t * D + 32 * w + 8 * hf;
-        *reinterpret_cast<uint4*>(orow) = pend[rt][0];
-        *reinterpret_cast<uint4*>(orow + 16) = pend[rt][1];
+      for (int rt = 0; rt < 2; ++rt) {
+        const int t = t_pend + 32 * rt + l32;
+        if (t < t_end) {
+          bf16* orow = reinterpret_cast<bf16*>(ob) + (int64_t)t * D + 32 * w + 8 * hf;
+          *reinterpret_cast<uint4*>(orow) = pend[rt][0];
+          *reinterpret_cast<uint4*>(orow + 16) = pend[rt][1];
+        }
       }
     }
+  }
+  if constexpr (MODE == kZeroStart) {
+    // Partial last sub-tile (n < 64 tokens, still in Vs and Kt): S += sum_{s<n}
+    // lam^(n-1-s) k_s^T v_s; S was decayed by lam^n in its phase 1.
+    const int n = (t_end - t_begin) - kSub * ((t_end - t_begin - 1) / kSub);
+    if (n < kSub) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const op_t vraw = ld_tr8<D, false>(Vs, 16 * kk, 32 * w, lane);
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int e = n - 1 - (16 * kk + crow(i, hf));
+          const float f = __shfl(tlane, e < 0 ? 0 : e);
+          x[i] = e >= 0 ? (float)vraw[i] * f : 0.0f;
+        }
+        op_t bhi, blo;
+        M::split(x, bhi, blo);
+#pragma unroll
+        for (int kt = 0; kt < NRT; ++kt) {
+          const op_t a = ld_tr8<D, true>(Kt, 16 * kk, 32 * kt, lane);
+          S[kt] = M::mma(a, bhi, S[kt]);
+          S[kt] = M::mma(a, blo, S[kt]);
+        }
+      }
+    }
+    // The chunk-end state from a zero start: U_c, natural (feature, column) order.
+    float* dst = states + ((int64_t)bh * nc + c) * D * D + col;
+#pragma unroll
+    for (int kt = 0; kt < NRT; ++kt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        dst[(32 * kt + 16 * (j >> 3) + 8 * hf + 4 * ((j >> 2) & 1) + (j & 3)) * D] = S[kt][j];
   }
 }
 
@@ -564,27 +653,56 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
 // Host-side launcher: the output pass on `st`, bracketed by the optional
 // timing events.
 
+// The events bracket the kernel that writes every output row: the
+// zero-start pass when there is one (bf16 inputs, block 64), else this one.
 template <typename TIn, typename TOut, int D, int BLK>
 static hipError_t launch_output_t(const PrefillArgs& a, hipStream_t st) {
+  const int BH = (int)(a.B * a.H);
+  const int nc = a.nc;
+  const bool timed = !a.zero_start;
+  if (timed && a.evt_begin) {
+    hipError_t e = hipEventRecord((hipEvent_t)a.evt_begin, st);
+    if (e != hipSuccess) return e;
+  }
+  if constexpr (BLK == 64 && sizeof(TIn) == 2)
+    hipLaunchKernelGGL((la_chunk_output64<TOut, D, kFromStart>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, a.decay,
+                       (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride,
+                       a.kv_in != nullptr ? 1 : 0);
+  else
+    hipLaunchKernelGGL((la_chunk_output<TIn, TOut, D, BLK>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (TOut*)a.out, (const float*)a.tbl,
+                       (const float*)a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
+  if (timed && a.evt_end) {
+    hipError_t e = hipEventRecord((hipEvent_t)a.evt_end, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipGetLastError();
+}
+
+template <typename TOut, int D>
+static hipError_t launch_zero_start_t(const PrefillArgs& a, hipStream_t st) {
   const int BH = (int)(a.B * a.H);
   const int nc = a.nc;
   if (a.evt_begin) {
     hipError_t e = hipEventRecord((hipEvent_t)a.evt_begin, st);
     if (e != hipSuccess) return e;
   }
-  if constexpr (BLK == 64 && sizeof(TIn) == 2)
-    hipLaunchKernelGGL((la_chunk_output64<TOut, D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, (const float*)a.tbl,
-                       (const float*)a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
-  else
-    hipLaunchKernelGGL((la_chunk_output<TIn, TOut, D, BLK>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
-                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (TOut*)a.out, (const float*)a.tbl,
-                       (const float*)a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
+  hipLaunchKernelGGL((la_chunk_output64<TOut, D, kZeroStart>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, a.decay,
+                     (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride,
+                     a.kv_in != nullptr ? 1 : 0);
   if (a.evt_end) {
     hipError_t e = hipEventRecord((hipEvent_t)a.evt_end, st);
     if (e != hipSuccess) return e;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_zero_start_pass(const PrefillArgs& a, hipStream_t st) {
+  if (!a.zero_start) return hipErrorInvalidValue;
+  if (a.out_dtype == kBF16) return a.d == 128 ? launch_zero_start_t<bf16, 128>(a, st) : launch_zero_start_t<bf16, 64>(a, st);
+  return a.d == 128 ? launch_zero_start_t<float, 128>(a, st) : launch_zero_start_t<float, 64>(a, st);
 }
 
 template <typename TIn, typename TOut, int D>

@@ -132,11 +132,14 @@ __global__ __launch_bounds__(D * 2, sizeof(TIn) == 2 ? 3 : 1) void la_chunk_stat
 //   Token s = 16kk + crow(i, h) of a full sub-tile (the row order of the
 // transpose-read operands): lam^(63-s) u = ul[i] * (lam^(48-16kk) u) with the
 // per-lane ul[i] = lam^(15 - crow(i, h)).
+//   With skip_decaying set, heads that decay within their chunk return at
+// once: the zero-start output pass produces their aggregates.
 template <int D>
 __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restrict__ k, const bf16* __restrict__ v,
                                                              const float* __restrict__ decay,
                                                              const float* __restrict__ tbl_all, float* __restrict__ ws,
-                                                             int H, int N, int L, int nc, int tbl_stride) {
+                                                             int H, int N, int L, int nc, int tbl_stride,
+                                                             int skip_decaying) {
   typedef Mfma<bf16> M;
   typedef M::op_t op_t;
   constexpr int NW = D / 32;
@@ -148,6 +151,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
   const int hh = bh % H;
+  if (skip_decaying && decays_within_chunk(carry_span(decay[hh]), L)) return;
   const int64_t base = (int64_t)bh * N * D;
   const bf16* kb = k + base;
   const bf16* vb = v + base;
@@ -283,30 +287,37 @@ __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ d
 }
 
 // ---------------------------------------------------------------------------
-// Host-side launcher: table, pass A, pass B on `st`.
+// Host-side launchers on `st`: the table and pass A; pass B.
 
 template <typename TIn, int D>
-static hipError_t launch_state_t(const PrefillArgs& a, hipStream_t st) {
+static hipError_t launch_aggregate_t(const PrefillArgs& a, hipStream_t st) {
   const int BH = (int)(a.B * a.H);
   const int nc = a.nc;
   hipLaunchKernelGGL(la_decay_table, dim3((unsigned)a.H), dim3(256), 0, st, a.decay, a.tbl, a.tbl_stride);
   if constexpr (sizeof(TIn) == 2)
     hipLaunchKernelGGL((la_chunk_state64<D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st, (const bf16*)a.k,
                        (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc,
-                       a.tbl_stride);
+                       a.tbl_stride, a.zero_start ? 1 : 0);
   else
     hipLaunchKernelGGL((la_chunk_state<TIn, D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st, (const TIn*)a.k,
                        (const TIn*)a.v, (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc,
                        a.tbl_stride);
-  const int64_t threads = (int64_t)BH * D * D / 4;
-  hipLaunchKernelGGL(la_chunk_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a.decay, a.states,
-                     a.kv_in, a.kv_out, BH, (int)a.H, (int)a.N, (int)a.L, nc, D);
   return hipGetLastError();
 }
 
-hipError_t launch_state_passes(const PrefillArgs& a, hipStream_t st) {
-  if (a.in_dtype == kBF16) return a.d == 128 ? launch_state_t<bf16, 128>(a, st) : launch_state_t<bf16, 64>(a, st);
-  return a.d == 128 ? launch_state_t<float, 128>(a, st) : launch_state_t<float, 64>(a, st);
+hipError_t launch_aggregate_pass(const PrefillArgs& a, hipStream_t st) {
+  if (a.in_dtype == kBF16)
+    return a.d == 128 ? launch_aggregate_t<bf16, 128>(a, st) : launch_aggregate_t<bf16, 64>(a, st);
+  return a.d == 128 ? launch_aggregate_t<float, 128>(a, st) : launch_aggregate_t<float, 64>(a, st);
+}
+
+hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st) {
+  const int BH = (int)(a.B * a.H);
+  const int D = (int)a.d;
+  const int64_t threads = (int64_t)BH * D * D / 4;
+  hipLaunchKernelGGL(la_chunk_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a.decay, a.states,
+                     a.kv_in, a.kv_out, BH, (int)a.H, (int)a.N, (int)a.L, a.nc, D);
+  return hipGetLastError();
 }
 
 }  // namespace la

@@ -111,6 +111,12 @@ def test_million_token_slices(dev, million, block):
     out = la.fwd(q, k, v, lam_t, kv_out=kv, block=block, out_dtype=torch.float32)
     torch.cuda.synchronize()
     e1, e2, _, _ = _slice_checks(q, k, v, lam, dev, out, t0, t0 + 8192, block)
+    # A slice across a chunk start: the rows whose outputs still depend on
+    # the chunk's start state (up to about 5400 for the slowest head here).
+    L = la.chunk_for(1, 64, N, block)
+    tb = 5 * L - 2048
+    say("million-token layer block", block, "chunk", L, "slice across the chunk start", 5 * L)
+    g1, g2, _, _ = _slice_checks(q, k, v, lam, dev, out, tb, tb + 8192, block)
     say("million-token layer block", block, "final slice")
     f1, f2, s_pref, s_win = _slice_checks(q, k, v, lam, dev, out, N - 8192, N, block)
     tol.assert_state(host(kv), s_pref, "kv_out vs oracle from GPU prefix state")
@@ -119,7 +125,8 @@ def test_million_token_slices(dev, million, block):
     o16 = la.fwd(q, k, v, lam_t, block=block)
     torch.cuda.synchronize()
     assert torch.equal(out[:, :, t0:t0 + 8192].to(torch.bfloat16), o16[:, :, t0:t0 + 8192])
-    print("interior %.3e / %.3e, final %.3e / %.3e (max|err|/RMS)" % (e1, e2, f1, f2))
+    print("interior %.3e / %.3e, chunk start %.3e / %.3e, final %.3e / %.3e (max|err|/RMS)" % (
+        e1, e2, g1, g2, f1, f2))
 
 
 def test_lambda_one_million_tokens(dev):

@@ -77,11 +77,14 @@ def test_ternary_exact_fp32(dev):
     assert np.array_equal(host(kv).astype(np.float64), s_ref)
 
 
+@pytest.mark.parametrize("lams", ["one", "zero_one"])
 @pytest.mark.parametrize("block", [64, 128, 256])
-def test_ternary_exact_bf16_f32out(dev, block):
-    say("ternary bf16->f32 lam=1 B1 H2 N1024 d128 block", block)
+def test_ternary_exact_bf16_f32out(dev, block, lams):
+    # lam = 0 keeps only the diagonal term q_r.k_r v_r (0^0 = 1), still exact;
+    # with block 64 that head takes the zero-start pass with no leading rows.
+    say("ternary bf16->f32 lam", lams, "B1 H2 N1024 d128 block", block)
     q, k, v = ternary_device(1, 2, 1024, 128, seed=2, device=dev, dtype=torch.bfloat16)
-    lam = lam_for(2, "one")
+    lam = lam_for(2, "one") if lams == "one" else np.array([0.0, 1.0], dtype=np.float32)
     out, kv = _run(q, k, v, lam, dev, block, out_dtype=torch.float32, chunk=256 if block < 256 else 512)
     o_ref, s_ref = oracle(host(q), host(k), host(v), lam)
     assert np.array_equal(host(out).astype(np.float64), o_ref)
@@ -179,6 +182,51 @@ def test_bf16_state_in_place(dev):
     o_ref, s_ref = oracle(host(q), host(k), host(v), lam, s_host)
     tol.assert_bf16_f32out(host(out), o_ref)
     tol.assert_state(host(s0), s_ref)
+
+
+# --- heads that decay within a chunk, next to heads that do not --------------
+# Chunk 1024, block 64, bf16 inputs.  A head whose start-state weight lam^(r+1)
+# falls below 2^-30 within a third of a chunk (here lam <= 0.9) is computed
+# from a zero chunk-start state and redone from the true start state on the
+# leading rows only; the others take the three-pass path.  Each head is held
+# to the tolerance on its own RMS, so the fast-decaying heads are not hidden
+# behind the large outputs of the lam ~ 1 heads.
+
+MIXED_LAMS = np.array([0.0, 1e-3, 0.3, 0.7, 0.9, 0.97, 0.999, 1.0], dtype=np.float32)
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n", [1, 63, 700, 2048, 2048 + 100, 3000 + 37])
+def test_bf16_mixed_decays(dev, n, d, with_state):
+    B, H = 2, 8
+    say("bf16 mixed decays B2 H8 N", n, "d", d, "kv_in", with_state, "chunk 1024 block 64")
+    q, k, v = qkv_device(B, H, n, d, seed=50 + n, device=dev)
+    s0 = state_device(B, H, d, seed=50 + n, device=dev) if with_state else None
+    o32, kv = _run(q, k, v, MIXED_LAMS, dev, 64, out_dtype=torch.float32, kv_in=s0, chunk=1024)
+    o16, kv16 = _run(q, k, v, MIXED_LAMS, dev, 64, out_dtype=torch.bfloat16, kv_in=s0, chunk=1024)
+    o_ref, s_ref = oracle(host(q), host(k), host(v), MIXED_LAMS, None if s0 is None else host(s0).astype(np.float64))
+    o_h, kv_h = host(o32), host(kv)
+    for h in range(H):
+        tol.assert_bf16_f32out(o_h[:, h], o_ref[:, h], "O head %d (lam %g)" % (h, MIXED_LAMS[h]))
+        tol.assert_state(kv_h[:, h], s_ref[:, h], "kv_out head %d (lam %g)" % (h, MIXED_LAMS[h]))
+    assert torch.equal(o32.to(torch.bfloat16), o16), "bf16 out must be RNE(fp32 out)"
+    assert torch.equal(kv, kv16)
+
+
+def test_bf16_mixed_decays_chunk_invariance(dev):
+    # The split between the two paths moves with the chunk size; the results
+    # must not (up to rounding).
+    say("bf16 mixed decays B1 H8 N5000 d128: chunk 256 / 1024 / 4096")
+    q, k, v = qkv_device(1, 8, 5000, 128, seed=60, device=dev)
+    s0 = state_device(1, 8, 128, seed=60, device=dev)
+    o_ref, s_ref = oracle(host(q), host(k), host(v), MIXED_LAMS, host(s0).astype(np.float64))
+    for chunk in (256, 1024, 4096):
+        o32, kv = _run(q, k, v, MIXED_LAMS, dev, 64, out_dtype=torch.float32, kv_in=s0, chunk=chunk)
+        o_h, kv_h = host(o32), host(kv)
+        for h in range(8):
+            tol.assert_bf16_f32out(o_h[:, h], o_ref[:, h], "O chunk %d head %d" % (chunk, h))
+            tol.assert_state(kv_h[:, h], s_ref[:, h], "kv_out chunk %d head %d" % (chunk, h))
 
 
 # --- long-range carries: lam = 1 and just below 1 -----------------------------
