@@ -5,19 +5,18 @@
 One step = one prefill of the million-token workload (B=1, H=64,
 N=1,048,576, d=128, bf16 inputs and output, block 64, fp32 state), i.e. all
 of its kernels: decay-power table, chunk aggregates of the heads that do not
-decay within a chunk, zero-start output pass of those that do (with their
-chunk aggregates), chunk scan, output pass from the chunk start states (the
-leading rows of each chunk for the decaying heads).  Inputs are synthetic
-(seeded, generated on the device) and resident in HBM before timing starts.
-Prints ONE JSON line:
+decay within a chunk, warm-start output pass of those that do, chunk scan,
+output pass from the chunk start states.  Inputs are synthetic (seeded,
+generated on the device) and resident in HBM before timing starts.  Prints
+ONE JSON line:
 
   value          whole-job prefill tokens/s (B*N / step time)
   roofline       the kernel that writes every output row (the dominant one:
-                 the zero-start output pass here, all 64 heads decay within a
-                 chunk): algorithmic bytes per launch (1024 B per head-token:
-                 q, k, v read + o written, bf16; plus the 4 d^2 bytes of each
-                 chunk aggregate it writes) over its mean duration from HIP
-                 events recorded around it on its own stream, against 8 TB/s
+                 the warm-start output pass here, all 64 heads decay within a
+                 chunk): algorithmic bytes per launch (1024 B per head-token of
+                 its heads: q, k, v read + o written, bf16) over its mean
+                 duration from HIP events recorded around it on its own
+                 stream, against 8 TB/s
   cpu_baseline   the fp64 oracle (plain-C recurrence) on a bounded sample of
                  the same workload, on this host's cores
   decode         256 sequences x 64 heads x d=128 decode step, 1000 in-place
@@ -59,7 +58,7 @@ def _hip():
 
 
 def decaying_heads(lam, chunk):
-    """Which heads the library puts through its zero-start pass (bf16 inputs,
+    """Which heads the library puts through its warm-start pass (bf16 inputs,
     block 64): those whose chunk-start state weighs at most 2^-30 of itself
     (lam^(r+1)) from row r = carry span on, with the span rounded up to whole
     64-token sub-tiles and at most a third of the chunk.  The kernels' rule,
@@ -144,15 +143,14 @@ def bench_prefill(args, dev):
     kern_ms = sum(kern) / len(kern)
     ht = B * H * N
     fast = sum(decaying_heads(decay_lambdas(H), chunk)) if block == 64 else H
-    nc = -(-N // chunk)
-    if block == 64:  # zero-start pass: its heads' q, k, v, o and chunk aggregates
-        alg_bytes = BYTES_PER_HT * B * fast * N + 4 * d * d * B * fast * nc
+    if block == 64:  # warm-start pass: its heads' q, k, v read and o written
+        alg_bytes = BYTES_PER_HT * B * fast * N
     else:            # output pass over every head
         alg_bytes = BYTES_PER_HT * ht
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     traffic = _traffic(alg_bytes) if block == 64 else None  # the counters were taken at block 64
     res = dict(
-        B=B, H=H, N=N, d=d, block=block, chunk=chunk, zero_start_heads=fast,
+        B=B, H=H, N=N, d=d, block=block, chunk=chunk, warm_start_heads=fast,
         ms_per_step=ms_step,
         tokens_per_s=B * N / (ms_step * 1e-3),
         output_kernel_ms=kern_ms,
@@ -282,7 +280,7 @@ def main():
                    "block": prefill["block"], "chunk": prefill["chunk"]},
         "roofline": prefill["roofline"],
         "output_kernel_ms": prefill["output_kernel_ms"],
-        "zero_start_heads": prefill["zero_start_heads"],
+        "warm_start_heads": prefill["warm_start_heads"],
         "step_hbm_frac": prefill["step_hbm_frac"],
         "mfma_alg_frac": prefill["mfma_alg_frac"],
         "cpu_baseline": cpu,

@@ -71,13 +71,14 @@ extern "C" {
  *               {64, 128, 256}.  The result does not depend on it beyond
  *               rounding.
  * Decays are meant to lie in [0, 1].  With bf16 inputs and block 64, a head
- * whose chunk-start state weighs at most 2^-30 of itself (lam^(r+1)) from
- * row r = span on, span = ceil(30 ln 2 / -ln lam) rounded up to a multiple
- * of 64 and at most a third of the chunk, is computed per chunk from a zero
- * start state, and only rows r < span of each chunk are computed again from
- * the true start state: in the other rows the start state's term
- * lam^(r+1) q_r S_start, at most 2^-30 of q_r S_start, is left out.  Every
- * other head, and every other dtype and block, is computed without omission.
+ * with span = ceil(30 ln 2 / -ln lam), rounded up to a multiple of 64, at
+ * most a third of the chunk (lam^span <= 2^-30) is computed per chunk from
+ * the state that the span tokens before the chunk build from zero: at token
+ * t of a chunk the state S_(c0-span-1) from before those tokens is left out
+ * of its term lam^(t-c0+span+1) S_(c0-span-1), at most 2^-30 of that state
+ * (c0 = the chunk's first token; the first chunk starts from kv_in exactly).
+ * Every other head, and every other dtype and block, is computed without
+ * omission.
  * Scratch (decay-power table and per-chunk states, see
  * lightning_attn_fwd_workspace_bytes) is allocated stream-ordered with
  * hipMallocAsync/hipFreeAsync on `stream`.
@@ -112,7 +113,7 @@ int lightning_attn_fwd_bf16_f32out(const void* q, const void* k, const void* v, 
  *               stream-ordered as lightning_attn_fwd does.
  *   evt_begin, evt_end : optional hipEvent_t (as void*), recorded on `stream`
  *               immediately before and after the kernel that writes every
- *               output row (the dominant kernel): the zero-start pass with
+ *               output row (the dominant kernel): the warm-start pass with
  *               bf16 inputs and block 64, the output pass otherwise; for
  *               timing; NULL = not recorded.
  */

@@ -150,11 +150,11 @@ int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const flo
   a.tbl = (float*)ws;
   a.tbl_stride = (int)tbl_stride_for(block);
   a.states = (float*)((char*)ws + tbl_bytes);
-  a.zero_start = a.in_dtype == la::kBF16 && block == 64;
+  a.warm_start = a.in_dtype == la::kBF16 && block == 64;
   a.evt_begin = evt_begin;
   a.evt_end = evt_end;
   hipError_t e = la::launch_aggregate_pass(a, st);
-  if (e == hipSuccess && a.zero_start) e = la::launch_zero_start_pass(a, st);
+  if (e == hipSuccess && a.warm_start) e = la::launch_warm_start_pass(a, st);
   if (e == hipSuccess) e = la::launch_scan_pass(a, st);
   if (e == hipSuccess) e = la::launch_output_pass(a, st);
   if (!workspace) {

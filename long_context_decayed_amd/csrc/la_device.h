@@ -45,10 +45,9 @@ __device__ __forceinline__ int carry_span(float lam) {
   return (int)(((r + 63) / 64) * 64);
 }
 
-// A head decays within its chunk of L tokens when 3 carry_span <= L.  Such a
-// head's chunk outputs are computed from a zero start state in one pass that
-// also yields the chunk aggregates, and only the first carry_span rows of
-// each chunk are then redone from the true start state.
+// A head decays within its chunk of L tokens when 3 carry_span <= L.  Each
+// chunk of such a head is then computed from the state that the carry_span
+// tokens before it build from zero, with no scan over chunks.
 __device__ __forceinline__ bool decays_within_chunk(int span, int L) { return 3ll * (long long)span <= (long long)L; }
 
 // MFMA traits.  One instruction contracts KW elements; every lane contributes

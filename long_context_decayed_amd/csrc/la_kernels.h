@@ -22,21 +22,22 @@ struct PrefillArgs {
   float* tbl;      // workspace: [H][tbl_stride] decay powers
   int tbl_stride;  // >= block + 1
   float* states;   // workspace: [B*H][nc][d][d]
-  bool zero_start; // bf16 inputs, block 64: decaying heads take the zero-start pass
+  bool warm_start; // bf16 inputs, block 64: decaying heads take the warm-start pass
   void* evt_begin; // optional hipEvent_t pair around the kernel that writes every output row
   void* evt_end;
 };
 
-// Decay table and pass A (chunk aggregates; with zero_start, of the heads
+// Decay table and pass A (chunk aggregates; with warm_start, of the heads
 // that do not decay within their chunk only): la_state.hip.
 hipError_t launch_aggregate_pass(const PrefillArgs& a, hipStream_t st);
-// Zero-start output pass of the decaying heads, with their aggregates; only
-// with zero_start: la_output.hip.
-hipError_t launch_zero_start_pass(const PrefillArgs& a, hipStream_t st);
-// Pass B (chunk scan: start states, final state): la_state.hip.
+// Warm-start output pass of the decaying heads (every output row and their
+// final state); only with warm_start: la_output.hip.
+hipError_t launch_warm_start_pass(const PrefillArgs& a, hipStream_t st);
+// Pass B (chunk scan: start states, final state; with warm_start, the
+// decaying heads' final states are only copied out): la_state.hip.
 hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st);
-// Pass C (outputs from the chunk start states; with zero_start, only the
-// leading rows of the decaying heads' chunks): la_output.hip.
+// Pass C (outputs from the chunk start states; with warm_start, of the
+// heads that do not decay within their chunk only): la_output.hip.
 hipError_t launch_output_pass(const PrefillArgs& a, hipStream_t st);
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* decay, void* out,

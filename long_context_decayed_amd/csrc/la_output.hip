@@ -20,12 +20,11 @@
 //   B  la_chunk_scan  : per (batch, head), S <- kv_in; for c: Sstart_c = S,
 //                       S = lam^(L_c) S + U_c; kv_out = S (fp32)         [la_state.hip]
 //   C  la_chunk_output: per chunk, the block loop above from Sstart_c (MFMA) [here]
-// With bf16 inputs and block 64, a head that decays within its chunk skips
-// pass A: before pass B, la_chunk_output64 in zero-start mode computes its
-// chunks from a zero start state, writing every output row and, as the state
-// reached at the chunk end, U_c; pass C then redoes only the leading rows of
-// its chunks (those on which the start state still weighs more than 2^-30 of
-// itself) from Sstart_c.  Q, K and V of such a head are read about once.
+// With bf16 inputs and block 64, a head that decays within its chunk takes
+// none of the three: la_chunk_output64 in warm-start mode computes each of
+// its chunks from the state built by the carry_span tokens before the chunk
+// (from zero; older tokens weigh at most 2^-30 there), so Q, K and V of such
+// a head are read about once and nothing waits on a scan.
 //
 // Precision recipe (bf16 inputs): products of two bf16 inputs are exact in the
 // fp32 MFMA accumulator.  Quantities formed in fp32 that feed an MFMA are
@@ -293,29 +292,29 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 //     and waited for at the end of the next phase 1.
 // Two workgroups per CU (80 KiB of LDS each).
 //
-// Two modes, by how the chunk's start state enters:
-//   kZeroStart  heads that decay within their chunk (decays_within_chunk):
-//               every row of the chunk from a zero start state, and the
-//               state reached at the chunk end, which is then the chunk
-//               aggregate U_c, stored to `states` for the scan.  Other heads
-//               return at once.
+// Two modes, by where the chunk's start state comes from:
+//   kWarmStart  heads that decay within their chunk (decays_within_chunk),
+//               whose state at any token is, to 2^-30 of the older state's
+//               own weight, made by the last carry_span tokens alone: chunk 0
+//               starts from kv_in (or zero); chunk c > 0 starts from zero
+//               carry_span tokens early and runs those tokens through the
+//               state update only (no outputs), then the chunk with outputs.
+//               The last chunk stores its end state (the final state) to its
+//               `states` slot.  One pass over Q, K, V, plus K and V of the
+//               warm-up tokens.  Other heads return at once.
 //   kFromStart  the chunk from its true start state Sstart_c (read from
-//               `states`): every row for the other heads; for decaying heads
-//               only the first carry_span rows, the only ones on which the
-//               start state weighs more than 2^-30 of itself, and nothing for
-//               chunk 0 when there is no initial state (its start state is
-//               zero).  Workgroups run in reverse order so that the longest
-//               ones (heads of slowest decay, last in the head order of the
-//               usual slope schedules) start first.
-enum { kZeroStart = 0, kFromStart = 1 };
+//               `states` after the scan), for the other heads; decaying heads
+//               return at once.
+enum { kWarmStart = 0, kFromStart = 1 };
 
 template <typename TOut, int D, int MODE>
 __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                               const bf16* __restrict__ v, TOut* __restrict__ o,
                                                               const float* __restrict__ decay,
                                                               const float* __restrict__ tbl_all,
-                                                              float* __restrict__ states, int H, int N, int L,
-                                                              int nc, int tbl_stride, int has_kv_in) {
+                                                              float* __restrict__ states,
+                                                              const float* __restrict__ kv_in, int H, int N, int L,
+                                                              int nc, int tbl_stride) {
   typedef Mfma<bf16> M;
   typedef M::op_t op_t;
   constexpr int NW = D / 32;
@@ -332,22 +331,13 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  const int blk = MODE == kFromStart ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
-  const int bh = blk / nc, c = blk - (blk / nc) * nc;
+  const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
   const int hh = bh % H;
   const int span = carry_span(decay[hh]);
   const bool decaying = decays_within_chunk(span, L);
+  if (decaying != (MODE == kWarmStart)) return;
   const int t_begin = c * L;
-  int t_end = min(N, t_begin + L);
-  if constexpr (MODE == kZeroStart) {
-    if (!decaying) return;
-  } else {
-    if (decaying) {
-      if (c == 0 && !has_kv_in) return;
-      t_end = min(t_end, t_begin + span);
-      if (t_end <= t_begin) return;
-    }
-  }
+  const int t_end = min(N, t_begin + L);
   const int64_t base = (int64_t)bh * N * D;
   const bf16* qb = q + base;
   const bf16* kb = k + base;
@@ -373,12 +363,12 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   rf[0] = tb[l32 + 1];
   rf[1] = tb[l32 + 33];
   const float d64 = tb[64];
-  // Zero-start mode hands on the exact chunk-end state, so its last sub-tile,
+  // Warm-start mode hands on the exact final state, so its last sub-tile,
   // when partial (n < 64 tokens, only at the end of the sequence), decays the
   // state by lam^n and weights token s by lam^(n-1-s): lam^e for e < 64 is
   // kept one per lane and fetched by lane shuffle.
   float tlane = 0.0f, d_last = 0.0f;
-  if constexpr (MODE == kZeroStart) {
+  if constexpr (MODE == kWarmStart) {
     tlane = tb[lane];
     d_last = tb[(t_end - t_begin) - kSub * ((t_end - t_begin - 1) / kSub)];
   }
@@ -393,18 +383,66 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   // value column col, where pf swaps bits 2 and 3:
   //   pf(crow(j, h)) = 16(j >> 3) + 8h + 4((j >> 2) & 1) + (j & 3).
   f32x16 S[NRT];
-  if constexpr (MODE == kZeroStart) {
-#pragma unroll
-    for (int kt = 0; kt < NRT; ++kt) S[kt] = zero16();
-  } else {
-    const float* src = states + ((int64_t)bh * nc + c) * D * D + col;
+  const float* s_src = MODE == kFromStart ? states + ((int64_t)bh * nc + c) * D * D
+                                          : (c == 0 && kv_in != nullptr ? kv_in + (int64_t)bh * D * D : nullptr);
+  if (s_src) {
 #pragma unroll
     for (int kt = 0; kt < NRT; ++kt)
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        S[kt][j] = src[(32 * kt + 16 * (j >> 3) + 8 * hf + 4 * ((j >> 2) & 1) + (j & 3)) * D];
+        S[kt][j] = s_src[(32 * kt + 16 * (j >> 3) + 8 * hf + 4 * ((j >> 2) & 1) + (j & 3)) * D + col];
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < NRT; ++kt) S[kt] = zero16();
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the state and the factors are in registers
+
+  // State update over one full sub-tile in (Kx, Vx): S += sum_s lam^(63-s)
+  // k_s^T v_s, tokens s = 16kk + crow(i, h).
+  auto update_full = [&](const bf16* Kx, const bf16* Vx) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const op_t vraw = ld_tr8<D, false>(Vx, 16 * kk, 32 * w, lane);
+      const float u = tb[48 - 16 * kk];
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * (ul[i] * u);
+      op_t bhi, blo;
+      M::split(x, bhi, blo);
+#pragma unroll
+      for (int kt = 0; kt < NRT; ++kt) {
+        const op_t a = ld_tr8<D, true>(Kx, 16 * kk, 32 * kt, lane);
+        S[kt] = M::mma(a, bhi, S[kt]);
+        S[kt] = M::mma(a, blo, S[kt]);
+      }
+    }
+  };
+
+  if constexpr (MODE == kWarmStart) {
+    if (c > 0 && span > 0) {
+      // Warm-up: the span tokens before the chunk (whole sub-tiles, as the
+      // chunk start and span are multiples of 64) through the state update
+      // alone, from S = 0, double-buffered in (Kt, Vs) and (Ks, Qs).
+      const int nwu = span / kSub;
+      const int64_t off0 = (int64_t)(t_begin - span) * D;
+      dma_tile<D, NW>(kb + off0, Kt, kSub, w, lane);
+      dma_tile<D, NW>(vb + off0, Vs, kSub, w, lane);
+      for (int j = 0; j < nwu; ++j) {
+        const bool odd = (j & 1) != 0;
+        // Sub-tile j is visible; every wave is done with the other buffer.
+        sync_lds_after_vmem<0>();
+        if (j + 1 < nwu) {
+          const int64_t offn = off0 + (int64_t)(j + 1) * kSub * D;
+          dma_tile<D, NW>(kb + offn, odd ? Kt : Ks, kSub, w, lane);
+          dma_tile<D, NW>(vb + offn, odd ? Vs : Qs, kSub, w, lane);
+        }
+#pragma unroll
+        for (int kt = 0; kt < NRT; ++kt) S[kt] *= d64;
+        update_full(odd ? Ks : Kt, odd ? Qs : Vs);
+      }
+      __syncthreads();  // every wave is done with the warm-up tiles
+    }
+  }
 
   {
     const int nv = min(kSub, t_end - t_begin);
@@ -460,7 +498,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
           }
         }
       }
-      if constexpr (MODE == kZeroStart)
+      if constexpr (MODE == kWarmStart)
         S[kt] *= more ? d64 : d_last;
       else
         S[kt] *= d64;
@@ -537,26 +575,9 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
       }
     }
 
-    // State update: S += sum_s lam^(63-s) k_s^T v_s, tokens s = 16kk + crow(i, h).
-    // A partial last sub-tile of zero-start mode is added after the loop.
-    if (!(MODE == kZeroStart && !more && t_end - t0 < kSub)) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const op_t vraw = ld_tr8<D, false>(Vs, 16 * kk, 32 * w, lane);
-        const float u = tb[48 - 16 * kk];
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * (ul[i] * u);
-        op_t bhi, blo;
-        M::split(x, bhi, blo);
-#pragma unroll
-        for (int kt = 0; kt < NRT; ++kt) {
-          const op_t a = ld_tr8<D, true>(Kt, 16 * kk, 32 * kt, lane);
-          S[kt] = M::mma(a, bhi, S[kt]);
-          S[kt] = M::mma(a, blo, S[kt]);
-        }
-      }
-    }
+    // State update.  A partial last sub-tile of warm-start mode is added
+    // after the loop.
+    if (!(MODE == kWarmStart && !more && t_end - t0 < kSub)) update_full(Kt, Vs);
 
     // The next sub-tile's Q and K (and this wave's older stores) are done
     // and visible; V, K^T and the score tiles are free from here on.
@@ -614,7 +635,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
       }
     }
   }
-  if constexpr (MODE == kZeroStart) {
+  if (MODE == kWarmStart && c == nc - 1) {
     // Partial last sub-tile (n < 64 tokens, still in Vs and Kt): S += sum_{s<n}
     // lam^(n-1-s) k_s^T v_s; S was decayed by lam^n in its phase 1.
     const int n = (t_end - t_begin) - kSub * ((t_end - t_begin - 1) / kSub);
@@ -639,7 +660,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
         }
       }
     }
-    // The chunk-end state from a zero start: U_c, natural (feature, column) order.
+    // The final state, natural (feature, column) order, to the last chunk's slot.
     float* dst = states + ((int64_t)bh * nc + c) * D * D + col;
 #pragma unroll
     for (int kt = 0; kt < NRT; ++kt)
@@ -654,12 +675,12 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
 // timing events.
 
 // The events bracket the kernel that writes every output row: the
-// zero-start pass when there is one (bf16 inputs, block 64), else this one.
+// warm-start pass when there is one (bf16 inputs, block 64), else this one.
 template <typename TIn, typename TOut, int D, int BLK>
 static hipError_t launch_output_t(const PrefillArgs& a, hipStream_t st) {
   const int BH = (int)(a.B * a.H);
   const int nc = a.nc;
-  const bool timed = !a.zero_start;
+  const bool timed = !a.warm_start;
   if (timed && a.evt_begin) {
     hipError_t e = hipEventRecord((hipEvent_t)a.evt_begin, st);
     if (e != hipSuccess) return e;
@@ -667,8 +688,7 @@ static hipError_t launch_output_t(const PrefillArgs& a, hipStream_t st) {
   if constexpr (BLK == 64 && sizeof(TIn) == 2)
     hipLaunchKernelGGL((la_chunk_output64<TOut, D, kFromStart>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, a.decay,
-                       (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride,
-                       a.kv_in != nullptr ? 1 : 0);
+                       (const float*)a.tbl, a.states, a.kv_in, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
   else
     hipLaunchKernelGGL((la_chunk_output<TIn, TOut, D, BLK>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                        (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (TOut*)a.out, (const float*)a.tbl,
@@ -681,17 +701,16 @@ static hipError_t launch_output_t(const PrefillArgs& a, hipStream_t st) {
 }
 
 template <typename TOut, int D>
-static hipError_t launch_zero_start_t(const PrefillArgs& a, hipStream_t st) {
+static hipError_t launch_warm_start_t(const PrefillArgs& a, hipStream_t st) {
   const int BH = (int)(a.B * a.H);
   const int nc = a.nc;
   if (a.evt_begin) {
     hipError_t e = hipEventRecord((hipEvent_t)a.evt_begin, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((la_chunk_output64<TOut, D, kZeroStart>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+  hipLaunchKernelGGL((la_chunk_output64<TOut, D, kWarmStart>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, a.decay,
-                     (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride,
-                     a.kv_in != nullptr ? 1 : 0);
+                     (const float*)a.tbl, a.states, a.kv_in, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
   if (a.evt_end) {
     hipError_t e = hipEventRecord((hipEvent_t)a.evt_end, st);
     if (e != hipSuccess) return e;
@@ -699,10 +718,10 @@ static hipError_t launch_zero_start_t(const PrefillArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_zero_start_pass(const PrefillArgs& a, hipStream_t st) {
-  if (!a.zero_start) return hipErrorInvalidValue;
-  if (a.out_dtype == kBF16) return a.d == 128 ? launch_zero_start_t<bf16, 128>(a, st) : launch_zero_start_t<bf16, 64>(a, st);
-  return a.d == 128 ? launch_zero_start_t<float, 128>(a, st) : launch_zero_start_t<float, 64>(a, st);
+hipError_t launch_warm_start_pass(const PrefillArgs& a, hipStream_t st) {
+  if (!a.warm_start) return hipErrorInvalidValue;
+  if (a.out_dtype == kBF16) return a.d == 128 ? launch_warm_start_t<bf16, 128>(a, st) : launch_warm_start_t<bf16, 64>(a, st);
+  return a.d == 128 ? launch_warm_start_t<float, 128>(a, st) : launch_warm_start_t<float, 64>(a, st);
 }
 
 template <typename TIn, typename TOut, int D>

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(D * 2, sizeof(TIn) == 2 ? 3 : 1) void la_chunk_stat
 // transpose-read operands): lam^(63-s) u = ul[i] * (lam^(48-16kk) u) with the
 // per-lane ul[i] = lam^(15 - crow(i, h)).
 //   With skip_decaying set, heads that decay within their chunk return at
-// once: the zero-start output pass produces their aggregates.
+// once: the warm-start output pass needs no aggregates.
 template <int D>
 __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restrict__ k, const bf16* __restrict__ v,
                                                              const float* __restrict__ decay,
@@ -251,14 +251,22 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
 
 // ---------------------------------------------------------------------------
 // Pass B.  One thread per 4 consecutive state elements of one (bh); serial
-// over chunks.  ws holds U_c on entry and Sstart_c on exit.
+// over chunks.  ws holds U_c on entry and Sstart_c on exit.  With warm set,
+// a head that decays within its chunk has its final state in its last
+// chunk's slot already (warm-start pass), which is only copied to kv_out.
 __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ decay, float* __restrict__ ws,
                                                      const float* __restrict__ kv_in, float* __restrict__ kv_out,
-                                                     int BH, int H, int N, int L, int nc, int D) {
+                                                     int BH, int H, int N, int L, int nc, int D, int warm) {
   const int per = D * D / 4;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)BH * per) return;
   const int bh = (int)(gid / per), e4 = (int)(gid - (int64_t)bh * per);
+  if (warm && decays_within_chunk(carry_span(decay[bh % H]), L)) {
+    if (kv_out)
+      reinterpret_cast<f32x4*>(kv_out)[(int64_t)bh * per + e4] =
+          reinterpret_cast<const f32x4*>(ws)[((int64_t)bh * nc + nc - 1) * per + e4];
+    return;
+  }
   const double lam = (double)decay[bh % H];
   const float dl = (float)pow_int(lam, L);
   const float dlast = (float)pow_int(lam, N - (nc - 1) * L);
@@ -297,7 +305,7 @@ static hipError_t launch_aggregate_t(const PrefillArgs& a, hipStream_t st) {
   if constexpr (sizeof(TIn) == 2)
     hipLaunchKernelGGL((la_chunk_state64<D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st, (const bf16*)a.k,
                        (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc,
-                       a.tbl_stride, a.zero_start ? 1 : 0);
+                       a.tbl_stride, a.warm_start ? 1 : 0);
   else
     hipLaunchKernelGGL((la_chunk_state<TIn, D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st, (const TIn*)a.k,
                        (const TIn*)a.v, (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc,
@@ -316,7 +324,7 @@ hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st) {
   const int D = (int)a.d;
   const int64_t threads = (int64_t)BH * D * D / 4;
   hipLaunchKernelGGL(la_chunk_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a.decay, a.states,
-                     a.kv_in, a.kv_out, BH, (int)a.H, (int)a.N, (int)a.L, a.nc, D);
+                     a.kv_in, a.kv_out, BH, (int)a.H, (int)a.N, (int)a.L, a.nc, D, a.warm_start ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -81,7 +81,7 @@ def test_ternary_exact_fp32(dev):
 @pytest.mark.parametrize("block", [64, 128, 256])
 def test_ternary_exact_bf16_f32out(dev, block, lams):
     # lam = 0 keeps only the diagonal term q_r.k_r v_r (0^0 = 1), still exact;
-    # with block 64 that head takes the zero-start pass with no leading rows.
+    # with block 64 that head takes the warm-start pass with no warm-up.
     say("ternary bf16->f32 lam", lams, "B1 H2 N1024 d128 block", block)
     q, k, v = ternary_device(1, 2, 1024, 128, seed=2, device=dev, dtype=torch.bfloat16)
     lam = lam_for(2, "one") if lams == "one" else np.array([0.0, 1.0], dtype=np.float32)
@@ -186,11 +186,11 @@ def test_bf16_state_in_place(dev):
 
 # --- heads that decay within a chunk, next to heads that do not --------------
 # Chunk 1024, block 64, bf16 inputs.  A head whose start-state weight lam^(r+1)
-# falls below 2^-30 within a third of a chunk (here lam <= 0.9) is computed
-# from a zero chunk-start state and redone from the true start state on the
-# leading rows only; the others take the three-pass path.  Each head is held
-# to the tolerance on its own RMS, so the fast-decaying heads are not hidden
-# behind the large outputs of the lam ~ 1 heads.
+# falls below 2^-30 within a third of a chunk (here lam <= 0.9) is computed per
+# chunk from the state that the preceding carry-span tokens build from zero;
+# the others take the three-pass path.  Each head is held to the tolerance on
+# its own RMS, so the fast-decaying heads are not hidden behind the large
+# outputs of the lam ~ 1 heads.
 
 MIXED_LAMS = np.array([0.0, 1e-3, 0.3, 0.7, 0.9, 0.97, 0.999, 1.0], dtype=np.float32)
 
@@ -212,6 +212,23 @@ def test_bf16_mixed_decays(dev, n, d, with_state):
         tol.assert_state(kv_h[:, h], s_ref[:, h], "kv_out head %d (lam %g)" % (h, MIXED_LAMS[h]))
     assert torch.equal(o32.to(torch.bfloat16), o16), "bf16 out must be RNE(fp32 out)"
     assert torch.equal(kv, kv16)
+
+
+def test_bf16_mixed_decays_state_in_place(dev):
+    # kv_in is kv_out: the first chunk of a fast head reads kv_in, and its final
+    # state reaches kv_out only after every chunk is done.
+    say("bf16 mixed decays in place B2 H8 N4100 d128 chunk 1024")
+    q, k, v = qkv_device(2, 8, 4100, 128, seed=70, device=dev)
+    s0 = state_device(2, 8, 128, seed=70, device=dev)
+    s_host = host(s0).astype(np.float64)
+    out = la.fwd(q, k, v, torch.from_numpy(MIXED_LAMS).to(dev), kv_in=s0, kv_out=s0, block=64,
+                 out_dtype=torch.float32, chunk=1024)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle(host(q), host(k), host(v), MIXED_LAMS, s_host)
+    o_h, s_h = host(out), host(s0)
+    for h in range(8):
+        tol.assert_bf16_f32out(o_h[:, h], o_ref[:, h], "O head %d" % h)
+        tol.assert_state(s_h[:, h], s_ref[:, h], "kv head %d" % h)
 
 
 def test_bf16_mixed_decays_chunk_invariance(dev):
