@@ -347,7 +347,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   const float* tb = tbl_all + (int64_t)hh * tbl_stride;  // lam^e, e <= 64
 
   // Decay factors (all exponents non-negative), j = 4jq + jj:
-  //   update, s = 16kk + crow(i, h):   lam^(63-s) = lam^(48-16kk) * ul[i],  ul[i] = lam^(15-crow(i,h))
+  //   update, s = 16kk + crow(i, h):   lam^(63-s) = wl[kk][i] = lam^(48-16kk) * ul[i],  ul[i] = lam^(15-crow(i,h))
   //   inter,  token p = 32rt + l:      lam^(p+1)  = rf[rt]
   //   off-diagonal score tile (r = 32 + l, s = crow(j, h)):
   //           lam^(r-s) = lam^(24-8jq) * ol[jj],  ol[jj] = lam^(l+4-4h+4-jj)
@@ -355,11 +355,15 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   //           0 (masked) for d < 0, kept in Dtab[jq][lane][jj].
   // They are loaded here, before the tile loop, so that the loop issues no
   // vector-memory loads of its own.
-  float ol[4], ul[8], rf[2];
+  float ol[4], ul[8], rf[2], wl[4][8];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) ol[jj] = tb[l32 + 8 - 4 * hf - jj];
 #pragma unroll
   for (int i = 0; i < 8; ++i) ul[i] = tb[15 - crow(i, hf)];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wl[kk][i] = ul[i] * tb[48 - 16 * kk];
   rf[0] = tb[l32 + 1];
   rf[1] = tb[l32 + 33];
   const float d64 = tb[64];
@@ -403,10 +407,9 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const op_t vraw = ld_tr8<D, false>(Vx, 16 * kk, 32 * w, lane);
-      const float u = tb[48 - 16 * kk];
       float x[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * (ul[i] * u);
+      for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * wl[kk][i];
       op_t bhi, blo;
       M::split(x, bhi, blo);
 #pragma unroll
@@ -514,9 +517,6 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
           }
         }
       }
-      // Keep the scheduler from hoisting every kt step's LDS operands at once
-      // (the register file is shared by two workgroups per CU).
-      __builtin_amdgcn_sched_barrier(0);
     }
     // Mask, decay and publish the score tiles as hi + lo operands.
 #pragma unroll
@@ -550,9 +550,13 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
         }
       }
     }
-    // Inter-term decay lam^(p+1), one factor per lane and token tile.
+    // Inter-term decay lam^(p+1), one factor per lane and token tile.  Written
+    // element by element: as a vector-by-scalar product the compiler hoists a
+    // 16-wide copy of each factor out of the loop (30 registers).
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) acc[rt] *= rf[rt];
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[rt][j] *= rf[rt];
 
     // This sub-tile's V and K^T copy (requested before the previous
     // sub-tile's kStores output stores, which may still be in flight) and
