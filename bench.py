@@ -20,7 +20,8 @@ ONE JSON line:
   cpu_baseline   the fp64 oracle (plain-C recurrence) on a bounded sample of
                  the same workload, on this host's cores
   decode         256 sequences x 64 heads x d=128 decode step, 1000 in-place
-                 steps timed as a whole: GB/s of state + token traffic
+                 steps timed as a whole: GB/s of state + token traffic; and
+                 the same rows through a slot table over a 512-slot pool
 
 Only one GPU is used; --gpus > 1 exits with a message.
 """
@@ -191,9 +192,28 @@ def bench_decode(args, dev):
     ms = e0.elapsed_time(e1)
     per_step_bytes = 2 * B * H * d * d * 4 + 4 * B * H * d * 2
     gbs = per_step_bytes * steps / (ms * 1e-3) / 1e9
-    return dict(workload="decode 256 seq x H=64 x d=128, fp32 state, bf16 q/k/v/o", steps=steps,
-                us_per_step=ms * 1e3 / steps, bytes_per_step=per_step_bytes, gb_per_s=gbs,
-                frac_hbm=gbs / HBM_PEAK_GBS)
+    res = dict(workload="decode 256 seq x H=64 x d=128, fp32 state, bf16 q/k/v/o", steps=steps,
+               us_per_step=ms * 1e3 / steps, bytes_per_step=per_step_bytes, gb_per_s=gbs,
+               frac_hbm=gbs / HBM_PEAK_GBS)
+    del s
+    # Serving form: the same 256 rows over a pool of 512 state slots, through a
+    # seeded random slot table (each row its own slot).
+    pool = state_device(2 * B, H, d, seed=9, device=dev)
+    g = torch.Generator().manual_seed(9)
+    slots = torch.randperm(2 * B, generator=g)[:B].to(torch.int32).to(dev)
+    for _ in range(10):
+        la.decode_slots(q, k, v, lam, pool, slots, out=o)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        la.decode_slots(q, k, v, lam, pool, slots, out=o)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    gbs = (per_step_bytes + B * 4) * steps / (ms * 1e-3) / 1e9
+    res["slots"] = dict(workload="the same 256 rows over a 512-slot state pool (seeded random slot table)",
+                        us_per_step=ms * 1e3 / steps, gb_per_s=gbs, frac_hbm=gbs / HBM_PEAK_GBS)
+    return res
 
 
 def cpu_baseline(sample, args):

@@ -148,6 +148,26 @@ int lightning_attn_decode_step(const void* q, const void* k, const void* v, cons
                                const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t d,
                                void* stream);
 
+/*
+ * Decode step over a pool of states (serving): the same step as
+ * lightning_attn_decode_step, with batch row b reading and writing, in
+ * place, the state of pool slot slots[b].  The recurrence has no position
+ * term, so requests at different positions share one call.
+ *   q, k, v   : bf16 [B][H][d]                       (read)
+ *   decay     : float [H]                            (read)
+ *   out       : bf16 [B][H][d]                       (written)
+ *   states    : float [num_slots][H][d][d]           (read and written in place)
+ *   slots     : int32 [B], device memory             (read)
+ *   B, H, num_slots >= 1; d in {64, 128}
+ * A row whose slot lies outside [0, num_slots) is idle: its output row is
+ * written as zeros and no state is touched.  Two rows naming the same slot
+ * race (undefined result).  Slots are device data, so their range is checked
+ * by the kernel, not before the launch.
+ */
+int lightning_attn_decode_slots(const void* q, const void* k, const void* v, const float* decay, void* out,
+                                float* states, const int32_t* slots, int64_t B, int64_t H, int64_t d,
+                                int64_t num_slots, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* lightning_attn_strerror(int status);
 

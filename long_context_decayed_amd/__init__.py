@@ -65,6 +65,8 @@ def load():
     lib.lightning_attn_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64]
     lib.lightning_attn_decode_step.restype = I
     lib.lightning_attn_decode_step.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, P]
+    lib.lightning_attn_decode_slots.restype = I
+    lib.lightning_attn_decode_slots.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, P]
     lib.lightning_attn_strerror.restype = ctypes.c_char_p
     lib.lightning_attn_strerror.argtypes = [I]
     lib.lightning_attn_runtime_version.restype = I
@@ -173,6 +175,32 @@ def decode_step(q, k, v, decay, kv_in=None, kv_out=None, out=None, stream=None):
     )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_decode_step")
+    return out
+
+
+def decode_slots(q, k, v, decay, states, slots, out=None, stream=None):
+    """Decode step over a state pool.  q, k, v: [B, H, d] bf16; decay fp32 [H];
+    states: fp32 [num_slots, H, d, d], updated in place for the rows' slots;
+    slots: int32 [B] on the device (out of range = idle row, zero output).
+    Returns o [B, H, d] bf16."""
+    lib = load()
+    B, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, torch.bfloat16, (B, H, d))
+    _check_dev("decay", decay, torch.float32, (H,))
+    if states.dim() != 4:
+        raise ValueError("states must be [num_slots, H, d, d]")
+    _check_dev("states", states, torch.float32, (states.shape[0], H, d, d))
+    _check_dev("slots", slots, torch.int32, (B,))
+    if out is None:
+        out = torch.empty((B, H, d), device=q.device, dtype=torch.bfloat16)
+    _check_dev("out", out, torch.bfloat16, (B, H, d))
+    rc = lib.lightning_attn_decode_slots(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(states), _ptr(slots), B, H, d, states.shape[0],
+        _stream(stream)
+    )
+    if rc != 0:
+        raise LightningAttnError(rc, "lightning_attn_decode_slots")
     return out
 
 

@@ -216,6 +216,25 @@ int lightning_attn_decode_step(const void* q, const void* k, const void* v, cons
   return from_hip(la::launch_decode(q, k, v, decay, out, kv_in, kv_out, B, H, d, (hipStream_t)stream));
 }
 
+int lightning_attn_decode_slots(const void* q, const void* k, const void* v, const float* decay, void* out,
+                                float* states, const int32_t* slots, int64_t B, int64_t H, int64_t d,
+                                int64_t num_slots, void* stream) {
+  if (!q || !k || !v || !decay || !out || !states || !slots) return LA_ERR_INVALID;
+  if (B < 1 || H < 1 || d < 1 || num_slots < 1) return LA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(decay, 4) ||
+      !aligned(states, 16) || !aligned(slots, 4))
+    return LA_ERR_INVALID;
+  if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+  if (B * H > kMaxGrid || num_slots > kMaxGrid) return LA_ERR_UNSUPPORTED;
+  const int64_t vec_bytes = B * H * d * 2, pool_bytes = num_slots * H * d * d * 4;
+  if (overlap(out, vec_bytes, q, vec_bytes) || overlap(out, vec_bytes, k, vec_bytes) ||
+      overlap(out, vec_bytes, v, vec_bytes) || overlap(out, vec_bytes, states, pool_bytes) ||
+      overlap(out, vec_bytes, slots, B * 4) || overlap(states, pool_bytes, slots, B * 4))
+    return LA_ERR_INVALID;
+  return from_hip(la::launch_decode(q, k, v, decay, out, states, states, B, H, d, (hipStream_t)stream,
+                                    (const int*)slots, num_slots));
+}
+
 const char* lightning_attn_strerror(int status) {
   switch (status) {
     case LA_OK: return "ok";

@@ -13,6 +13,11 @@
 // threads x 1 pair.)  The products k[i] v[j] of two bf16 values are exact in
 // fp32; o is reduced over the RG row groups in LDS in a fixed order and
 // rounded once to bf16.
+//
+// Serving form: with a slot table, batch row b reads and writes the state of
+// pool slot slots[b] (states [num_slots][H][d][d], in place); a row whose
+// slot lies outside [0, num_slots) is idle: its output is zero and no state
+// is touched.
 
 #include <hip/hip_runtime.h>
 
@@ -27,7 +32,8 @@ constexpr int kDecPairs = 2;      // pairs per workgroup
 template <int D>
 __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ decay, bf16* __restrict__ o, const float* kv_in, float* kv_out, int H, int64_t pairs) {
+    const float* __restrict__ decay, bf16* __restrict__ o, const float* kv_in, float* kv_out, int H, int64_t pairs,
+    const int* __restrict__ slots, int64_t num_slots) {
   constexpr int TPR = D / 4;              // threads per row
   constexpr int RG = kDecThreads / TPR;   // row groups
   constexpr int RPT = D / RG;             // rows per thread
@@ -36,9 +42,17 @@ __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
 
   const int sub = threadIdx.x / kDecThreads, tid = threadIdx.x % kDecThreads;
   const int64_t pair = (int64_t)blockIdx.x * kDecPairs + sub;
-  const bool valid = pair < pairs;  // no early return: every thread reaches the barriers
+  bool valid = pair < pairs;  // no early return: every thread reaches the barriers
   const int cg = tid % TPR, rg = tid / TPR;
-  const float lam = valid ? decay[pair % H] : 0.0f;
+  const int64_t b = pair / H, hh = pair - (pair / H) * H;
+  int64_t srow = b;  // state row of this pair: the batch row, or its slot
+  bool idle = false;
+  if (slots && valid) {
+    srow = slots[b];
+    idle = srow < 0 || srow >= num_slots;
+    valid = !idle;
+  }
+  const float lam = valid ? decay[hh] : 0.0f;
   if (valid && tid < D) {
     qs[sub][tid] = (float)q[pair * D + tid];
     ks[sub][tid] = (float)k[pair * D + tid];
@@ -48,7 +62,7 @@ __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
     const bf16x4 vb = *reinterpret_cast<const bf16x4*>(v + pair * D + 4 * cg);
     vv = f32x4{(float)vb[0], (float)vb[1], (float)vb[2], (float)vb[3]};
   }
-  const int64_t sbase = pair * D * D;
+  const int64_t sbase = (srow * H + hh) * D * D;
   f32x4 s[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
@@ -72,27 +86,30 @@ __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
   }
   part[sub][rg][cg] = acc;
   __syncthreads();
-  if (valid && tid < TPR) {
+  if ((valid || idle) && tid < TPR) {
     f32x4 r = part[sub][0][tid];
 #pragma unroll
     for (int g = 1; g < RG; ++g) r += part[sub][g][tid];
     bf16x4 ob;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ob[i] = (bf16)r[i];
+    for (int i = 0; i < 4; ++i) ob[i] = idle ? (bf16)0.0f : (bf16)r[i];
     *reinterpret_cast<bf16x4*>(o + pair * D + 4 * tid) = ob;
   }
 }
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* decay, void* out,
-                         const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t d, hipStream_t st) {
+                         const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t d, hipStream_t st,
+                         const int* slots, int64_t num_slots) {
   const int64_t pairs = B * H;
   const unsigned grid = (unsigned)((pairs + kDecPairs - 1) / kDecPairs);
   if (d == 128)
     hipLaunchKernelGGL(la_decode_kernel<128>, dim3(grid), dim3(kDecThreads * kDecPairs), 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, decay, (bf16*)out, kv_in, kv_out, (int)H, pairs);
+                       (const bf16*)k, (const bf16*)v, decay, (bf16*)out, kv_in, kv_out, (int)H, pairs, slots,
+                       num_slots);
   else
     hipLaunchKernelGGL(la_decode_kernel<64>, dim3(grid), dim3(kDecThreads * kDecPairs), 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, decay, (bf16*)out, kv_in, kv_out, (int)H, pairs);
+                       (const bf16*)k, (const bf16*)v, decay, (bf16*)out, kv_in, kv_out, (int)H, pairs, slots,
+                       num_slots);
   return hipGetLastError();
 }
 

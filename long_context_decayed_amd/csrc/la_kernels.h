@@ -40,7 +40,10 @@ hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st);
 // heads that do not decay within their chunk only): la_output.hip.
 hipError_t launch_output_pass(const PrefillArgs& a, hipStream_t st);
 
+// Decode step; with `slots` (device int32[B]) batch row b uses state row
+// slots[b] of kv_in / kv_out ([num_slots][H][d][d]); rows out of range idle.
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* decay, void* out,
-                         const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t d, hipStream_t st);
+                         const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t d, hipStream_t st,
+                         const int* slots = nullptr, int64_t num_slots = 0);
 
 }  // namespace la

@@ -133,6 +133,19 @@ def test_decode_validation(lib):
     assert f(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[0], None, None, 1, 1, 128, None) == LA_ERR_INVALID
 
 
+def test_decode_slots_validation(lib):
+    f = lib.lightning_attn_decode_slots
+    ok = (FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], FAKE[5], FAKE[6])
+    assert f(None, *ok[1:], 1, 1, 128, 4, None) == LA_ERR_INVALID
+    assert f(*ok[:6], None, 1, 1, 128, 4, None) == LA_ERR_INVALID          # no slot table
+    assert f(*ok[:5], None, FAKE[6], 1, 1, 128, 4, None) == LA_ERR_INVALID  # no pool
+    assert f(*ok, 1, 1, 128, 0, None) == LA_ERR_INVALID                    # empty pool
+    assert f(*ok, 0, 1, 128, 4, None) == LA_ERR_INVALID
+    assert f(*ok, 1, 1, 96, 4, None) == LA_ERR_UNSUPPORTED
+    assert f(*ok[:4], FAKE[0], *ok[5:], 1, 1, 128, 4, None) == LA_ERR_INVALID   # out overlaps q
+    assert f(*ok[:5], FAKE[6], FAKE[6], 1, 1, 128, 4, None) == LA_ERR_INVALID   # slots inside the pool
+
+
 def test_strerror(lib):
     for code in range(6):
         s = lib.lightning_attn_strerror(code).decode()

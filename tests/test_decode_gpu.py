@@ -113,3 +113,70 @@ def test_prefill_then_decode_matches_longer_prefill(dev):
                             host(kv_full).astype(np.float64))
     tol.assert_bf16_f32out(host(o1)[:, :, 0], r1)
     tol.assert_bf16_out(host(o2), r1)
+
+
+# --- serving form: a pool of states addressed through a slot table ---------
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_slots_against_oracle(dev, d):
+    say("decode over a slot table, pool 12 x H8 d", d)
+    H, P = 8, 12
+    slots_h = np.array([5, 0, -1, 11, 3, 12, 7], dtype=np.int32)  # -1 and 12: idle rows
+    B = len(slots_h)
+    q, k, v = _tokens(B, H, d, 6, dev)
+    lam = lam_for(H, "spec")
+    pool = state_device(P, H, d, seed=6, device=dev)
+    pool0 = host(pool).astype(np.float64)
+    slots = torch.from_numpy(slots_h).to(dev)
+    o = la.decode_slots(q, k, v, torch.from_numpy(lam).to(dev), pool, slots)
+    torch.cuda.synchronize()
+    active = [(b, int(s)) for b, s in enumerate(slots_h) if 0 <= s < P]
+    rows = np.array([b for b, _ in active])
+    sl = np.array([s for _, s in active])
+    o_ref, s_ref = ora.decode_step(host(q)[rows], host(k)[rows], host(v)[rows], lam.astype(np.float64), pool0[sl])
+    tol.assert_bf16_out(host(o)[rows], o_ref)
+    pool1 = host(pool).astype(np.float64)
+    tol.assert_state(pool1[sl], s_ref)
+    idle = [b for b in range(B) if b not in rows]
+    assert np.all(host(o)[idle] == 0.0), "idle rows must be zero"
+    untouched = [s for s in range(P) if s not in sl]
+    assert np.array_equal(pool1[untouched], pool0[untouched]), "slots not named must not change"
+
+
+def test_decode_slots_identity_matches_decode_step(dev):
+    say("decode_slots with slots = 0..B-1 vs decode_step, B64 H64 d128")
+    B, H, d = 64, 64, 128
+    q, k, v = _tokens(B, H, d, 7, dev)
+    lam_t = torch.from_numpy(decay_lambdas(H)).to(dev)
+    s0 = state_device(B, H, d, seed=7, device=dev)
+    pool = s0.clone()
+    kv = torch.empty_like(s0)
+    o1 = la.decode_step(q, k, v, lam_t, kv_in=s0, kv_out=kv)
+    o2 = la.decode_slots(q, k, v, lam_t, pool, torch.arange(B, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(kv, pool)
+
+
+def test_decode_slots_interleaved_requests(dev):
+    # Three steps with different request sets: each slot's state must follow
+    # the recurrence over exactly the tokens its rows brought, in order.
+    say("decode_slots: 3 steps of interleaved requests, pool 6 x H4 d64")
+    H, P, d = 4, 6, 64
+    lam = lam_for(H, "spec")
+    lam_t = torch.from_numpy(lam).to(dev)
+    pool = state_device(P, H, d, seed=8, device=dev)
+    ref = host(pool).astype(np.float64)
+    tables = [np.array([0, 2, 4], np.int32), np.array([4, 1, -1, 0], np.int32), np.array([3, 4], np.int32)]
+    for step, tab in enumerate(tables):
+        q, k, v = _tokens(len(tab), H, d, 20 + step, dev)
+        o = la.decode_slots(q, k, v, lam_t, pool, torch.from_numpy(tab).to(dev))
+        torch.cuda.synchronize()
+        for b, s in enumerate(tab):
+            if s < 0:
+                assert np.all(host(o)[b] == 0.0)
+                continue
+            o_ref, s_new = ora.decode_step(host(q)[b:b + 1], host(k)[b:b + 1], host(v)[b:b + 1],
+                                           lam.astype(np.float64), ref[s:s + 1])
+            ref[s] = s_new[0]
+            tol.assert_bf16_out(host(o)[b:b + 1], o_ref)
+    tol.assert_state(host(pool), ref)
