@@ -8,6 +8,10 @@ Parity status of each function (what pins it lives in tests/test_oracle.py):
   quadratic, recurrent, state_at, decode_step, decode_repeated, window --
   pinned by hand-derived exact values, closed forms, textbook reductions,
   invariants and brute force; none is "parity unpinned".
+  backward_quadratic and crec.backward (gradients) -- pinned in
+  tests/test_oracle_bwd.py by a hand-worked example, exact central
+  differences of the forward oracle, closed forms at lam = 0 and 1 and the
+  split-sequence rule.
 """
 from .lightning import (  # noqa: F401
     decay_matrix,
@@ -17,4 +21,5 @@ from .lightning import (  # noqa: F401
     decode_step,
     decode_repeated,
     window,
+    backward_quadratic,
 )

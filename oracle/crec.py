@@ -43,6 +43,13 @@ def _load():
             ctypes.c_void_p,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
         ]
+        lib.lcd_oracle_backward.restype = ctypes.c_int
+        lib.lcd_oracle_backward.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+        ]
         lib.lcd_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -84,3 +91,37 @@ def recurrent(q, k, v, lam, s0=None, o_range=None, threads=0, want_state=True):
     if rc != 0:
         raise MemoryError("oracle recurrence could not allocate its scratch state")
     return o, s_fin
+
+
+def backward(q, k, v, lam, dout, s0=None, dsn=None, threads=0):
+    """fp64 gradients of the recurrence (adjoint recurrence in plain C) for
+    arrays [..., N, d]: dout = dL/dO, dsn = dL/dS_final (None = 0).
+    Returns (dQ, dK, dV [..., N, d], dS0 [..., d, d]) in float64."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    dout = np.ascontiguousarray(dout, dtype=np.float32)
+    lead = q.shape[:-2]
+    n, d = q.shape[-2], q.shape[-1]
+    assert k.shape == q.shape and v.shape == q.shape and dout.shape == q.shape
+    pairs = int(np.prod(lead)) if lead else 1
+    lam_p = np.ascontiguousarray(
+        np.broadcast_to(np.asarray(lam, dtype=np.float64), lead).reshape(pairs)
+    )
+    def st(x):
+        if x is None:
+            return None
+        return np.ascontiguousarray(np.broadcast_to(np.asarray(x, dtype=np.float64), lead + (d, d)))
+    s0, dsn = st(s0), st(dsn)
+    dq = np.zeros(lead + (n, d)); dk = np.zeros(lead + (n, d)); dv = np.zeros(lead + (n, d))
+    ds0 = np.zeros(lead + (d, d))
+    rc = lib.lcd_oracle_backward(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, lam_p.ctypes.data,
+        None if s0 is None else s0.ctypes.data, dout.ctypes.data, None if dsn is None else dsn.ctypes.data,
+        dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, ds0.ctypes.data,
+        pairs, n, d, int(threads),
+    )
+    if rc != 0:
+        raise MemoryError("oracle backward could not allocate its scratch state")
+    return dq, dk, dv, ds0

@@ -29,6 +29,20 @@ Readings taken where the pages are silent (each is pinned by a test):
   * No 1/sqrt(d) scale and no normaliser; inputs arrive pre-scaled.
   * The state is indexed S[key_dim, value_dim] (S = sum of k^T v).
 
+Gradients (the backward pass; the pages are silent on it, so it is the
+derivative of the function above and nothing more): for a loss L with
+dL/dO = dO and dL/dS_final = dSN,
+
+    dQ  = ((dO V^T) * M) K     + diag(lambda^(t+1)) dO S0^T
+    dK  = ((dO V^T) * M)^T Q   + diag(lambda^(N-1-s)) V dSN^T
+    dV  = ((Q K^T) * M)^T dO   + diag(lambda^(N-1-s)) K dSN
+    dS0 = Q^T diag(lambda^(t+1)) dO + lambda^N dSN
+
+(`backward_quadratic`, matrix calculus on the quadratic form).  The token
+form of the same gradients, an adjoint recurrence run from the last token
+back, is in recurrence.c (`crec.backward`); the two are checked against each
+other, against finite differences and against autograd.
+
 Every function works in float64 on whatever bits it is given: callers pass the
 exact values a GPU consumed (bf16 or fp32, upcast), and lambda as the fp32
 value the GPU received, upcast, never recomputed.
@@ -48,6 +62,7 @@ __all__ = [
     "decode_step",
     "decode_repeated",
     "window",
+    "backward_quadratic",
 ]
 
 
@@ -198,3 +213,43 @@ def window(q, k, v, lam, t0, t1, w, s0=None):
     init = s0 if (start == 0) else None
     o, _ = recurrent(q[..., start:t1, :], k[..., start:t1, :], v[..., start:t1, :], lam, init)
     return o[..., t0 - start:, :]
+
+
+def backward_quadratic(q, k, v, lam, dout, s0=None, dsn=None):
+    """Gradients of L with dL/dO = dout and dL/dS_final = dsn, from the masked
+    matrix form (matrix calculus; brute force, small N only):
+
+        dQ  = ((dO V^T) * M) K   + diag(lam^(t+1)) dO S0^T
+        dK  = ((dO V^T) * M)^T Q + diag(lam^(N-1-s)) V dSN^T
+        dV  = ((Q K^T) * M)^T dO + diag(lam^(N-1-s)) K dSN
+        dS0 = Q^T diag(lam^(t+1)) dO + lam^N dSN
+
+    Returns (dQ, dK, dV [..., N, d], dS0 [..., d, d])."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    lead = _lead(q)
+    n, d = q.shape[-2], q.shape[-1]
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    ds0 = np.zeros(lead + (d, d))
+    for idx in _iter_lead(lead):
+        lm = _lam_at(lam, lead, idx)
+        qi, ki, vi, gi = q[idx], k[idx], v[idx], g[idx]
+        m = decay_matrix(lm, n)
+        gv = (gi @ vi.T) * m          # (dO V^T) * M
+        qk = (qi @ ki.T) * m          # (Q K^T) * M
+        dq[idx] = gv @ ki
+        dk[idx] = gv.T @ qi
+        dv[idx] = qk.T @ gi
+        row = _pow_int(lm, np.arange(1, n + 1))              # lam^(t+1)
+        ds = (row[:, None] * qi).T @ gi
+        if s0 is not None:
+            dq[idx] += row[:, None] * (gi @ _f64(s0)[idx].T)
+        if dsn is not None:
+            dsi = _f64(dsn)[idx]
+            w = _pow_int(lm, np.arange(n - 1, -1, -1))       # lam^(N-1-s)
+            dk[idx] += w[:, None] * (vi @ dsi.T)
+            dv[idx] += w[:, None] * (ki @ dsi)
+            ds = ds + (lm ** n) * dsi
+        ds0[idx] = ds
+    return dq, dk, dv, ds0
