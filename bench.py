@@ -19,6 +19,7 @@ ONE JSON line:
                  stream, against 8 TB/s
   cpu_baseline   the fp64 oracle (plain-C recurrence) on a bounded sample of
                  the same workload, on this host's cores
+  backward       the backward pass of the same layer (dq, dk, dv from dout)
   decode         256 sequences x 64 heads x d=128 decode step, 1000 in-place
                  steps timed as a whole: GB/s of state + token traffic; and
                  the same rows through a slot table over a 512-slot pool
@@ -160,13 +161,47 @@ def bench_prefill(args, dev):
         step_hbm_frac=BYTES_PER_HT * ht / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         mfma_alg_frac=FLOP_PER_HT * ht / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
     )
+    del out, ws
+    if args.backward:
+        res["backward"] = bench_backward(args, dev, q, k, v, lam)
     sample = None
     if args.cpu_baseline:
         sample = (q, k, v, decay_lambdas(H))
     else:
         del q, k, v
-    del out, ws
     return res, sample
+
+
+def bench_backward(args, dev, q, k, v, lam):
+    """The backward pass of the same layer (dq, dk, dv from dout; three
+    prefill-shaped passes), timed with events on the current stream."""
+    import torch
+    import long_context_decayed_amd as la
+    from long_context_decayed_amd.inputs import qkv_device
+
+    B, H, N, d = q.shape
+    log("backward: B=%d H=%d N=%d d=%d bf16" % (B, H, N, d))
+    g = qkv_device(B, H, N, d, seed=5, device=dev, slice_tokens=65536)[0]
+    ws = torch.empty(la.lib_bwd_workspace_bytes(B, H, N, d), device=dev, dtype=torch.uint8)
+    outs = None
+    for _ in range(max(1, args.warmup)):
+        outs = la.bwd(q, k, v, lam, g, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    steps = max(1, args.steps // 2)
+    e0.record()
+    for _ in range(steps):
+        outs = la.bwd(q, k, v, lam, g, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del outs, g, ws
+    ht = B * H * N
+    min_bytes = 7 * 2 * d * ht     # q, k, v, dout read + dq, dk, dv written, bf16
+    gbs = min_bytes / (ms * 1e-3) / 1e9
+    return dict(workload="backward of the same layer: dq, dk, dv (bf16) from dout, zero initial state and "
+                         "final-state gradient", steps=steps, ms_per_step=ms, tokens_per_s=B * N / (ms * 1e-3),
+                min_bytes_per_step=min_bytes, gb_per_s_vs_min_bytes=gbs, frac_hbm=gbs / HBM_PEAK_GBS)
 
 
 def bench_decode(args, dev):
@@ -254,6 +289,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", dest="decode", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--no-backward", dest="backward", action="store_false")
     ap.add_argument("--cpu-tokens", type=int, default=1 << 20)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a known-size "
@@ -303,6 +339,7 @@ def main():
         "warm_start_heads": prefill["warm_start_heads"],
         "step_hbm_frac": prefill["step_hbm_frac"],
         "mfma_alg_frac": prefill["mfma_alg_frac"],
+        "backward": prefill.get("backward"),
         "cpu_baseline": cpu,
         "decode": dec,
     }

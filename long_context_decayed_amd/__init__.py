@@ -65,6 +65,10 @@ def load():
     lib.lightning_attn_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64]
     lib.lightning_attn_decode_step.restype = I
     lib.lightning_attn_decode_step.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, P]
+    lib.lightning_attn_bwd.restype = I
+    lib.lightning_attn_bwd.argtypes = [P] * 11 + [I64, I64, I64, I64, I, P, SZ, P]
+    lib.lightning_attn_bwd_workspace_bytes.restype = SZ
+    lib.lightning_attn_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64]
     lib.lightning_attn_decode_slots.restype = I
     lib.lightning_attn_decode_slots.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, P]
     lib.lightning_attn_strerror.restype = ctypes.c_char_p
@@ -108,6 +112,10 @@ def _check_dev(name, t, dtype=None, shape=None):
 def chunk_for(B, H, N, block=256, chunk=0):
     """Chunk length the library uses (chunk=0: its default)."""
     return int(load().lightning_attn_fwd_chunk(B, H, N, block, chunk))
+
+
+def lib_bwd_workspace_bytes(B, H, N, d):
+    return int(load().lightning_attn_bwd_workspace_bytes(B, H, N, d))
 
 
 def workspace_bytes(B, H, N, d, block=256, chunk=0):
@@ -176,6 +184,42 @@ def decode_step(q, k, v, decay, kv_in=None, kv_out=None, out=None, stream=None):
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_decode_step")
     return out
+
+
+def bwd(q, k, v, decay, dout, kv_in=None, dkv_out=None, out_dtype=None, dkv_in=False, workspace=None,
+        stream=None):
+    """Backward pass.  q, k, v, dout: [B, H, N, d] bf16 device tensors; decay fp32
+    [H]; kv_in: the forward's initial state, dkv_out: dL/d(kv_out), fp32
+    [B, H, d, d] or None.  Returns (dq, dk, dv, dkv_in) with dq, dk, dv in
+    out_dtype (default bf16); dkv_in is an fp32 tensor when asked for (True, or
+    a tensor to write into), else None."""
+    lib = load()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check_dev(name, t, torch.bfloat16, (B, H, N, d))
+    _check_dev("decay", decay, torch.float32, (H,))
+    for name, t in (("kv_in", kv_in), ("dkv_out", dkv_out)):
+        if t is not None:
+            _check_dev(name, t, torch.float32, (B, H, d, d))
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    code = {torch.bfloat16: 0, torch.float32: 1}[out_dtype]
+    dq, dk, dv = (torch.empty((B, H, N, d), device=q.device, dtype=out_dtype) for _ in range(3))
+    if dkv_in is True:
+        dkv_in = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32)
+    elif dkv_in is False:
+        dkv_in = None
+    if dkv_in is not None:
+        _check_dev("dkv_in", dkv_in, torch.float32, (B, H, d, d))
+    need = lib_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    rc = lib.lightning_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(dout), _ptr(kv_in), _ptr(dkv_out), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(dkv_in), B, H, N, d, code, _ptr(workspace), workspace.numel(), _stream(stream)
+    )
+    if rc != 0:
+        raise LightningAttnError(rc, "lightning_attn_bwd")
+    return dq, dk, dv, dkv_in
 
 
 def decode_slots(q, k, v, decay, states, slots, out=None, stream=None):

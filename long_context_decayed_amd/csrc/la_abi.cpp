@@ -36,8 +36,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool valid_block(int64_t block) { return block == 64 || block == 128 || block == 256; }
 
-// Default chunk: 4096 tokens, halved while the chunk-parallel passes would
-// launch fewer than 1024 workgroups, never below max(block, 256), and never
+// Default chunk: 16384 tokens, halved while the chunk-parallel passes would
+// launch fewer than 2048 workgroups, never below max(block, 256), and never
 // longer than the sequence rounded up to a whole block.
 int64_t pick_chunk(int64_t B, int64_t H, int64_t N, int64_t block) {
   // Long chunks keep the chunk-state traffic small (each chunk moves four
@@ -106,6 +106,17 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* d
   return LA_OK;
 }
 
+// The kernels of one prefill-shaped pass, in order, on `st`.
+hipError_t run_passes(const la::PrefillArgs& a, hipStream_t st) {
+  hipError_t e = la::launch_aggregate_pass(a, st);
+  if (e == hipSuccess && a.warm_start) e = la::launch_warm_start_pass(a, st);
+  if (e == hipSuccess) e = la::launch_scan_pass(a, st);
+  if (e == hipSuccess) e = la::launch_output_pass(a, st);
+  return e;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
 }  // namespace
 
 extern "C" {
@@ -151,12 +162,11 @@ int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const flo
   a.tbl_stride = (int)tbl_stride_for(block);
   a.states = (float*)((char*)ws + tbl_bytes);
   a.warm_start = a.in_dtype == la::kBF16 && block == 64;
+  a.rev = false;
+  a.scale_kv_out = false;
   a.evt_begin = evt_begin;
   a.evt_end = evt_end;
-  hipError_t e = la::launch_aggregate_pass(a, st);
-  if (e == hipSuccess && a.warm_start) e = la::launch_warm_start_pass(a, st);
-  if (e == hipSuccess) e = la::launch_scan_pass(a, st);
-  if (e == hipSuccess) e = la::launch_output_pass(a, st);
+  hipError_t e = run_passes(a, st);
   if (!workspace) {
     hipError_t f = hipFreeAsync(ws, st);
     if (e == hipSuccess) e = f;
@@ -183,6 +193,131 @@ int lightning_attn_fwd_bf16_f32out(const void* q, const void* k, const void* v, 
                                    int64_t N, int64_t d, int64_t block, void* stream) {
   return lightning_attn_fwd_ex(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, LA_DTYPE_BF16,
                                LA_DTYPE_F32, 0, nullptr, 0, nullptr, nullptr, stream);
+}
+
+size_t lightning_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  const int64_t L = pick_chunk(B, H, N, 64);
+  return align256(workspace_layout(B, H, N, d, 64, L, nullptr)) + 2 * align256((size_t)(B * H * d * d) * sizeof(float));
+}
+
+int lightning_attn_bwd(const void* q, const void* k, const void* v, const float* decay, const void* dout,
+                       const float* kv_in, const float* dkv_out, void* dq, void* dk, void* dv, float* dkv_in,
+                       int64_t B, int64_t H, int64_t N, int64_t d, int out_dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !decay || !dout || !dq || !dk || !dv) return LA_ERR_INVALID;
+  if (B < 1 || H < 1 || N < 1 || d < 1) return LA_ERR_INVALID;
+  if (out_dtype != LA_DTYPE_BF16 && out_dtype != LA_DTYPE_F32) return LA_ERR_INVALID;
+  const void* ptrs16[] = {q, k, v, dout, dq, dk, dv, kv_in, dkv_out, dkv_in};
+  for (const void* p : ptrs16)
+    if (!aligned(p, 16)) return LA_ERR_INVALID;
+  if (!aligned(decay, 4)) return LA_ERR_INVALID;
+  if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+  if (N > kMaxTokens) return LA_ERR_UNSUPPORTED;
+  const int64_t L = pick_chunk(B, H, N, 64);
+  if (B * H > kMaxGrid || B * H * ceil_div(N, L) > kMaxGrid) return LA_ERR_UNSUPPORTED;
+  const int64_t in_bytes = B * H * N * d * 2, out_bytes = B * H * N * d * (out_dtype == LA_DTYPE_BF16 ? 2 : 4);
+  const int64_t st_bytes = B * H * d * d * 4;
+  // outputs: apart from every input and from each other; dkv_in may be dkv_out itself
+  const void* outs[] = {dq, dk, dv};
+  const void* ins[] = {q, k, v, dout};
+  for (const void* o : outs) {
+    for (const void* i : ins)
+      if (overlap(o, out_bytes, i, in_bytes)) return LA_ERR_INVALID;
+    if (overlap(o, out_bytes, kv_in, st_bytes) || overlap(o, out_bytes, dkv_out, st_bytes) ||
+        overlap(o, out_bytes, dkv_in, st_bytes))
+      return LA_ERR_INVALID;
+  }
+  if (overlap(dq, out_bytes, dk, out_bytes) || overlap(dq, out_bytes, dv, out_bytes) ||
+      overlap(dk, out_bytes, dv, out_bytes))
+    return LA_ERR_INVALID;
+  if (dkv_in && dkv_in != dkv_out) {
+    for (const void* i : ins)
+      if (overlap(dkv_in, st_bytes, i, in_bytes)) return LA_ERR_INVALID;
+    if (overlap(dkv_in, st_bytes, kv_in, st_bytes) || overlap(dkv_in, st_bytes, dkv_out, st_bytes))
+      return LA_ERR_INVALID;
+  }
+  const size_t fwd_need = align256(workspace_layout(B, H, N, d, 64, L, nullptr));
+  const size_t need = fwd_need + 2 * align256((size_t)st_bytes);
+  if (workspace) {
+    if (workspace_bytes < need) return LA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return LA_ERR_INVALID;
+  }
+
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = workspace;
+  if (!ws) {
+    hipError_t e = hipMallocAsync(&ws, need, st);
+    if (e != hipSuccess) return e == hipErrorOutOfMemory ? LA_ERR_NOMEM : LA_ERR_HIP;
+  }
+  size_t tbl_bytes = 0;
+  workspace_layout(B, H, N, d, 64, L, &tbl_bytes);
+  float* s0t = (float*)((char*)ws + fwd_need);
+  float* dsnt = (float*)((char*)ws + fwd_need + align256((size_t)st_bytes));
+
+  la::PrefillArgs a;
+  a.decay = decay;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.block = 64;
+  a.L = L;
+  a.nc = (int)ceil_div(N, L);
+  a.in_dtype = la::kBF16;
+  a.out_dtype = out_dtype == LA_DTYPE_BF16 ? la::kBF16 : la::kF32;
+  a.tbl = (float*)ws;
+  a.tbl_stride = (int)tbl_stride_for(64);
+  a.states = (float*)((char*)ws + tbl_bytes);
+  a.warm_start = true;
+  a.evt_begin = nullptr;
+  a.evt_end = nullptr;
+
+  hipError_t e = hipSuccess;
+  if (kv_in) e = la::launch_transpose_states(kv_in, s0t, B * H, d, st);
+  if (e == hipSuccess && dkv_out) e = la::launch_transpose_states(dkv_out, dsnt, B * H, d, st);
+  // dQ: dq_t = dO_t S_t^T, a forward pass over (dO, V, K) from S0^T.
+  if (e == hipSuccess) {
+    a.q = dout;
+    a.k = v;
+    a.v = k;
+    a.out = dq;
+    a.kv_in = kv_in ? s0t : nullptr;
+    a.kv_out = nullptr;
+    a.rev = false;
+    a.scale_kv_out = false;
+    e = run_passes(a, st);
+  }
+  // dK: dk_t = v_t G_t^T, G^T run last token first over (V, dO, Q) from dSN^T.
+  if (e == hipSuccess) {
+    a.q = v;
+    a.k = dout;
+    a.v = q;
+    a.out = dk;
+    a.kv_in = dkv_out ? dsnt : nullptr;
+    a.kv_out = nullptr;
+    a.rev = true;
+    a.scale_kv_out = false;
+    e = run_passes(a, st);
+  }
+  // dV: dv_t = k_t G_t, G run last token first over (K, Q, dO) from dSN; its
+  // final state is G_0, and dS0 = lam G_0.
+  if (e == hipSuccess) {
+    a.q = k;
+    a.k = q;
+    a.v = dout;
+    a.out = dv;
+    a.kv_in = dkv_out;
+    a.kv_out = dkv_in;
+    a.rev = true;
+    a.scale_kv_out = true;
+    e = run_passes(a, st);
+  }
+  if (!workspace) {
+    hipError_t f = hipFreeAsync(ws, st);
+    if (e == hipSuccess) e = f;
+  }
+  return from_hip(e);
 }
 
 int64_t lightning_attn_fwd_chunk(int64_t B, int64_t H, int64_t N, int64_t block, int64_t chunk) {

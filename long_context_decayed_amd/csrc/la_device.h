@@ -332,10 +332,11 @@ __device__ __forceinline__ void sync_lds_after_vmem() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-// Rows [0, nvalid) of a 64-row tile (src: its row 0, wave-uniform) into the
+// Rows [0, nvalid) of a 64-row tile (src: its row 0, wave-uniform; row r at
+// src + r * RS elements, RS = -D for a tile read last row first) into the
 // swizzled LDS tile dst; rows >= nvalid become zero.  The NW waves split the
 // instructions.  Full tile: NI / NW 16-byte instructions per wave.
-template <int D, int NW>
+template <int D, int NW, int RS = D>
 __device__ __forceinline__ void dma_tile(const bf16* __restrict__ src, bf16* dst, int nvalid, int w, int lane) {
   const uint32_t t0 = lds_addr(dst);
   if (nvalid >= kSub) {
@@ -345,12 +346,12 @@ __device__ __forceinline__ void dma_tile(const bf16* __restrict__ src, bf16* dst
     for (int m = 0; m < NI / NW; ++m) {
       const int qi = w + NW * m;
       const int row = RPI * qi + rr;
-      dma_dwordx4(src + row * D + ((pc ^ swz(row)) << 3), t0 + 1024 * qi);
+      dma_dwordx4(src + row * RS + ((pc ^ swz(row)) << 3), t0 + 1024 * qi);
     }
   } else if (lane < D / 2) {
     for (int r = w; r < kSub; r += NW) {
       if (r < nvalid)
-        dma_dword(src + r * D + (((lane >> 2) ^ swz(r)) << 3) + 2 * (lane & 3), t0 + 2 * r * D);
+        dma_dword(src + r * RS + (((lane >> 2) ^ swz(r)) << 3) + 2 * (lane & 3), t0 + 2 * r * D);
       else
         *reinterpret_cast<uint32_t*>(dst + r * D + 2 * lane) = 0u;
     }

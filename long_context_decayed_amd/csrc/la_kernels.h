@@ -23,6 +23,8 @@ struct PrefillArgs {
   int tbl_stride;  // >= block + 1
   float* states;   // workspace: [B*H][nc][d][d]
   bool warm_start; // bf16 inputs, block 64: decaying heads take the warm-start pass
+  bool rev;        // tokens last first, kv_in entering undecayed (backward; bf16, block 64 only)
+  bool scale_kv_out; // kv_out = lam * final state (backward: gradient of kv_in)
   void* evt_begin; // optional hipEvent_t pair around the kernel that writes every output row
   void* evt_end;
 };
@@ -42,6 +44,9 @@ hipError_t launch_output_pass(const PrefillArgs& a, hipStream_t st);
 
 // Decode step; with `slots` (device int32[B]) batch row b uses state row
 // slots[b] of kv_in / kv_out ([num_slots][H][d][d]); rows out of range idle.
+// dst[bh] = src[bh]^T for BH fp32 d x d states: la_state.hip.
+hipError_t launch_transpose_states(const float* src, float* dst, int64_t BH, int64_t d, hipStream_t st);
+
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* decay, void* out,
                          const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t d, hipStream_t st,
                          const int* slots = nullptr, int64_t num_slots = 0);

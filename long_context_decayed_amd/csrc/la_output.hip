@@ -305,9 +305,15 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 //   kFromStart  the chunk from its true start state Sstart_c (read from
 //               `states` after the scan), for the other heads; decaying heads
 //               return at once.
+// REV: the reverse-time passes of the backward.  Token t of the pass is row
+// N-1-t of the tensors (rows are read and written last first), and the
+// initial state enters the first token undecayed: S_0 = kv_in + k_0^T v_0,
+// as the gradient of the final state does in the adjoint recurrence.  Only
+// the first sub-tile of chunk 0 differs: its rows take lam^p instead of
+// lam^(p+1) and it hands the state on decayed by lam^(n-1) instead of lam^n.
 enum { kWarmStart = 0, kFromStart = 1 };
 
-template <typename TOut, int D, int MODE>
+template <typename TOut, int D, int MODE, bool REV>
 __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                               const bf16* __restrict__ v, TOut* __restrict__ o,
                                                               const float* __restrict__ decay,
@@ -322,6 +328,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   constexpr int MAXT = (3 + NW - 1) / NW;  // score tiles per wave
   constexpr int kStores = sizeof(TOut) == 2 ? 2 * 2 : 2 * 4;  // output store instructions per sub-tile
   constexpr bool kDefer = sizeof(TOut) == 2;  // bf16 rows are stored during the next sub-tile's phase 1
+  constexpr int RS = REV ? -D : D;             // elements from one token's row to the next
   __shared__ __attribute__((aligned(16))) bf16 Qs[kSub * D];
   __shared__ __attribute__((aligned(16))) bf16 Ks[kSub * D];  // score operands (phase 1)
   __shared__ __attribute__((aligned(16))) bf16 Kt[kSub * D];  // update operands (phase 2)
@@ -338,7 +345,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   if (decaying != (MODE == kWarmStart)) return;
   const int t_begin = c * L;
   const int t_end = min(N, t_begin + L);
-  const int64_t base = (int64_t)bh * N * D;
+  const int64_t base = (int64_t)bh * N * D + (REV ? (int64_t)(N - 1) * D : 0);
   const bf16* qb = q + base;
   const bf16* kb = k + base;
   const bf16* vb = v + base;
@@ -372,9 +379,18 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   // state by lam^n and weights token s by lam^(n-1-s): lam^e for e < 64 is
   // kept one per lane and fetched by lane shuffle.
   float tlane = 0.0f, d_last = 0.0f;
+  const int n_last = (t_end - t_begin) - kSub * ((t_end - t_begin - 1) / kSub);  // tokens of the last sub-tile
   if constexpr (MODE == kWarmStart) {
     tlane = tb[lane];
-    d_last = tb[(t_end - t_begin) - kSub * ((t_end - t_begin - 1) / kSub)];
+    d_last = tb[n_last];
+  }
+  // REV, first sub-tile of chunk 0: lam^p for row p, state decayed by
+  // lam^63 (lam^(n-1) if it is also the last, partial one).
+  float rfu[2] = {0.0f, 0.0f}, d_first = 0.0f;
+  if constexpr (REV) {
+    rfu[0] = tb[l32];
+    rfu[1] = tb[l32 + 32];
+    d_first = (t_end - t_begin <= kSub) ? tb[n_last - 1] : tb[63];
   }
   for (int e = tid; e < 4 * 64; e += NW * 64) {
     const int jq = e >> 6, ln = e & 63;
@@ -427,17 +443,17 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
       // chunk start and span are multiples of 64) through the state update
       // alone, from S = 0, double-buffered in (Kt, Vs) and (Ks, Qs).
       const int nwu = span / kSub;
-      const int64_t off0 = (int64_t)(t_begin - span) * D;
-      dma_tile<D, NW>(kb + off0, Kt, kSub, w, lane);
-      dma_tile<D, NW>(vb + off0, Vs, kSub, w, lane);
+      const int64_t off0 = (int64_t)(t_begin - span) * RS;
+      dma_tile<D, NW, RS>(kb + off0, Kt, kSub, w, lane);
+      dma_tile<D, NW, RS>(vb + off0, Vs, kSub, w, lane);
       for (int j = 0; j < nwu; ++j) {
         const bool odd = (j & 1) != 0;
         // Sub-tile j is visible; every wave is done with the other buffer.
         sync_lds_after_vmem<0>();
         if (j + 1 < nwu) {
-          const int64_t offn = off0 + (int64_t)(j + 1) * kSub * D;
-          dma_tile<D, NW>(kb + offn, odd ? Kt : Ks, kSub, w, lane);
-          dma_tile<D, NW>(vb + offn, odd ? Vs : Qs, kSub, w, lane);
+          const int64_t offn = off0 + (int64_t)(j + 1) * kSub * RS;
+          dma_tile<D, NW, RS>(kb + offn, odd ? Kt : Ks, kSub, w, lane);
+          dma_tile<D, NW, RS>(vb + offn, odd ? Vs : Qs, kSub, w, lane);
         }
 #pragma unroll
         for (int kt = 0; kt < NRT; ++kt) S[kt] *= d64;
@@ -449,11 +465,11 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
 
   {
     const int nv = min(kSub, t_end - t_begin);
-    const int64_t off = (int64_t)t_begin * D;
-    dma_tile<D, NW>(qb + off, Qs, nv, w, lane);
-    dma_tile<D, NW>(kb + off, Ks, nv, w, lane);
-    dma_tile<D, NW>(kb + off, Kt, nv, w, lane);
-    dma_tile<D, NW>(vb + off, Vs, nv, w, lane);
+    const int64_t off = (int64_t)t_begin * RS;
+    dma_tile<D, NW, RS>(qb + off, Qs, nv, w, lane);
+    dma_tile<D, NW, RS>(kb + off, Ks, nv, w, lane);
+    dma_tile<D, NW, RS>(kb + off, Kt, nv, w, lane);
+    dma_tile<D, NW, RS>(vb + off, Vs, nv, w, lane);
     sync_lds_after_vmem<0>();
   }
   // bf16 output of the previous sub-tile, packed and lane-swapped, stored
@@ -464,8 +480,9 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   int t_pend = 0;
   for (int t0 = t_begin; t0 < t_end; t0 += kSub) {
     const bool more = t0 + kSub < t_end;
+    const bool first = REV && c == 0 && t0 == t_begin;
     const int nv_next = min(kSub, t_end - t0 - kSub);
-    const int64_t off_next = (int64_t)(t0 + kSub) * D;
+    const int64_t off_next = (int64_t)(t0 + kSub) * RS;
 
     // Phase 1.  Inter term acc[rt] = S_b^T Q^T for tokens 32rt + l (S split
     // into bf16 hi + lo on the fly) and this wave's score tiles P^T = K Q^T,
@@ -501,7 +518,9 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
           }
         }
       }
-      if constexpr (MODE == kWarmStart)
+      if (REV && first)
+        S[kt] *= d_first;
+      else if constexpr (MODE == kWarmStart)
         S[kt] *= more ? d64 : d_last;
       else
         S[kt] *= d64;
@@ -512,7 +531,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
 #pragma unroll
           for (int q = 0; q < 4 / NRT; ++q) {
             const int e = kt * (4 / NRT) + q, rt = e >> 1, pp = e & 1;
-            bf16* orow = reinterpret_cast<bf16*>(ob) + (int64_t)(t_pend + 32 * rt + l32) * D + 32 * w + 16 * pp + 8 * hf;
+            bf16* orow = reinterpret_cast<bf16*>(ob) + (int64_t)(t_pend + 32 * rt + l32) * RS + 32 * w + 16 * pp + 8 * hf;
             *reinterpret_cast<uint4*>(orow) = pend[rt][pp];
           }
         }
@@ -554,17 +573,19 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
     // element by element: as a vector-by-scalar product the compiler hoists a
     // 16-wide copy of each factor out of the loop (30 registers).
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 2; ++rt) {
+      const float r = (REV && first) ? rfu[rt] : rf[rt];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[rt][j] *= rf[rt];
+      for (int j = 0; j < 16; ++j) acc[rt][j] *= r;
+    }
 
     // This sub-tile's V and K^T copy (requested before the previous
     // sub-tile's kStores output stores, which may still be in flight) and
     // the score tiles become visible; Q and the score copy of K are free.
     sync_lds_after_vmem<kStores>();
     if (more) {
-      dma_tile<D, NW>(qb + off_next, Qs, nv_next, w, lane);
-      dma_tile<D, NW>(kb + off_next, Ks, nv_next, w, lane);
+      dma_tile<D, NW, RS>(qb + off_next, Qs, nv_next, w, lane);
+      dma_tile<D, NW, RS>(kb + off_next, Ks, nv_next, w, lane);
     }
 
     // Phase 2.  Intra-block term acc[rt] += V^T P^T over the shared score tiles.
@@ -587,8 +608,8 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
     // and visible; V, K^T and the score tiles are free from here on.
     sync_lds_after_vmem<0>();
     if (more) {
-      dma_tile<D, NW>(kb + off_next, Kt, nv_next, w, lane);
-      dma_tile<D, NW>(vb + off_next, Vs, nv_next, w, lane);
+      dma_tile<D, NW, RS>(kb + off_next, Kt, nv_next, w, lane);
+      dma_tile<D, NW, RS>(vb + off_next, Vs, nv_next, w, lane);
     }
 
     // Output rows.  Lane (h, l) holds token t0 + 32rt + l, columns 32w + 8jq
@@ -616,7 +637,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
       for (int rt = 0; rt < 2; ++rt) {
         const int t = t0 + 32 * rt + l32;
         if (t < t_end) {
-          TOut* orow = ob + (int64_t)t * D + 32 * w + 4 * hf;
+          TOut* orow = ob + (int64_t)t * RS + 32 * w + 4 * hf;
 #pragma unroll
           for (int jq = 0; jq < 4; ++jq)
             *reinterpret_cast<f32x4*>(orow + 8 * jq) =
@@ -632,7 +653,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
       for (int rt = 0; rt < 2; ++rt) {
         const int t = t_pend + 32 * rt + l32;
         if (t < t_end) {
-          bf16* orow = reinterpret_cast<bf16*>(ob) + (int64_t)t * D + 32 * w + 8 * hf;
+          bf16* orow = reinterpret_cast<bf16*>(ob) + (int64_t)t * RS + 32 * w + 8 * hf;
           *reinterpret_cast<uint4*>(orow) = pend[rt][0];
           *reinterpret_cast<uint4*>(orow + 16) = pend[rt][1];
         }
@@ -680,6 +701,19 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
 
 // The events bracket the kernel that writes every output row: the
 // warm-start pass when there is one (bf16 inputs, block 64), else this one.
+template <typename TOut, int D, int MODE>
+static void launch_fast(const PrefillArgs& a, hipStream_t st) {
+  const unsigned grid = (unsigned)(a.B * a.H * a.nc);
+  if (a.rev)
+    hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, true>), dim3(grid), dim3(D * 2), 0, st, (const bf16*)a.q,
+                       (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, a.decay, (const float*)a.tbl, a.states,
+                       a.kv_in, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride);
+  else
+    hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, false>), dim3(grid), dim3(D * 2), 0, st, (const bf16*)a.q,
+                       (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, a.decay, (const float*)a.tbl, a.states,
+                       a.kv_in, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride);
+}
+
 template <typename TIn, typename TOut, int D, int BLK>
 static hipError_t launch_output_t(const PrefillArgs& a, hipStream_t st) {
   const int BH = (int)(a.B * a.H);
@@ -690,9 +724,7 @@ static hipError_t launch_output_t(const PrefillArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if constexpr (BLK == 64 && sizeof(TIn) == 2)
-    hipLaunchKernelGGL((la_chunk_output64<TOut, D, kFromStart>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, a.decay,
-                       (const float*)a.tbl, a.states, a.kv_in, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
+    launch_fast<TOut, D, kFromStart>(a, st);
   else
     hipLaunchKernelGGL((la_chunk_output<TIn, TOut, D, BLK>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                        (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (TOut*)a.out, (const float*)a.tbl,
@@ -706,15 +738,11 @@ static hipError_t launch_output_t(const PrefillArgs& a, hipStream_t st) {
 
 template <typename TOut, int D>
 static hipError_t launch_warm_start_t(const PrefillArgs& a, hipStream_t st) {
-  const int BH = (int)(a.B * a.H);
-  const int nc = a.nc;
   if (a.evt_begin) {
     hipError_t e = hipEventRecord((hipEvent_t)a.evt_begin, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((la_chunk_output64<TOut, D, kWarmStart>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
-                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, a.decay,
-                     (const float*)a.tbl, a.states, a.kv_in, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
+  launch_fast<TOut, D, kWarmStart>(a, st);
   if (a.evt_end) {
     hipError_t e = hipEventRecord((hipEvent_t)a.evt_end, st);
     if (e != hipSuccess) return e;

@@ -133,8 +133,10 @@ __global__ __launch_bounds__(D * 2, sizeof(TIn) == 2 ? 3 : 1) void la_chunk_stat
 // transpose-read operands): lam^(63-s) u = ul[i] * (lam^(48-16kk) u) with the
 // per-lane ul[i] = lam^(15 - crow(i, h)).
 //   With skip_decaying set, heads that decay within their chunk return at
-// once: the warm-start output pass needs no aggregates.
-template <int D>
+// once: the warm-start output pass needs no aggregates.  REV reads the
+// tokens last first (token t of the pass is row N-1-t), for the reverse-time
+// passes of the backward; the aggregates start from zero either way.
+template <int D, bool REV>
 __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restrict__ k, const bf16* __restrict__ v,
                                                              const float* __restrict__ decay,
                                                              const float* __restrict__ tbl_all, float* __restrict__ ws,
@@ -152,7 +154,8 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
   const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
   const int hh = bh % H;
   if (skip_decaying && decays_within_chunk(carry_span(decay[hh]), L)) return;
-  const int64_t base = (int64_t)bh * N * D;
+  constexpr int RS = REV ? -D : D;  // elements from one token's row to the next
+  const int64_t base = (int64_t)bh * N * D + (REV ? (int64_t)(N - 1) * D : 0);
   const bf16* kb = k + base;
   const bf16* vb = v + base;
   const int t_begin = c * L;
@@ -173,9 +176,9 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
   const int nsub = (lc + kSub - 1) / kSub;
   const int n_last = lc - (nsub - 1) * kSub;  // 1..64
   {
-    const int64_t off = (int64_t)(t_begin + (nsub - 1) * kSub) * D;
-    dma_tile<D, NW>(kb + off, Ks[0], n_last, w, lane);
-    dma_tile<D, NW>(vb + off, Vs[0], n_last, w, lane);
+    const int64_t off = (int64_t)(t_begin + (nsub - 1) * kSub) * RS;
+    dma_tile<D, NW, RS>(kb + off, Ks[0], n_last, w, lane);
+    dma_tile<D, NW, RS>(vb + off, Vs[0], n_last, w, lane);
   }
   double ud = 1.0;  // u_b of the next full sub-tile
   int b = nsub - 1, cur = 0;
@@ -184,9 +187,9 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
     // tokens s < n_last get lam^(n_last-1-s), the rest 0.
     sync_lds_after_vmem<0>();
     if (b > 0) {
-      const int64_t off = (int64_t)(t_begin + (b - 1) * kSub) * D;
-      dma_tile<D, NW>(kb + off, Ks[1], kSub, w, lane);
-      dma_tile<D, NW>(vb + off, Vs[1], kSub, w, lane);
+      const int64_t off = (int64_t)(t_begin + (b - 1) * kSub) * RS;
+      dma_tile<D, NW, RS>(kb + off, Ks[1], kSub, w, lane);
+      dma_tile<D, NW, RS>(vb + off, Vs[1], kSub, w, lane);
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -215,9 +218,9 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
     // with the other buffer, which now receives sub-tile b - 1.
     sync_lds_after_vmem<0>();
     if (b > 0) {
-      const int64_t off = (int64_t)(t_begin + (b - 1) * kSub) * D;
-      dma_tile<D, NW>(kb + off, Ks[cur ^ 1], kSub, w, lane);
-      dma_tile<D, NW>(vb + off, Vs[cur ^ 1], kSub, w, lane);
+      const int64_t off = (int64_t)(t_begin + (b - 1) * kSub) * RS;
+      dma_tile<D, NW, RS>(kb + off, Ks[cur ^ 1], kSub, w, lane);
+      dma_tile<D, NW, RS>(vb + off, Vs[cur ^ 1], kSub, w, lane);
     }
     const bf16* Kc = Ks[cur];
     const bf16* Vc = Vs[cur];
@@ -254,22 +257,29 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
 // over chunks.  ws holds U_c on entry and Sstart_c on exit.  With warm set,
 // a head that decays within its chunk has its final state in its last
 // chunk's slot already (warm-start pass), which is only copied to kv_out.
+// With undecayed set, kv_in enters the first token without decay (chunk 0
+// hands on lam^(L_0 - 1) kv_in + U_0); with scale_out, kv_out receives lam
+// times the final state (the backward's gradient of the initial state).
 __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ decay, float* __restrict__ ws,
                                                      const float* __restrict__ kv_in, float* __restrict__ kv_out,
-                                                     int BH, int H, int N, int L, int nc, int D, int warm) {
+                                                     int BH, int H, int N, int L, int nc, int D, int warm,
+                                                     int undecayed, int scale_out) {
   const int per = D * D / 4;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)BH * per) return;
   const int bh = (int)(gid / per), e4 = (int)(gid - (int64_t)bh * per);
+  const float out_f = scale_out ? decay[bh % H] : 1.0f;
   if (warm && decays_within_chunk(carry_span(decay[bh % H]), L)) {
     if (kv_out)
       reinterpret_cast<f32x4*>(kv_out)[(int64_t)bh * per + e4] =
-          reinterpret_cast<const f32x4*>(ws)[((int64_t)bh * nc + nc - 1) * per + e4];
+          out_f * reinterpret_cast<const f32x4*>(ws)[((int64_t)bh * nc + nc - 1) * per + e4];
     return;
   }
   const double lam = (double)decay[bh % H];
   const float dl = (float)pow_int(lam, L);
   const float dlast = (float)pow_int(lam, N - (nc - 1) * L);
+  // chunk 0's factor on the state it receives (one power less when undecayed)
+  const float d0 = (float)pow_int(lam, (nc == 1 ? N : L) - (undecayed ? 1 : 0));
   f32x4 S = {0.f, 0.f, 0.f, 0.f};
   if (kv_in) S = reinterpret_cast<const f32x4*>(kv_in)[(int64_t)bh * per + e4];
   f32x4* U = reinterpret_cast<f32x4*>(ws) + (int64_t)bh * nc * per + e4;
@@ -281,17 +291,37 @@ __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ d
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       U[(int64_t)(c + i) * per] = S;
-      const float f = (c + i == nc - 1) ? dlast : dl;
+      const float f = (c + i == 0) ? d0 : (c + i == nc - 1) ? dlast : dl;
       S = f * S + u[i];
     }
   }
   for (; c < nc; ++c) {
     const f32x4 u = U[(int64_t)c * per];
     U[(int64_t)c * per] = S;
-    const float f = (c == nc - 1) ? dlast : dl;
+    const float f = (c == 0) ? d0 : (c == nc - 1) ? dlast : dl;
     S = f * S + u;
   }
-  if (kv_out) reinterpret_cast<f32x4*>(kv_out)[(int64_t)bh * per + e4] = S;
+  if (kv_out) reinterpret_cast<f32x4*>(kv_out)[(int64_t)bh * per + e4] = out_f * S;
+}
+
+// ---------------------------------------------------------------------------
+// dst[bh] = src[bh]^T for BH fp32 d x d states (the backward passes take the
+// transposed initial state and final-state gradient).  One thread per
+// element; writes are contiguous.
+__global__ __launch_bounds__(256) void la_transpose_states(const float* __restrict__ src, float* __restrict__ dst,
+                                                           int64_t BH, int D) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per = (int64_t)D * D;
+  if (gid >= BH * per) return;
+  const int64_t bh = gid / per;
+  const int e = (int)(gid - bh * per), i = e / D, j = e - (e / D) * D;
+  dst[gid] = src[bh * per + (int64_t)j * D + i];
+}
+
+hipError_t launch_transpose_states(const float* src, float* dst, int64_t BH, int64_t d, hipStream_t st) {
+  const int64_t n = BH * d * d;
+  hipLaunchKernelGGL(la_transpose_states, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, dst, BH, (int)d);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -302,11 +332,16 @@ static hipError_t launch_aggregate_t(const PrefillArgs& a, hipStream_t st) {
   const int BH = (int)(a.B * a.H);
   const int nc = a.nc;
   hipLaunchKernelGGL(la_decay_table, dim3((unsigned)a.H), dim3(256), 0, st, a.decay, a.tbl, a.tbl_stride);
-  if constexpr (sizeof(TIn) == 2)
-    hipLaunchKernelGGL((la_chunk_state64<D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st, (const bf16*)a.k,
-                       (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc,
-                       a.tbl_stride, a.warm_start ? 1 : 0);
-  else
+  if constexpr (sizeof(TIn) == 2) {
+    if (a.rev)
+      hipLaunchKernelGGL((la_chunk_state64<D, true>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+                         (const bf16*)a.k, (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H,
+                         (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0);
+    else
+      hipLaunchKernelGGL((la_chunk_state64<D, false>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+                         (const bf16*)a.k, (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H,
+                         (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0);
+  } else
     hipLaunchKernelGGL((la_chunk_state<TIn, D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st, (const TIn*)a.k,
                        (const TIn*)a.v, (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc,
                        a.tbl_stride);
@@ -324,7 +359,8 @@ hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st) {
   const int D = (int)a.d;
   const int64_t threads = (int64_t)BH * D * D / 4;
   hipLaunchKernelGGL(la_chunk_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a.decay, a.states,
-                     a.kv_in, a.kv_out, BH, (int)a.H, (int)a.N, (int)a.L, a.nc, D, a.warm_start ? 1 : 0);
+                     a.kv_in, a.kv_out, BH, (int)a.H, (int)a.N, (int)a.L, a.nc, D, a.warm_start ? 1 : 0,
+                     a.rev ? 1 : 0, a.scale_kv_out ? 1 : 0);
   return hipGetLastError();
 }
 
