@@ -11,6 +11,9 @@
   truncation error is at most lam_max^8193 = e^-32 of the state.
 * Long-range carries: lam = 1 over 2^20 tokens (nothing decays, so every
   chunk's contribution reaches the end).
+* Backward of the million-token layer: the interior and the final slice of
+  dq, dk, dv against the gradient oracle (prefix state from the GPU forward,
+  a future window for the adjoint).
 """
 import numpy as np
 import pytest
@@ -20,7 +23,8 @@ import long_context_decayed_amd as la
 import oracle as ora
 from long_context_decayed_amd.inputs import decay_lambdas, qkv_device, state_device
 import tolerances as tol
-from gpu_helpers import host, lam_for, oracle, require_gpu, say
+from gpu_helpers import host, lam_for, oracle, oracle_threads, require_gpu, say
+from oracle import crec
 
 pytestmark = pytest.mark.gpu
 
@@ -145,3 +149,33 @@ def test_lambda_one_million_tokens(dev):
     kh, vh = host(k).astype(np.float64), host(v).astype(np.float64)
     st = np.matmul(np.swapaxes(kh, -1, -2), vh)
     tol.assert_state(host(kv), st, "kv_out vs K^T V")
+
+
+def test_million_token_backward_slices(dev, million):
+    """Backward at the million-token size, on slices the oracle can compute.
+
+    dq on [t0, t0+w) needs the forward state at t0: the oracle starts from the
+    GPU forward's kv_out of the prefix.  dk and dv on the slice need the adjoint
+    state from the future: the oracle runs the slice plus the next w tokens
+    with a zero final-state gradient, whose truncation is at most lam_max^w =
+    e^-32 of that state.  The last slice is exact (the sequence ends there)."""
+    q, k, v, lam, t0 = million
+    B, H, N, d = q.shape
+    w = 8192
+    lam_t = torch.from_numpy(lam).to(dev)
+    g = qkv_device(B, H, N, d, seed=30, device=dev, slice_tokens=65536)[0]
+    dq, dk, dv, _ = la.bwd(q, k, v, lam_t, g, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for a in (t0, N - w):
+        say("million-token backward: slice at", a)
+        kv_pre = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+        la.fwd(q[:, :, :a].contiguous(), k[:, :, :a].contiguous(), v[:, :, :a].contiguous(), lam_t, kv_out=kv_pre,
+               block=64)
+        torch.cuda.synchronize()
+        b = min(N, a + 2 * w)
+        sl = lambda x: host(x[:, :, a:b])
+        rq, rk, rv, _ = crec.backward(sl(q), sl(k), sl(v), lam.astype(np.float64), sl(g),
+                                      host(kv_pre).astype(np.float64), None, threads=oracle_threads())
+        for got, ref, name in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+            e = tol.assert_bf16_f32out(host(got[:, :, a:a + w]), ref[:, :, :w], "%s slice %d" % (name, a))
+            print("%s slice at %d: max|err|/RMS %.3e" % (name, a, e))
