@@ -123,6 +123,22 @@ int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const flo
                           size_t workspace_bytes, void* evt_begin, void* evt_end, void* stream);
 
 /*
+ * Prefill into a pool of states (serving: chunked prefill of several
+ * requests into their existing states).  The same computation as
+ * lightning_attn_fwd_ex with kv_in = kv_out, except that batch row b starts
+ * from, and writes its final state back to, pool slot slots[b] (in place).
+ *   states    : float [num_slots][H][d][d]           (read and written)
+ *   slots     : int32 [B], device memory             (read)
+ *   other arguments as lightning_attn_fwd_ex (default chunk, stream-ordered
+ *   workspace allocation)
+ * A row whose slot lies outside [0, num_slots) starts from a zero state and
+ * keeps no final state.  Two rows naming the same slot race (undefined).
+ */
+int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const float* decay, void* out,
+                             float* states, const int32_t* slots, int64_t B, int64_t H, int64_t N, int64_t d,
+                             int64_t num_slots, int64_t block, int in_dtype, int out_dtype, void* stream);
+
+/*
  * Backward pass of the bf16 prefill: the gradients of a loss L given
  * dout = dL/dO and dkv_out = dL/d(kv_out).  This is the derivative of the
  * recurrence above (the pages print no backward pass).  With the adjoint

@@ -65,6 +65,8 @@ def load():
     lib.lightning_attn_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64]
     lib.lightning_attn_decode_step.restype = I
     lib.lightning_attn_decode_step.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, P]
+    lib.lightning_attn_fwd_slots.restype = I
+    lib.lightning_attn_fwd_slots.argtypes = [P] * 7 + [I64, I64, I64, I64, I64, I64, I, I, P]
     lib.lightning_attn_bwd.restype = I
     lib.lightning_attn_bwd.argtypes = [P] * 11 + [I64, I64, I64, I64, I, P, SZ, P]
     lib.lightning_attn_bwd_workspace_bytes.restype = SZ
@@ -186,6 +188,35 @@ def decode_step(q, k, v, decay, kv_in=None, kv_out=None, out=None, stream=None):
     return out
 
 
+def fwd_slots(q, k, v, decay, states, slots, block=64, out=None, out_dtype=None, stream=None):
+    """Prefill into a state pool.  q, k, v: [B, H, N, d]; states: fp32
+    [num_slots, H, d, d], read and written in place for the rows' slots;
+    slots: int32 [B] on the device (out of range: zero start, no write-back).
+    Returns out [B, H, N, d] in out_dtype (default: the input dtype)."""
+    lib = load()
+    B, H, N, d = q.shape
+    if q.dtype not in _DT:
+        raise TypeError("q must be bfloat16 or float32")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype, (B, H, N, d))
+    _check_dev("decay", decay, torch.float32, (H,))
+    if states.dim() != 4:
+        raise ValueError("states must be [num_slots, H, d, d]")
+    _check_dev("states", states, torch.float32, (states.shape[0], H, d, d))
+    _check_dev("slots", slots, torch.int32, (B,))
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, H, N, d), device=q.device, dtype=out_dtype)
+    _check_dev("out", out, out_dtype, (B, H, N, d))
+    rc = lib.lightning_attn_fwd_slots(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(states), _ptr(slots), B, H, N, d,
+        states.shape[0], block, _DT[q.dtype], _DT[out_dtype], _stream(stream)
+    )
+    if rc != 0:
+        raise LightningAttnError(rc, "lightning_attn_fwd_slots")
+    return out
+
+
 def bwd(q, k, v, decay, dout, kv_in=None, dkv_out=None, out_dtype=None, dkv_in=False, workspace=None,
         stream=None):
     """Backward pass.  q, k, v, dout: [B, H, N, d] bf16 device tensors; decay fp32
@@ -202,7 +233,7 @@ def bwd(q, k, v, decay, dout, kv_in=None, dkv_out=None, out_dtype=None, dkv_in=F
         if t is not None:
             _check_dev(name, t, torch.float32, (B, H, d, d))
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
-    code = {torch.bfloat16: 0, torch.float32: 1}[out_dtype]
+    code = _DT[out_dtype]
     dq, dk, dv = (torch.empty((B, H, N, d), device=q.device, dtype=out_dtype) for _ in range(3))
     if dkv_in is True:
         dkv_in = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32)

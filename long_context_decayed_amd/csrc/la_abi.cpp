@@ -117,6 +117,11 @@ hipError_t run_passes(const la::PrefillArgs& a, hipStream_t st) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+int prefill_run(const void* q, const void* k, const void* v, const float* decay, void* out, const float* kv_in,
+                float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, int in_dtype,
+                int out_dtype, int64_t L, void* workspace, size_t workspace_bytes, void* evt_begin, void* evt_end,
+                void* stream, const int* slots, int64_t num_slots);
+
 }  // namespace
 
 extern "C" {
@@ -128,6 +133,39 @@ int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const flo
   int64_t L = 0;
   int rc = validate_prefill(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, in_dtype, out_dtype, chunk, &L);
   if (rc != LA_OK) return rc;
+  return prefill_run(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, in_dtype, out_dtype, L, workspace,
+                     workspace_bytes, evt_begin, evt_end, stream, nullptr, 0);
+}
+
+int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const float* decay, void* out,
+                             float* states, const int32_t* slots, int64_t B, int64_t H, int64_t N, int64_t d,
+                             int64_t num_slots, int64_t block, int in_dtype, int out_dtype, void* stream) {
+  if (!states || !slots || num_slots < 1) return LA_ERR_INVALID;
+  if (!aligned(states, 16) || !aligned(slots, 4)) return LA_ERR_INVALID;
+  if (num_slots > kMaxGrid) return LA_ERR_UNSUPPORTED;
+  // validate the token tensors alone, then the pool against them
+  int64_t L = 0;
+  int rc = validate_prefill(q, k, v, decay, out, nullptr, nullptr, B, H, N, d, block, in_dtype, out_dtype, 0, &L);
+  if (rc != LA_OK) return rc;
+  const int64_t in_es = in_dtype == LA_DTYPE_BF16 ? 2 : 4, out_es = out_dtype == LA_DTYPE_BF16 ? 2 : 4;
+  const int64_t in_bytes = B * H * N * d * in_es, out_bytes = B * H * N * d * out_es;
+  const int64_t pool_bytes = num_slots * H * d * d * 4;
+  if (overlap(states, pool_bytes, q, in_bytes) || overlap(states, pool_bytes, k, in_bytes) ||
+      overlap(states, pool_bytes, v, in_bytes) || overlap(states, pool_bytes, out, out_bytes) ||
+      overlap(states, pool_bytes, slots, B * 4) || overlap(out, out_bytes, slots, B * 4))
+    return LA_ERR_INVALID;
+  return prefill_run(q, k, v, decay, out, states, states, B, H, N, d, block, in_dtype, out_dtype, L, nullptr, 0,
+                     nullptr, nullptr, stream, (const int*)slots, num_slots);
+}
+
+}  // extern "C"
+
+namespace {
+
+int prefill_run(const void* q, const void* k, const void* v, const float* decay, void* out, const float* kv_in,
+                float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, int in_dtype,
+                int out_dtype, int64_t L, void* workspace, size_t workspace_bytes, void* evt_begin, void* evt_end,
+                void* stream, const int* slots, int64_t num_slots) {
   size_t tbl_bytes = 0;
   const size_t need = workspace_layout(B, H, N, d, block, L, &tbl_bytes);
   if (workspace) {
@@ -164,6 +202,8 @@ int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const flo
   a.warm_start = a.in_dtype == la::kBF16 && block == 64;
   a.rev = false;
   a.scale_kv_out = false;
+  a.slots = slots;
+  a.num_slots = num_slots;
   a.evt_begin = evt_begin;
   a.evt_end = evt_end;
   hipError_t e = run_passes(a, st);
@@ -173,6 +213,10 @@ int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const flo
   }
   return from_hip(e);
 }
+
+}  // namespace
+
+extern "C" {
 
 int lightning_attn_fwd(const void* q, const void* k, const void* v, const float* decay, void* out,
                        const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
@@ -270,6 +314,8 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
   a.tbl_stride = (int)tbl_stride_for(64);
   a.states = (float*)((char*)ws + tbl_bytes);
   a.warm_start = true;
+  a.slots = nullptr;
+  a.num_slots = 0;
   a.evt_begin = nullptr;
   a.evt_end = nullptr;
 

@@ -50,6 +50,16 @@ __device__ __forceinline__ int carry_span(float lam) {
 // tokens before it build from zero, with no scan over chunks.
 __device__ __forceinline__ bool decays_within_chunk(int span, int L) { return 3ll * (long long)span <= (long long)L; }
 
+// Row of the initial / final state array that (batch, head) pair bh uses:
+// bh itself, or, with a slot table, slot slots[b] of a pool of num_slots
+// (each of H heads); -1 when the slot is out of range (no state: start from
+// zero and keep no final state).
+__device__ __forceinline__ int64_t state_row(int64_t bh, int H, const int* slots, int64_t num_slots) {
+  if (!slots) return bh;
+  const int64_t b = bh / H, s = slots[b];
+  return (s >= 0 && s < num_slots) ? s * H + (bh - b * H) : -1;
+}
+
 // MFMA traits.  One instruction contracts KW elements; every lane contributes
 // EPL of them (lanes 0-31 and 32-63 split the contraction).  A and B use the
 // same (lane half, element) -> k correspondence, so any fixed permutation of

@@ -320,7 +320,8 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
                                                               const float* __restrict__ tbl_all,
                                                               float* __restrict__ states,
                                                               const float* __restrict__ kv_in, int H, int N, int L,
-                                                              int nc, int tbl_stride) {
+                                                              int nc, int tbl_stride, const int* __restrict__ slots,
+                                                              int64_t num_slots) {
   typedef Mfma<bf16> M;
   typedef M::op_t op_t;
   constexpr int NW = D / 32;
@@ -403,8 +404,9 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   // value column col, where pf swaps bits 2 and 3:
   //   pf(crow(j, h)) = 16(j >> 3) + 8h + 4((j >> 2) & 1) + (j & 3).
   f32x16 S[NRT];
+  const int64_t srow = (MODE == kWarmStart && c == 0 && kv_in != nullptr) ? state_row(bh, H, slots, num_slots) : -1;
   const float* s_src = MODE == kFromStart ? states + ((int64_t)bh * nc + c) * D * D
-                                          : (c == 0 && kv_in != nullptr ? kv_in + (int64_t)bh * D * D : nullptr);
+                                          : (srow >= 0 ? kv_in + srow * D * D : nullptr);
   if (s_src) {
 #pragma unroll
     for (int kt = 0; kt < NRT; ++kt)
@@ -707,11 +709,11 @@ static void launch_fast(const PrefillArgs& a, hipStream_t st) {
   if (a.rev)
     hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, true>), dim3(grid), dim3(D * 2), 0, st, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, a.decay, (const float*)a.tbl, a.states,
-                       a.kv_in, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride);
+                       a.kv_in, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots, a.num_slots);
   else
     hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, false>), dim3(grid), dim3(D * 2), 0, st, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, a.decay, (const float*)a.tbl, a.states,
-                       a.kv_in, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride);
+                       a.kv_in, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots, a.num_slots);
 }
 
 template <typename TIn, typename TOut, int D, int BLK>

@@ -263,15 +263,21 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
 __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ decay, float* __restrict__ ws,
                                                      const float* __restrict__ kv_in, float* __restrict__ kv_out,
                                                      int BH, int H, int N, int L, int nc, int D, int warm,
-                                                     int undecayed, int scale_out) {
+                                                     int undecayed, int scale_out, const int* __restrict__ slots,
+                                                     int64_t num_slots) {
   const int per = D * D / 4;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)BH * per) return;
   const int bh = (int)(gid / per), e4 = (int)(gid - (int64_t)bh * per);
+  const int64_t srow = state_row(bh, H, slots, num_slots);  // kv_in / kv_out row; -1: none
+  if (srow < 0) {
+    kv_in = nullptr;
+    kv_out = nullptr;
+  }
   const float out_f = scale_out ? decay[bh % H] : 1.0f;
   if (warm && decays_within_chunk(carry_span(decay[bh % H]), L)) {
     if (kv_out)
-      reinterpret_cast<f32x4*>(kv_out)[(int64_t)bh * per + e4] =
+      reinterpret_cast<f32x4*>(kv_out)[srow * per + e4] =
           out_f * reinterpret_cast<const f32x4*>(ws)[((int64_t)bh * nc + nc - 1) * per + e4];
     return;
   }
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ d
   // chunk 0's factor on the state it receives (one power less when undecayed)
   const float d0 = (float)pow_int(lam, (nc == 1 ? N : L) - (undecayed ? 1 : 0));
   f32x4 S = {0.f, 0.f, 0.f, 0.f};
-  if (kv_in) S = reinterpret_cast<const f32x4*>(kv_in)[(int64_t)bh * per + e4];
+  if (kv_in) S = reinterpret_cast<const f32x4*>(kv_in)[srow * per + e4];
   f32x4* U = reinterpret_cast<f32x4*>(ws) + (int64_t)bh * nc * per + e4;
   int c = 0;
   for (; c + 4 <= nc; c += 4) {
@@ -301,7 +307,7 @@ __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ d
     const float f = (c == 0) ? d0 : (c == nc - 1) ? dlast : dl;
     S = f * S + u;
   }
-  if (kv_out) reinterpret_cast<f32x4*>(kv_out)[(int64_t)bh * per + e4] = out_f * S;
+  if (kv_out) reinterpret_cast<f32x4*>(kv_out)[srow * per + e4] = out_f * S;
 }
 
 // ---------------------------------------------------------------------------
@@ -360,7 +366,7 @@ hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st) {
   const int64_t threads = (int64_t)BH * D * D / 4;
   hipLaunchKernelGGL(la_chunk_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a.decay, a.states,
                      a.kv_in, a.kv_out, BH, (int)a.H, (int)a.N, (int)a.L, a.nc, D, a.warm_start ? 1 : 0,
-                     a.rev ? 1 : 0, a.scale_kv_out ? 1 : 0);
+                     a.rev ? 1 : 0, a.scale_kv_out ? 1 : 0, a.slots, a.num_slots);
   return hipGetLastError();
 }
 

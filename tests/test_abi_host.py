@@ -146,6 +146,23 @@ def test_decode_slots_validation(lib):
     assert f(*ok[:5], FAKE[6], FAKE[6], 1, 1, 128, 4, None) == LA_ERR_INVALID   # slots inside the pool
 
 
+def test_fwd_slots_validation(lib):
+    f = lib.lightning_attn_fwd_slots
+    base = [FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], FAKE[5], FAKE[6], 1, 1, 128, 64, 4, 64, 0, 0, None]
+    assert f(*base[:5], None, *base[6:]) == LA_ERR_INVALID          # no pool
+    assert f(*base[:6], None, *base[7:]) == LA_ERR_INVALID          # no slot table
+    a = list(base); a[11] = 0
+    assert f(*a) == LA_ERR_INVALID                                  # empty pool
+    a = list(base); a[12] = 100
+    assert f(*a) == LA_ERR_INVALID                                  # bad block
+    a = list(base); a[10] = 96
+    assert f(*a) == LA_ERR_UNSUPPORTED
+    a = list(base); a[5] = FAKE[0]
+    assert f(*a) == LA_ERR_INVALID                                  # pool overlaps q
+    a = list(base); a[6] = FAKE[5]
+    assert f(*a) == LA_ERR_INVALID                                  # slot table inside the pool
+
+
 def test_bwd_validation(lib):
     f = lib.lightning_attn_bwd
     q, k, v, dec, g = FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4]

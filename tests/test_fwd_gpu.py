@@ -258,3 +258,42 @@ def test_bf16_long_range_carry(dev, mode):
     o_ref, s_ref = oracle(host(q), host(k), host(v), lam)
     tol.assert_bf16_f32out(host(o32), o_ref)
     tol.assert_state(host(kv), s_ref)
+
+
+# --- prefill into a pool of states (serving) ----------------------------------
+
+@pytest.mark.parametrize("block,n", [(64, 100), (64, 2048 + 37), (256, 700)])
+def test_fwd_slots_against_oracle(dev, block, n):
+    say("prefill into a state pool: pool 10 x H8, rows -> slots [7, 2, -1, 9], N", n, "block", block)
+    H, P, d = 8, 10, 64
+    slots_h = np.array([7, 2, -1, 9], dtype=np.int32)
+    B = len(slots_h)
+    q, k, v = qkv_device(B, H, n, d, seed=100 + n, device=dev)
+    pool = state_device(P, H, d, seed=100 + n, device=dev)
+    pool0 = host(pool).astype(np.float64)
+    o = la.fwd_slots(q, k, v, torch.from_numpy(MIXED_LAMS).to(dev), pool, torch.from_numpy(slots_h).to(dev),
+                     block=block, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    pool1 = host(pool).astype(np.float64)
+    for b, s in enumerate(slots_h):
+        s0 = pool0[s] if 0 <= s < P else None
+        o_ref, s_ref = oracle(host(q)[b], host(k)[b], host(v)[b], MIXED_LAMS, s0)
+        for h in range(H):
+            tol.assert_bf16_f32out(host(o)[b, h], o_ref[h], "row %d head %d" % (b, h))
+            if 0 <= s < P:
+                tol.assert_state(pool1[s, h], s_ref[h], "slot %d head %d" % (s, h))
+    untouched = [s for s in range(P) if s not in slots_h]
+    assert np.array_equal(pool1[untouched], pool0[untouched]), "slots not named must not change"
+
+
+def test_fwd_slots_identity_matches_fwd(dev):
+    say("fwd_slots with slots = 0..B-1 vs fwd with kv_in = kv_out, B3 H8 N3000")
+    B, H, n, d = 3, 8, 3000, 128
+    q, k, v = qkv_device(B, H, n, d, seed=110, device=dev)
+    lam_t = torch.from_numpy(MIXED_LAMS).to(dev)
+    s0 = state_device(B, H, d, seed=110, device=dev)
+    pool = s0.clone()
+    o1 = la.fwd(q, k, v, lam_t, kv_in=s0, kv_out=s0, block=64)
+    o2 = la.fwd_slots(q, k, v, lam_t, pool, torch.arange(B, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s0, pool)
