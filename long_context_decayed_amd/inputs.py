@@ -11,6 +11,10 @@ Workload recipe
   with ALiBi-style slopes.  With H heads the slope of head h is
   2^(-(8/H)(h+1)) and the decay is lambda_h = exp(-slope), evaluated in float64
   and rounded once to float32 (H = 64: lambda_0 = 0.39971, lambda_63 = 0.99610).
+* Depth-scaled decays.  The same field says the slopes are scaled down
+  linearly with depth without giving the law; the plainest reading is
+  slope_h * (1 - l / (L - 1)) for layer l of L, so the first layer has the
+  slopes above and the last has none (lambda = 1).
 * Q, K, V ~ N(0, 1) / sqrt(d): Gaussian stand-ins for the SiLU-activated
   projections of a trained layer (no weights are involved).
 * Initial states ~ N(0, std^2) in float32 (std = 0.1 by default).
@@ -22,6 +26,7 @@ import torch
 
 __all__ = [
     "decay_lambdas",
+    "decay_lambdas_depth",
     "qkv_cpu",
     "qkv_device",
     "state_device",
@@ -33,6 +38,14 @@ __all__ = [
 def decay_lambdas(h_count):
     """float32[H]: lambda_h = exp(-2^(-(8/H)(h+1))), fp64 then one rounding."""
     lam = [math.exp(-(2.0 ** (-(8.0 / h_count) * (h + 1)))) for h in range(h_count)]
+    return np.asarray(lam, dtype=np.float64).astype(np.float32)
+
+
+def decay_lambdas_depth(h_count, layer, n_layers):
+    """float32[H] for layer `layer` of `n_layers`: the slopes of decay_lambdas
+    scaled by (1 - layer / (n_layers - 1)), fp64 then one rounding."""
+    scale = 1.0 - layer / (n_layers - 1) if n_layers > 1 else 1.0
+    lam = [math.exp(-(2.0 ** (-(8.0 / h_count) * (h + 1))) * scale) for h in range(h_count)]
     return np.asarray(lam, dtype=np.float64).astype(np.float32)
 
 

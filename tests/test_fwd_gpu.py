@@ -7,7 +7,8 @@ import pytest
 import torch
 
 import long_context_decayed_amd as la
-from long_context_decayed_amd.inputs import decay_lambdas, qkv_cpu, qkv_device, state_device, ternary_device
+from long_context_decayed_amd.inputs import (decay_lambdas, decay_lambdas_depth, qkv_cpu, qkv_device, state_device,
+                                             ternary_device)
 import tolerances as tol
 from gpu_helpers import host, lam_for, oracle, require_gpu, say
 
@@ -297,3 +298,23 @@ def test_fwd_slots_identity_matches_fwd(dev):
     o2 = la.fwd_slots(q, k, v, lam_t, pool, torch.arange(B, dtype=torch.int32, device=dev))
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s0, pool)
+
+
+# --- decays of a 70-layer stack, scaled down linearly with depth ---------------
+
+@pytest.mark.parametrize("chunk", [0, 4096])
+@pytest.mark.parametrize("layer", [0, 23, 46, 69])
+def test_bf16_depth_scaled_decays(dev, layer, chunk):
+    # The slopes shrink with depth, so deeper layers move heads from the
+    # warm-start path to the three-pass path; the last layer has lam = 1.
+    say("bf16 depth-scaled decays layer", layer, "of 70, B1 H64 N4133 d128 chunk", chunk)
+    lam = decay_lambdas_depth(64, layer, 70)
+    q, k, v = qkv_device(1, 64, 4133, 128, seed=120 + layer, device=dev)
+    s0 = state_device(1, 64, 128, seed=120 + layer, device=dev)
+    o32, kv = _run(q, k, v, lam, dev, 64, out_dtype=torch.float32, kv_in=s0, chunk=chunk)
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lam, host(s0).astype(np.float64))
+    o_h, kv_h = host(o32), host(kv)
+    for h in range(0, 64, 9):
+        tol.assert_bf16_f32out(o_h[:, h], o_ref[:, h], "O head %d" % h)
+    tol.assert_bf16_f32out(o_h, o_ref)
+    tol.assert_state(kv_h, s_ref, "kv_out")
