@@ -12,6 +12,9 @@ Parity status of each function (what pins it lives in tests/test_oracle.py):
   tests/test_oracle_bwd.py by a hand-worked example, exact central
   differences of the forward oracle, closed forms at lam = 0 and 1 and the
   split-sequence rule.
+  silu, rmsnorm_heads, sigmoid_gate (the steps either side of the core) --
+  pinned in tests/test_oracle_fused.py by closed-form values, limits and
+  invariants.
 """
 from .lightning import (  # noqa: F401
     decay_matrix,
@@ -22,4 +25,7 @@ from .lightning import (  # noqa: F401
     decode_repeated,
     window,
     backward_quadratic,
+    silu,
+    rmsnorm_heads,
+    sigmoid_gate,
 )

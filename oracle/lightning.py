@@ -38,7 +38,16 @@ dL/dO = dO and dL/dS_final = dSN,
     dV  = ((Q K^T) * M)^T dO   + diag(lambda^(N-1-s)) K dSN
     dS0 = Q^T diag(lambda^(t+1)) dO + lambda^N dSN
 
-(`backward_quadratic`, matrix calculus on the quadratic form).  The token
+(`backward_quadratic`, matrix calculus on the quadratic form).
+
+The steps either side of the core (the same field of the fact sheet: SiLU on
+Q, K, V and an RMSNorm on the output; its "output gate" field: a sigmoid gate
+on the lightning output after that norm, before the output projection):
+
+    silu(x)        = x * sigmoid(x),   sigmoid(x) = 1 / (1 + exp(-x))
+    rmsnorm_heads  y = o / sqrt(mean_d(o^2) + eps) * gamma[h]   (per head, over
+                   the d features of one token; eps = 1e-5 as the block norms)
+    gate           y * sigmoid(g)  The token
 form of the same gradients, an adjoint recurrence run from the last token
 back, is in recurrence.c (`crec.backward`); the two are checked against each
 other, against finite differences and against autograd.
@@ -63,6 +72,9 @@ __all__ = [
     "decode_repeated",
     "window",
     "backward_quadratic",
+    "silu",
+    "rmsnorm_heads",
+    "sigmoid_gate",
 ]
 
 
@@ -253,3 +265,30 @@ def backward_quadratic(q, k, v, lam, dout, s0=None, dsn=None):
             ds = ds + (lm ** n) * dsi
         ds0[idx] = ds
     return dq, dk, dv, ds0
+
+
+def _sigmoid(x):
+    x = _f64(x)
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def silu(x):
+    """x * sigmoid(x), elementwise, float64."""
+    x = _f64(x)
+    return x * _sigmoid(x)
+
+
+def rmsnorm_heads(o, gamma=None, eps=1e-5):
+    """Per-head RMSNorm over the feature axis of o [..., H, N, d]:
+    o / sqrt(mean(o^2) + eps), times gamma [H, d] (the same for every token)
+    when given.  One token per head is o[..., H, 1, d]."""
+    o = _f64(o)
+    y = o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    if gamma is not None:
+        y = y * _f64(gamma)[:, None, :]
+    return y
+
+
+def sigmoid_gate(y, g):
+    """y * sigmoid(g), elementwise, float64."""
+    return _f64(y) * _sigmoid(g)
