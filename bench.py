@@ -20,9 +20,12 @@ ONE JSON line:
   cpu_baseline   the fp64 oracle (plain-C recurrence) on a bounded sample of
                  the same workload, on this host's cores
   backward       the backward pass of the same layer (dq, dk, dv from dout)
+  epilogue_prologue  per-head RMSNorm + sigmoid gate of the output and SiLU
+                 on one input, as their own passes over the same layer
   decode         256 sequences x 64 heads x d=128 decode step, 1000 in-place
                  steps timed as a whole: GB/s of state + token traffic; and
-                 the same rows through a slot table over a 512-slot pool
+                 the same rows through a slot table over a 512-slot pool, and
+                 those with SiLU, per-head RMSNorm and gate fused
 
 Only one GPU is used; --gpus > 1 exits with a message.
 """
@@ -161,7 +164,10 @@ def bench_prefill(args, dev):
         step_hbm_frac=BYTES_PER_HT * ht / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         mfma_alg_frac=FLOP_PER_HT * ht / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
     )
-    del out, ws
+    del ws
+    if args.fused:
+        res["epilogue_prologue"] = bench_norm_gate_silu(args, dev, out)
+    del out
     if args.backward:
         res["backward"] = bench_backward(args, dev, q, k, v, lam)
     sample = None
@@ -170,6 +176,40 @@ def bench_prefill(args, dev):
     else:
         del q, k, v
     return res, sample
+
+
+def _time_ms(fn, reps):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def bench_norm_gate_silu(args, dev, out):
+    """The layer's elementwise steps either side of the core as the prefill's
+    own passes, on the million-token output: per-head RMSNorm + sigmoid gate
+    (o and gate read, y written) and SiLU in place on one input tensor."""
+    import torch
+    import long_context_decayed_amd as la
+    from long_context_decayed_amd.inputs import qkv_device
+
+    B, H, N, d = out.shape
+    log("epilogue (norm + gate) and prologue (SiLU) passes on [%d, %d, %d, %d] bf16" % (B, H, N, d))
+    gate = qkv_device(B, H, N, d, seed=6, device=dev, slice_tokens=65536)[0]
+    gamma = torch.ones((H, d), device=dev, dtype=torch.float32)
+    y = torch.empty_like(out)
+    ms_ng = _time_ms(lambda: la.norm_gate(out, gamma=gamma, gate=gate, out=y), 5)
+    ms_si = _time_ms(lambda: la.silu_(gate), 5)
+    nbytes = out.numel() * 2
+    del gate, y
+    return dict(norm_gate_ms=ms_ng, norm_gate_gb_per_s=3 * nbytes / (ms_ng * 1e-3) / 1e9,
+                silu_ms_per_tensor=ms_si, silu_gb_per_s=2 * nbytes / (ms_si * 1e-3) / 1e9)
 
 
 def bench_backward(args, dev, q, k, v, lam):
@@ -248,6 +288,15 @@ def bench_decode(args, dev):
     gbs = (per_step_bytes + B * 4) * steps / (ms * 1e-3) / 1e9
     res["slots"] = dict(workload="the same 256 rows over a 512-slot state pool (seeded random slot table)",
                         us_per_step=ms * 1e3 / steps, gb_per_s=gbs, frac_hbm=gbs / HBM_PEAK_GBS)
+    if args.fused:
+        # the same, with SiLU on q, k, v, the per-head RMSNorm and the sigmoid gate fused in
+        gate = q.clone()
+        gamma = torch.ones((H, d), device=dev, dtype=torch.float32)
+        ms = _time_ms(lambda: la.decode_fused(q, k, v, lam, pool, slots, silu=True, gamma=gamma, gate=gate, out=o),
+                      steps)
+        gbs = (per_step_bytes + B * 4 + B * H * d * 2) / (ms * 1e-3) / 1e9
+        res["fused"] = dict(workload="the slot-table rows with SiLU on q, k, v, per-head RMSNorm and sigmoid gate "
+                                     "fused", us_per_step=ms * 1e3, gb_per_s=gbs, frac_hbm=gbs / HBM_PEAK_GBS)
     return res
 
 
@@ -290,6 +339,8 @@ def main():
     ap.add_argument("--no-decode", dest="decode", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--no-backward", dest="backward", action="store_false")
+    ap.add_argument("--no-fused", dest="fused", action="store_false",
+                    help="skip the SiLU / RMSNorm / gate measurements")
     ap.add_argument("--cpu-tokens", type=int, default=1 << 20)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a known-size "
@@ -340,6 +391,7 @@ def main():
         "step_hbm_frac": prefill["step_hbm_frac"],
         "mfma_alg_frac": prefill["mfma_alg_frac"],
         "backward": prefill.get("backward"),
+        "epilogue_prologue": prefill.get("epilogue_prologue"),
         "cpu_baseline": cpu,
         "decode": dec,
     }

@@ -213,6 +213,42 @@ int lightning_attn_decode_slots(const void* q, const void* k, const void* v, con
                                 float* states, const int32_t* slots, int64_t B, int64_t H, int64_t d,
                                 int64_t num_slots, void* stream);
 
+/*
+ * The lightning layer's elementwise steps either side of the core (the
+ * MiniMax-M1 fact sheet: SiLU on Q, K, V and an RMSNorm on the output, in its
+ * "linear / SSM layer configuration" field; a sigmoid gate after that norm,
+ * before the output projection, in its "output gate" field).  The norm is
+ * taken per head over the d features of a token, o / sqrt(mean(o^2) + eps)
+ * times gamma[h]; eps = 1e-5 matches the block norms.
+ *
+ * Decode step with them fused (no extra memory pass): the step of
+ * lightning_attn_decode_slots (slots == NULL: row b uses state row b, and
+ * num_slots >= B), with
+ *   silu != 0 : q, k, v <- SiLU(q), SiLU(k), SiLU(v) as they are read
+ *   gamma     : float [H][d] or NULL (no norm)
+ *   gate      : bf16 [B][H][d] or NULL (no gate): o <- o * sigmoid(gate)
+ *   eps       : in [0, 1]
+ */
+int lightning_attn_decode_fused(const void* q, const void* k, const void* v, const float* decay, void* out,
+                                float* states, const int32_t* slots, int64_t num_slots, int silu,
+                                const float* gamma, float eps, const void* gate, int64_t B, int64_t H, int64_t d,
+                                void* stream);
+
+/*
+ * Prefill epilogue as its own pass (the block-64 prefill kernel has no room
+ * to take it in): out = RMSNorm_head(o) * gamma[h] * sigmoid(gate).
+ *   o      : o_dtype (LA_DTYPE_BF16 or LA_DTYPE_F32) [B][H][N][d]   (read)
+ *   gate   : bf16 [B][H][N][d] or NULL (no gate)                   (read)
+ *   gamma  : float [H][d] or NULL (no norm)                        (read)
+ *   out    : bf16 [B][H][N][d] (written; may be o itself when o is bf16)
+ */
+int lightning_attn_norm_gate(const void* o, int o_dtype, const void* gate, const float* gamma, float eps, void* out,
+                             int64_t B, int64_t H, int64_t N, int64_t d, void* stream);
+
+/* Prefill prologue as its own pass: x <- SiLU(x) over n bf16 elements in place
+ * (apply to Q, K and V before lightning_attn_fwd). */
+int lightning_attn_silu(void* x, int64_t n, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* lightning_attn_strerror(int status);
 

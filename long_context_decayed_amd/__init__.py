@@ -65,6 +65,12 @@ def load():
     lib.lightning_attn_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64]
     lib.lightning_attn_decode_step.restype = I
     lib.lightning_attn_decode_step.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, P]
+    lib.lightning_attn_decode_fused.restype = I
+    lib.lightning_attn_decode_fused.argtypes = [P] * 7 + [I64, I, P, ctypes.c_float, P, I64, I64, I64, P]
+    lib.lightning_attn_norm_gate.restype = I
+    lib.lightning_attn_norm_gate.argtypes = [P, I, P, P, ctypes.c_float, P, I64, I64, I64, I64, P]
+    lib.lightning_attn_silu.restype = I
+    lib.lightning_attn_silu.argtypes = [P, I64, P]
     lib.lightning_attn_fwd_slots.restype = I
     lib.lightning_attn_fwd_slots.argtypes = [P] * 7 + [I64, I64, I64, I64, I64, I64, I, I, P]
     lib.lightning_attn_bwd.restype = I
@@ -277,6 +283,69 @@ def decode_slots(q, k, v, decay, states, slots, out=None, stream=None):
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_decode_slots")
     return out
+
+
+def decode_fused(q, k, v, decay, states, slots=None, silu=True, gamma=None, gate=None, eps=1e-5, out=None,
+                 stream=None):
+    """Decode step with SiLU on q, k, v (silu=True), per-head RMSNorm of o
+    (gamma fp32 [H, d]) and o * sigmoid(gate) (gate bf16 [B, H, d]) fused.
+    states: fp32 [num_slots, H, d, d] in place; slots: int32 [B] or None
+    (row b uses state row b).  Returns o [B, H, d] bf16."""
+    lib = load()
+    B, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, torch.bfloat16, (B, H, d))
+    _check_dev("decay", decay, torch.float32, (H,))
+    if states.dim() != 4:
+        raise ValueError("states must be [num_slots, H, d, d]")
+    _check_dev("states", states, torch.float32, (states.shape[0], H, d, d))
+    if slots is not None:
+        _check_dev("slots", slots, torch.int32, (B,))
+    if gamma is not None:
+        _check_dev("gamma", gamma, torch.float32, (H, d))
+    if gate is not None:
+        _check_dev("gate", gate, torch.bfloat16, (B, H, d))
+    if out is None:
+        out = torch.empty((B, H, d), device=q.device, dtype=torch.bfloat16)
+    _check_dev("out", out, torch.bfloat16, (B, H, d))
+    rc = lib.lightning_attn_decode_fused(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(states), _ptr(slots), states.shape[0],
+        1 if silu else 0, _ptr(gamma), float(eps), _ptr(gate), B, H, d, _stream(stream)
+    )
+    if rc != 0:
+        raise LightningAttnError(rc, "lightning_attn_decode_fused")
+    return out
+
+
+def norm_gate(o, gamma=None, gate=None, eps=1e-5, out=None, stream=None):
+    """Per-head RMSNorm (gamma fp32 [H, d]) and sigmoid gate (gate bf16, o's
+    shape) of a prefill output o [B, H, N, d] (bf16 or fp32), into bf16 out
+    (o itself allowed when o is bf16)."""
+    lib = load()
+    B, H, N, d = o.shape
+    _check_dev("o", o, None, (B, H, N, d))
+    if gamma is not None:
+        _check_dev("gamma", gamma, torch.float32, (H, d))
+    if gate is not None:
+        _check_dev("gate", gate, torch.bfloat16, (B, H, N, d))
+    if out is None:
+        out = torch.empty((B, H, N, d), device=o.device, dtype=torch.bfloat16)
+    _check_dev("out", out, torch.bfloat16, (B, H, N, d))
+    rc = lib.lightning_attn_norm_gate(_ptr(o), _DT[o.dtype], _ptr(gate), _ptr(gamma), float(eps), _ptr(out),
+                                      B, H, N, d, _stream(stream))
+    if rc != 0:
+        raise LightningAttnError(rc, "lightning_attn_norm_gate")
+    return out
+
+
+def silu_(x, stream=None):
+    """x <- SiLU(x) in place (bf16 device tensor); returns x."""
+    lib = load()
+    _check_dev("x", x, torch.bfloat16)
+    rc = lib.lightning_attn_silu(_ptr(x), x.numel(), _stream(stream))
+    if rc != 0:
+        raise LightningAttnError(rc, "lightning_attn_silu")
+    return x
 
 
 def runtime_version():

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblightning_attn.so")
 
-SOURCES = ["la_abi.cpp", "la_state.hip", "la_output.hip", "la_decode.hip"]
+SOURCES = ["la_abi.cpp", "la_state.hip", "la_output.hip", "la_decode.hip", "la_fused.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

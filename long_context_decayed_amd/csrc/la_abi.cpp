@@ -416,6 +416,56 @@ int lightning_attn_decode_slots(const void* q, const void* k, const void* v, con
                                     (const int*)slots, num_slots));
 }
 
+int lightning_attn_decode_fused(const void* q, const void* k, const void* v, const float* decay, void* out,
+                                float* states, const int32_t* slots, int64_t num_slots, int silu,
+                                const float* gamma, float eps, const void* gate, int64_t B, int64_t H, int64_t d,
+                                void* stream) {
+  if (!q || !k || !v || !decay || !out || !states) return LA_ERR_INVALID;
+  if (B < 1 || H < 1 || d < 1 || num_slots < 1) return LA_ERR_INVALID;
+  if (!slots && num_slots < B) return LA_ERR_INVALID;
+  if (!(eps >= 0.0f) || eps > 1.0f) return LA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(decay, 4) ||
+      !aligned(states, 16) || !aligned(slots, 4) || !aligned(gamma, 16) || !aligned(gate, 16))
+    return LA_ERR_INVALID;
+  if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+  if (B * H > kMaxGrid || num_slots > kMaxGrid) return LA_ERR_UNSUPPORTED;
+  const int64_t vec_bytes = B * H * d * 2, pool_bytes = num_slots * H * d * d * 4;
+  if (overlap(out, vec_bytes, q, vec_bytes) || overlap(out, vec_bytes, k, vec_bytes) ||
+      overlap(out, vec_bytes, v, vec_bytes) || overlap(out, vec_bytes, states, pool_bytes) ||
+      overlap(out, vec_bytes, slots, B * 4) || overlap(states, pool_bytes, slots, B * 4) ||
+      overlap(out, vec_bytes, gate, vec_bytes) || overlap(out, vec_bytes, gamma, H * d * 4) ||
+      overlap(states, pool_bytes, gate, vec_bytes) || overlap(states, pool_bytes, gamma, H * d * 4))
+    return LA_ERR_INVALID;
+  la::DecodeFusion fz{silu ? 1 : 0, gamma, eps, gate};
+  return from_hip(la::launch_decode(q, k, v, decay, out, states, states, B, H, d, (hipStream_t)stream,
+                                    (const int*)slots, num_slots, &fz));
+}
+
+int lightning_attn_norm_gate(const void* o, int o_dtype, const void* gate, const float* gamma, float eps, void* out,
+                             int64_t B, int64_t H, int64_t N, int64_t d, void* stream) {
+  if (!o || !out) return LA_ERR_INVALID;
+  if (B < 1 || H < 1 || N < 1 || d < 1) return LA_ERR_INVALID;
+  if (o_dtype != LA_DTYPE_BF16 && o_dtype != LA_DTYPE_F32) return LA_ERR_INVALID;
+  if (!(eps >= 0.0f) || eps > 1.0f) return LA_ERR_INVALID;
+  if (!aligned(o, 16) || !aligned(out, 16) || !aligned(gate, 16) || !aligned(gamma, 16)) return LA_ERR_INVALID;
+  if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+  const int64_t rows = B * H * N;
+  if (rows * (d / 8) / 256 + 1 > kMaxGrid) return LA_ERR_UNSUPPORTED;
+  const int64_t o_bytes = rows * d * (o_dtype == LA_DTYPE_BF16 ? 2 : 4), y_bytes = rows * d * 2;
+  const bool in_place = out == o && o_dtype == LA_DTYPE_BF16;
+  if (!in_place && overlap(out, y_bytes, o, o_bytes)) return LA_ERR_INVALID;
+  if (overlap(out, y_bytes, gate, y_bytes) || overlap(out, y_bytes, gamma, H * d * 4)) return LA_ERR_INVALID;
+  return from_hip(la::launch_norm_gate(o, o_dtype == LA_DTYPE_BF16 ? la::kBF16 : la::kF32, gate, gamma, eps, out,
+                                       rows, H, N, d, (hipStream_t)stream));
+}
+
+int lightning_attn_silu(void* x, int64_t n, void* stream) {
+  if (n < 0 || (n > 0 && !x)) return LA_ERR_INVALID;
+  if (!aligned(x, 16)) return LA_ERR_INVALID;
+  if (n == 0) return LA_OK;
+  return from_hip(la::launch_silu(x, n, (hipStream_t)stream));
+}
+
 const char* lightning_attn_strerror(int status) {
   switch (status) {
     case LA_OK: return "ok";

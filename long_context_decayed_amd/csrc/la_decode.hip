@@ -18,6 +18,13 @@
 // pool slot slots[b] (states [num_slots][H][d][d], in place); a row whose
 // slot lies outside [0, num_slots) is idle: its output is zero and no state
 // is touched.
+//
+// Fused form (the layer's elementwise steps either side of the core; the
+// MiniMax-M1 fact sheet, "linear / SSM layer configuration" and "output gate"
+// fields): SiLU on q, k, v as they are read; per-head RMSNorm of o over its d
+// features, o / sqrt(mean(o^2) + eps) * gamma[h]; then o * sigmoid(gate).
+// Each is optional; the row of o is whole in the threads that store it, so
+// they add no memory pass.
 
 #include <hip/hip_runtime.h>
 
@@ -27,13 +34,16 @@
 namespace la {
 
 constexpr int kDecThreads = 128;  // threads per (sequence, head) pair
+
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
 constexpr int kDecPairs = 2;      // pairs per workgroup
 
 template <int D>
 __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ decay, bf16* __restrict__ o, const float* kv_in, float* kv_out, int H, int64_t pairs,
-    const int* __restrict__ slots, int64_t num_slots) {
+    const int* __restrict__ slots, int64_t num_slots, int silu, const float* __restrict__ gamma, float eps,
+    const bf16* __restrict__ gate) {
   constexpr int TPR = D / 4;              // threads per row
   constexpr int RG = kDecThreads / TPR;   // row groups
   constexpr int RPT = D / RG;             // rows per thread
@@ -54,13 +64,17 @@ __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
   }
   const float lam = valid ? decay[hh] : 0.0f;
   if (valid && tid < D) {
-    qs[sub][tid] = (float)q[pair * D + tid];
-    ks[sub][tid] = (float)k[pair * D + tid];
+    const float qf = (float)q[pair * D + tid], kf = (float)k[pair * D + tid];
+    qs[sub][tid] = silu ? qf * sigmoid_f(qf) : qf;
+    ks[sub][tid] = silu ? kf * sigmoid_f(kf) : kf;
   }
   f32x4 vv = {0.f, 0.f, 0.f, 0.f};
   if (valid) {
     const bf16x4 vb = *reinterpret_cast<const bf16x4*>(v + pair * D + 4 * cg);
     vv = f32x4{(float)vb[0], (float)vb[1], (float)vb[2], (float)vb[3]};
+    if (silu)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[i] *= sigmoid_f(vv[i]);
   }
   const int64_t sbase = (srow * H + hh) * D * D;
   f32x4 s[RPT];
@@ -90,6 +104,20 @@ __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
     f32x4 r = part[sub][0][tid];
 #pragma unroll
     for (int g = 1; g < RG; ++g) r += part[sub][g][tid];
+    if (gamma) {
+      // the TPR lanes of this group hold the whole row: reduce across them
+      float ss = r[0] * r[0] + r[1] * r[1] + r[2] * r[2] + r[3] * r[3];
+#pragma unroll
+      for (int m = TPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, TPR);
+      const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+      const f32x4 gm = *reinterpret_cast<const f32x4*>(gamma + hh * D + 4 * tid);
+      r = r * inv * gm;
+    }
+    if (gate) {
+      const bf16x4 gb = *reinterpret_cast<const bf16x4*>(gate + pair * D + 4 * tid);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] *= sigmoid_f((float)gb[i]);
+    }
     bf16x4 ob;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ob[i] = idle ? (bf16)0.0f : (bf16)r[i];
@@ -99,17 +127,21 @@ __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* decay, void* out,
                          const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t d, hipStream_t st,
-                         const int* slots, int64_t num_slots) {
+                         const int* slots, int64_t num_slots, const DecodeFusion* fz) {
+  const int silu = fz ? fz->silu : 0;
+  const float* gamma = fz ? fz->gamma : nullptr;
+  const float eps = fz ? fz->eps : 0.0f;
+  const bf16* gate = fz ? (const bf16*)fz->gate : nullptr;
   const int64_t pairs = B * H;
   const unsigned grid = (unsigned)((pairs + kDecPairs - 1) / kDecPairs);
   if (d == 128)
     hipLaunchKernelGGL(la_decode_kernel<128>, dim3(grid), dim3(kDecThreads * kDecPairs), 0, st, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, decay, (bf16*)out, kv_in, kv_out, (int)H, pairs, slots,
-                       num_slots);
+                       num_slots, silu, gamma, eps, gate);
   else
     hipLaunchKernelGGL(la_decode_kernel<64>, dim3(grid), dim3(kDecThreads * kDecPairs), 0, st, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, decay, (bf16*)out, kv_in, kv_out, (int)H, pairs, slots,
-                       num_slots);
+                       num_slots, silu, gamma, eps, gate);
   return hipGetLastError();
 }
 

@@ -44,13 +44,31 @@ hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st);
 // heads that do not decay within their chunk only): la_output.hip.
 hipError_t launch_output_pass(const PrefillArgs& a, hipStream_t st);
 
-// Decode step; with `slots` (device int32[B]) batch row b uses state row
-// slots[b] of kv_in / kv_out ([num_slots][H][d][d]); rows out of range idle.
 // dst[bh] = src[bh]^T for BH fp32 d x d states: la_state.hip.
 hipError_t launch_transpose_states(const float* src, float* dst, int64_t BH, int64_t d, hipStream_t st);
 
+// Optional elementwise steps fused into the decode step: SiLU on q, k, v;
+// per-head RMSNorm of o (gamma [H][d], eps); o * sigmoid(gate), gate bf16 [B][H][d].
+struct DecodeFusion {
+  int silu;
+  const float* gamma;
+  float eps;
+  const void* gate;
+};
+
+// Decode step (la_decode.hip); with `slots` (device int32[B]) batch row b uses
+// state row slots[b] of kv_in / kv_out ([num_slots][H][d][d]); rows whose slot
+// is out of range are idle.
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* decay, void* out,
                          const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t d, hipStream_t st,
-                         const int* slots = nullptr, int64_t num_slots = 0);
+                         const int* slots = nullptr, int64_t num_slots = 0, const DecodeFusion* fz = nullptr);
+
+// Per-head RMSNorm of o (bf16 or fp32 [rows][d], rows = B*H*N, head of a row =
+// (row / N) % H) times gamma [H][d] when given, times sigmoid(gate) when given
+// (bf16 [rows][d]), into bf16 out (may be o itself when o is bf16): la_fused.hip.
+hipError_t launch_norm_gate(const void* o, int o_dtype, const void* gate, const float* gamma, float eps, void* out,
+                            int64_t rows, int64_t H, int64_t N, int64_t d, hipStream_t st);
+// x <- x * sigmoid(x) over n bf16 elements in place: la_fused.hip.
+hipError_t launch_silu(void* x, int64_t n, hipStream_t st);
 
 }  // namespace la

@@ -163,6 +163,37 @@ def test_fwd_slots_validation(lib):
     assert f(*a) == LA_ERR_INVALID                                  # slot table inside the pool
 
 
+def test_fused_validation(lib):
+    f = lib.lightning_attn_decode_fused
+    ok = [FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], FAKE[5], None, 4, 1, None, ctypes.c_float(1e-5), None,
+          4, 2, 128, None]
+    a = list(ok); a[5] = None
+    assert f(*a) == LA_ERR_INVALID                      # no pool
+    a = list(ok); a[7] = 3
+    assert f(*a) == LA_ERR_INVALID                      # no slot table and fewer slots than rows
+    a = list(ok); a[10] = ctypes.c_float(-1.0)
+    assert f(*a) == LA_ERR_INVALID                      # negative eps
+    a = list(ok); a[14] = 96
+    assert f(*a) == LA_ERR_UNSUPPORTED
+    a = list(ok); a[11] = FAKE[4]
+    assert f(*a) == LA_ERR_INVALID                      # gate is the output
+    g = lib.lightning_attn_norm_gate
+    base = [FAKE[0], 0, None, None, ctypes.c_float(1e-5), FAKE[1], 1, 2, 100, 128, None]
+    a = list(base); a[1] = 5
+    assert g(*a) == LA_ERR_INVALID                      # bad dtype
+    a = list(base); a[9] = 96
+    assert g(*a) == LA_ERR_UNSUPPORTED
+    a = list(base); a[5] = ctypes.c_void_p(FAKE[0].value + 256)
+    assert g(*a) == LA_ERR_INVALID                      # out overlaps o, not in place
+    a = list(base); a[1] = 1; a[5] = FAKE[0]
+    assert g(*a) == LA_ERR_INVALID                      # in place needs a bf16 o
+    s = lib.lightning_attn_silu
+    assert s(None, 5, None) == LA_ERR_INVALID
+    assert s(FAKE[0], -1, None) == LA_ERR_INVALID
+    assert s(None, 0, None) == LA_OK                    # nothing to do, no device call
+    assert s(ctypes.c_void_p(FAKE[0].value + 2), 8, None) == LA_ERR_INVALID
+
+
 def test_bwd_validation(lib):
     f = lib.lightning_attn_bwd
     q, k, v, dec, g = FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4]

@@ -1,0 +1,131 @@
+"""GPU parity of the elementwise steps either side of the core (SiLU on
+Q, K, V; per-head RMSNorm and sigmoid gate of the output) against the fp64
+oracle: fused into the decode step, and as the prefill's own passes."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_decayed_amd as la
+import oracle as ora
+from long_context_decayed_amd.inputs import decay_lambdas, qkv_device, state_device
+import tolerances as tol
+from gpu_helpers import host, oracle, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+LAMS8 = np.array([0.0, 1e-3, 0.3, 0.7, 0.9, 0.97, 0.999, 1.0], dtype=np.float32)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _tok(b, h, d, seed, dev, scale=3.0):
+    # pre-activation values: a wider spread than the core's inputs, so that
+    # SiLU's bend near zero and its linear tail are both exercised
+    q, k, v = qkv_device(b, h, 1, d, seed=seed, device=dev)
+    return tuple((t[:, :, 0] * scale * d ** 0.5 / 4).to(torch.bfloat16).contiguous() for t in (q, k, v))
+
+
+def _gamma(h, d, seed, dev):
+    g = torch.Generator().manual_seed(seed)
+    return (1.0 + 0.25 * torch.randn((h, d), generator=g)).to(torch.float32).to(dev)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_fused_against_oracle(dev, d):
+    say("decode fused (silu, norm, gate) over a slot table, pool 9 x H8 d", d)
+    H, P = 8, 9
+    slots_h = np.array([4, -1, 0, 8, 2, 9, 6], dtype=np.int32)
+    B = len(slots_h)
+    q, k, v = _tok(B, H, d, 140 + d, dev)
+    gate = _tok(B, H, d, 150 + d, dev)[0]
+    gamma = _gamma(H, d, 160 + d, dev)
+    pool = state_device(P, H, d, seed=140 + d, device=dev)
+    pool0 = host(pool).astype(np.float64)
+    o = la.decode_fused(q, k, v, torch.from_numpy(LAMS8).to(dev), pool, torch.from_numpy(slots_h).to(dev),
+                        silu=True, gamma=gamma, gate=gate, eps=1e-5)
+    torch.cuda.synchronize()
+    act = [(b, int(s)) for b, s in enumerate(slots_h) if 0 <= s < P]
+    rows = np.array([b for b, _ in act])
+    sl = np.array([s for _, s in act])
+    qs, ks, vs = (ora.silu(host(t)[rows]) for t in (q, k, v))
+    o_core, s_ref = ora.decode_step(qs, ks, vs, LAMS8.astype(np.float64), pool0[sl])
+    y = ora.rmsnorm_heads(o_core[:, :, None, :], host(gamma), eps=1e-5)[:, :, 0, :]
+    y = ora.sigmoid_gate(y, host(gate)[rows])
+    tol.assert_bf16_out(host(o)[rows], y)
+    tol.assert_state(host(pool).astype(np.float64)[sl], s_ref)
+    idle = [b for b in range(B) if b not in rows]
+    assert np.all(host(o)[idle] == 0.0)
+
+
+def test_decode_fused_without_steps_is_decode_slots(dev):
+    say("decode fused with every step off vs decode_slots, B32 H64 d128")
+    B, H, d = 32, 64, 128
+    q, k, v = _tok(B, H, d, 170, dev, scale=1.0)
+    lam_t = torch.from_numpy(decay_lambdas(H)).to(dev)
+    pool_a = state_device(B, H, d, seed=170, device=dev)
+    pool_b = pool_a.clone()
+    slots = torch.arange(B, dtype=torch.int32, device=dev)
+    o1 = la.decode_slots(q, k, v, lam_t, pool_a, slots)
+    o2 = la.decode_fused(q, k, v, lam_t, pool_b, None, silu=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(pool_a, pool_b)
+
+
+@pytest.mark.parametrize("odt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128])
+def test_norm_gate_against_oracle(dev, d, odt):
+    say("prefill norm + gate B2 H4 N1001 d", d, "o", odt)
+    B, H, N = 2, 4, 1001
+    o = qkv_device(B, H, N, d, seed=180 + d, device=dev, dtype=torch.float32)[0].to(odt) * 7.0
+    gate = qkv_device(B, H, N, d, seed=190 + d, device=dev)[0] * 8.0
+    gamma = _gamma(H, d, 200 + d, dev)
+    y = la.norm_gate(o, gamma=gamma, gate=gate, eps=1e-5)
+    torch.cuda.synchronize()
+    ref = ora.sigmoid_gate(ora.rmsnorm_heads(host(o), host(gamma), eps=1e-5), host(gate))
+    tol.assert_bf16_out(host(y), ref)
+    # only the final rounding to bf16 (and fp32 arithmetic) separates them
+    err = np.abs(host(y).astype(np.float64) - ref)
+    assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max())
+    # the norm alone, in place
+    o2 = o.to(torch.bfloat16).contiguous()
+    ref2 = ora.rmsnorm_heads(host(o2), host(gamma), eps=1e-5)
+    la.norm_gate(o2, gamma=gamma, out=o2)
+    torch.cuda.synchronize()
+    assert np.all(np.abs(host(o2) - ref2) <= 2.0 ** -8 * np.abs(ref2) + 1e-6 * np.abs(ref2).max())
+
+
+@pytest.mark.parametrize("n", [8, 13, 100003])
+def test_silu_against_oracle(dev, n):
+    say("silu in place, n", n)
+    g = torch.Generator(device=dev).manual_seed(n)
+    x = (torch.randn(n, device=dev, generator=g) * 4).to(torch.bfloat16)
+    ref = ora.silu(host(x))
+    la.silu_(x)
+    torch.cuda.synchronize()
+    assert np.all(np.abs(host(x) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+
+
+def test_layer_core_pipeline(dev):
+    # pre-activations -> SiLU -> lightning prefill -> per-head norm and gate,
+    # against the same chain in the oracle
+    say("layer core pipeline B1 H8 N2000 d128: silu -> fwd -> norm_gate")
+    B, H, N, d = 1, 8, 2000, 128
+    q, k, v = (t * 2.0 for t in qkv_device(B, H, N, d, seed=210, device=dev))
+    q, k, v = (t.contiguous() for t in (q, k, v))
+    gate = qkv_device(B, H, N, d, seed=211, device=dev)[0] * 8.0
+    gamma = _gamma(H, d, 212, dev)
+    qa, ka, va = (la.silu_(t.clone()) for t in (q, k, v))
+    o = la.fwd(qa, ka, va, torch.from_numpy(LAMS8).to(dev), block=64, out_dtype=torch.float32)
+    y = la.norm_gate(o, gamma=gamma, gate=gate, eps=1e-5)
+    torch.cuda.synchronize()
+    # the oracle takes the GPU's bf16 SiLU outputs (the prefill's inputs) and
+    # checks that step on its own
+    for a, raw in ((qa, q), (ka, k), (va, v)):
+        ref = ora.silu(host(raw))
+        assert np.all(np.abs(host(a) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+    o_ref, _ = oracle(host(qa), host(ka), host(va), LAMS8)
+    y_ref = ora.sigmoid_gate(ora.rmsnorm_heads(o_ref, host(gamma), eps=1e-5), host(gate))
+    for h in range(H):
+        tol.assert_bf16_out(host(y)[:, h], y_ref[:, h], "head %d" % h)
