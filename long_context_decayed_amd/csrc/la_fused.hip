@@ -21,70 +21,90 @@ namespace la {
 __device__ __forceinline__ float sigmoid_fast(float x) { return 1.0f / (1.0f + expf(-x)); }
 
 // y = o / sqrt(mean(o^2) + eps) * gamma[h] * sigmoid(g) per row of d features.
+// Each lane group of TPR lanes handles RU rows, 256/TPR*RU rows per block; all
+// loads of a thread are issued before any arithmetic.
 template <typename TO, int D>
 __global__ __launch_bounds__(256) void la_norm_gate(const TO* __restrict__ o, const bf16* __restrict__ gate,
                                                     const float* __restrict__ gamma, float eps, bf16* out,
                                                     int64_t rows, int H, int64_t N) {
-  constexpr int TPR = D / 8;  // lanes per row, 8 features each
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = gid / TPR;
-  const int part = (int)(gid - row * TPR);
-  const bool valid = row < rows;  // every lane joins the shuffles below
-  float x[8];
-  if (valid) {
-    const TO* src = o + row * D + 8 * part;
-    if constexpr (sizeof(TO) == 2) {
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(src);
+  constexpr int TPR = D / 8, RPB = 256 / TPR, RU = 4;
+  const int part = threadIdx.x % TPR;
+  const int64_t row0 = (int64_t)blockIdx.x * RPB * RU + threadIdx.x / TPR;
+  float x[RU][8];
+  bf16x8 gv[RU];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (float)b[i];
+  for (int u = 0; u < RU; ++u) {
+    const int64_t row = row0 + (int64_t)u * RPB;
+    if (row < rows) {
+      const TO* src = o + row * D + 8 * part;
+      if constexpr (sizeof(TO) == 2) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(src);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[u][i] = (float)b[i];
+      } else {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src), b = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[u][i] = a[i];
+          x[u][4 + i] = b[i];
+        }
+      }
+      if (gate) gv[u] = *reinterpret_cast<const bf16x8*>(gate + row * D + 8 * part);
     } else {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(src), b = *reinterpret_cast<const f32x4*>(src + 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = a[i];
-        x[4 + i] = b[i];
+      for (int i = 0; i < 8; ++i) x[u][i] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    const int64_t row = row0 + (int64_t)u * RPB;
+    if (gamma) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += x[u][i] * x[u][i];
+#pragma unroll
+      for (int m = TPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, TPR);
+      const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+      if (row < rows) {
+        const int hh = (int)((row / N) % H);
+        const float* gm = gamma + (int64_t)hh * D + 8 * part;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[u][i] *= inv * gm[i];
       }
     }
-  } else {
+    if (row < rows) {
+      if (gate)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = 0.0f;
-  }
-  if (gamma) {
-    float ss = 0.0f;
+        for (int i = 0; i < 8; ++i) x[u][i] *= sigmoid_fast((float)gv[u][i]);
+      bf16x8 y;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
-#pragma unroll
-    for (int m = TPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, TPR);
-    const float inv = 1.0f / sqrtf(ss / (float)D + eps);
-    if (valid) {
-      const int hh = (int)((row / N) % H);
-      const float* gm = gamma + (int64_t)hh * D + 8 * part;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] *= inv * gm[i];
+      for (int i = 0; i < 8; ++i) y[i] = (bf16)x[u][i];
+      *reinterpret_cast<bf16x8*>(out + row * D + 8 * part) = y;
     }
   }
-  if (!valid) return;
-  if (gate) {
-    const bf16x8 g = *reinterpret_cast<const bf16x8*>(gate + row * D + 8 * part);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] *= sigmoid_fast((float)g[i]);
-  }
-  bf16x8 y;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = (bf16)x[i];
-  *reinterpret_cast<bf16x8*>(out + row * D + 8 * part) = y;
 }
 
-// x <- x * sigmoid(x), 8 bf16 elements per thread and step, grid-stride.
+// x <- x * sigmoid(x): 4 chunks of 8 bf16 elements per thread, all loads
+// issued before any arithmetic.
 __global__ __launch_bounds__(256) void la_silu(bf16* __restrict__ x, int64_t n8, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
-    bf16x8 b = *reinterpret_cast<const bf16x8*>(x + 8 * i);
+  const int64_t base = (int64_t)blockIdx.x * blockDim.x * 4 + threadIdx.x;
+  bf16x8 b[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float f = (float)b[j];
-      b[j] = (bf16)(f * sigmoid_fast(f));
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = base + u * 256;
+    if (i < n8) b[u] = *reinterpret_cast<const bf16x8*>(x + 8 * i);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = base + u * 256;
+    if (i < n8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float f = (float)b[u][j];
+        b[u][j] = (bf16)(f * sigmoid_fast(f));
+      }
+      *reinterpret_cast<bf16x8*>(x + 8 * i) = b[u];
     }
-    *reinterpret_cast<bf16x8*>(x + 8 * i) = b;
   }
   // a tail of n % 8 elements, one thread
   if (blockIdx.x == 0 && threadIdx.x == 0)
@@ -96,8 +116,8 @@ __global__ __launch_bounds__(256) void la_silu(bf16* __restrict__ x, int64_t n8,
 
 hipError_t launch_norm_gate(const void* o, int o_dtype, const void* gate, const float* gamma, float eps, void* out,
                             int64_t rows, int64_t H, int64_t N, int64_t d, hipStream_t st) {
-  const int64_t threads = rows * (d / 8);
-  const unsigned grid = (unsigned)((threads + 255) / 256);
+  const int64_t rows_per_block = (256 / (d / 8)) * 4;
+  const unsigned grid = (unsigned)((rows + rows_per_block - 1) / rows_per_block);
   if (o_dtype == kBF16) {
     if (d == 128)
       hipLaunchKernelGGL((la_norm_gate<bf16, 128>), dim3(grid), dim3(256), 0, st, (const bf16*)o, (const bf16*)gate,
@@ -118,8 +138,7 @@ hipError_t launch_norm_gate(const void* o, int o_dtype, const void* gate, const 
 
 hipError_t launch_silu(void* x, int64_t n, hipStream_t st) {
   const int64_t n8 = n / 8;
-  int64_t blocks = (n8 + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
+  int64_t blocks = (n8 + 1023) / 1024;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(la_silu, dim3((unsigned)blocks), dim3(256), 0, st, (bf16*)x, n8, n);
   return hipGetLastError();
