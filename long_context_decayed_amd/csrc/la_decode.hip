@@ -34,9 +34,9 @@
 namespace la {
 
 constexpr int kDecThreads = 128;  // threads per (sequence, head) pair
+constexpr int kDecPairs = 2;      // pairs per workgroup
 
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
-constexpr int kDecPairs = 2;      // pairs per workgroup
 
 template <int D>
 __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(

@@ -8,8 +8,9 @@
 // The block-64 prefill kernel has no room to take them in (it uses all 80 KiB
 // of LDS per workgroup and nearly all of its registers, and the per-head norm
 // would need a cross-wave reduction); the decode step fuses them (la_decode.hip).
-// Both passes here are bound by HBM: 16-byte loads and stores, one row of d
-// features per d/8 lanes, the row's sum of squares reduced across those lanes.
+// Both passes here are bound by HBM: 16-byte non-temporal loads and stores
+// (the data is touched once), one row of d features per d/8 lanes, the row's
+// sum of squares reduced across those lanes.
 
 #include <hip/hip_runtime.h>
 
@@ -17,6 +18,8 @@
 #include "la_kernels.h"
 
 namespace la {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float sigmoid_fast(float x) { return 1.0f / (1.0f + expf(-x)); }
 
@@ -38,7 +41,7 @@ __global__ __launch_bounds__(256) void la_norm_gate(const TO* __restrict__ o, co
     if (row < rows) {
       const TO* src = o + row * D + 8 * part;
       if constexpr (sizeof(TO) == 2) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(src);
+        const bf16x8 b = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src)));
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[u][i] = (float)b[i];
       } else {
@@ -49,7 +52,8 @@ __global__ __launch_bounds__(256) void la_norm_gate(const TO* __restrict__ o, co
           x[u][4 + i] = b[i];
         }
       }
-      if (gate) gv[u] = *reinterpret_cast<const bf16x8*>(gate + row * D + 8 * part);
+      if (gate)
+        gv[u] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gate + row * D + 8 * part)));
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[u][i] = 0.0f;
@@ -79,7 +83,7 @@ __global__ __launch_bounds__(256) void la_norm_gate(const TO* __restrict__ o, co
       bf16x8 y;
 #pragma unroll
       for (int i = 0; i < 8; ++i) y[i] = (bf16)x[u][i];
-      *reinterpret_cast<bf16x8*>(out + row * D + 8 * part) = y;
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, y), reinterpret_cast<u32x4*>(out + row * D + 8 * part));
     }
   }
 }
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(256) void la_silu(bf16* __restrict__ x, int64_t n8,
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int64_t i = base + u * 256;
-    if (i < n8) b[u] = *reinterpret_cast<const bf16x8*>(x + 8 * i);
+    if (i < n8) b[u] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + 8 * i)));
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(256) void la_silu(bf16* __restrict__ x, int64_t n8,
         const float f = (float)b[u][j];
         b[u][j] = (bf16)(f * sigmoid_fast(f));
       }
-      *reinterpret_cast<bf16x8*>(x + 8 * i) = b[u];
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, b[u]), reinterpret_cast<u32x4*>(x + 8 * i));
     }
   }
   // a tail of n % 8 elements, one thread

@@ -28,10 +28,9 @@
 //
 // Precision recipe (bf16 inputs): products of two bf16 inputs are exact in the
 // fp32 MFMA accumulator.  Quantities formed in fp32 that feed an MFMA are
-// rounded: the state S used in q S and the decayed values lam^(..) v used in
-// the state update go in as a bf16 hi + lo pair (~16 significant bits); the
-// masked, decayed scores P go in as one bf16 with block 64 and as a hi + lo
-// pair with longer blocks (their rounding error grows with the window).
+// rounded: the state S used in q S, the decayed values lam^(..) v used in
+// the state update and the masked, decayed scores P go in as a bf16 hi + lo
+// pair (~16 significant bits; a single bf16 P was the dominant error).
 // Accumulation is fp32 throughout and the state stays fp32.
 
 #include <hip/hip_runtime.h>
