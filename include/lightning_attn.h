@@ -139,28 +139,30 @@ int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const 
                              int64_t num_slots, int64_t block, int in_dtype, int out_dtype, void* stream);
 
 /*
- * Backward pass of the bf16 prefill: the gradients of a loss L given
+ * Backward pass of the prefill: the gradients of a loss L given
  * dout = dL/dO and dkv_out = dL/d(kv_out).  This is the derivative of the
  * recurrence above (the pages print no backward pass).  With the adjoint
  * G_t = dL/dS_t = lam G_{t+1} + q_t^T dout_t, G_{N-1} = dkv_out + q_{N-1}^T dout_{N-1}:
  *     dq_t = dout_t S_t^T,  dk_t = v_t G_t^T,  dv_t = k_t G_t,  dkv_in = lam G_0.
  * Each of dq, dk, dv is computed as a prefill-shaped pass (dk and dv run the
- * tokens last first) with the kernels of lightning_attn_fwd at block 64, so
- * the same omission below 2^-30 applies to heads that decay within a chunk.
- *   q, k, v, dout : bf16 [B][H][N][d]              (read)
+ * tokens last first) with the kernels of lightning_attn_fwd_ex at block 64,
+ * so with bf16 inputs the same omission below 2^-30 applies to heads that
+ * decay within a chunk.
+ *   q, k, v, dout : in_dtype [B][H][N][d]          (read)
  *   decay         : float [H]                      (read)
  *   kv_in         : float [B][H][d][d] or NULL     (read: the forward's initial state; NULL = zero)
  *   dkv_out       : float [B][H][d][d] or NULL     (read: dL/d(kv_out); NULL = zero)
  *   dq, dk, dv    : out_dtype [B][H][N][d]         (written)
  *   dkv_in        : float [B][H][d][d] or NULL     (written: dL/d(kv_in); may be dkv_out itself)
- *   B, H, N >= 1; d in {64, 128}; out_dtype LA_DTYPE_BF16 or LA_DTYPE_F32
+ *   B, H, N >= 1; d in {64, 128}; in_dtype / out_dtype as lightning_attn_fwd_ex
+ *   (bf16 in: bf16 or fp32 out; fp32 in: fp32 out)
  *   workspace     : device scratch of at least lightning_attn_bwd_workspace_bytes()
  *                   bytes, 256-byte aligned; NULL = allocated stream-ordered
  * Outputs may not overlap inputs or each other.
  */
 int lightning_attn_bwd(const void* q, const void* k, const void* v, const float* decay, const void* dout,
                        const float* kv_in, const float* dkv_out, void* dq, void* dk, void* dv, float* dkv_in,
-                       int64_t B, int64_t H, int64_t N, int64_t d, int out_dtype, void* workspace,
+                       int64_t B, int64_t H, int64_t N, int64_t d, int in_dtype, int out_dtype, void* workspace,
                        size_t workspace_bytes, void* stream);
 
 /* Bytes of scratch lightning_attn_bwd needs for these sizes (0 on invalid

@@ -74,7 +74,7 @@ def load():
     lib.lightning_attn_fwd_slots.restype = I
     lib.lightning_attn_fwd_slots.argtypes = [P] * 7 + [I64, I64, I64, I64, I64, I64, I, I, P]
     lib.lightning_attn_bwd.restype = I
-    lib.lightning_attn_bwd.argtypes = [P] * 11 + [I64, I64, I64, I64, I, P, SZ, P]
+    lib.lightning_attn_bwd.argtypes = [P] * 11 + [I64, I64, I64, I64, I, I, P, SZ, P]
     lib.lightning_attn_bwd_workspace_bytes.restype = SZ
     lib.lightning_attn_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64]
     lib.lightning_attn_decode_slots.restype = I
@@ -225,20 +225,22 @@ def fwd_slots(q, k, v, decay, states, slots, block=64, out=None, out_dtype=None,
 
 def bwd(q, k, v, decay, dout, kv_in=None, dkv_out=None, out_dtype=None, dkv_in=False, workspace=None,
         stream=None):
-    """Backward pass.  q, k, v, dout: [B, H, N, d] bf16 device tensors; decay fp32
-    [H]; kv_in: the forward's initial state, dkv_out: dL/d(kv_out), fp32
-    [B, H, d, d] or None.  Returns (dq, dk, dv, dkv_in) with dq, dk, dv in
-    out_dtype (default bf16); dkv_in is an fp32 tensor when asked for (True, or
-    a tensor to write into), else None."""
+    """Backward pass.  q, k, v, dout: [B, H, N, d] device tensors, all bf16 or all
+    fp32; decay fp32 [H]; kv_in: the forward's initial state, dkv_out:
+    dL/d(kv_out), fp32 [B, H, d, d] or None.  Returns (dq, dk, dv, dkv_in) with
+    dq, dk, dv in out_dtype (default: the input dtype); dkv_in is an fp32
+    tensor when asked for (True, or a tensor to write into), else None."""
     lib = load()
     B, H, N, d = q.shape
+    if q.dtype not in _DT:
+        raise TypeError("q must be bfloat16 or float32")
     for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
-        _check_dev(name, t, torch.bfloat16, (B, H, N, d))
+        _check_dev(name, t, q.dtype, (B, H, N, d))
     _check_dev("decay", decay, torch.float32, (H,))
     for name, t in (("kv_in", kv_in), ("dkv_out", dkv_out)):
         if t is not None:
             _check_dev(name, t, torch.float32, (B, H, d, d))
-    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    out_dtype = q.dtype if out_dtype is None else out_dtype
     code = _DT[out_dtype]
     dq, dk, dv = (torch.empty((B, H, N, d), device=q.device, dtype=out_dtype) for _ in range(3))
     if dkv_in is True:
@@ -252,7 +254,8 @@ def bwd(q, k, v, decay, dout, kv_in=None, dkv_out=None, out_dtype=None, dkv_in=F
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
     rc = lib.lightning_attn_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(dout), _ptr(kv_in), _ptr(dkv_out), _ptr(dq), _ptr(dk),
-        _ptr(dv), _ptr(dkv_in), B, H, N, d, code, _ptr(workspace), workspace.numel(), _stream(stream)
+        _ptr(dv), _ptr(dkv_in), B, H, N, d, _DT[q.dtype], code, _ptr(workspace), workspace.numel(),
+        _stream(stream)
     )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_bwd")

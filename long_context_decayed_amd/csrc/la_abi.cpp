@@ -247,20 +247,24 @@ size_t lightning_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64
 
 int lightning_attn_bwd(const void* q, const void* k, const void* v, const float* decay, const void* dout,
                        const float* kv_in, const float* dkv_out, void* dq, void* dk, void* dv, float* dkv_in,
-                       int64_t B, int64_t H, int64_t N, int64_t d, int out_dtype, void* workspace,
+                       int64_t B, int64_t H, int64_t N, int64_t d, int in_dtype, int out_dtype, void* workspace,
                        size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !decay || !dout || !dq || !dk || !dv) return LA_ERR_INVALID;
   if (B < 1 || H < 1 || N < 1 || d < 1) return LA_ERR_INVALID;
-  if (out_dtype != LA_DTYPE_BF16 && out_dtype != LA_DTYPE_F32) return LA_ERR_INVALID;
+  if ((in_dtype != LA_DTYPE_BF16 && in_dtype != LA_DTYPE_F32) ||
+      (out_dtype != LA_DTYPE_BF16 && out_dtype != LA_DTYPE_F32))
+    return LA_ERR_INVALID;
   const void* ptrs16[] = {q, k, v, dout, dq, dk, dv, kv_in, dkv_out, dkv_in};
   for (const void* p : ptrs16)
     if (!aligned(p, 16)) return LA_ERR_INVALID;
   if (!aligned(decay, 4)) return LA_ERR_INVALID;
   if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+  if (!prefill_supported(in_dtype, out_dtype, d, 64)) return LA_ERR_UNSUPPORTED;
   if (N > kMaxTokens) return LA_ERR_UNSUPPORTED;
   const int64_t L = pick_chunk(B, H, N, 64);
   if (B * H > kMaxGrid || B * H * ceil_div(N, L) > kMaxGrid) return LA_ERR_UNSUPPORTED;
-  const int64_t in_bytes = B * H * N * d * 2, out_bytes = B * H * N * d * (out_dtype == LA_DTYPE_BF16 ? 2 : 4);
+  const int64_t in_bytes = B * H * N * d * (in_dtype == LA_DTYPE_BF16 ? 2 : 4);
+  const int64_t out_bytes = B * H * N * d * (out_dtype == LA_DTYPE_BF16 ? 2 : 4);
   const int64_t st_bytes = B * H * d * d * 4;
   // outputs: apart from every input and from each other; dkv_in may be dkv_out itself
   const void* outs[] = {dq, dk, dv};
@@ -308,12 +312,12 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
   a.block = 64;
   a.L = L;
   a.nc = (int)ceil_div(N, L);
-  a.in_dtype = la::kBF16;
+  a.in_dtype = in_dtype == LA_DTYPE_BF16 ? la::kBF16 : la::kF32;
   a.out_dtype = out_dtype == LA_DTYPE_BF16 ? la::kBF16 : la::kF32;
   a.tbl = (float*)ws;
   a.tbl_stride = (int)tbl_stride_for(64);
   a.states = (float*)((char*)ws + tbl_bytes);
-  a.warm_start = true;
+  a.warm_start = a.in_dtype == la::kBF16;
   a.slots = nullptr;
   a.num_slots = 0;
   a.evt_begin = nullptr;

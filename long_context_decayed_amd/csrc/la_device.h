@@ -220,13 +220,16 @@ struct RowTile {
   static constexpr int PER = TOTAL / NT;
   uint4 r[PER];
 
+  // Rows t0 .. t0 + 63 (those below t_end; zeros beyond) of a row-major
+  // [N][D] array; row t at src + t * RS elements (RS = -D: rows last first).
+  template <int RS = D>
   __device__ __forceinline__ void load(const T* __restrict__ src, int t0, int t_end, int tid) {
-    const T* base = src + (int64_t)t0 * D;
+    const T* base = src + (int64_t)t0 * RS;
     if (t0 + 64 <= t_end) {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int idx = tid + i * NT;
-        r[i] = *reinterpret_cast<const uint4*>(base + (idx / CPR) * D + (idx % CPR) * VEC);
+        r[i] = *reinterpret_cast<const uint4*>(base + (idx / CPR) * RS + (idx % CPR) * VEC);
       }
     } else {
 #pragma unroll
@@ -234,7 +237,7 @@ struct RowTile {
         const int idx = tid + i * NT;
         const int row = idx / CPR;
         if (t0 + row < t_end)
-          r[i] = *reinterpret_cast<const uint4*>(base + row * D + (idx % CPR) * VEC);
+          r[i] = *reinterpret_cast<const uint4*>(base + row * RS + (idx % CPR) * VEC);
         else
           r[i] = make_uint4(0u, 0u, 0u, 0u);
       }

@@ -53,8 +53,11 @@ namespace la {
 //   update S += sum_s lam^(BLK-1-s) k_s^T v_s               (decayed v as hi + lo)
 // with S pre-decayed by lam^BLK once per block.  With BLK = 64 the state is
 // split into hi/lo on the fly; with longer blocks the block-start split is
-// kept in registers for the block's later sub-tiles.
-template <typename TIn, typename TOut, int D, int BLK>
+// kept in registers for the block's later sub-tiles.  REV: the reverse-time
+// passes of the backward (rows last first; the initial state enters the
+// first token undecayed, so the first block of chunk 0 takes one decay power
+// less in its rows and in the state it hands on), as in la_chunk_output64.
+template <typename TIn, typename TOut, int D, int BLK, bool REV>
 __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) void la_chunk_output(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                                          const TIn* __restrict__ v, TOut* __restrict__ o,
                                                          const float* __restrict__ tbl_all,
@@ -78,7 +81,8 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
   const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
   const int hh = bh % H;
-  const int64_t base = (int64_t)bh * N * D;
+  constexpr int RS = REV ? -D : D;  // elements from one token's row to the next
+  const int64_t base = (int64_t)bh * N * D + (REV ? (int64_t)(N - 1) * D : 0);
   const TIn* qb = q + base;
   const TIn* kb = k + base;
   const TIn* vb = v + base;
@@ -102,9 +106,9 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
   constexpr bool kPrefetch = !(BLK == 64 && sizeof(TIn) == 2);
   RowTile<TIn, D, NT> pq, pk, pv;
   if (kPrefetch) {
-    pq.load(qb, t_begin, t_end, tid);
-    pk.load(kb, t_begin, t_end, tid);
-    pv.load(vb, t_begin, t_end, tid);
+    pq.template load<RS>(qb, t_begin, t_end, tid);
+    pk.template load<RS>(kb, t_begin, t_end, tid);
+    pv.template load<RS>(vb, t_begin, t_end, tid);
   }
 
   int jb = 0;  // sub-tile index within the current block
@@ -112,20 +116,22 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
     TIn* Kj = Ks + jb * kSub * LD;
     TIn* Vj = Vs + jb * kSub * LD;
     if (!kPrefetch) {
-      pq.load(qb, t0, t_end, tid);
-      pk.load(kb, t0, t_end, tid);
-      pv.load(vb, t0, t_end, tid);
+      pq.template load<RS>(qb, t0, t_end, tid);
+      pk.template load<RS>(kb, t0, t_end, tid);
+      pv.template load<RS>(vb, t0, t_end, tid);
     }
     pq.template store<LD>(Qs, tid);
     pk.template store<LD>(Kj, tid);
     pv.template store<LD>(Vj, tid);
     __syncthreads();
     if (kPrefetch && t0 + kSub < t_end) {
-      pq.load(qb, t0 + kSub, t_end, tid);
-      pk.load(kb, t0 + kSub, t_end, tid);
-      pv.load(vb, t0 + kSub, t_end, tid);
+      pq.template load<RS>(qb, t0 + kSub, t_end, tid);
+      pk.template load<RS>(kb, t0 + kSub, t_end, tid);
+      pv.template load<RS>(vb, t0 + kSub, t_end, tid);
     }
 
+    // REV: the first block of chunk 0 takes one decay power less.
+    const int sh = (REV && c == 0 && t0 - t_begin < BLK) ? 1 : 0;
     // Inter-block: acc[rt] = diag(lam^(p+1)) Q S_b.
     f32x16 acc[2];
     acc[0] = zero16();
@@ -147,12 +153,12 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
             if (M::kSplit) acc[rt] = M::mma(a, lo, acc[rt]);
           }
         }
-        S[kt] *= tbl[BLK];
+        S[kt] *= tbl[BLK - sh];
       }
     } else {
       if (jb == 0) {
         // Block start: keep S_b as MFMA B operands, then pre-decay S by lam^BLK.
-        const float dblk = tbl[BLK];
+        const float dblk = tbl[BLK - sh];
 #pragma unroll
         for (int kt = 0; kt < SNAP; ++kt) {
 #pragma unroll
@@ -182,7 +188,7 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[rt][j] *= tbl[kSub * jb + 32 * rt + crow(j, hf) + 1];
+      for (int j = 0; j < 16; ++j) acc[rt][j] *= tbl[kSub * jb + 32 * rt + crow(j, hf) + 1 - sh];
 
     // Intra-block: for every earlier-or-current sub-tile jk of the block,
     // P^T = K_jk Q^T (32x32 tiles), masked and decayed by lam^(p-s), then acc += P V_jk.
@@ -254,7 +260,7 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int t = t0 + 32 * rt + crow(j, hf);
-        if (t < t_end) ob[(int64_t)t * D + col] = from_f32<TOut>(acc[rt][j]);
+        if (t < t_end) ob[(int64_t)t * RS + col] = from_f32<TOut>(acc[rt][j]);
       }
     __syncthreads();
   }
@@ -726,8 +732,16 @@ static hipError_t launch_output_t(const PrefillArgs& a, hipStream_t st) {
   }
   if constexpr (BLK == 64 && sizeof(TIn) == 2)
     launch_fast<TOut, D, kFromStart>(a, st);
-  else
-    hipLaunchKernelGGL((la_chunk_output<TIn, TOut, D, BLK>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+  else if (a.rev) {
+    // the backward's reverse passes reach the general kernel with fp32 inputs at block 64 only
+    if constexpr (BLK == 64 && sizeof(TIn) == 4)
+      hipLaunchKernelGGL((la_chunk_output<TIn, TOut, D, BLK, true>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+                         (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (TOut*)a.out, (const float*)a.tbl,
+                         (const float*)a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
+    else
+      return hipErrorInvalidValue;
+  } else
+    hipLaunchKernelGGL((la_chunk_output<TIn, TOut, D, BLK, false>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                        (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (TOut*)a.out, (const float*)a.tbl,
                        (const float*)a.states, (int)a.H, (int)a.N, (int)a.L, nc, a.tbl_stride);
   if (timed && a.evt_end) {

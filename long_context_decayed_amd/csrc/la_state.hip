@@ -34,7 +34,7 @@ __global__ void la_decay_table(const float* __restrict__ decay, float* __restric
 // row-major LDS tiles with transpose reads.  For full sub-tiles the decay
 // lam^(63-s) of token s = 16kk + 8h + i is the wave-uniform power
 // lam^(55-16kk-i) times the per-half-wave power lam^(8(1-h)).
-template <typename TIn, int D>
+template <typename TIn, int D, bool REV>
 __global__ __launch_bounds__(D * 2, sizeof(TIn) == 2 ? 3 : 1) void la_chunk_state(const TIn* __restrict__ k, const TIn* __restrict__ v,
                                                            const float* __restrict__ tbl_all,
                                                            float* __restrict__ ws, int H, int N, int L, int nc,
@@ -55,7 +55,8 @@ __global__ __launch_bounds__(D * 2, sizeof(TIn) == 2 ? 3 : 1) void la_chunk_stat
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5;
   const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
   const int hh = bh % H;
-  const int64_t base = (int64_t)bh * N * D;
+  constexpr int RS = REV ? -D : D;  // elements from one token's row to the next (REV: rows last first)
+  const int64_t base = (int64_t)bh * N * D + (REV ? (int64_t)(N - 1) * D : 0);
   const TIn* kb = k + base;
   const TIn* vb = v + base;
   const int t_begin = c * L;
@@ -68,16 +69,16 @@ __global__ __launch_bounds__(D * 2, sizeof(TIn) == 2 ? 3 : 1) void la_chunk_stat
   for (int kt = 0; kt < NRT; ++kt) U[kt] = zero16();
 
   RowTile<TIn, D, NT> pk, pv;
-  pk.load(kb, t_begin, t_end, tid);
-  pv.load(vb, t_begin, t_end, tid);
+  pk.template load<RS>(kb, t_begin, t_end, tid);
+  pv.template load<RS>(vb, t_begin, t_end, tid);
   for (int t0 = t_begin; t0 < t_end; t0 += kSub) {
     const int n = min(kSub, t_end - t0);
     pk.template store<LD>(Ks, tid);
     pv.template store<LD>(Vs, tid);
     __syncthreads();
     if (t0 + kSub < t_end) {  // next sub-tile's loads overlap this one's MFMAs
-      pk.load(kb, t0 + kSub, t_end, tid);
-      pv.load(vb, t0 + kSub, t_end, tid);
+      pk.template load<RS>(kb, t0 + kSub, t_end, tid);
+      pv.template load<RS>(vb, t0 + kSub, t_end, tid);
     }
     const float dn = tb[n];
 #pragma unroll
@@ -347,10 +348,14 @@ static hipError_t launch_aggregate_t(const PrefillArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((la_chunk_state64<D, false>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                          (const bf16*)a.k, (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H,
                          (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0);
-  } else
-    hipLaunchKernelGGL((la_chunk_state<TIn, D>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st, (const TIn*)a.k,
+  } else if (a.rev)
+    hipLaunchKernelGGL((la_chunk_state<TIn, D, true>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st, (const TIn*)a.k,
                        (const TIn*)a.v, (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc,
                        a.tbl_stride);
+  else
+    hipLaunchKernelGGL((la_chunk_state<TIn, D, false>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+                       (const TIn*)a.k, (const TIn*)a.v, (const float*)a.tbl, a.states, (int)a.H, (int)a.N,
+                       (int)a.L, nc, a.tbl_stride);
   return hipGetLastError();
 }
 

@@ -199,17 +199,20 @@ def test_bwd_validation(lib):
     q, k, v, dec, g = FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4]
     dq, dk, dv = FAKE[5], FAKE[6], FAKE[7]
     args = lambda **kw: [kw.get("q", q), k, v, dec, kw.get("g", g), None, None, kw.get("dq", dq), dk, dv, None,
-                         kw.get("B", 1), 1, kw.get("N", 128), kw.get("d", 128), kw.get("od", 0), None, 0, None]
+                         kw.get("B", 1), 1, kw.get("N", 128), kw.get("d", 128), kw.get("idt", 0), kw.get("od", 0),
+                         None, 0, None]
     assert f(*args(q=None)) == LA_ERR_INVALID
     assert f(*args(g=None)) == LA_ERR_INVALID
     assert f(*args(B=0)) == LA_ERR_INVALID
     assert f(*args(od=7)) == LA_ERR_INVALID
+    assert f(*args(idt=7)) == LA_ERR_INVALID
+    assert f(*args(idt=1, od=0)) == LA_ERR_UNSUPPORTED           # fp32 in needs fp32 out
     assert f(*args(d=96)) == LA_ERR_UNSUPPORTED
     assert f(*args(dq=FAKE[0])) == LA_ERR_INVALID            # dq overlaps q
     assert f(*args(dq=ctypes.c_void_p(FAKE[5].value + 8))) == LA_ERR_INVALID   # misaligned
     small = (ctypes.c_uint8 * 16)()
     a = args()
-    a[16], a[17] = FAKE[5], 16                                 # workspace too small
+    a[17], a[18] = FAKE[5], 16                                 # workspace too small
     assert f(*a) == LA_ERR_WORKSPACE
     need = lib.lightning_attn_bwd_workspace_bytes(1, 64, 1 << 20, 128)
     fwd = lib.lightning_attn_fwd_workspace_bytes(1, 64, 1 << 20, 128, 64, 0)

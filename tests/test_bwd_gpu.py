@@ -120,3 +120,40 @@ def test_bwd_dkv_in_place(dev):
                        threads=oracle_threads())[3]
     for h in range(H):
         tol.assert_state(host(dsn)[:, h], rs[:, h], "dS0 head %d" % h)
+
+
+# --- fp32 inputs: the general kernels, reversed for dK and dV ----------------
+
+def test_bwd_fp32_tiny_workload(dev):
+    say("bwd fp32 B1 H2 N1024 d64 (the tiny fp32 workload, seed 0)")
+    from long_context_decayed_amd.inputs import qkv_cpu
+    q, k, v = (t.to(dev) for t in qkv_cpu(1, 2, 1024, 64, seed=0))
+    g = qkv_cpu(1, 2, 1024, 64, seed=1)[0].to(dev)
+    lam = decay_lambdas(2)
+    dq, dk, dv, ds0 = la.bwd(q, k, v, torch.from_numpy(lam).to(dev), g, dkv_in=True)
+    torch.cuda.synchronize()
+    assert dq.dtype == torch.float32
+    rq, rk, rv, rs = _grad_oracle(q, k, v, lam, g, None, None)
+    for got, ref, name in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+        tol.assert_fp32(host(got), ref, name)
+    tol.assert_fp32(host(ds0), rs, "dS0")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_fp32_mixed_decays_with_states(dev, d):
+    say("bwd fp32 mixed decays B2 H8 N777 d", d, "with states")
+    B, H, n = 2, 8, 777
+    from long_context_decayed_amd.inputs import qkv_cpu
+    q, k, v = (t.to(dev) for t in qkv_cpu(B, H, n, d, seed=40 + d))
+    g = qkv_cpu(B, H, n, d, seed=50 + d)[0].to(dev)
+    s0 = state_device(B, H, d, seed=40 + d, device=dev)
+    dsn = state_device(B, H, d, seed=50 + d, device=dev)
+    dq, dk, dv, ds0 = la.bwd(q, k, v, torch.from_numpy(MIXED_LAMS).to(dev), g, kv_in=s0, dkv_out=dsn, dkv_in=True)
+    torch.cuda.synchronize()
+    rq, rk, rv, rs = _grad_oracle(q, k, v, MIXED_LAMS, g, s0, dsn)
+    for got, ref, name in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+        got_h = host(got)
+        for h in range(H):
+            tol.assert_fp32(got_h[:, h], ref[:, h], "%s head %d" % (name, h))
+    for h in range(H):
+        tol.assert_fp32(host(ds0)[:, h], rs[:, h], "dS0 head %d" % h)
