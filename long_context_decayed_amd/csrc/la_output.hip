@@ -278,10 +278,10 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 //   * the state's accumulator rows hold the features in an order with bits 2
 //     and 3 of the row index swapped, so the 8 features a lane contributes to
 //     one MFMA step are contiguous in Q and K: one 16-byte LDS read;
-//   * Q, K and V tiles arrive by 16-byte LDS DMA; K is brought in twice (the
-//     second read is served by L2), as the row-read operand of the score
-//     tiles and as the transpose-read operand of the state update, so that
-//     each copy is needed in one phase only;
+//   * Q, K and V tiles arrive by 16-byte LDS DMA; K is kept twice in LDS, as
+//     the row-read operand of the score tiles and as the transpose-read
+//     operand of the state update, so that each copy is needed in one phase
+//     only; the second copy is made from the first inside LDS;
 //   * the 3 causal 32x32 score tiles P^T = K Q^T of a sub-tile are computed
 //     by one wave each, masked, decayed and shared through LDS as bf16 hi + lo
 //     MFMA operands (~16 bits of P);
@@ -292,9 +292,9 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 //     score copy of K are only read in phase 1 (inter term and scores), so
 //     the next ones are requested at the barrier that ends phase 1 and waited
 //     for at the one that ends phase 2; V and the update copy of K are only
-//     read in phase 2 (P V and the state update), so the next ones are
-//     requested after that barrier, ahead of this sub-tile's output stores,
-//     and waited for at the end of the next phase 1.
+//     read in phase 2 (P V and the state update), so after that barrier the
+//     next V is requested, ahead of this sub-tile's output stores, and the
+//     next K copied over; both are waited for at the end of the next phase 1.
 // Two workgroups per CU (80 KiB of LDS each).
 //
 // Two modes, by where the chunk's start state comes from:
@@ -615,8 +615,16 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
     // and visible; V, K^T and the score tiles are free from here on.
     sync_lds_after_vmem<0>();
     if (more) {
-      dma_tile<D, NW, RS>(kb + off_next, Kt, nv_next, w, lane);
       dma_tile<D, NW, RS>(vb + off_next, Vs, nv_next, w, lane);
+      // The next sub-tile's K^T copy from its score copy, already in LDS.
+      constexpr int NCH = kSub * D * 2 / 16 / (NW * 64);  // 16-byte chunks per thread
+      const uint4* ksrc = reinterpret_cast<const uint4*>(Ks);
+      uint4* kdst = reinterpret_cast<uint4*>(Kt);
+      uint4 tmp[NCH];
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) tmp[i] = ksrc[tid + NW * 64 * i];
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) kdst[tid + NW * 64 * i] = tmp[i];
     }
 
     // Output rows.  Lane (h, l) holds token t0 + 32rt + l, columns 32w + 8jq
