@@ -2,6 +2,8 @@
 
 Sizes run in seconds, span several tiles, blocks and chunks, and include
 ragged tails.  Each case prints its name before touching the GPU."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -318,3 +320,19 @@ def test_bf16_depth_scaled_decays(dev, layer, chunk):
         tol.assert_bf16_f32out(o_h[:, h], o_ref[:, h], "O head %d" % h)
     tol.assert_bf16_f32out(o_h, o_ref)
     tol.assert_state(kv_h, s_ref, "kv_out")
+
+
+def test_bf16_classification_boundary(dev):
+    # At chunk 1536 a head takes the warm-start path when its carry span (30 ln 2
+    # / -ln lam rounded up to 64) is at most 512: lam with 30 ln 2 / -ln lam =
+    # 511.5 and 512 sit on the warm-start side, 512.5 just past it (span 576).
+    lams = np.array([math.exp(-30 * math.log(2) / t) for t in (448.2, 511.5, 512.0, 512.5)], dtype=np.float32)
+    say("bf16 decays at the warm-start boundary, chunk 1536, B2 H4 N5000 d128, with state")
+    q, k, v = qkv_device(2, 4, 5000, 128, seed=130, device=dev)
+    s0 = state_device(2, 4, 128, seed=130, device=dev)
+    o32, kv = _run(q, k, v, lams, dev, 64, out_dtype=torch.float32, kv_in=s0, chunk=1536)
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lams, host(s0).astype(np.float64))
+    o_h, kv_h = host(o32), host(kv)
+    for h in range(4):
+        tol.assert_bf16_f32out(o_h[:, h], o_ref[:, h], "O head %d (lam %.7f)" % (h, lams[h]))
+        tol.assert_state(kv_h[:, h], s_ref[:, h], "kv_out head %d" % h)
