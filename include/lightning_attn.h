@@ -59,6 +59,13 @@ extern "C" {
 #define LA_DTYPE_BF16 0
 #define LA_DTYPE_F32 1
 
+/* Flags of lightning_attn_fwd_ex, lightning_attn_fwd_slots, lightning_attn_bwd.
+ * LA_FLAG_EXACT: every head by the exact chunked path (chunk aggregates, scan,
+ * outputs from the chunk start states), never the warm start described at
+ * lightning_attn_fwd; for inputs whose magnitudes vary so much over time that
+ * 2^-30 of a state older than the carry span still matters. */
+#define LA_FLAG_EXACT 1u
+
 /*
  * Prefill, bf16 Q/K/V/O, fp32 accumulation and fp32 state.
  *   q, k, v   : bf16 [B][H][N][d]            (read)
@@ -78,7 +85,10 @@ extern "C" {
  * of its term lam^(t-c0+span+1) S_(c0-span-1), at most 2^-30 of that state
  * (c0 = the chunk's first token; the first chunk starts from kv_in exactly).
  * Every other head, and every other dtype and block, is computed without
- * omission.
+ * omission.  The bound is relative to the omitted term, not to the output:
+ * a token whose k^T v is ~10^8 times the typical one, just before a chunk's
+ * warm-up window, can move outputs of the chunk by ~10% of their size.  The
+ * _ex entry point with LA_FLAG_EXACT takes the exact path for every head.
  * Scratch (decay-power table and per-chunk states, see
  * lightning_attn_fwd_workspace_bytes) is allocated stream-ordered with
  * hipMallocAsync/hipFreeAsync on `stream`.
@@ -107,6 +117,7 @@ int lightning_attn_fwd_bf16_f32out(const void* q, const void* k, const void* v, 
  *               default (lightning_attn_fwd_chunk); otherwise a positive
  *               multiple of block.  The result does not depend on it beyond
  *               rounding.
+ *   flags     : 0, or LA_FLAG_EXACT
  *   workspace : device scratch of at least lightning_attn_fwd_workspace_bytes()
  *               bytes, 256-byte aligned, owned by the caller and not used
  *               after the enqueued work completes; NULL = allocate
@@ -119,8 +130,8 @@ int lightning_attn_fwd_bf16_f32out(const void* q, const void* k, const void* v, 
  */
 int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const float* decay, void* out,
                           const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
-                          int64_t block, int in_dtype, int out_dtype, int64_t chunk, void* workspace,
-                          size_t workspace_bytes, void* evt_begin, void* evt_end, void* stream);
+                          int64_t block, int in_dtype, int out_dtype, int64_t chunk, unsigned int flags,
+                          void* workspace, size_t workspace_bytes, void* evt_begin, void* evt_end, void* stream);
 
 /*
  * Prefill into a pool of states (serving: chunked prefill of several
@@ -136,7 +147,8 @@ int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const flo
  */
 int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const float* decay, void* out,
                              float* states, const int32_t* slots, int64_t B, int64_t H, int64_t N, int64_t d,
-                             int64_t num_slots, int64_t block, int in_dtype, int out_dtype, void* stream);
+                             int64_t num_slots, int64_t block, int in_dtype, int out_dtype, unsigned int flags,
+                             void* stream);
 
 /*
  * Backward pass of the prefill: the gradients of a loss L given
@@ -155,15 +167,15 @@ int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const 
  *   dq, dk, dv    : out_dtype [B][H][N][d]         (written)
  *   dkv_in        : float [B][H][d][d] or NULL     (written: dL/d(kv_in); may be dkv_out itself)
  *   B, H, N >= 1; d in {64, 128}; in_dtype / out_dtype as lightning_attn_fwd_ex
- *   (bf16 in: bf16 or fp32 out; fp32 in: fp32 out)
+ *   (bf16 in: bf16 or fp32 out; fp32 in: fp32 out); flags: 0 or LA_FLAG_EXACT
  *   workspace     : device scratch of at least lightning_attn_bwd_workspace_bytes()
  *                   bytes, 256-byte aligned; NULL = allocated stream-ordered
  * Outputs may not overlap inputs or each other.
  */
 int lightning_attn_bwd(const void* q, const void* k, const void* v, const float* decay, const void* dout,
                        const float* kv_in, const float* dkv_out, void* dq, void* dk, void* dv, float* dkv_in,
-                       int64_t B, int64_t H, int64_t N, int64_t d, int in_dtype, int out_dtype, void* workspace,
-                       size_t workspace_bytes, void* stream);
+                       int64_t B, int64_t H, int64_t N, int64_t d, int in_dtype, int out_dtype, unsigned int flags,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of scratch lightning_attn_bwd needs for these sizes (0 on invalid
  * arguments). */

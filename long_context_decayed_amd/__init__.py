@@ -29,6 +29,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblightnin
 
 LA_DTYPE_BF16 = 0
 LA_DTYPE_F32 = 1
+LA_FLAG_EXACT = 1
 _DT = {torch.bfloat16: LA_DTYPE_BF16, torch.float32: LA_DTYPE_F32}
 
 _lib = None
@@ -58,7 +59,7 @@ def load():
         fn.restype = I
         fn.argtypes = fwd_args + [P]
     lib.lightning_attn_fwd_ex.restype = I
-    lib.lightning_attn_fwd_ex.argtypes = fwd_args + [I, I, I64, P, SZ, P, P, P]
+    lib.lightning_attn_fwd_ex.argtypes = fwd_args + [I, I, I64, ctypes.c_uint, P, SZ, P, P, P]
     lib.lightning_attn_fwd_chunk.restype = I64
     lib.lightning_attn_fwd_chunk.argtypes = [I64, I64, I64, I64, I64]
     lib.lightning_attn_fwd_workspace_bytes.restype = SZ
@@ -72,9 +73,9 @@ def load():
     lib.lightning_attn_silu.restype = I
     lib.lightning_attn_silu.argtypes = [P, I64, P]
     lib.lightning_attn_fwd_slots.restype = I
-    lib.lightning_attn_fwd_slots.argtypes = [P] * 7 + [I64, I64, I64, I64, I64, I64, I, I, P]
+    lib.lightning_attn_fwd_slots.argtypes = [P] * 7 + [I64, I64, I64, I64, I64, I64, I, I, ctypes.c_uint, P]
     lib.lightning_attn_bwd.restype = I
-    lib.lightning_attn_bwd.argtypes = [P] * 11 + [I64, I64, I64, I64, I, I, P, SZ, P]
+    lib.lightning_attn_bwd.argtypes = [P] * 11 + [I64, I64, I64, I64, I, I, ctypes.c_uint, P, SZ, P]
     lib.lightning_attn_bwd_workspace_bytes.restype = SZ
     lib.lightning_attn_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64]
     lib.lightning_attn_decode_slots.restype = I
@@ -131,14 +132,15 @@ def workspace_bytes(B, H, N, d, block=256, chunk=0):
 
 
 def fwd(q, k, v, decay, kv_in=None, kv_out=None, block=256, out=None, out_dtype=None, chunk=0,
-        workspace=None, events=None, stream=None):
+        workspace=None, events=None, exact=False, stream=None):
     """Prefill.  q, k, v: [B, H, N, d] bf16 or fp32 device tensors; decay: fp32 [H];
     kv_in / kv_out: fp32 [B, H, d, d] or None.  Returns out [B, H, N, d] in
     out_dtype (default: the input dtype).
 
     workspace: a uint8 device tensor of at least workspace_bytes(...) bytes;
     None allocates one from torch's caching allocator.  events: optional pair
-    of hipEvent_t handles (ints) recorded around the output kernel."""
+    of hipEvent_t handles (ints) recorded around the kernel that writes every
+    output row.  exact: every head by the exact chunked path (no warm start)."""
     lib = load()
     if q.dtype not in _DT:
         raise TypeError("q must be bfloat16 or float32")
@@ -164,7 +166,7 @@ def fwd(q, k, v, decay, kv_in=None, kv_out=None, block=256, out=None, out_dtype=
     e0, e1 = (None, None) if events is None else (ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
     rc = lib.lightning_attn_fwd_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(kv_in), _ptr(kv_out),
-        B, H, N, d, block, _DT[q.dtype], _DT[odt], chunk,
+        B, H, N, d, block, _DT[q.dtype], _DT[odt], chunk, LA_FLAG_EXACT if exact else 0,
         _ptr(workspace), workspace.numel(), e0, e1, _stream(stream),
     )
     if rc != 0:
@@ -194,7 +196,7 @@ def decode_step(q, k, v, decay, kv_in=None, kv_out=None, out=None, stream=None):
     return out
 
 
-def fwd_slots(q, k, v, decay, states, slots, block=64, out=None, out_dtype=None, stream=None):
+def fwd_slots(q, k, v, decay, states, slots, block=64, out=None, out_dtype=None, exact=False, stream=None):
     """Prefill into a state pool.  q, k, v: [B, H, N, d]; states: fp32
     [num_slots, H, d, d], read and written in place for the rows' slots;
     slots: int32 [B] on the device (out of range: zero start, no write-back).
@@ -216,7 +218,7 @@ def fwd_slots(q, k, v, decay, states, slots, block=64, out=None, out_dtype=None,
     _check_dev("out", out, out_dtype, (B, H, N, d))
     rc = lib.lightning_attn_fwd_slots(
         _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(states), _ptr(slots), B, H, N, d,
-        states.shape[0], block, _DT[q.dtype], _DT[out_dtype], _stream(stream)
+        states.shape[0], block, _DT[q.dtype], _DT[out_dtype], LA_FLAG_EXACT if exact else 0, _stream(stream)
     )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_fwd_slots")
@@ -224,7 +226,7 @@ def fwd_slots(q, k, v, decay, states, slots, block=64, out=None, out_dtype=None,
 
 
 def bwd(q, k, v, decay, dout, kv_in=None, dkv_out=None, out_dtype=None, dkv_in=False, workspace=None,
-        stream=None):
+        exact=False, stream=None):
     """Backward pass.  q, k, v, dout: [B, H, N, d] device tensors, all bf16 or all
     fp32; decay fp32 [H]; kv_in: the forward's initial state, dkv_out:
     dL/d(kv_out), fp32 [B, H, d, d] or None.  Returns (dq, dk, dv, dkv_in) with
@@ -254,8 +256,8 @@ def bwd(q, k, v, decay, dout, kv_in=None, dkv_out=None, out_dtype=None, dkv_in=F
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
     rc = lib.lightning_attn_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(dout), _ptr(kv_in), _ptr(dkv_out), _ptr(dq), _ptr(dk),
-        _ptr(dv), _ptr(dkv_in), B, H, N, d, _DT[q.dtype], code, _ptr(workspace), workspace.numel(),
-        _stream(stream)
+        _ptr(dv), _ptr(dkv_in), B, H, N, d, _DT[q.dtype], code, LA_FLAG_EXACT if exact else 0, _ptr(workspace),
+        workspace.numel(), _stream(stream)
     )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_bwd")

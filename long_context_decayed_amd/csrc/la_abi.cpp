@@ -120,7 +120,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 int prefill_run(const void* q, const void* k, const void* v, const float* decay, void* out, const float* kv_in,
                 float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, int in_dtype,
                 int out_dtype, int64_t L, void* workspace, size_t workspace_bytes, void* evt_begin, void* evt_end,
-                void* stream, const int* slots, int64_t num_slots);
+                void* stream, const int* slots, int64_t num_slots, bool exact);
 
 }  // namespace
 
@@ -128,18 +128,21 @@ extern "C" {
 
 int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const float* decay, void* out,
                           const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
-                          int64_t block, int in_dtype, int out_dtype, int64_t chunk, void* workspace,
-                          size_t workspace_bytes, void* evt_begin, void* evt_end, void* stream) {
+                          int64_t block, int in_dtype, int out_dtype, int64_t chunk, unsigned int flags,
+                          void* workspace, size_t workspace_bytes, void* evt_begin, void* evt_end, void* stream) {
+  if (flags & ~LA_FLAG_EXACT) return LA_ERR_INVALID;
   int64_t L = 0;
   int rc = validate_prefill(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, in_dtype, out_dtype, chunk, &L);
   if (rc != LA_OK) return rc;
   return prefill_run(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, in_dtype, out_dtype, L, workspace,
-                     workspace_bytes, evt_begin, evt_end, stream, nullptr, 0);
+                     workspace_bytes, evt_begin, evt_end, stream, nullptr, 0, (flags & LA_FLAG_EXACT) != 0);
 }
 
 int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const float* decay, void* out,
                              float* states, const int32_t* slots, int64_t B, int64_t H, int64_t N, int64_t d,
-                             int64_t num_slots, int64_t block, int in_dtype, int out_dtype, void* stream) {
+                             int64_t num_slots, int64_t block, int in_dtype, int out_dtype, unsigned int flags,
+                             void* stream) {
+  if (flags & ~LA_FLAG_EXACT) return LA_ERR_INVALID;
   if (!states || !slots || num_slots < 1) return LA_ERR_INVALID;
   if (!aligned(states, 16) || !aligned(slots, 4)) return LA_ERR_INVALID;
   if (num_slots > kMaxGrid) return LA_ERR_UNSUPPORTED;
@@ -155,7 +158,7 @@ int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const 
       overlap(states, pool_bytes, slots, B * 4) || overlap(out, out_bytes, slots, B * 4))
     return LA_ERR_INVALID;
   return prefill_run(q, k, v, decay, out, states, states, B, H, N, d, block, in_dtype, out_dtype, L, nullptr, 0,
-                     nullptr, nullptr, stream, (const int*)slots, num_slots);
+                     nullptr, nullptr, stream, (const int*)slots, num_slots, (flags & LA_FLAG_EXACT) != 0);
 }
 
 }  // extern "C"
@@ -165,7 +168,7 @@ namespace {
 int prefill_run(const void* q, const void* k, const void* v, const float* decay, void* out, const float* kv_in,
                 float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, int in_dtype,
                 int out_dtype, int64_t L, void* workspace, size_t workspace_bytes, void* evt_begin, void* evt_end,
-                void* stream, const int* slots, int64_t num_slots) {
+                void* stream, const int* slots, int64_t num_slots, bool exact) {
   size_t tbl_bytes = 0;
   const size_t need = workspace_layout(B, H, N, d, block, L, &tbl_bytes);
   if (workspace) {
@@ -199,7 +202,7 @@ int prefill_run(const void* q, const void* k, const void* v, const float* decay,
   a.tbl = (float*)ws;
   a.tbl_stride = (int)tbl_stride_for(block);
   a.states = (float*)((char*)ws + tbl_bytes);
-  a.warm_start = a.in_dtype == la::kBF16 && block == 64;
+  a.warm_start = a.in_dtype == la::kBF16 && block == 64 && !exact;
   a.rev = false;
   a.scale_kv_out = false;
   a.slots = slots;
@@ -222,21 +225,21 @@ int lightning_attn_fwd(const void* q, const void* k, const void* v, const float*
                        const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
                        int64_t block, void* stream) {
   return lightning_attn_fwd_ex(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, LA_DTYPE_BF16,
-                               LA_DTYPE_BF16, 0, nullptr, 0, nullptr, nullptr, stream);
+                               LA_DTYPE_BF16, 0, 0u, nullptr, 0, nullptr, nullptr, stream);
 }
 
 int lightning_attn_fwd_f32(const void* q, const void* k, const void* v, const float* decay, void* out,
                            const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
                            int64_t block, void* stream) {
   return lightning_attn_fwd_ex(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, LA_DTYPE_F32,
-                               LA_DTYPE_F32, 0, nullptr, 0, nullptr, nullptr, stream);
+                               LA_DTYPE_F32, 0, 0u, nullptr, 0, nullptr, nullptr, stream);
 }
 
 int lightning_attn_fwd_bf16_f32out(const void* q, const void* k, const void* v, const float* decay,
                                    void* out, const float* kv_in, float* kv_out, int64_t B, int64_t H,
                                    int64_t N, int64_t d, int64_t block, void* stream) {
   return lightning_attn_fwd_ex(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, LA_DTYPE_BF16,
-                               LA_DTYPE_F32, 0, nullptr, 0, nullptr, nullptr, stream);
+                               LA_DTYPE_F32, 0, 0u, nullptr, 0, nullptr, nullptr, stream);
 }
 
 size_t lightning_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
@@ -247,8 +250,9 @@ size_t lightning_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64
 
 int lightning_attn_bwd(const void* q, const void* k, const void* v, const float* decay, const void* dout,
                        const float* kv_in, const float* dkv_out, void* dq, void* dk, void* dv, float* dkv_in,
-                       int64_t B, int64_t H, int64_t N, int64_t d, int in_dtype, int out_dtype, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       int64_t B, int64_t H, int64_t N, int64_t d, int in_dtype, int out_dtype, unsigned int flags,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (flags & ~LA_FLAG_EXACT) return LA_ERR_INVALID;
   if (!q || !k || !v || !decay || !dout || !dq || !dk || !dv) return LA_ERR_INVALID;
   if (B < 1 || H < 1 || N < 1 || d < 1) return LA_ERR_INVALID;
   if ((in_dtype != LA_DTYPE_BF16 && in_dtype != LA_DTYPE_F32) ||
@@ -317,7 +321,7 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
   a.tbl = (float*)ws;
   a.tbl_stride = (int)tbl_stride_for(64);
   a.states = (float*)((char*)ws + tbl_bytes);
-  a.warm_start = a.in_dtype == la::kBF16;
+  a.warm_start = a.in_dtype == la::kBF16 && !(flags & LA_FLAG_EXACT);
   a.slots = nullptr;
   a.num_slots = 0;
   a.evt_begin = nullptr;

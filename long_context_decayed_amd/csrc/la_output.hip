@@ -326,7 +326,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
                                                               float* __restrict__ states,
                                                               const float* __restrict__ kv_in, int H, int N, int L,
                                                               int nc, int tbl_stride, const int* __restrict__ slots,
-                                                              int64_t num_slots) {
+                                                              int64_t num_slots, int warm) {
   typedef Mfma<bf16> M;
   typedef M::op_t op_t;
   constexpr int NW = D / 32;
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
   const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
   const int hh = bh % H;
   const int span = carry_span(decay[hh]);
-  const bool decaying = decays_within_chunk(span, L);
+  const bool decaying = warm && decays_within_chunk(span, L);  // warm = 0: every head from its start state
   if (decaying != (MODE == kWarmStart)) return;
   const int t_begin = c * L;
   const int t_end = min(N, t_begin + L);
@@ -722,11 +722,13 @@ static void launch_fast(const PrefillArgs& a, hipStream_t st) {
   if (a.rev)
     hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, true>), dim3(grid), dim3(D * 2), 0, st, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, a.decay, (const float*)a.tbl, a.states,
-                       a.kv_in, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots, a.num_slots);
+                       a.kv_in, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots, a.num_slots,
+                       a.warm_start ? 1 : 0);
   else
     hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, false>), dim3(grid), dim3(D * 2), 0, st, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, a.decay, (const float*)a.tbl, a.states,
-                       a.kv_in, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots, a.num_slots);
+                       a.kv_in, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots, a.num_slots,
+                       a.warm_start ? 1 : 0);
 }
 
 template <typename TIn, typename TOut, int D, int BLK>

@@ -54,9 +54,9 @@ def test_library_is_gfx950_only(lib):
 
 
 def _fwd(lib, q=FAKE[0], k=FAKE[1], v=FAKE[2], decay=FAKE[3], out=FAKE[4], kv_in=None, kv_out=None,
-         B=1, H=2, N=128, d=64, block=64, ind=0, outd=0, chunk=0, ws=None, wsb=0):
+         B=1, H=2, N=128, d=64, block=64, ind=0, outd=0, chunk=0, ws=None, wsb=0, flags=0):
     return lib.lightning_attn_fwd_ex(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, ind, outd, chunk,
-                                     ws, wsb, None, None, None)
+                                     flags, ws, wsb, None, None, None)
 
 
 def test_null_pointers_rejected(lib):
@@ -146,9 +146,14 @@ def test_decode_slots_validation(lib):
     assert f(*ok[:5], FAKE[6], FAKE[6], 1, 1, 128, 4, None) == LA_ERR_INVALID   # slots inside the pool
 
 
+def test_unknown_flags_rejected(lib):
+    assert _fwd(lib, flags=2) == LA_ERR_INVALID
+    assert _fwd(lib, flags=0x80000000) == LA_ERR_INVALID
+
+
 def test_fwd_slots_validation(lib):
     f = lib.lightning_attn_fwd_slots
-    base = [FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], FAKE[5], FAKE[6], 1, 1, 128, 64, 4, 64, 0, 0, None]
+    base = [FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], FAKE[5], FAKE[6], 1, 1, 128, 64, 4, 64, 0, 0, 0, None]
     assert f(*base[:5], None, *base[6:]) == LA_ERR_INVALID          # no pool
     assert f(*base[:6], None, *base[7:]) == LA_ERR_INVALID          # no slot table
     a = list(base); a[11] = 0
@@ -161,6 +166,8 @@ def test_fwd_slots_validation(lib):
     assert f(*a) == LA_ERR_INVALID                                  # pool overlaps q
     a = list(base); a[6] = FAKE[5]
     assert f(*a) == LA_ERR_INVALID                                  # slot table inside the pool
+    a = list(base); a[15] = 4
+    assert f(*a) == LA_ERR_INVALID                                  # unknown flag
 
 
 def test_fused_validation(lib):
@@ -200,19 +207,20 @@ def test_bwd_validation(lib):
     dq, dk, dv = FAKE[5], FAKE[6], FAKE[7]
     args = lambda **kw: [kw.get("q", q), k, v, dec, kw.get("g", g), None, None, kw.get("dq", dq), dk, dv, None,
                          kw.get("B", 1), 1, kw.get("N", 128), kw.get("d", 128), kw.get("idt", 0), kw.get("od", 0),
-                         None, 0, None]
+                         kw.get("fl", 0), None, 0, None]
     assert f(*args(q=None)) == LA_ERR_INVALID
     assert f(*args(g=None)) == LA_ERR_INVALID
     assert f(*args(B=0)) == LA_ERR_INVALID
     assert f(*args(od=7)) == LA_ERR_INVALID
     assert f(*args(idt=7)) == LA_ERR_INVALID
     assert f(*args(idt=1, od=0)) == LA_ERR_UNSUPPORTED           # fp32 in needs fp32 out
+    assert f(*args(fl=2)) == LA_ERR_INVALID                        # unknown flag
     assert f(*args(d=96)) == LA_ERR_UNSUPPORTED
     assert f(*args(dq=FAKE[0])) == LA_ERR_INVALID            # dq overlaps q
     assert f(*args(dq=ctypes.c_void_p(FAKE[5].value + 8))) == LA_ERR_INVALID   # misaligned
     small = (ctypes.c_uint8 * 16)()
     a = args()
-    a[17], a[18] = FAKE[5], 16                                 # workspace too small
+    a[18], a[19] = FAKE[5], 16                                 # workspace too small
     assert f(*a) == LA_ERR_WORKSPACE
     need = lib.lightning_attn_bwd_workspace_bytes(1, 64, 1 << 20, 128)
     fwd = lib.lightning_attn_fwd_workspace_bytes(1, 64, 1 << 20, 128, 64, 0)

@@ -157,3 +157,21 @@ def test_bwd_fp32_mixed_decays_with_states(dev, d):
             tol.assert_fp32(got_h[:, h], ref[:, h], "%s head %d" % (name, h))
     for h in range(H):
         tol.assert_fp32(host(ds0)[:, h], rs[:, h], "dS0 head %d" % h)
+
+
+def test_bwd_exact_flag(dev):
+    say("bwd exact flag, mixed decays B1 H8 N2100 d64 with states")
+    B, H, N, d = 1, 8, 2100, 64
+    q, k, v = qkv_device(B, H, N, d, seed=160, device=dev)
+    g = qkv_device(B, H, N, d, seed=161, device=dev)[0]
+    s0 = state_device(B, H, d, seed=160, device=dev)
+    dsn = state_device(B, H, d, seed=161, device=dev)
+    dq, dk, dv, ds0 = la.bwd(q, k, v, torch.from_numpy(MIXED_LAMS).to(dev), g, kv_in=s0, dkv_out=dsn,
+                             out_dtype=torch.float32, dkv_in=True, exact=True)
+    torch.cuda.synchronize()
+    rq, rk, rv, rs = _grad_oracle(q, k, v, MIXED_LAMS, g, s0, dsn)
+    _check_heads(dq, rq, "dQ", H)
+    _check_heads(dk, rk, "dK", H)
+    _check_heads(dv, rv, "dV", H)
+    for h in range(H):
+        tol.assert_state(host(ds0)[:, h], rs[:, h], "dS0 head %d" % h)

@@ -336,3 +336,46 @@ def test_bf16_classification_boundary(dev):
     for h in range(4):
         tol.assert_bf16_f32out(o_h[:, h], o_ref[:, h], "O head %d (lam %.7f)" % (h, lams[h]))
         tol.assert_state(kv_h[:, h], s_ref[:, h], "kv_out head %d" % h)
+
+
+# --- the exact path on demand --------------------------------------------------
+
+def test_exact_flag_with_a_spike_before_the_warm_up_window(dev):
+    # lam = 0.7 at chunk 256 takes the warm start (carry span 64): chunk 1
+    # starts from zero at token 192.  A token at 190 whose k and v are 1e5
+    # times the others still weighs lam^66 * 1e10 ~ 0.6 of a typical term on
+    # the first rows of chunk 1: the warm start leaves it out (it bounds the
+    # omission by 2^-30 of that term, not of the output), the exact path not.
+    say("exact flag: spike before the warm-up window, B1 H1 N512 d128 chunk 256")
+    q, k, v = qkv_device(1, 1, 512, 128, seed=140, device=dev)
+    k[:, :, 190] *= 1e5
+    v[:, :, 190] *= 1e5
+    lam = np.array([0.7], dtype=np.float32)
+    o_ref, _ = oracle(host(q), host(k), host(v), lam)
+    rows = slice(256, 320)
+    r = tol.rms(o_ref[:, :, rows])
+    warm = la.fwd(q, k, v, torch.from_numpy(lam).to(dev), block=64, chunk=256, out_dtype=torch.float32)
+    exact = la.fwd(q, k, v, torch.from_numpy(lam).to(dev), block=64, chunk=256, out_dtype=torch.float32, exact=True)
+    torch.cuda.synchronize()
+    e_exact = tol.assert_bf16_f32out(host(exact)[:, :, rows], o_ref[:, :, rows], "exact, rows 256-319")
+    e_warm = tol.bf16_rms_error(host(warm)[:, :, rows], o_ref[:, :, rows], r)
+    print("rows 256-319: exact %.3e, warm start %.3e (max|err| / RMS of those rows)" % (e_exact, e_warm))
+    assert e_warm > 0.1, "the spike should be visible to the exact path only"
+    # away from the spike's reach both agree with the oracle
+    far = slice(400, 512)
+    for o in (warm, exact):
+        tol.assert_bf16_f32out(host(o)[:, :, far], o_ref[:, :, far], "rows 400-511")
+
+
+def test_exact_flag_matches_oracle_on_mixed_decays(dev):
+    say("exact flag: mixed decays B2 H8 N3037 d128 chunk 1024, with state")
+    q, k, v = qkv_device(2, 8, 3037, 128, seed=150, device=dev)
+    s0 = state_device(2, 8, 128, seed=150, device=dev)
+    kv = torch.empty_like(s0)
+    o = la.fwd(q, k, v, torch.from_numpy(MIXED_LAMS).to(dev), kv_in=s0, kv_out=kv, block=64, chunk=1024,
+               out_dtype=torch.float32, exact=True)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle(host(q), host(k), host(v), MIXED_LAMS, host(s0).astype(np.float64))
+    for h in range(8):
+        tol.assert_bf16_f32out(host(o)[:, h], o_ref[:, h], "O head %d" % h)
+        tol.assert_state(host(kv)[:, h], s_ref[:, h], "kv_out head %d" % h)
