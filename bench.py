@@ -19,6 +19,8 @@ ONE JSON line:
                  stream, against 8 TB/s
   cpu_baseline   the fp64 oracle (plain-C recurrence) on a bounded sample of
                  the same workload, on this host's cores
+  exact_path     the same step with every head on the exact chunked path
+                 (LA_FLAG_EXACT: no warm start)
   backward       the backward pass of the same layer (dq, dk, dv from dout)
   epilogue_prologue  per-head RMSNorm + sigmoid gate of the output and SiLU
                  on one input, as their own passes over the same layer
@@ -164,6 +166,11 @@ def bench_prefill(args, dev):
         step_hbm_frac=BYTES_PER_HT * ht / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         mfma_alg_frac=FLOP_PER_HT * ht / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
     )
+    if args.exact:
+        # the same step with every head on the exact chunked path (LA_FLAG_EXACT)
+        ms_exact = _time_ms(lambda: la.fwd(q, k, v, lam, kv_out=kv_out, block=block, out=out, workspace=ws,
+                                           exact=True), max(1, args.steps // 2))
+        res["exact"] = dict(ms_per_step=ms_exact, tokens_per_s=B * N / (ms_exact * 1e-3))
     del ws
     if args.fused:
         res["epilogue_prologue"] = bench_norm_gate_silu(args, dev, out)
@@ -339,6 +346,8 @@ def main():
     ap.add_argument("--no-decode", dest="decode", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--no-backward", dest="backward", action="store_false")
+    ap.add_argument("--no-exact", dest="exact", action="store_false",
+                    help="skip the step timed with every head on the exact chunked path")
     ap.add_argument("--no-fused", dest="fused", action="store_false",
                     help="skip the SiLU / RMSNorm / gate measurements")
     ap.add_argument("--cpu-tokens", type=int, default=1 << 20)
@@ -390,6 +399,7 @@ def main():
         "warm_start_heads": prefill["warm_start_heads"],
         "step_hbm_frac": prefill["step_hbm_frac"],
         "mfma_alg_frac": prefill["mfma_alg_frac"],
+        "exact_path": prefill.get("exact"),
         "backward": prefill.get("backward"),
         "epilogue_prologue": prefill.get("epilogue_prologue"),
         "cpu_baseline": cpu,
