@@ -293,8 +293,9 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 //     the next ones are requested at the barrier that ends phase 1 and waited
 //     for at the one that ends phase 2; V and the update copy of K are only
 //     read in phase 2 (P V and the state update), so after that barrier the
-//     next V is requested, ahead of this sub-tile's output stores, and the
-//     next K copied over; both are waited for at the end of the next phase 1.
+//     next V is requested, ahead of this sub-tile's output stores, and waited
+//     for at the end of the next phase 1, during which the K copy is made
+//     (with 4 waves by the one that computes no score tile).
 // Two workgroups per CU (80 KiB of LDS each).
 //
 // Two modes, by where the chunk's start state comes from:
@@ -544,6 +545,26 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
         }
       }
     }
+    // This sub-tile's K^T copy from its score copy (in LDS since the last
+    // barrier; the previous K^T is no longer read): with 4 waves by the one
+    // that has no score tile, in its share of phase 1, else by all waves.
+    if (t0 != t_begin) {
+      constexpr int CW = (NW == 4) ? 1 : NW;            // copying waves
+      constexpr int NCH = kSub * D * 2 / 16 / (CW * 64);  // 16-byte chunks per lane
+      if (NW != 4 || w == NW - 1) {
+        const int ct = (NW == 4) ? lane : tid;
+        const uint4* ksrc = reinterpret_cast<const uint4*>(Ks);
+        uint4* kdst = reinterpret_cast<uint4*>(Kt);
+#pragma unroll
+        for (int b = 0; b < NCH; b += 4) {
+          uint4 tmp[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tmp[i] = ksrc[ct + CW * 64 * (b + i)];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kdst[ct + CW * 64 * (b + i)] = tmp[i];
+        }
+      }
+    }
     // Mask, decay and publish the score tiles as hi + lo operands.
 #pragma unroll
     for (int m = 0; m < MAXT; ++m) {
@@ -616,15 +637,6 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
     sync_lds_after_vmem<0>();
     if (more) {
       dma_tile<D, NW, RS>(vb + off_next, Vs, nv_next, w, lane);
-      // The next sub-tile's K^T copy from its score copy, already in LDS.
-      constexpr int NCH = kSub * D * 2 / 16 / (NW * 64);  // 16-byte chunks per thread
-      const uint4* ksrc = reinterpret_cast<const uint4*>(Ks);
-      uint4* kdst = reinterpret_cast<uint4*>(Kt);
-      uint4 tmp[NCH];
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) tmp[i] = ksrc[tid + NW * 64 * i];
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) kdst[tid + NW * 64 * i] = tmp[i];
     }
 
     // Output rows.  Lane (h, l) holds token t0 + 32rt + l, columns 32w + 8jq
