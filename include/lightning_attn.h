@@ -31,8 +31,8 @@
  *    synchronisation.  A kernel fault surfaces at the caller's next sync.
  *  - The caller owns every buffer.  The library never frees or retains
  *    caller memory.
- *  - kv_in may equal kv_out (in-place state update).  out must not overlap
- *    q, k, v, kv_in or kv_out.
+ *  - kv_in may equal kv_out (in-place state update); otherwise the two must
+ *    not overlap.  out must not overlap q, k, v, kv_in or kv_out.
  *  - Arguments are validated before any HIP call, so validation errors are
  *    returned without touching the device.  Nothing is thrown across the ABI.
  *
@@ -51,7 +51,8 @@ extern "C" {
 
 #define LA_OK 0
 #define LA_ERR_INVALID 1      /* NULL pointer, size <= 0, bad block/chunk, misaligned pointer, overlap */
-#define LA_ERR_UNSUPPORTED 2  /* d not in {64, 128}; dtype/block combination not built; N*d >= 2^31 */
+#define LA_ERR_UNSUPPORTED 2  /* d not in {64, 128}; dtype/block combination not built; N > 2^24;
+                                 B, H, B*H or num_slots*H >= 2^31; B*H*N > 2^48 */
 #define LA_ERR_HIP 3          /* a HIP runtime call or kernel launch failed */
 #define LA_ERR_NOMEM 4        /* the library's own workspace allocation failed */
 #define LA_ERR_WORKSPACE 5    /* caller workspace too small */
@@ -260,7 +261,8 @@ int lightning_attn_norm_gate(const void* o, int o_dtype, const void* gate, const
                              int64_t B, int64_t H, int64_t N, int64_t d, void* stream);
 
 /* Prefill prologue as its own pass: x <- SiLU(x) over n bf16 elements in place
- * (apply to Q, K and V before lightning_attn_fwd). */
+ * (apply to Q, K and V before lightning_attn_fwd).  0 <= n <= 2^44; n = 0 is
+ * a no-op. */
 int lightning_attn_silu(void* x, int64_t n, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */

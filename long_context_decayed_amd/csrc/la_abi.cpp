@@ -12,6 +12,15 @@ namespace {
 
 constexpr int64_t kMaxTokens = int64_t(1) << 24;  // keeps N * d < 2^31 for per-head offsets
 constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxHeadTokens = int64_t(1) << 48;  // B * H * N: byte counts stay far inside int64
+
+// Sizes the byte arithmetic below can hold: B, H and the row count (B * H,
+// or num_slots * H for a state pool) below 2^31 each, B * H * N <= 2^48.
+bool dims_fit(int64_t B, int64_t H, int64_t N, int64_t pool_rows = 0) {
+  if (B > kMaxGrid || H > kMaxGrid || N > kMaxTokens || pool_rows > kMaxGrid) return false;
+  if (B * H > kMaxGrid || pool_rows * H > kMaxGrid) return false;
+  return B * H * N <= kMaxHeadTokens;
+}
 
 // dtype / head-dim / block combinations the kernels are built for.  fp32
 // tiles are twice as large, so fp32 with d = 128 is limited to block 64 by
@@ -30,6 +39,12 @@ bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
   if (!a || !b) return false;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
   return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+// An input and an output state tensor are either the same tensor (in place:
+// every (b, h) state is read before it is written) or apart.
+bool states_apart_or_same(const void* in, const void* out, int64_t bytes) {
+  return in == out || !overlap(in, bytes, out, bytes);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -92,7 +107,7 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* d
     return LA_ERR_INVALID;
   if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
   if (!prefill_supported(in_dtype, out_dtype, d, block)) return LA_ERR_UNSUPPORTED;
-  if (N > kMaxTokens) return LA_ERR_UNSUPPORTED;
+  if (!dims_fit(B, H, N)) return LA_ERR_UNSUPPORTED;
   int rc = resolve_chunk(B, H, N, block, chunk, L);
   if (rc != LA_OK) return rc;
   if (B * H > kMaxGrid || B * H * ceil_div(N, *L) > kMaxGrid) return LA_ERR_UNSUPPORTED;
@@ -101,7 +116,7 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* d
   const int64_t st_bytes = B * H * d * d * 4;
   if (overlap(out, out_bytes, q, in_bytes) || overlap(out, out_bytes, k, in_bytes) ||
       overlap(out, out_bytes, v, in_bytes) || overlap(out, out_bytes, kv_in, st_bytes) ||
-      overlap(out, out_bytes, kv_out, st_bytes))
+      overlap(out, out_bytes, kv_out, st_bytes) || !states_apart_or_same(kv_in, kv_out, st_bytes))
     return LA_ERR_INVALID;
   return LA_OK;
 }
@@ -145,7 +160,7 @@ int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const 
   if (flags & ~LA_FLAG_EXACT) return LA_ERR_INVALID;
   if (!states || !slots || num_slots < 1) return LA_ERR_INVALID;
   if (!aligned(states, 16) || !aligned(slots, 4)) return LA_ERR_INVALID;
-  if (num_slots > kMaxGrid) return LA_ERR_UNSUPPORTED;
+  if (!dims_fit(B, H, N, num_slots)) return LA_ERR_UNSUPPORTED;
   // validate the token tensors alone, then the pool against them
   int64_t L = 0;
   int rc = validate_prefill(q, k, v, decay, out, nullptr, nullptr, B, H, N, d, block, in_dtype, out_dtype, 0, &L);
@@ -264,7 +279,7 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
   if (!aligned(decay, 4)) return LA_ERR_INVALID;
   if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
   if (!prefill_supported(in_dtype, out_dtype, d, 64)) return LA_ERR_UNSUPPORTED;
-  if (N > kMaxTokens) return LA_ERR_UNSUPPORTED;
+  if (!dims_fit(B, H, N)) return LA_ERR_UNSUPPORTED;
   const int64_t L = pick_chunk(B, H, N, 64);
   if (B * H > kMaxGrid || B * H * ceil_div(N, L) > kMaxGrid) return LA_ERR_UNSUPPORTED;
   const int64_t in_bytes = B * H * N * d * (in_dtype == LA_DTYPE_BF16 ? 2 : 4);
@@ -396,11 +411,11 @@ int lightning_attn_decode_step(const void* q, const void* k, const void* v, cons
       !aligned(kv_in, 16) || !aligned(kv_out, 16))
     return LA_ERR_INVALID;
   if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
-  if (B * H > kMaxGrid) return LA_ERR_UNSUPPORTED;
+  if (!dims_fit(B, H, 1)) return LA_ERR_UNSUPPORTED;
   const int64_t vec_bytes = B * H * d * 2, st_bytes = B * H * d * d * 4;
   if (overlap(out, vec_bytes, q, vec_bytes) || overlap(out, vec_bytes, k, vec_bytes) ||
       overlap(out, vec_bytes, v, vec_bytes) || overlap(out, vec_bytes, kv_in, st_bytes) ||
-      overlap(out, vec_bytes, kv_out, st_bytes))
+      overlap(out, vec_bytes, kv_out, st_bytes) || !states_apart_or_same(kv_in, kv_out, st_bytes))
     return LA_ERR_INVALID;
   return from_hip(la::launch_decode(q, k, v, decay, out, kv_in, kv_out, B, H, d, (hipStream_t)stream));
 }
@@ -414,7 +429,7 @@ int lightning_attn_decode_slots(const void* q, const void* k, const void* v, con
       !aligned(states, 16) || !aligned(slots, 4))
     return LA_ERR_INVALID;
   if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
-  if (B * H > kMaxGrid || num_slots > kMaxGrid) return LA_ERR_UNSUPPORTED;
+  if (!dims_fit(B, H, 1, num_slots)) return LA_ERR_UNSUPPORTED;
   const int64_t vec_bytes = B * H * d * 2, pool_bytes = num_slots * H * d * d * 4;
   if (overlap(out, vec_bytes, q, vec_bytes) || overlap(out, vec_bytes, k, vec_bytes) ||
       overlap(out, vec_bytes, v, vec_bytes) || overlap(out, vec_bytes, states, pool_bytes) ||
@@ -436,7 +451,7 @@ int lightning_attn_decode_fused(const void* q, const void* k, const void* v, con
       !aligned(states, 16) || !aligned(slots, 4) || !aligned(gamma, 16) || !aligned(gate, 16))
     return LA_ERR_INVALID;
   if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
-  if (B * H > kMaxGrid || num_slots > kMaxGrid) return LA_ERR_UNSUPPORTED;
+  if (!dims_fit(B, H, 1, num_slots)) return LA_ERR_UNSUPPORTED;
   const int64_t vec_bytes = B * H * d * 2, pool_bytes = num_slots * H * d * d * 4;
   if (overlap(out, vec_bytes, q, vec_bytes) || overlap(out, vec_bytes, k, vec_bytes) ||
       overlap(out, vec_bytes, v, vec_bytes) || overlap(out, vec_bytes, states, pool_bytes) ||
@@ -457,6 +472,7 @@ int lightning_attn_norm_gate(const void* o, int o_dtype, const void* gate, const
   if (!(eps >= 0.0f) || eps > 1.0f) return LA_ERR_INVALID;
   if (!aligned(o, 16) || !aligned(out, 16) || !aligned(gate, 16) || !aligned(gamma, 16)) return LA_ERR_INVALID;
   if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+  if (!dims_fit(B, H, N)) return LA_ERR_UNSUPPORTED;
   const int64_t rows = B * H * N;
   if (rows * (d / 8) / 256 + 1 > kMaxGrid) return LA_ERR_UNSUPPORTED;
   const int64_t o_bytes = rows * d * (o_dtype == LA_DTYPE_BF16 ? 2 : 4), y_bytes = rows * d * 2;
@@ -470,6 +486,7 @@ int lightning_attn_norm_gate(const void* o, int o_dtype, const void* gate, const
 int lightning_attn_silu(void* x, int64_t n, void* stream) {
   if (n < 0 || (n > 0 && !x)) return LA_ERR_INVALID;
   if (!aligned(x, 16)) return LA_ERR_INVALID;
+  if (n > (int64_t(1) << 44)) return LA_ERR_UNSUPPORTED;  // the grid of 8192-element workgroups fits 31 bits
   if (n == 0) return LA_OK;
   return from_hip(la::launch_silu(x, n, (hipStream_t)stream));
 }

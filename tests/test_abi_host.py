@@ -240,3 +240,46 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(la, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         la.load()
+
+
+def test_sizes_beyond_the_byte_arithmetic_rejected(lib):
+    """B, H and the row counts stay below 2^31 and B*H*N below 2^48, so that no
+    byte count overflows int64 (the pointers are fake; nothing is launched)."""
+    big = 1 << 40
+    for kw in (dict(B=big), dict(H=big), dict(B=1 << 16, H=1 << 16), dict(B=1 << 20, H=1 << 10, N=1 << 24)):
+        assert _fwd(lib, **kw) == LA_ERR_UNSUPPORTED, kw
+    # B*H*N = 2^48 exactly passes validation (pointers 2^57 apart, one chunk so the
+    # grid fits) and stops at the too-small workspace, before any HIP call
+    far = [ctypes.c_void_p((i + 1) << 57) for i in range(6)]
+    assert _fwd(lib, *far[:5], B=1 << 14, H=1 << 10, N=1 << 24, chunk=1 << 24, ws=far[5], wsb=1) == LA_ERR_WORKSPACE
+    dec = lib.lightning_attn_decode_step
+    assert dec(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], None, None, big, big, 64, None) == LA_ERR_UNSUPPORTED
+    slots = lib.lightning_attn_decode_slots
+    assert slots(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], FAKE[5], FAKE[6], 1, 1 << 16, 64, 1 << 16,
+                 None) == LA_ERR_UNSUPPORTED
+    fs = lib.lightning_attn_fwd_slots
+    assert fs(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], FAKE[5], FAKE[6], 1, 1 << 16, 64, 64, 1 << 16, 64, 0, 0,
+              0, None) == LA_ERR_UNSUPPORTED
+    bwd = lib.lightning_attn_bwd
+    assert bwd(*FAKE[:5], None, None, FAKE[5], FAKE[6], FAKE[7], None, big, 2, 64, 64, 0, 0, 0, None, 0,
+               None) == LA_ERR_UNSUPPORTED
+    ng = lib.lightning_attn_norm_gate
+    assert ng(FAKE[0], 0, None, None, ctypes.c_float(1e-5), FAKE[1], big, big, 64, 64, None) == LA_ERR_UNSUPPORTED
+    assert lib.lightning_attn_silu(FAKE[0], (1 << 44) + 8, None) == LA_ERR_UNSUPPORTED
+
+
+def test_partially_overlapping_states_rejected(lib):
+    """kv_in and kv_out are the same tensor or apart: a shifted alias would let
+    one (b, h) overwrite another's state before it is read."""
+    st = 2 * 64 * 64 * 4  # B=1, H=2, d=64
+    base = FAKE[5].value
+    same = dict(kv_in=ctypes.c_void_p(base), kv_out=ctypes.c_void_p(base))
+    shifted = dict(kv_in=ctypes.c_void_p(base), kv_out=ctypes.c_void_p(base + 64 * 64 * 4))
+    apart = dict(kv_in=ctypes.c_void_p(base), kv_out=ctypes.c_void_p(base + st))
+    assert _fwd(lib, **shifted) == LA_ERR_INVALID
+    # validation passes for the other two; they then stop at the too-small workspace
+    for kw in (same, apart):
+        assert _fwd(lib, ws=FAKE[6], wsb=1, **kw) == LA_ERR_WORKSPACE
+    dec = lib.lightning_attn_decode_step
+    assert dec(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], shifted["kv_in"], shifted["kv_out"], 1, 2, 64,
+               None) == LA_ERR_INVALID
