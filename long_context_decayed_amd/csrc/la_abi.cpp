@@ -257,10 +257,24 @@ int lightning_attn_fwd_bf16_f32out(const void* q, const void* k, const void* v, 
                                LA_DTYPE_F32, 0, 0u, nullptr, 0, nullptr, nullptr, stream);
 }
 
+// Backward workspace: the forward layout (decay table, chunk states of the
+// first problem), chunk states of the second (the dK and dV passes run side by
+// side), then the transposed S0 and dS_N.
+size_t bwd_workspace_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t L, size_t* states2_off,
+                            size_t* s0t_off, size_t* dsnt_off) {
+  size_t tbl_bytes = 0;
+  const size_t fwd = align256(workspace_layout(B, H, N, d, 64, L, &tbl_bytes));
+  const size_t states = align256(fwd - tbl_bytes);
+  const size_t st = align256((size_t)(B * H * d * d) * sizeof(float));
+  if (states2_off) *states2_off = fwd;
+  if (s0t_off) *s0t_off = fwd + states;
+  if (dsnt_off) *dsnt_off = fwd + states + st;
+  return fwd + states + 2 * st;
+}
+
 size_t lightning_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
-  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
-  const int64_t L = pick_chunk(B, H, N, 64);
-  return align256(workspace_layout(B, H, N, d, 64, L, nullptr)) + 2 * align256((size_t)(B * H * d * d) * sizeof(float));
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128) || !dims_fit(B, H, N)) return 0;
+  return bwd_workspace_layout(B, H, N, d, pick_chunk(B, H, N, 64), nullptr, nullptr, nullptr);
 }
 
 int lightning_attn_bwd(const void* q, const void* k, const void* v, const float* decay, const void* dout,
@@ -304,8 +318,8 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
     if (overlap(dkv_in, st_bytes, kv_in, st_bytes) || overlap(dkv_in, st_bytes, dkv_out, st_bytes))
       return LA_ERR_INVALID;
   }
-  const size_t fwd_need = align256(workspace_layout(B, H, N, d, 64, L, nullptr));
-  const size_t need = fwd_need + 2 * align256((size_t)st_bytes);
+  size_t states2_off = 0, s0t_off = 0, dsnt_off = 0;
+  const size_t need = bwd_workspace_layout(B, H, N, d, L, &states2_off, &s0t_off, &dsnt_off);
   if (workspace) {
     if (workspace_bytes < need) return LA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return LA_ERR_INVALID;
@@ -319,8 +333,8 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
   }
   size_t tbl_bytes = 0;
   workspace_layout(B, H, N, d, 64, L, &tbl_bytes);
-  float* s0t = (float*)((char*)ws + fwd_need);
-  float* dsnt = (float*)((char*)ws + fwd_need + align256((size_t)st_bytes));
+  float* s0t = (float*)((char*)ws + s0t_off);
+  float* dsnt = (float*)((char*)ws + dsnt_off);
 
   la::PrefillArgs a;
   a.decay = decay;
@@ -358,29 +372,38 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
     e = run_passes(a, st);
   }
   // dK: dk_t = v_t G_t^T, G^T run last token first over (V, dO, Q) from dSN^T.
-  if (e == hipSuccess) {
-    a.q = v;
-    a.k = dout;
-    a.v = q;
-    a.out = dk;
-    a.kv_in = dkv_out ? dsnt : nullptr;
-    a.kv_out = nullptr;
-    a.rev = true;
-    a.scale_kv_out = false;
-    e = run_passes(a, st);
-  }
+  la::PrefillArgs ak = a;
+  ak.q = v;
+  ak.k = dout;
+  ak.v = q;
+  ak.out = dk;
+  ak.kv_in = dkv_out ? dsnt : nullptr;
+  ak.kv_out = nullptr;
+  ak.rev = true;
+  ak.scale_kv_out = false;
   // dV: dv_t = k_t G_t, G run last token first over (K, Q, dO) from dSN; its
   // final state is G_0, and dS0 = lam G_0.
-  if (e == hipSuccess) {
-    a.q = k;
-    a.k = q;
-    a.v = dout;
-    a.out = dv;
-    a.kv_in = dkv_out;
-    a.kv_out = dkv_in;
-    a.rev = true;
-    a.scale_kv_out = true;
-    e = run_passes(a, st);
+  la::PrefillArgs av = ak;
+  av.q = k;
+  av.k = q;
+  av.v = dout;
+  av.out = dv;
+  av.kv_in = dkv_out;
+  av.kv_out = dkv_in;
+  av.scale_kv_out = true;
+  av.states = (float*)((char*)ws + states2_off);
+  if (a.in_dtype == la::kBF16) {
+    // Both read Q and dO: their workgroups for one chunk run side by side, so
+    // those tiles come from HBM about once.
+    if (e == hipSuccess) e = la::launch_aggregate_pass(ak, st);
+    if (e == hipSuccess) e = la::launch_aggregate_pass(av, st);
+    if (e == hipSuccess && a.warm_start) e = la::launch_warm_start_pair(ak, av, st);
+    if (e == hipSuccess) e = la::launch_scan_pass(ak, st);
+    if (e == hipSuccess) e = la::launch_scan_pass(av, st);
+    if (e == hipSuccess) e = la::launch_output_pair(ak, av, st);
+  } else {
+    if (e == hipSuccess) e = run_passes(ak, st);
+    if (e == hipSuccess) e = run_passes(av, st);
   }
   if (!workspace) {
     hipError_t f = hipFreeAsync(ws, st);

@@ -44,6 +44,14 @@ hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st);
 // heads that do not decay within their chunk only): la_output.hip.
 hipError_t launch_output_pass(const PrefillArgs& a, hipStream_t st);
 
+// Two problems of one shape (bf16 inputs, block 64) in one grid, the two
+// workgroups of each (bh, chunk) side by side, so that tensors both read
+// are fetched from HBM about once: the warm-start pass and the output pass
+// (pass C) of a and b.  Each problem has its own tensors and chunk states;
+// flags, decays and the decay table are a's: la_output.hip.
+hipError_t launch_warm_start_pair(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st);
+hipError_t launch_output_pair(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st);
+
 // dst[bh] = src[bh]^T for BH fp32 d x d states: la_state.hip.
 hipError_t launch_transpose_states(const float* src, float* dst, int64_t BH, int64_t d, hipStream_t st);
 

@@ -40,6 +40,12 @@
 
 namespace la {
 
+// log2 of the distance between the two workgroups of a pair.  Workgroups
+// are dealt to the 8 XCDs in turn, so i and i + 8 land on one XCD and share
+// its L2.  (Measured on the 1,048,576-token, 64-head backward: 43.2 ms at
+// distance 8, 44.2 ms at distance 1, 44.3 ms unpaired.)
+constexpr int kPairShift = 3;
+
 // ---------------------------------------------------------------------------
 // Pass C.  One workgroup per (bh, chunk); D/32 waves.  Wave w owns columns
 // [32w, 32w + 32) of the fp32 state S (NRT accumulator tiles) and of the
@@ -317,17 +323,30 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 // as the gradient of the final state does in the adjoint recurrence.  Only
 // the first sub-tile of chunk 0 differs: its rows take lam^p instead of
 // lam^(p+1) and it hands the state on decayed by lam^(n-1) instead of lam^n.
+//
+// Paired launch (pair_shift >= 0): two problems of one shape, with their own
+// tensors and chunk states, share a grid; workgroup i serves problem
+// (i >> pair_shift) & 1, so the two workgroups of one (bh, chunk) start
+// 2^pair_shift apart and read the tensors the problems share at about the
+// same time, the second often from L2.  The backward's dK and dV passes run
+// this way: both read Q and dO.
 enum { kWarmStart = 0, kFromStart = 1 };
 
+struct Operands {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  void* o;
+  float* states;       // chunk states of this problem
+  const float* kv_in;  // initial states, or null
+};
+
 template <typename TOut, int D, int MODE, bool REV>
-__global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                              const bf16* __restrict__ v, TOut* __restrict__ o,
+__global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Operands p1,
                                                               const float* __restrict__ decay,
-                                                              const float* __restrict__ tbl_all,
-                                                              float* __restrict__ states,
-                                                              const float* __restrict__ kv_in, int H, int N, int L,
+                                                              const float* __restrict__ tbl_all, int H, int N, int L,
                                                               int nc, int tbl_stride, const int* __restrict__ slots,
-                                                              int64_t num_slots, int warm) {
+                                                              int64_t num_slots, int warm, int nblk, int pair_shift) {
   typedef Mfma<bf16> M;
   typedef M::op_t op_t;
   constexpr int NW = D / 32;
@@ -345,7 +364,19 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
+  int blk = blockIdx.x, pi = 0;
+  if (pair_shift >= 0) {
+    pi = (blk >> pair_shift) & 1;
+    blk = ((blk >> (pair_shift + 1)) << pair_shift) | (blk & ((1 << pair_shift) - 1));
+    if (blk >= nblk) return;  // padding of the last group
+  }
+  const bf16* __restrict__ q = pi ? p1.q : p0.q;
+  const bf16* __restrict__ k = pi ? p1.k : p0.k;
+  const bf16* __restrict__ v = pi ? p1.v : p0.v;
+  TOut* __restrict__ o = static_cast<TOut*>(pi ? p1.o : p0.o);
+  float* __restrict__ states = pi ? p1.states : p0.states;
+  const float* __restrict__ kv_in = pi ? p1.kv_in : p0.kv_in;
+  const int bh = blk / nc, c = blk - (blk / nc) * nc;
   const int hh = bh % H;
   const int span = carry_span(decay[hh]);
   const bool decaying = warm && decays_within_chunk(span, L);  // warm = 0: every head from its start state
@@ -728,19 +759,27 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(const bf16* __rest
 
 // The events bracket the kernel that writes every output row: the
 // warm-start pass when there is one (bf16 inputs, block 64), else this one.
+static Operands operands_of(const PrefillArgs& a) {
+  return Operands{(const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.out, a.states, a.kv_in};
+}
+
+// One problem (b == nullptr), or two of one shape in one grid (the pair's
+// flags, decays and table are a's).
 template <typename TOut, int D, int MODE>
-static void launch_fast(const PrefillArgs& a, hipStream_t st) {
-  const unsigned grid = (unsigned)(a.B * a.H * a.nc);
+static void launch_fast(const PrefillArgs& a, hipStream_t st, const PrefillArgs* b = nullptr) {
+  const int nblk = (int)(a.B * a.H * a.nc);
+  const int shift = b ? kPairShift : -1;
+  const int64_t half = int64_t(1) << kPairShift;  // workgroups of one problem per group of the pair
+  const unsigned grid = b ? (unsigned)((nblk + half - 1) / half * 2 * half) : (unsigned)nblk;
+  const Operands p0 = operands_of(a), p1 = b ? operands_of(*b) : p0;
   if (a.rev)
-    hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, true>), dim3(grid), dim3(D * 2), 0, st, (const bf16*)a.q,
-                       (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, a.decay, (const float*)a.tbl, a.states,
-                       a.kv_in, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots, a.num_slots,
-                       a.warm_start ? 1 : 0);
+    hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, true>), dim3(grid), dim3(D * 2), 0, st, p0, p1, a.decay,
+                       (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots, a.num_slots,
+                       a.warm_start ? 1 : 0, nblk, shift);
   else
-    hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, false>), dim3(grid), dim3(D * 2), 0, st, (const bf16*)a.q,
-                       (const bf16*)a.k, (const bf16*)a.v, (TOut*)a.out, a.decay, (const float*)a.tbl, a.states,
-                       a.kv_in, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots, a.num_slots,
-                       a.warm_start ? 1 : 0);
+    hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, false>), dim3(grid), dim3(D * 2), 0, st, p0, p1, a.decay,
+                       (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots, a.num_slots,
+                       a.warm_start ? 1 : 0, nblk, shift);
 }
 
 template <typename TIn, typename TOut, int D, int BLK>
@@ -801,6 +840,31 @@ static hipError_t launch_output_d(const PrefillArgs& a, hipStream_t st) {
     case 256: return launch_output_t<TIn, TOut, D, 256>(a, st);
   }
   return hipErrorInvalidValue;
+}
+
+template <int MODE>
+static hipError_t launch_pair_mode(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st) {
+  if (a.in_dtype != kBF16 || b.in_dtype != kBF16 || a.block != 64 || b.block != 64 || a.B != b.B || a.H != b.H ||
+      a.N != b.N || a.nc != b.nc || a.d != b.d || a.out_dtype != b.out_dtype || a.rev != b.rev ||
+      a.warm_start != b.warm_start)
+    return hipErrorInvalidValue;
+  if (MODE == kWarmStart && !a.warm_start) return hipErrorInvalidValue;
+  if (a.out_dtype == kBF16) {
+    if (a.d == 128) launch_fast<bf16, 128, MODE>(a, st, &b);
+    else launch_fast<bf16, 64, MODE>(a, st, &b);
+  } else {
+    if (a.d == 128) launch_fast<float, 128, MODE>(a, st, &b);
+    else launch_fast<float, 64, MODE>(a, st, &b);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_warm_start_pair(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st) {
+  return launch_pair_mode<kWarmStart>(a, b, st);
+}
+
+hipError_t launch_output_pair(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st) {
+  return launch_pair_mode<kFromStart>(a, b, st);
 }
 
 hipError_t launch_output_pass(const PrefillArgs& a, hipStream_t st) {

@@ -224,7 +224,8 @@ def test_bwd_validation(lib):
     assert f(*a) == LA_ERR_WORKSPACE
     need = lib.lightning_attn_bwd_workspace_bytes(1, 64, 1 << 20, 128)
     fwd = lib.lightning_attn_fwd_workspace_bytes(1, 64, 1 << 20, 128, 64, 0)
-    assert need == fwd + 2 * 64 * 128 * 128 * 4
+    tbl = 64 * 128 * 4  # decay table: H rows of 128 floats (block + 1 rounded up to 64)
+    assert need == fwd + (fwd - tbl) + 2 * 64 * 128 * 128 * 4  # second chunk-state area, S0^T, dS_N^T
     assert lib.lightning_attn_bwd_workspace_bytes(1, 1, 0, 128) == 0
 
 
