@@ -160,7 +160,8 @@ int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const 
  * Each of dq, dk, dv is computed as a prefill-shaped pass (dk and dv run the
  * tokens last first) with the kernels of lightning_attn_fwd_ex at block 64,
  * so with bf16 inputs the same omission below 2^-30 applies to heads that
- * decay within a chunk.
+ * decay within a chunk.  With bf16 inputs the dk and dv passes share their
+ * kernel launches (each keeps its own chunk states in the workspace).
  *   q, k, v, dout : in_dtype [B][H][N][d]          (read)
  *   decay         : float [H]                      (read)
  *   kv_in         : float [B][H][d][d] or NULL     (read: the forward's initial state; NULL = zero)
@@ -179,7 +180,8 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of scratch lightning_attn_bwd needs for these sizes (0 on invalid
- * arguments). */
+ * arguments): the decay table, two sets of chunk states (B*H*ceil(N/L) d x d
+ * fp32 each, L the default chunk at block 64) and two B*H d x d fp32 states. */
 size_t lightning_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
 
 /* Chunk length the library uses for (B, H, N, block) when `chunk` is 0, or
