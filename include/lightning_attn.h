@@ -77,7 +77,9 @@ extern "C" {
  *   B, H, N   : >= 1;  d in {64, 128}
  *   block     : intra-block length of the blockwise algorithm, one of
  *               {64, 128, 256}.  The result does not depend on it beyond
- *               rounding.
+ *               rounding.  64 is the tuned path (the 64-token kernels with
+ *               LDS DMA and the warm start); 128 and 256 run a general
+ *               kernel that is several times slower.
  * Decays are meant to lie in [0, 1].  With bf16 inputs and block 64, a head
  * with span = ceil(30 ln 2 / -ln lam), rounded up to a multiple of 64, at
  * most a third of the chunk (lam^span <= 2^-30) is computed per chunk from

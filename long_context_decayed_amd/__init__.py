@@ -6,8 +6,12 @@ runs in the library's HIP kernels.  torch supplies device memory and the
 current stream.  If the library has not been built the calls raise; there is
 no CPU fallback.
 
-    out = fwd(q, k, v, decay, kv_in=None, kv_out=None, block=256)
+    out = fwd(q, k, v, decay, kv_in=None, kv_out=None, block=64)
     o   = decode_step(q, k, v, decay, kv_in, kv_out)
+    dq, dk, dv, dkv_in = bwd(q, k, v, decay, dout)
+
+block 64 is the tuned path; 128 and 256 give the same result up to rounding
+through a general, slower kernel.
 """
 import ctypes
 import os
@@ -18,9 +22,17 @@ __all__ = [
     "LIB_PATH",
     "LightningAttnError",
     "load",
+    "LA_FLAG_EXACT",
     "fwd",
+    "fwd_slots",
+    "bwd",
     "decode_step",
+    "decode_slots",
+    "decode_fused",
+    "norm_gate",
+    "silu_",
     "workspace_bytes",
+    "lib_bwd_workspace_bytes",
     "chunk_for",
     "runtime_version",
 ]
@@ -118,7 +130,7 @@ def _check_dev(name, t, dtype=None, shape=None):
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
 
 
-def chunk_for(B, H, N, block=256, chunk=0):
+def chunk_for(B, H, N, block=64, chunk=0):
     """Chunk length the library uses (chunk=0: its default)."""
     return int(load().lightning_attn_fwd_chunk(B, H, N, block, chunk))
 
@@ -127,11 +139,11 @@ def lib_bwd_workspace_bytes(B, H, N, d):
     return int(load().lightning_attn_bwd_workspace_bytes(B, H, N, d))
 
 
-def workspace_bytes(B, H, N, d, block=256, chunk=0):
+def workspace_bytes(B, H, N, d, block=64, chunk=0):
     return int(load().lightning_attn_fwd_workspace_bytes(B, H, N, d, block, chunk))
 
 
-def fwd(q, k, v, decay, kv_in=None, kv_out=None, block=256, out=None, out_dtype=None, chunk=0,
+def fwd(q, k, v, decay, kv_in=None, kv_out=None, block=64, out=None, out_dtype=None, chunk=0,
         workspace=None, events=None, exact=False, stream=None):
     """Prefill.  q, k, v: [B, H, N, d] bf16 or fp32 device tensors; decay: fp32 [H];
     kv_in / kv_out: fp32 [B, H, d, d] or None.  Returns out [B, H, N, d] in
