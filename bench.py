@@ -23,7 +23,10 @@ ONE JSON line:
                  (LA_FLAG_EXACT: no warm start)
   backward       the backward pass of the same layer (dq, dk, dv from dout)
   epilogue_prologue  per-head RMSNorm + sigmoid gate of the output and SiLU
-                 on one input, as their own passes over the same layer
+                 on one input, as their own passes over the same layer; and
+                 the prefill step with SiLU on q, k, v fused into its tile
+                 loads (LA_FLAG_SILU_QKV) beside the step plus three SiLU
+                 passes
   decode         256 sequences x 64 heads x d=128 decode step, 1000 in-place
                  steps timed as a whole: GB/s of state + token traffic; and
                  the same rows through a slot table over a 512-slot pool, and
@@ -171,9 +174,18 @@ def bench_prefill(args, dev):
         ms_exact = _time_ms(lambda: la.fwd(q, k, v, lam, kv_out=kv_out, block=block, out=out, workspace=ws,
                                            exact=True), max(1, args.steps // 2))
         res["exact"] = dict(ms_per_step=ms_exact, tokens_per_s=B * N / (ms_exact * 1e-3))
+    ms_silu = None
+    if args.fused and block == 64:
+        # the same step on pre-activations, SiLU applied to the tiles as they load
+        ms_silu = _time_ms(lambda: la.fwd(q, k, v, lam, kv_out=kv_out, block=block, out=out, workspace=ws,
+                                          silu=True), max(1, args.steps // 2))
     del ws
     if args.fused:
-        res["epilogue_prologue"] = bench_norm_gate_silu(args, dev, out)
+        ep = bench_norm_gate_silu(args, dev, out)
+        if ms_silu is not None:
+            ep["prefill_silu_fused_ms"] = ms_silu
+            ep["prefill_plus_silu_passes_ms"] = ms_step + 3 * ep["silu_ms_per_tensor"]
+        res["epilogue_prologue"] = ep
     del out
     if args.backward:
         res["backward"] = bench_backward(args, dev, q, k, v, lam)

@@ -66,6 +66,17 @@ extern "C" {
  * lightning_attn_fwd; for inputs whose magnitudes vary so much over time that
  * 2^-30 of a state older than the carry span still matters. */
 #define LA_FLAG_EXACT 1u
+/* LA_FLAG_SILU_QKV (lightning_attn_fwd_ex and lightning_attn_fwd_slots only):
+ * q, k, v are the pre-activation projections; the kernels apply
+ * SiLU(x) = x / (1 + e^-x) to every element as its tile arrives in on-chip
+ * memory, rounded once to bf16, exactly as if lightning_attn_silu had been
+ * run over q, k and v first (the MiniMax-M1 fact sheet, "linear / SSM layer
+ * configuration" field: SiLU on Q, K, V), so the activations make no extra
+ * pass through HBM and q, k, v are left unchanged.  bf16 inputs and block 64
+ * only (LA_ERR_UNSUPPORTED otherwise).  SiLU and the sigmoid gate use the
+ * hardware base-2 exponential and reciprocal (about 1 ulp each) in every
+ * entry point. */
+#define LA_FLAG_SILU_QKV 2u
 
 /*
  * Prefill, bf16 Q/K/V/O, fp32 accumulation and fp32 state.
@@ -120,7 +131,7 @@ int lightning_attn_fwd_bf16_f32out(const void* q, const void* k, const void* v, 
  *               default (lightning_attn_fwd_chunk); otherwise a positive
  *               multiple of block.  The result does not depend on it beyond
  *               rounding.
- *   flags     : 0, or LA_FLAG_EXACT
+ *   flags     : 0, or LA_FLAG_EXACT and/or LA_FLAG_SILU_QKV
  *   workspace : device scratch of at least lightning_attn_fwd_workspace_bytes()
  *               bytes, 256-byte aligned, owned by the caller and not used
  *               after the enqueued work completes; NULL = allocate

@@ -23,6 +23,7 @@ __all__ = [
     "LightningAttnError",
     "load",
     "LA_FLAG_EXACT",
+    "LA_FLAG_SILU_QKV",
     "fwd",
     "fwd_slots",
     "bwd",
@@ -42,6 +43,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblightnin
 LA_DTYPE_BF16 = 0
 LA_DTYPE_F32 = 1
 LA_FLAG_EXACT = 1
+LA_FLAG_SILU_QKV = 2
 _DT = {torch.bfloat16: LA_DTYPE_BF16, torch.float32: LA_DTYPE_F32}
 
 _lib = None
@@ -143,8 +145,12 @@ def workspace_bytes(B, H, N, d, block=64, chunk=0):
     return int(load().lightning_attn_fwd_workspace_bytes(B, H, N, d, block, chunk))
 
 
+def _fwd_flags(exact, silu):
+    return (LA_FLAG_EXACT if exact else 0) | (LA_FLAG_SILU_QKV if silu else 0)
+
+
 def fwd(q, k, v, decay, kv_in=None, kv_out=None, block=64, out=None, out_dtype=None, chunk=0,
-        workspace=None, events=None, exact=False, stream=None):
+        workspace=None, events=None, exact=False, silu=False, stream=None):
     """Prefill.  q, k, v: [B, H, N, d] bf16 or fp32 device tensors; decay: fp32 [H];
     kv_in / kv_out: fp32 [B, H, d, d] or None.  Returns out [B, H, N, d] in
     out_dtype (default: the input dtype).
@@ -152,7 +158,9 @@ def fwd(q, k, v, decay, kv_in=None, kv_out=None, block=64, out=None, out_dtype=N
     workspace: a uint8 device tensor of at least workspace_bytes(...) bytes;
     None allocates one from torch's caching allocator.  events: optional pair
     of hipEvent_t handles (ints) recorded around the kernel that writes every
-    output row.  exact: every head by the exact chunked path (no warm start)."""
+    output row.  exact: every head by the exact chunked path (no warm start).
+    silu: q, k, v are pre-activations; SiLU is applied inside the kernels as
+    their tiles load (bf16, block 64), q, k, v themselves are not changed."""
     lib = load()
     if q.dtype not in _DT:
         raise TypeError("q must be bfloat16 or float32")
@@ -178,7 +186,7 @@ def fwd(q, k, v, decay, kv_in=None, kv_out=None, block=64, out=None, out_dtype=N
     e0, e1 = (None, None) if events is None else (ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
     rc = lib.lightning_attn_fwd_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(kv_in), _ptr(kv_out),
-        B, H, N, d, block, _DT[q.dtype], _DT[odt], chunk, LA_FLAG_EXACT if exact else 0,
+        B, H, N, d, block, _DT[q.dtype], _DT[odt], chunk, _fwd_flags(exact, silu),
         _ptr(workspace), workspace.numel(), e0, e1, _stream(stream),
     )
     if rc != 0:
@@ -208,7 +216,8 @@ def decode_step(q, k, v, decay, kv_in=None, kv_out=None, out=None, stream=None):
     return out
 
 
-def fwd_slots(q, k, v, decay, states, slots, block=64, out=None, out_dtype=None, exact=False, stream=None):
+def fwd_slots(q, k, v, decay, states, slots, block=64, out=None, out_dtype=None, exact=False, silu=False,
+              stream=None):
     """Prefill into a state pool.  q, k, v: [B, H, N, d]; states: fp32
     [num_slots, H, d, d], read and written in place for the rows' slots;
     slots: int32 [B] on the device (out of range: zero start, no write-back).
@@ -230,7 +239,7 @@ def fwd_slots(q, k, v, decay, states, slots, block=64, out=None, out_dtype=None,
     _check_dev("out", out, out_dtype, (B, H, N, d))
     rc = lib.lightning_attn_fwd_slots(
         _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(states), _ptr(slots), B, H, N, d,
-        states.shape[0], block, _DT[q.dtype], _DT[out_dtype], LA_FLAG_EXACT if exact else 0, _stream(stream)
+        states.shape[0], block, _DT[q.dtype], _DT[out_dtype], _fwd_flags(exact, silu), _stream(stream)
     )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_fwd_slots")

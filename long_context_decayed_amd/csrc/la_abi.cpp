@@ -135,7 +135,14 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 int prefill_run(const void* q, const void* k, const void* v, const float* decay, void* out, const float* kv_in,
                 float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, int in_dtype,
                 int out_dtype, int64_t L, void* workspace, size_t workspace_bytes, void* evt_begin, void* evt_end,
-                void* stream, const int* slots, int64_t num_slots, bool exact);
+                void* stream, const int* slots, int64_t num_slots, unsigned int flags);
+
+constexpr unsigned int kFwdFlags = LA_FLAG_EXACT | LA_FLAG_SILU_QKV;
+
+// SiLU on the tiles is built into the block-64 bf16 kernels only.
+bool flags_supported(unsigned int flags, int in_dtype, int64_t block) {
+  return !(flags & LA_FLAG_SILU_QKV) || (in_dtype == LA_DTYPE_BF16 && block == 64);
+}
 
 }  // namespace
 
@@ -145,19 +152,20 @@ int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const flo
                           const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
                           int64_t block, int in_dtype, int out_dtype, int64_t chunk, unsigned int flags,
                           void* workspace, size_t workspace_bytes, void* evt_begin, void* evt_end, void* stream) {
-  if (flags & ~LA_FLAG_EXACT) return LA_ERR_INVALID;
+  if (flags & ~kFwdFlags) return LA_ERR_INVALID;
   int64_t L = 0;
   int rc = validate_prefill(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, in_dtype, out_dtype, chunk, &L);
   if (rc != LA_OK) return rc;
+  if (!flags_supported(flags, in_dtype, block)) return LA_ERR_UNSUPPORTED;
   return prefill_run(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, in_dtype, out_dtype, L, workspace,
-                     workspace_bytes, evt_begin, evt_end, stream, nullptr, 0, (flags & LA_FLAG_EXACT) != 0);
+                     workspace_bytes, evt_begin, evt_end, stream, nullptr, 0, flags);
 }
 
 int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const float* decay, void* out,
                              float* states, const int32_t* slots, int64_t B, int64_t H, int64_t N, int64_t d,
                              int64_t num_slots, int64_t block, int in_dtype, int out_dtype, unsigned int flags,
                              void* stream) {
-  if (flags & ~LA_FLAG_EXACT) return LA_ERR_INVALID;
+  if (flags & ~kFwdFlags) return LA_ERR_INVALID;
   if (!states || !slots || num_slots < 1) return LA_ERR_INVALID;
   if (!aligned(states, 16) || !aligned(slots, 4)) return LA_ERR_INVALID;
   if (!dims_fit(B, H, N, num_slots)) return LA_ERR_UNSUPPORTED;
@@ -165,6 +173,7 @@ int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const 
   int64_t L = 0;
   int rc = validate_prefill(q, k, v, decay, out, nullptr, nullptr, B, H, N, d, block, in_dtype, out_dtype, 0, &L);
   if (rc != LA_OK) return rc;
+  if (!flags_supported(flags, in_dtype, block)) return LA_ERR_UNSUPPORTED;
   const int64_t in_es = in_dtype == LA_DTYPE_BF16 ? 2 : 4, out_es = out_dtype == LA_DTYPE_BF16 ? 2 : 4;
   const int64_t in_bytes = B * H * N * d * in_es, out_bytes = B * H * N * d * out_es;
   const int64_t pool_bytes = num_slots * H * d * d * 4;
@@ -173,7 +182,7 @@ int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const 
       overlap(states, pool_bytes, slots, B * 4) || overlap(out, out_bytes, slots, B * 4))
     return LA_ERR_INVALID;
   return prefill_run(q, k, v, decay, out, states, states, B, H, N, d, block, in_dtype, out_dtype, L, nullptr, 0,
-                     nullptr, nullptr, stream, (const int*)slots, num_slots, (flags & LA_FLAG_EXACT) != 0);
+                     nullptr, nullptr, stream, (const int*)slots, num_slots, flags);
 }
 
 }  // extern "C"
@@ -183,7 +192,8 @@ namespace {
 int prefill_run(const void* q, const void* k, const void* v, const float* decay, void* out, const float* kv_in,
                 float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, int in_dtype,
                 int out_dtype, int64_t L, void* workspace, size_t workspace_bytes, void* evt_begin, void* evt_end,
-                void* stream, const int* slots, int64_t num_slots, bool exact) {
+                void* stream, const int* slots, int64_t num_slots, unsigned int flags) {
+  const bool exact = (flags & LA_FLAG_EXACT) != 0;
   size_t tbl_bytes = 0;
   const size_t need = workspace_layout(B, H, N, d, block, L, &tbl_bytes);
   if (workspace) {
@@ -197,7 +207,7 @@ int prefill_run(const void* q, const void* k, const void* v, const float* decay,
     hipError_t e = hipMallocAsync(&ws, need, st);
     if (e != hipSuccess) return e == hipErrorOutOfMemory ? LA_ERR_NOMEM : LA_ERR_HIP;
   }
-  la::PrefillArgs a;
+  la::PrefillArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -220,6 +230,7 @@ int prefill_run(const void* q, const void* k, const void* v, const float* decay,
   a.warm_start = a.in_dtype == la::kBF16 && block == 64 && !exact;
   a.rev = false;
   a.scale_kv_out = false;
+  a.silu = (flags & LA_FLAG_SILU_QKV) != 0;
   a.slots = slots;
   a.num_slots = num_slots;
   a.evt_begin = evt_begin;
@@ -336,7 +347,7 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
   float* s0t = (float*)((char*)ws + s0t_off);
   float* dsnt = (float*)((char*)ws + dsnt_off);
 
-  la::PrefillArgs a;
+  la::PrefillArgs a{};  // silu stays false: the backward takes activated inputs
   a.decay = decay;
   a.B = B;
   a.H = H;

@@ -36,8 +36,6 @@ namespace la {
 constexpr int kDecThreads = 128;  // threads per (sequence, head) pair
 constexpr int kDecPairs = 2;      // pairs per workgroup
 
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
-
 template <int D>
 __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -65,8 +63,8 @@ __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
   const float lam = valid ? decay[hh] : 0.0f;
   if (valid && tid < D) {
     const float qf = (float)q[pair * D + tid], kf = (float)k[pair * D + tid];
-    qs[sub][tid] = silu ? qf * sigmoid_f(qf) : qf;
-    ks[sub][tid] = silu ? kf * sigmoid_f(kf) : kf;
+    qs[sub][tid] = silu ? silu_hw(qf) : qf;
+    ks[sub][tid] = silu ? silu_hw(kf) : kf;
   }
   f32x4 vv = {0.f, 0.f, 0.f, 0.f};
   if (valid) {
@@ -74,7 +72,7 @@ __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
     vv = f32x4{(float)vb[0], (float)vb[1], (float)vb[2], (float)vb[3]};
     if (silu)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vv[i] *= sigmoid_f(vv[i]);
+      for (int i = 0; i < 4; ++i) vv[i] = silu_hw(vv[i]);
   }
   const int64_t sbase = (srow * H + hh) * D * D;
   f32x4 s[RPT];
@@ -116,7 +114,7 @@ __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
     if (gate) {
       const bf16x4 gb = *reinterpret_cast<const bf16x4*>(gate + pair * D + 4 * tid);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] *= sigmoid_f((float)gb[i]);
+      for (int i = 0; i < 4; ++i) r[i] *= sigmoid_hw((float)gb[i]);
     }
     bf16x4 ob;
 #pragma unroll

@@ -344,6 +344,23 @@ template <int N>
 __device__ __forceinline__ void sync_lds_after_vmem() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
+// Wait until at most N of this wave's vector-memory instructions are in
+// flight (no barrier).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// sigmoid(x) = 1 / (1 + e^-x) and SiLU(x) = x sigmoid(x) with the hardware
+// base-2 exponential and reciprocal (about 1 ulp each, far below the bf16
+// rounding every caller applies next): every kernel that applies SiLU or the
+// gate uses these, so SiLU fused into a tile load equals the SiLU pass
+// bit for bit.  x -> -inf gives e^-x = inf and a product of -0; x -> +inf
+// gives x.
+__device__ __forceinline__ float sigmoid_hw(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
+}
+__device__ __forceinline__ float silu_hw(float x) { return x * sigmoid_hw(x); }
 
 // Rows [0, nvalid) of a 64-row tile (src: its row 0, wave-uniform; row r at
 // src + r * RS elements, RS = -D for a tile read last row first) into the
@@ -367,6 +384,36 @@ __device__ __forceinline__ void dma_tile(const bf16* __restrict__ src, bf16* dst
         dma_dword(src + r * RS + (((lane >> 2) ^ swz(r)) << 3) + 2 * (lane & 3), t0 + 2 * r * D);
       else
         *reinterpret_cast<uint32_t*>(dst + r * D + 2 * lane) = 0u;
+    }
+  }
+}
+
+// SiLU in place over the part of an LDS tile that this wave's dma_tile call
+// (same nvalid) wrote: the wave calls it after waiting for its own transfers
+// and before the barrier that publishes the tile, so no other wave reads the
+// tile in between.  Each lane rewrites exactly the bytes its transfers
+// brought (16 per full-tile instruction, 4 per row of a partial tile); the
+// zero rows of a partial tile stay zero (SiLU(0) = 0).  Values are rounded
+// to bf16 once, as a SiLU pass over the tensor would store them.
+template <int D, int NW>
+__device__ __forceinline__ void silu_own(bf16* dst, int nvalid, int w, int lane) {
+  if (nvalid >= kSub) {
+    constexpr int CPR = D / 8, RPI = 64 / CPR, NI = kSub / RPI;
+#pragma unroll
+    for (int m = 0; m < NI / NW; ++m) {
+      bf16x8* p = reinterpret_cast<bf16x8*>(reinterpret_cast<char*>(dst) + 1024 * (w + NW * m) + 16 * lane);
+      bf16x8 x = *p;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = (bf16)silu_hw((float)x[j]);
+      *p = x;
+    }
+  } else if (lane < D / 2) {
+    for (int r = w; r < nvalid; r += NW) {
+      bf16x2* p = reinterpret_cast<bf16x2*>(dst + r * D + 2 * lane);
+      bf16x2 x = *p;
+      x[0] = (bf16)silu_hw((float)x[0]);
+      x[1] = (bf16)silu_hw((float)x[1]);
+      *p = x;
     }
   }
 }

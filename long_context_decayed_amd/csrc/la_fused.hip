@@ -5,12 +5,14 @@
 // field (SiLU on Q, K, V; RMSNorm on the output) and its "output gate" field
 // (a sigmoid gate after that norm, before the output projection).
 //
-// The block-64 prefill kernel has no room to take them in (it uses all 80 KiB
-// of LDS per workgroup and nearly all of its registers, and the per-head norm
-// would need a cross-wave reduction); the decode step fuses them (la_decode.hip).
-// Both passes here are bound by HBM: 16-byte non-temporal loads and stores
-// (the data is touched once), one row of d features per d/8 lanes, the row's
-// sum of squares reduced across those lanes.
+// The block-64 prefill kernels can also apply SiLU to the tiles as they load
+// them (la_output.hip, la_state.hip; same silu_hw, so the results agree bit
+// for bit); the epilogue has no room there (the output pass uses all 80 KiB
+// of LDS per workgroup and nearly all of its registers, and the per-head
+// norm would need a cross-wave reduction).  The decode step fuses all of
+// them (la_decode.hip).  Both passes here are bound by HBM: 16-byte
+// non-temporal loads and stores (the data is touched once), one row of d
+// features per d/8 lanes, the row's sum of squares reduced across those lanes.
 
 #include <hip/hip_runtime.h>
 
@@ -20,8 +22,6 @@
 namespace la {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float sigmoid_fast(float x) { return 1.0f / (1.0f + expf(-x)); }
 
 // y = o / sqrt(mean(o^2) + eps) * gamma[h] * sigmoid(g) per row of d features.
 // Each lane group of TPR lanes handles RU rows, 256/TPR*RU rows per block; all
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void la_norm_gate(const TO* __restrict__ o, co
     if (row < rows) {
       if (gate)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[u][i] *= sigmoid_fast((float)gv[u][i]);
+        for (int i = 0; i < 8; ++i) x[u][i] *= sigmoid_hw((float)gv[u][i]);
       bf16x8 y;
 #pragma unroll
       for (int i = 0; i < 8; ++i) y[i] = (bf16)x[u][i];
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void la_silu(bf16* __restrict__ x, int64_t n8,
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float f = (float)b[u][j];
-        b[u][j] = (bf16)(f * sigmoid_fast(f));
+        b[u][j] = (bf16)silu_hw(f);
       }
       __builtin_nontemporal_store(__builtin_bit_cast(u32x4, b[u]), reinterpret_cast<u32x4*>(x + 8 * i));
     }
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void la_silu(bf16* __restrict__ x, int64_t n8,
   if (blockIdx.x == 0 && threadIdx.x == 0)
     for (int64_t j = 8 * n8; j < n; ++j) {
       const float f = (float)x[j];
-      x[j] = (bf16)(f * sigmoid_fast(f));
+      x[j] = (bf16)silu_hw(f);
     }
 }
 

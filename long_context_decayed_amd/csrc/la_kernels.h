@@ -25,6 +25,7 @@ struct PrefillArgs {
   bool warm_start; // bf16 inputs, block 64: decaying heads take the warm-start pass
   bool rev;        // tokens last first, kv_in entering undecayed (backward; bf16, block 64 only)
   bool scale_kv_out; // kv_out = lam * final state (backward: gradient of kv_in)
+  bool silu;         // q, k, v are pre-activations: SiLU applied as tiles load (bf16, block 64, forward only)
   const int* slots;  // optional slot table: kv_in / kv_out rows of pool slots (device int32[B])
   int64_t num_slots;
   void* evt_begin; // optional hipEvent_t pair around the kernel that writes every output row

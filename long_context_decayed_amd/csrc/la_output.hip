@@ -323,6 +323,10 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 // as the gradient of the final state does in the adjoint recurrence.  Only
 // the first sub-tile of chunk 0 differs: its rows take lam^p instead of
 // lam^(p+1) and it hands the state on decayed by lam^(n-1) instead of lam^n.
+// SILU: q, k, v are pre-activations; every tile gets SiLU in LDS (silu_own)
+// by the waves that brought it, between their own wait and the barrier
+// that publishes it (the fact sheet's "linear / SSM layer configuration"
+// field puts SiLU on Q, K and V), so the activations never make an HBM pass.
 //
 // Paired launch (pair_shift >= 0): two problems of one shape, with their own
 // tensors and chunk states, share a grid; workgroup i serves problem
@@ -341,7 +345,7 @@ struct Operands {
   const float* kv_in;  // initial states, or null
 };
 
-template <typename TOut, int D, int MODE, bool REV>
+template <typename TOut, int D, int MODE, bool REV, bool SILU>
 __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Operands p1,
                                                               const float* __restrict__ decay,
                                                               const float* __restrict__ tbl_all, int H, int N, int L,
@@ -422,14 +426,12 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
     tlane = tb[lane];
     d_last = tb[n_last];
   }
-  // REV, first sub-tile of chunk 0: lam^p for row p, state decayed by
-  // lam^63 (lam^(n-1) if it is also the last, partial one).
-  float rfu[2] = {0.0f, 0.0f}, d_first = 0.0f;
-  if constexpr (REV) {
-    rfu[0] = tb[l32];
-    rfu[1] = tb[l32 + 32];
-    d_first = (t_end - t_begin <= kSub) ? tb[n_last - 1] : tb[63];
-  }
+  // REV, first sub-tile of chunk 0: lam^p for row p (taken from the
+  // neighbouring lane's rf when needed, so that nothing more stays live
+  // across the loop), state decayed by lam^63 (lam^(n-1) if it is also the
+  // last, partial one).
+  float d_first = 0.0f;
+  if constexpr (REV) d_first = (t_end - t_begin <= kSub) ? tb[n_last - 1] : tb[63];
   for (int e = tid; e < 4 * 64; e += NW * 64) {
     const int jq = e >> 6, ln = e & 63;
     const int dd = (ln & 31) - 4 * (ln >> 5) - 8 * jq;
@@ -488,6 +490,11 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
       for (int j = 0; j < nwu; ++j) {
         const bool odd = (j & 1) != 0;
         // Sub-tile j is visible; every wave is done with the other buffer.
+        if constexpr (SILU) {
+          wait_vmem<0>();
+          silu_own<D, NW>(odd ? Ks : Kt, kSub, w, lane);
+          silu_own<D, NW>(odd ? Qs : Vs, kSub, w, lane);
+        }
         sync_lds_after_vmem<0>();
         if (j + 1 < nwu) {
           const int64_t offn = off0 + (int64_t)(j + 1) * kSub * RS;
@@ -509,6 +516,13 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
     dma_tile<D, NW, RS>(kb + off, Ks, nv, w, lane);
     dma_tile<D, NW, RS>(kb + off, Kt, nv, w, lane);
     dma_tile<D, NW, RS>(vb + off, Vs, nv, w, lane);
+    if constexpr (SILU) {
+      wait_vmem<0>();
+      silu_own<D, NW>(Qs, nv, w, lane);
+      silu_own<D, NW>(Ks, nv, w, lane);
+      silu_own<D, NW>(Kt, nv, w, lane);
+      silu_own<D, NW>(Vs, nv, w, lane);
+    }
     sync_lds_after_vmem<0>();
   }
   // bf16 output of the previous sub-tile, packed and lane-swapped, stored
@@ -631,9 +645,17 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
     // Inter-term decay lam^(p+1), one factor per lane and token tile.  Written
     // element by element: as a vector-by-scalar product the compiler hoists a
     // 16-wide copy of each factor out of the loop (30 registers).
+    float r_tile[2] = {rf[0], rf[1]};
+    if (REV && first) {
+      // lam^p = rf of row p - 1: lane l - 1 of the same tile, or for l = 0,
+      // lam^0 = 1 (tile 0) and lam^32 = rf[0] of lane 31 (tile 1).
+      const float up0 = __shfl(rf[0], lane - 1), up1 = __shfl(rf[1], lane - 1), top = __shfl(rf[0], lane + 31);
+      r_tile[0] = l32 == 0 ? 1.0f : up0;
+      r_tile[1] = l32 == 0 ? top : up1;
+    }
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      const float r = (REV && first) ? rfu[rt] : rf[rt];
+      const float r = r_tile[rt];
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[rt][j] *= r;
     }
@@ -641,6 +663,12 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
     // This sub-tile's V and K^T copy (requested before the previous
     // sub-tile's kStores output stores, which may still be in flight) and
     // the score tiles become visible; Q and the score copy of K are free.
+    if constexpr (SILU) {
+      if (t0 != t_begin) {  // the first sub-tile's V came with the initial tiles
+        wait_vmem<kStores>();
+        silu_own<D, NW>(Vs, min(kSub, t_end - t0), w, lane);
+      }
+    }
     sync_lds_after_vmem<kStores>();
     if (more) {
       dma_tile<D, NW, RS>(qb + off_next, Qs, nv_next, w, lane);
@@ -665,6 +693,13 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
 
     // The next sub-tile's Q and K (and this wave's older stores) are done
     // and visible; V, K^T and the score tiles are free from here on.
+    if constexpr (SILU) {
+      if (more) {
+        wait_vmem<0>();
+        silu_own<D, NW>(Qs, nv_next, w, lane);
+        silu_own<D, NW>(Ks, nv_next, w, lane);
+      }
+    }
     sync_lds_after_vmem<0>();
     if (more) {
       dma_tile<D, NW, RS>(vb + off_next, Vs, nv_next, w, lane);
@@ -743,13 +778,16 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
         }
       }
     }
-    // The final state, natural (feature, column) order, to the last chunk's slot.
-    float* dst = states + ((int64_t)bh * nc + c) * D * D + col;
+    // The final state, natural (feature, column) order, to the last chunk's
+    // slot.  The lane's column and half are taken from the hardware lane id
+    // here, so that they need not stay live (or spilled) across the loop.
+    const int ln = __lane_id(), lh = ln >> 5;
+    float* dst = states + ((int64_t)bh * nc + c) * D * D + 32 * w + (ln & 31);
 #pragma unroll
     for (int kt = 0; kt < NRT; ++kt)
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        dst[(32 * kt + 16 * (j >> 3) + 8 * hf + 4 * ((j >> 2) & 1) + (j & 3)) * D] = S[kt][j];
+        dst[(32 * kt + 16 * (j >> 3) + 8 * lh + 4 * ((j >> 2) & 1) + (j & 3)) * D] = S[kt][j];
   }
 }
 
@@ -772,18 +810,23 @@ static void launch_fast(const PrefillArgs& a, hipStream_t st, const PrefillArgs*
   const int64_t half = int64_t(1) << kPairShift;  // workgroups of one problem per group of the pair
   const unsigned grid = b ? (unsigned)((nblk + half - 1) / half * 2 * half) : (unsigned)nblk;
   const Operands p0 = operands_of(a), p1 = b ? operands_of(*b) : p0;
-  if (a.rev)
-    hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, true>), dim3(grid), dim3(D * 2), 0, st, p0, p1, a.decay,
-                       (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots, a.num_slots,
-                       a.warm_start ? 1 : 0, nblk, shift);
+  if (a.rev)  // the backward: no SiLU
+    hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, true, false>), dim3(grid), dim3(D * 2), 0, st, p0, p1,
+                       a.decay, (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots,
+                       a.num_slots, a.warm_start ? 1 : 0, nblk, shift);
+  else if (a.silu)
+    hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, false, true>), dim3(grid), dim3(D * 2), 0, st, p0, p1,
+                       a.decay, (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots,
+                       a.num_slots, a.warm_start ? 1 : 0, nblk, shift);
   else
-    hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, false>), dim3(grid), dim3(D * 2), 0, st, p0, p1, a.decay,
-                       (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots, a.num_slots,
-                       a.warm_start ? 1 : 0, nblk, shift);
+    hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, false, false>), dim3(grid), dim3(D * 2), 0, st, p0, p1,
+                       a.decay, (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots,
+                       a.num_slots, a.warm_start ? 1 : 0, nblk, shift);
 }
 
 template <typename TIn, typename TOut, int D, int BLK>
 static hipError_t launch_output_t(const PrefillArgs& a, hipStream_t st) {
+  if (a.silu && !(BLK == 64 && sizeof(TIn) == 2)) return hipErrorInvalidValue;  // SiLU: block-64 bf16 kernels only
   const int BH = (int)(a.B * a.H);
   const int nc = a.nc;
   const bool timed = !a.warm_start;
@@ -846,7 +889,7 @@ template <int MODE>
 static hipError_t launch_pair_mode(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st) {
   if (a.in_dtype != kBF16 || b.in_dtype != kBF16 || a.block != 64 || b.block != 64 || a.B != b.B || a.H != b.H ||
       a.N != b.N || a.nc != b.nc || a.d != b.d || a.out_dtype != b.out_dtype || a.rev != b.rev ||
-      a.warm_start != b.warm_start)
+      a.warm_start != b.warm_start || a.silu != b.silu)
     return hipErrorInvalidValue;
   if (MODE == kWarmStart && !a.warm_start) return hipErrorInvalidValue;
   if (a.out_dtype == kBF16) {

@@ -136,8 +136,10 @@ __global__ __launch_bounds__(D * 2, sizeof(TIn) == 2 ? 3 : 1) void la_chunk_stat
 //   With skip_decaying set, heads that decay within their chunk return at
 // once: the warm-start output pass needs no aggregates.  REV reads the
 // tokens last first (token t of the pass is row N-1-t), for the reverse-time
-// passes of the backward; the aggregates start from zero either way.
-template <int D, bool REV>
+// passes of the backward; the aggregates start from zero either way.  SILU:
+// k and v are pre-activations, given SiLU in LDS as each tile arrives (as in
+// the output pass).
+template <int D, bool REV, bool SILU>
 __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restrict__ k, const bf16* __restrict__ v,
                                                              const float* __restrict__ decay,
                                                              const float* __restrict__ tbl_all, float* __restrict__ ws,
@@ -186,6 +188,11 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
   if (n_last < kSub) {
     // The partial last sub-tile (peeled, so the main loop has one path):
     // tokens s < n_last get lam^(n_last-1-s), the rest 0.
+    if constexpr (SILU) {
+      wait_vmem<0>();
+      silu_own<D, NW>(Ks[0], n_last, w, lane);
+      silu_own<D, NW>(Vs[0], n_last, w, lane);
+    }
     sync_lds_after_vmem<0>();
     if (b > 0) {
       const int64_t off = (int64_t)(t_begin + (b - 1) * kSub) * RS;
@@ -217,6 +224,11 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
   for (; b >= 0; --b, cur ^= 1) {
     // Sub-tile b (full) is in buffer cur and visible; every wave is done
     // with the other buffer, which now receives sub-tile b - 1.
+    if constexpr (SILU) {
+      wait_vmem<0>();
+      silu_own<D, NW>(Ks[cur], kSub, w, lane);
+      silu_own<D, NW>(Vs[cur], kSub, w, lane);
+    }
     sync_lds_after_vmem<0>();
     if (b > 0) {
       const int64_t off = (int64_t)(t_begin + (b - 1) * kSub) * RS;
@@ -340,14 +352,20 @@ static hipError_t launch_aggregate_t(const PrefillArgs& a, hipStream_t st) {
   const int nc = a.nc;
   hipLaunchKernelGGL(la_decay_table, dim3((unsigned)a.H), dim3(256), 0, st, a.decay, a.tbl, a.tbl_stride);
   if constexpr (sizeof(TIn) == 2) {
-    if (a.rev)
-      hipLaunchKernelGGL((la_chunk_state64<D, true>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+    if (a.rev)  // the backward: no SiLU
+      hipLaunchKernelGGL((la_chunk_state64<D, true, false>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+                         (const bf16*)a.k, (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H,
+                         (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0);
+    else if (a.silu)
+      hipLaunchKernelGGL((la_chunk_state64<D, false, true>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                          (const bf16*)a.k, (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H,
                          (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0);
     else
-      hipLaunchKernelGGL((la_chunk_state64<D, false>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
+      hipLaunchKernelGGL((la_chunk_state64<D, false, false>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                          (const bf16*)a.k, (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H,
                          (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0);
+  } else if (a.silu) {
+    return hipErrorInvalidValue;  // SiLU: bf16 inputs only
   } else if (a.rev)
     hipLaunchKernelGGL((la_chunk_state<TIn, D, true>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st, (const TIn*)a.k,
                        (const TIn*)a.v, (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc,

@@ -147,8 +147,24 @@ def test_decode_slots_validation(lib):
 
 
 def test_unknown_flags_rejected(lib):
-    assert _fwd(lib, flags=2) == LA_ERR_INVALID
+    assert _fwd(lib, flags=4) == LA_ERR_INVALID
     assert _fwd(lib, flags=0x80000000) == LA_ERR_INVALID
+
+
+def test_silu_flag_rules(lib):
+    """LA_FLAG_SILU_QKV (2): forward entry points only, bf16 inputs, block 64."""
+    # accepted: validation passes and stops at the too-small workspace, before any HIP call
+    for flags in (2, 3):
+        assert _fwd(lib, flags=flags, ws=FAKE[5], wsb=1) == LA_ERR_WORKSPACE
+    assert _fwd(lib, flags=2, ind=1, outd=1) == LA_ERR_UNSUPPORTED        # fp32 inputs
+    for block in (128, 256):
+        assert _fwd(lib, flags=2, block=block) == LA_ERR_UNSUPPORTED
+    f = lib.lightning_attn_fwd_slots
+    base = [FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], FAKE[5], FAKE[6], 1, 1, 128, 64, 4, 256, 0, 0, 2, None]
+    assert f(*base) == LA_ERR_UNSUPPORTED                                 # block 256
+    bwd = lib.lightning_attn_bwd
+    assert bwd(*FAKE[:5], None, None, FAKE[5], FAKE[6], FAKE[7], None, 1, 2, 64, 64, 0, 0, 2, None, 0,
+               None) == LA_ERR_INVALID                                   # the backward takes activated inputs
 
 
 def test_fwd_slots_validation(lib):

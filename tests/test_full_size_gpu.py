@@ -179,3 +179,23 @@ def test_million_token_backward_slices(dev, million):
         for got, ref, name in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
             e = tol.assert_bf16_f32out(host(got[:, :, a:a + w]), ref[:, :, :w], "%s slice %d" % (name, a))
             print("%s slice at %d: max|err|/RMS %.3e" % (name, a, e))
+
+
+def test_million_token_silu_fused_is_silu_pass_then_prefill(dev, million):
+    """At the million-token size, in the bench's launch configuration (block
+    64, default chunk): the prefill with SiLU fused into its tile loads equals,
+    bit for bit, the SiLU pass over q, k, v followed by the plain prefill (the
+    plain prefill is checked against the oracle on slices above)."""
+    q, k, v, lam, _ = million
+    B, H, N, d = q.shape
+    lam_t = torch.from_numpy(lam).to(dev)
+    say("million-token prefill: fused SiLU vs SiLU pass + prefill")
+    kv1, kv2 = (torch.empty((B, H, d, d), device=dev, dtype=torch.float32) for _ in range(2))
+    o1 = la.fwd(q, k, v, lam_t, kv_out=kv1, block=64, silu=True)
+    acts = [la.silu_(t.clone()) for t in (q, k, v)]
+    o2 = la.fwd(*acts, lam_t, kv_out=kv2, block=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(kv1, kv2)
+    del acts, o1, o2
+    torch.cuda.empty_cache()

@@ -129,3 +129,69 @@ def test_layer_core_pipeline(dev):
     y_ref = ora.sigmoid_gate(ora.rmsnorm_heads(o_ref, host(gamma), eps=1e-5), host(gate))
     for h in range(H):
         tol.assert_bf16_out(host(y)[:, h], y_ref[:, h], "head %d" % h)
+
+
+def _preact(B, H, N, d, seed, dev, scale=2.5):
+    # pre-activation projections: a wider spread than the core's inputs so
+    # that SiLU's bend and both of its tails are exercised
+    return tuple((t * scale).contiguous() for t in qkv_device(B, H, N, d, seed=seed, device=dev))
+
+
+@pytest.mark.parametrize("d,N,odt,exact", [(128, 2500, torch.bfloat16, False), (128, 2500, torch.float32, False),
+                                          (64, 1100, torch.float32, False), (128, 700, torch.float32, True),
+                                          (128, 63, torch.bfloat16, False)])
+def test_prefill_silu_fused_is_silu_pass_then_prefill(dev, d, N, odt, exact):
+    """SiLU on the tiles as they load == the SiLU pass over q, k, v first, bit
+    for bit (outputs and final state), on decays that take both the warm-start
+    and the chunked paths (so the chunk-aggregate kernel's SiLU is covered),
+    with an initial state and a ragged last tile; q, k, v are left unchanged."""
+    say("prefill + fused SiLU vs SiLU pass + prefill: B2 H8 N", N, "d", d, odt, "exact", exact)
+    B, H = 2, 8
+    q, k, v = _preact(B, H, N, d, 300 + d + N, dev)
+    keep = [t.clone() for t in (q, k, v)]
+    s0 = state_device(B, H, d, seed=301, device=dev)
+    lam = torch.from_numpy(LAMS8).to(dev)
+    kv1, kv2 = (torch.empty((B, H, d, d), device=dev, dtype=torch.float32) for _ in range(2))
+    o1 = la.fwd(q, k, v, lam, kv_in=s0, kv_out=kv1, block=64, chunk=256, out_dtype=odt, exact=exact, silu=True)
+    qa, ka, va = (la.silu_(t.clone()) for t in (q, k, v))
+    o2 = la.fwd(qa, ka, va, lam, kv_in=s0, kv_out=kv2, block=64, chunk=256, out_dtype=odt, exact=exact)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(kv1, kv2)
+    for a, b in zip((q, k, v), keep):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_silu_fused_against_oracle(dev, d):
+    """The fused path against the oracle chain: SiLU in fp64 (rounded to bf16,
+    as the activations are stored), then the fp64 recurrence."""
+    say("prefill + fused SiLU vs oracle: B1 H8 N1500 d", d)
+    B, H, N = 1, 8, 1500
+    q, k, v = _preact(B, H, N, d, 320 + d, dev)
+    s0 = state_device(B, H, d, seed=321, device=dev)
+    kv = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    o = la.fwd(q, k, v, torch.from_numpy(LAMS8).to(dev), kv_in=s0, kv_out=kv, block=64, chunk=512,
+               out_dtype=torch.float32, silu=True)
+    torch.cuda.synchronize()
+    act = [torch.from_numpy(ora.silu(host(t))).to(torch.bfloat16).to(torch.float32).numpy() for t in (q, k, v)]
+    o_ref, s_ref = oracle(*act, LAMS8, host(s0).astype(np.float64))
+    for h in range(H):
+        tol.assert_bf16_f32out(host(o)[:, h], o_ref[:, h], "O head %d" % h)
+        tol.assert_state(host(kv)[:, h], s_ref[:, h], "state head %d" % h)
+
+
+def test_pooled_prefill_silu_fused(dev):
+    say("pooled prefill + fused SiLU vs SiLU pass + pooled prefill: pool 6, B4 H4 N900 d128")
+    B, H, N, d, P = 4, 4, 900, 128, 6
+    q, k, v = _preact(B, H, N, d, 330, dev)
+    slots = torch.tensor([3, -1, 0, 5], dtype=torch.int32, device=dev)
+    lam = torch.from_numpy(LAMS8[[0, 3, 6, 7]].copy()).to(dev)
+    pool1 = state_device(P, H, d, seed=331, device=dev)
+    pool2 = pool1.clone()
+    o1 = la.fwd_slots(q, k, v, lam, pool1, slots, out_dtype=torch.float32, silu=True)
+    qa, ka, va = (la.silu_(t.clone()) for t in (q, k, v))
+    o2 = la.fwd_slots(qa, ka, va, lam, pool2, slots, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(pool1, pool2)
