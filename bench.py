@@ -368,8 +368,8 @@ def main():
                          "reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(sequence, head and batch sharding are described in DESIGN.md but not built)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(sharding by sequence, head and batch is designed but not built)", file=sys.stderr)
         sys.exit(2)
 
     import torch

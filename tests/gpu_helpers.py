@@ -14,7 +14,7 @@ from oracle import crec
 def require_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
-    # On a GPU machine the HIP library must be there: load() raises otherwise.
+    # With a GPU present the HIP library must be there: load() raises otherwise.
     la.load()
     return torch.device("cuda:0")
 
