@@ -21,6 +21,10 @@ ONE JSON line:
                  the same workload, on this host's cores
   exact_path     the same step with every head on the exact chunked path
                  (LA_FLAG_EXACT: no warm start)
+  depth_scaled   the same step with the decays of layers 0, 23, 46 and 69 of
+                 a 70-layer stack (slopes scaled down linearly with depth):
+                 deeper layers decay more slowly, so fewer heads take the
+                 warm start
   backward       the backward pass of the same layer (dq, dk, dv from dout)
   epilogue_prologue  per-head RMSNorm + sigmoid gate of the output and SiLU
                  on one input, as their own passes over the same layer; and
@@ -110,7 +114,7 @@ def _traffic(launch_alg_bytes):
 def bench_prefill(args, dev):
     import torch
     import long_context_decayed_amd as la
-    from long_context_decayed_amd.inputs import decay_lambdas, qkv_device
+    from long_context_decayed_amd.inputs import decay_lambdas, decay_lambdas_depth, qkv_device
 
     B, H, N, d, block = 1, 64, args.tokens, 128, args.block
     log("generating inputs B=%d H=%d N=%d d=%d bf16 (seed 3)" % (B, H, N, d))
@@ -174,6 +178,17 @@ def bench_prefill(args, dev):
         ms_exact = _time_ms(lambda: la.fwd(q, k, v, lam, kv_out=kv_out, block=block, out=out, workspace=ws,
                                            exact=True), max(1, args.steps // 2))
         res["exact"] = dict(ms_per_step=ms_exact, tokens_per_s=B * N / (ms_exact * 1e-3))
+    if args.depth:
+        rows = []
+        for layer in (0, 23, 46, 69):
+            lam_np = decay_lambdas_depth(H, layer, 70)
+            lam_l = torch.from_numpy(lam_np).to(dev)
+            ms_l = _time_ms(lambda: la.fwd(q, k, v, lam_l, kv_out=kv_out, block=block, out=out, workspace=ws),
+                            max(1, args.steps // 3))
+            rows.append(dict(layer=layer, warm_start_heads=sum(decaying_heads(lam_np, chunk)) if block == 64 else 0,
+                             ms_per_step=ms_l, tokens_per_s=B * N / (ms_l * 1e-3)))
+        res["depth_scaled"] = dict(n_layers=70, layers=rows,
+                                   mean_ms_over_sampled_layers=sum(r["ms_per_step"] for r in rows) / len(rows))
     ms_silu = None
     if args.fused and block == 64:
         # the same step on pre-activations, SiLU applied to the tiles as they load
@@ -360,6 +375,8 @@ def main():
     ap.add_argument("--no-backward", dest="backward", action="store_false")
     ap.add_argument("--no-exact", dest="exact", action="store_false",
                     help="skip the step timed with every head on the exact chunked path")
+    ap.add_argument("--no-depth", dest="depth", action="store_false",
+                    help="skip the steps timed with the decays of deeper layers")
     ap.add_argument("--no-fused", dest="fused", action="store_false",
                     help="skip the SiLU / RMSNorm / gate measurements")
     ap.add_argument("--cpu-tokens", type=int, default=1 << 20)
@@ -412,6 +429,7 @@ def main():
         "step_hbm_frac": prefill["step_hbm_frac"],
         "mfma_alg_frac": prefill["mfma_alg_frac"],
         "exact_path": prefill.get("exact"),
+        "depth_scaled": prefill.get("depth_scaled"),
         "backward": prefill.get("backward"),
         "epilogue_prologue": prefill.get("epilogue_prologue"),
         "cpu_baseline": cpu,
