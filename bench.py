@@ -111,6 +111,16 @@ def _traffic(launch_alg_bytes):
     return rec.get("bytes_per_launch")
 
 
+def _device_info(dev):
+    """What the numbers were measured on."""
+    import torch
+    import long_context_decayed_amd as la
+    p = torch.cuda.get_device_properties(dev)
+    return dict(name=p.name, arch=getattr(p, "gcnArchName", None), compute_units=p.multi_processor_count,
+                memory_gib=round(p.total_memory / 2 ** 30, 1), hip_runtime=la.runtime_version(),
+                torch=torch.__version__, torch_hip=torch.version.hip)
+
+
 def bench_prefill(args, dev):
     import torch
     import long_context_decayed_amd as la
@@ -434,6 +444,7 @@ def main():
         "epilogue_prologue": prefill.get("epilogue_prologue"),
         "cpu_baseline": cpu,
         "decode": dec,
+        "device": _device_info(dev),
     }
     print(json.dumps(line), flush=True)
 
