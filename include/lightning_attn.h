@@ -35,6 +35,10 @@
  *    not overlap.  out must not overlap q, k, v, kv_in or kv_out.
  *  - Arguments are validated before any HIP call, so validation errors are
  *    returned without touching the device.  Nothing is thrown across the ABI.
+ *  - The library keeps no state between calls: calls on different streams
+ *    may run at once.  Given a caller workspace (or none needed, as in the
+ *    decode steps), a call allocates, frees, copies and synchronises nothing
+ *    and issues no memset, so it can be captured in a HIP graph.
  *
  * Status codes: LA_OK, or one of the LA_ERR_* values below;
  * lightning_attn_strerror() names them.
