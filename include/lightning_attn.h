@@ -97,7 +97,8 @@ extern "C" {
  *               kernel that is several times slower.
  * Decays are meant to lie in [0, 1].  With bf16 inputs and block 64, a head
  * with span = ceil(30 ln 2 / -ln lam), rounded up to a multiple of 64, at
- * most a third of the chunk (lam^span <= 2^-30) is computed per chunk from
+ * most a third of the warm-start chunk (lam^span <= 2^-30; the chunk is
+ * lightning_attn_fwd_warm_chunk) is computed per chunk of that length from
  * the state that the span tokens before the chunk build from zero: at token
  * t of a chunk the state S_(c0-span-1) from before those tokens is left out
  * of its term lam^(t-c0+span+1) S_(c0-span-1), at most 2^-30 of that state
@@ -135,6 +136,13 @@ int lightning_attn_fwd_bf16_f32out(const void* q, const void* k, const void* v, 
  *               default (lightning_attn_fwd_chunk); otherwise a positive
  *               multiple of block.  The result does not depend on it beyond
  *               rounding.
+ *   warm_chunk: tokens per chunk of the warm-start pass (bf16 inputs, block
+ *               64): which heads decay within a chunk is judged against it,
+ *               and those heads are computed chunk by chunk at this length;
+ *               0 picks the default (lightning_attn_fwd_warm_chunk: with
+ *               chunk 0, up to four times the default chunk; with an
+ *               explicit chunk, that chunk); otherwise a multiple of 64, at
+ *               least the scan's chunk.  Ignored by the other paths.
  *   flags     : 0, or LA_FLAG_EXACT and/or LA_FLAG_SILU_QKV
  *   workspace : device scratch of at least lightning_attn_fwd_workspace_bytes()
  *               bytes, 256-byte aligned, owned by the caller and not used
@@ -148,8 +156,9 @@ int lightning_attn_fwd_bf16_f32out(const void* q, const void* k, const void* v, 
  */
 int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const float* decay, void* out,
                           const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
-                          int64_t block, int in_dtype, int out_dtype, int64_t chunk, unsigned int flags,
-                          void* workspace, size_t workspace_bytes, void* evt_begin, void* evt_end, void* stream);
+                          int64_t block, int in_dtype, int out_dtype, int64_t chunk, int64_t warm_chunk,
+                          unsigned int flags, void* workspace, size_t workspace_bytes, void* evt_begin, void* evt_end,
+                          void* stream);
 
 /*
  * Prefill into a pool of states (serving: chunked prefill of several
@@ -206,6 +215,17 @@ size_t lightning_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64
  * starts at 16384 tokens and halves while B*H*ceil(N/chunk) < 2048, down to
  * max(block, 256), then is capped at N rounded up to a whole block. */
 int64_t lightning_attn_fwd_chunk(int64_t B, int64_t H, int64_t N, int64_t block, int64_t chunk);
+
+/* Warm-start chunk the library uses for (B, H, N, block, chunk, warm_chunk)
+ * (see lightning_attn_fwd_ex); -1 on invalid arguments.  The default with
+ * chunk 0 doubles the default chunk, at most twice, while the warm-start pass
+ * keeps at least 1024 workgroups (B*H*ceil(N/warm_chunk) >= 1024) and the
+ * chunk fits in N rounded up to whole chunks: longer chunks let more heads
+ * take the warm start and shorten its warm-up windows relative to the chunk,
+ * while the exact path keeps the shorter chunks.  The pooled prefill and the
+ * backward use the default. */
+int64_t lightning_attn_fwd_warm_chunk(int64_t B, int64_t H, int64_t N, int64_t block, int64_t chunk,
+                                      int64_t warm_chunk);
 
 /* Bytes of scratch lightning_attn_fwd_ex needs for these sizes (0 on invalid
  * arguments).  Layout: the decay-power table, then B*H*ceil(N/chunk) float32

@@ -35,6 +35,7 @@ __all__ = [
     "workspace_bytes",
     "lib_bwd_workspace_bytes",
     "chunk_for",
+    "warm_chunk_for",
     "runtime_version",
 ]
 
@@ -73,9 +74,11 @@ def load():
         fn.restype = I
         fn.argtypes = fwd_args + [P]
     lib.lightning_attn_fwd_ex.restype = I
-    lib.lightning_attn_fwd_ex.argtypes = fwd_args + [I, I, I64, ctypes.c_uint, P, SZ, P, P, P]
+    lib.lightning_attn_fwd_ex.argtypes = fwd_args + [I, I, I64, I64, ctypes.c_uint, P, SZ, P, P, P]
     lib.lightning_attn_fwd_chunk.restype = I64
     lib.lightning_attn_fwd_chunk.argtypes = [I64, I64, I64, I64, I64]
+    lib.lightning_attn_fwd_warm_chunk.restype = I64
+    lib.lightning_attn_fwd_warm_chunk.argtypes = [I64, I64, I64, I64, I64, I64]
     lib.lightning_attn_fwd_workspace_bytes.restype = SZ
     lib.lightning_attn_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64]
     lib.lightning_attn_decode_step.restype = I
@@ -137,6 +140,11 @@ def chunk_for(B, H, N, block=64, chunk=0):
     return int(load().lightning_attn_fwd_chunk(B, H, N, block, chunk))
 
 
+def warm_chunk_for(B, H, N, block=64, chunk=0, warm_chunk=0):
+    """Warm-start chunk length the library uses (0s: its defaults)."""
+    return int(load().lightning_attn_fwd_warm_chunk(B, H, N, block, chunk, warm_chunk))
+
+
 def lib_bwd_workspace_bytes(B, H, N, d):
     return int(load().lightning_attn_bwd_workspace_bytes(B, H, N, d))
 
@@ -150,7 +158,7 @@ def _fwd_flags(exact, silu):
 
 
 def fwd(q, k, v, decay, kv_in=None, kv_out=None, block=64, out=None, out_dtype=None, chunk=0,
-        workspace=None, events=None, exact=False, silu=False, stream=None):
+        workspace=None, events=None, exact=False, silu=False, warm_chunk=0, stream=None):
     """Prefill.  q, k, v: [B, H, N, d] bf16 or fp32 device tensors; decay: fp32 [H];
     kv_in / kv_out: fp32 [B, H, d, d] or None.  Returns out [B, H, N, d] in
     out_dtype (default: the input dtype).
@@ -160,7 +168,9 @@ def fwd(q, k, v, decay, kv_in=None, kv_out=None, block=64, out=None, out_dtype=N
     of hipEvent_t handles (ints) recorded around the kernel that writes every
     output row.  exact: every head by the exact chunked path (no warm start).
     silu: q, k, v are pre-activations; SiLU is applied inside the kernels as
-    their tiles load (bf16, block 64), q, k, v themselves are not changed."""
+    their tiles load (bf16, block 64), q, k, v themselves are not changed.
+    warm_chunk: chunk of the warm-start pass (0: the library's default,
+    warm_chunk_for)."""
     lib = load()
     if q.dtype not in _DT:
         raise TypeError("q must be bfloat16 or float32")
@@ -186,7 +196,7 @@ def fwd(q, k, v, decay, kv_in=None, kv_out=None, block=64, out=None, out_dtype=N
     e0, e1 = (None, None) if events is None else (ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
     rc = lib.lightning_attn_fwd_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(kv_in), _ptr(kv_out),
-        B, H, N, d, block, _DT[q.dtype], _DT[odt], chunk, _fwd_flags(exact, silu),
+        B, H, N, d, block, _DT[q.dtype], _DT[odt], chunk, warm_chunk, _fwd_flags(exact, silu),
         _ptr(workspace), workspace.numel(), e0, e1, _stream(stream),
     )
     if rc != 0:

@@ -66,6 +66,19 @@ int64_t pick_chunk(int64_t B, int64_t H, int64_t N, int64_t block) {
   return L;
 }
 
+// Default warm-start chunk: the scan's chunk L doubled up to twice (4L) while
+// the warm-start pass keeps at least 1024 workgroups (two rounds at two per
+// CU) and the chunk stays within the sequence.  Longer chunks let more heads
+// take the warm start (a carry span up to a third of the chunk) and shorten
+// its warm-up windows relative to the chunk, while the heads on the exact
+// path keep the shorter chunks and the workgroups they need.
+int64_t pick_warm_chunk(int64_t B, int64_t H, int64_t N, int64_t L) {
+  int64_t Lw = L;
+  const int64_t cap = ceil_div(N, L) * L;
+  while (Lw < 4 * L && 2 * Lw <= kMaxTokens && 2 * Lw <= cap && B * H * ceil_div(N, 2 * Lw) >= 1024) Lw *= 2;
+  return Lw;
+}
+
 int resolve_chunk(int64_t B, int64_t H, int64_t N, int64_t block, int64_t chunk, int64_t* L) {
   if (B < 1 || H < 1 || N < 1 || !valid_block(block)) return LA_ERR_INVALID;
   if (chunk == 0) {
@@ -74,6 +87,20 @@ int resolve_chunk(int64_t B, int64_t H, int64_t N, int64_t block, int64_t chunk,
     if (chunk < 0 || chunk % block != 0 || chunk > kMaxTokens) return LA_ERR_INVALID;
     *L = chunk;
   }
+  return LA_OK;
+}
+
+// The warm-start chunk for (chunk, warm_chunk): 0 takes the default (with
+// chunk 0, pick_warm_chunk; with an explicit chunk, that chunk); otherwise a
+// positive multiple of 64 (the warm-start kernels' block), at least L.
+int resolve_warm_chunk(int64_t B, int64_t H, int64_t N, int64_t chunk, int64_t warm_chunk, int64_t L,
+                       int64_t* Lw) {
+  if (warm_chunk == 0) {
+    *Lw = chunk == 0 ? pick_warm_chunk(B, H, N, L) : L;
+    return LA_OK;
+  }
+  if (warm_chunk < L || warm_chunk % 64 != 0 || warm_chunk > kMaxTokens) return LA_ERR_INVALID;
+  *Lw = warm_chunk;
   return LA_OK;
 }
 
@@ -134,8 +161,8 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 int prefill_run(const void* q, const void* k, const void* v, const float* decay, void* out, const float* kv_in,
                 float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, int in_dtype,
-                int out_dtype, int64_t L, void* workspace, size_t workspace_bytes, void* evt_begin, void* evt_end,
-                void* stream, const int* slots, int64_t num_slots, unsigned int flags);
+                int out_dtype, int64_t L, int64_t Lw, void* workspace, size_t workspace_bytes, void* evt_begin,
+                void* evt_end, void* stream, const int* slots, int64_t num_slots, unsigned int flags);
 
 constexpr unsigned int kFwdFlags = LA_FLAG_EXACT | LA_FLAG_SILU_QKV;
 
@@ -150,14 +177,17 @@ extern "C" {
 
 int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const float* decay, void* out,
                           const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
-                          int64_t block, int in_dtype, int out_dtype, int64_t chunk, unsigned int flags,
-                          void* workspace, size_t workspace_bytes, void* evt_begin, void* evt_end, void* stream) {
+                          int64_t block, int in_dtype, int out_dtype, int64_t chunk, int64_t warm_chunk,
+                          unsigned int flags, void* workspace, size_t workspace_bytes, void* evt_begin, void* evt_end,
+                          void* stream) {
   if (flags & ~kFwdFlags) return LA_ERR_INVALID;
-  int64_t L = 0;
+  int64_t L = 0, Lw = 0;
   int rc = validate_prefill(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, in_dtype, out_dtype, chunk, &L);
   if (rc != LA_OK) return rc;
+  rc = resolve_warm_chunk(B, H, N, chunk, warm_chunk, L, &Lw);
+  if (rc != LA_OK) return rc;
   if (!flags_supported(flags, in_dtype, block)) return LA_ERR_UNSUPPORTED;
-  return prefill_run(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, in_dtype, out_dtype, L, workspace,
+  return prefill_run(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, in_dtype, out_dtype, L, Lw, workspace,
                      workspace_bytes, evt_begin, evt_end, stream, nullptr, 0, flags);
 }
 
@@ -181,8 +211,9 @@ int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const 
       overlap(states, pool_bytes, v, in_bytes) || overlap(states, pool_bytes, out, out_bytes) ||
       overlap(states, pool_bytes, slots, B * 4) || overlap(out, out_bytes, slots, B * 4))
     return LA_ERR_INVALID;
-  return prefill_run(q, k, v, decay, out, states, states, B, H, N, d, block, in_dtype, out_dtype, L, nullptr, 0,
-                     nullptr, nullptr, stream, (const int*)slots, num_slots, flags);
+  return prefill_run(q, k, v, decay, out, states, states, B, H, N, d, block, in_dtype, out_dtype, L,
+                     pick_warm_chunk(B, H, N, L), nullptr, 0, nullptr, nullptr, stream, (const int*)slots, num_slots,
+                     flags);
 }
 
 }  // extern "C"
@@ -191,8 +222,8 @@ namespace {
 
 int prefill_run(const void* q, const void* k, const void* v, const float* decay, void* out, const float* kv_in,
                 float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, int in_dtype,
-                int out_dtype, int64_t L, void* workspace, size_t workspace_bytes, void* evt_begin, void* evt_end,
-                void* stream, const int* slots, int64_t num_slots, unsigned int flags) {
+                int out_dtype, int64_t L, int64_t Lw, void* workspace, size_t workspace_bytes, void* evt_begin,
+                void* evt_end, void* stream, const int* slots, int64_t num_slots, unsigned int flags) {
   const bool exact = (flags & LA_FLAG_EXACT) != 0;
   size_t tbl_bytes = 0;
   const size_t need = workspace_layout(B, H, N, d, block, L, &tbl_bytes);
@@ -222,6 +253,8 @@ int prefill_run(const void* q, const void* k, const void* v, const float* decay,
   a.block = block;
   a.L = L;
   a.nc = (int)ceil_div(N, L);
+  a.L_warm = Lw;
+  a.nc_warm = (int)ceil_div(N, Lw);
   a.in_dtype = in_dtype == LA_DTYPE_BF16 ? la::kBF16 : la::kF32;
   a.out_dtype = out_dtype == LA_DTYPE_BF16 ? la::kBF16 : la::kF32;
   a.tbl = (float*)ws;
@@ -251,21 +284,21 @@ int lightning_attn_fwd(const void* q, const void* k, const void* v, const float*
                        const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
                        int64_t block, void* stream) {
   return lightning_attn_fwd_ex(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, LA_DTYPE_BF16,
-                               LA_DTYPE_BF16, 0, 0u, nullptr, 0, nullptr, nullptr, stream);
+                               LA_DTYPE_BF16, 0, 0, 0u, nullptr, 0, nullptr, nullptr, stream);
 }
 
 int lightning_attn_fwd_f32(const void* q, const void* k, const void* v, const float* decay, void* out,
                            const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
                            int64_t block, void* stream) {
   return lightning_attn_fwd_ex(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, LA_DTYPE_F32,
-                               LA_DTYPE_F32, 0, 0u, nullptr, 0, nullptr, nullptr, stream);
+                               LA_DTYPE_F32, 0, 0, 0u, nullptr, 0, nullptr, nullptr, stream);
 }
 
 int lightning_attn_fwd_bf16_f32out(const void* q, const void* k, const void* v, const float* decay,
                                    void* out, const float* kv_in, float* kv_out, int64_t B, int64_t H,
                                    int64_t N, int64_t d, int64_t block, void* stream) {
   return lightning_attn_fwd_ex(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, LA_DTYPE_BF16,
-                               LA_DTYPE_F32, 0, 0u, nullptr, 0, nullptr, nullptr, stream);
+                               LA_DTYPE_F32, 0, 0, 0u, nullptr, 0, nullptr, nullptr, stream);
 }
 
 // Backward workspace: the forward layout (decay table, chunk states of the
@@ -356,6 +389,8 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
   a.block = 64;
   a.L = L;
   a.nc = (int)ceil_div(N, L);
+  a.L_warm = pick_warm_chunk(B, H, N, L);
+  a.nc_warm = (int)ceil_div(N, a.L_warm);
   a.in_dtype = in_dtype == LA_DTYPE_BF16 ? la::kBF16 : la::kF32;
   a.out_dtype = out_dtype == LA_DTYPE_BF16 ? la::kBF16 : la::kF32;
   a.tbl = (float*)ws;
@@ -427,6 +462,14 @@ int64_t lightning_attn_fwd_chunk(int64_t B, int64_t H, int64_t N, int64_t block,
   int64_t L = 0;
   if (resolve_chunk(B, H, N, block, chunk, &L) != LA_OK) return -1;
   return L;
+}
+
+int64_t lightning_attn_fwd_warm_chunk(int64_t B, int64_t H, int64_t N, int64_t block, int64_t chunk,
+                                      int64_t warm_chunk) {
+  int64_t L = 0, Lw = 0;
+  if (resolve_chunk(B, H, N, block, chunk, &L) != LA_OK) return -1;
+  if (resolve_warm_chunk(B, H, N, chunk, warm_chunk, L, &Lw) != LA_OK) return -1;
+  return Lw;
 }
 
 size_t lightning_attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,

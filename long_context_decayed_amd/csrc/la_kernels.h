@@ -18,6 +18,8 @@ struct PrefillArgs {
   float* kv_out;
   int64_t B, H, N, d, block, L;
   int nc;          // number of chunks, ceil(N / L)
+  int64_t L_warm;  // chunk of the warm-start pass (>= L); which heads decay within a chunk is judged by it
+  int nc_warm;     // ceil(N / L_warm)
   int in_dtype, out_dtype;
   float* tbl;      // workspace: [H][tbl_stride] decay powers
   int tbl_stride;  // >= block + 1

@@ -317,6 +317,11 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 //   kFromStart  the chunk from its true start state Sstart_c (read from
 //               `states` after the scan), for the other heads; decaying heads
 //               return at once.
+// Which heads decay is judged against Lw, the warm-start chunk, in every
+// kernel alike.  The warm-start pass chunks by Lw (L = Lw, nc = its chunk
+// count), the other passes by the scan's chunk; `states` holds nc_ws slots
+// per head (the scan's chunks) and the warm-start pass leaves each final
+// state in the last of them.
 // REV: the reverse-time passes of the backward.  Token t of the pass is row
 // N-1-t of the tensors (rows are read and written last first), and the
 // initial state enters the first token undecayed: S_0 = kv_in + k_0^T v_0,
@@ -350,7 +355,8 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
                                                               const float* __restrict__ decay,
                                                               const float* __restrict__ tbl_all, int H, int N, int L,
                                                               int nc, int tbl_stride, const int* __restrict__ slots,
-                                                              int64_t num_slots, int warm, int nblk, int pair_shift) {
+                                                              int64_t num_slots, int warm, int nblk, int pair_shift,
+                                                              int Lw, int nc_ws) {
   typedef Mfma<bf16> M;
   typedef M::op_t op_t;
   constexpr int NW = D / 32;
@@ -383,7 +389,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
   const int bh = blk / nc, c = blk - (blk / nc) * nc;
   const int hh = bh % H;
   const int span = carry_span(decay[hh]);
-  const bool decaying = warm && decays_within_chunk(span, L);  // warm = 0: every head from its start state
+  const bool decaying = warm && decays_within_chunk(span, Lw);  // warm = 0: every head from its start state
   if (decaying != (MODE == kWarmStart)) return;
   const int t_begin = c * L;
   const int t_end = min(N, t_begin + L);
@@ -444,7 +450,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
   //   pf(crow(j, h)) = 16(j >> 3) + 8h + 4((j >> 2) & 1) + (j & 3).
   f32x16 S[NRT];
   const int64_t srow = (MODE == kWarmStart && c == 0 && kv_in != nullptr) ? state_row(bh, H, slots, num_slots) : -1;
-  const float* s_src = MODE == kFromStart ? states + ((int64_t)bh * nc + c) * D * D
+  const float* s_src = MODE == kFromStart ? states + ((int64_t)bh * nc_ws + c) * D * D
                                           : (srow >= 0 ? kv_in + srow * D * D : nullptr);
   if (s_src) {
 #pragma unroll
@@ -782,7 +788,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
     // slot.  The lane's column and half are taken from the hardware lane id
     // here, so that they need not stay live (or spilled) across the loop.
     const int ln = __lane_id(), lh = ln >> 5;
-    float* dst = states + ((int64_t)bh * nc + c) * D * D + 32 * w + (ln & 31);
+    float* dst = states + ((int64_t)bh * nc_ws + nc_ws - 1) * D * D + 32 * w + (ln & 31);
 #pragma unroll
     for (int kt = 0; kt < NRT; ++kt)
 #pragma unroll
@@ -805,23 +811,26 @@ static Operands operands_of(const PrefillArgs& a) {
 // flags, decays and table are a's).
 template <typename TOut, int D, int MODE>
 static void launch_fast(const PrefillArgs& a, hipStream_t st, const PrefillArgs* b = nullptr) {
-  const int nblk = (int)(a.B * a.H * a.nc);
+  // the warm-start pass chunks by the warm chunk, the others by the scan's
+  const int ncm = MODE == kWarmStart ? a.nc_warm : a.nc;
+  const int Lm = (int)(MODE == kWarmStart ? a.L_warm : a.L);
+  const int nblk = (int)(a.B * a.H * ncm);
   const int shift = b ? kPairShift : -1;
   const int64_t half = int64_t(1) << kPairShift;  // workgroups of one problem per group of the pair
   const unsigned grid = b ? (unsigned)((nblk + half - 1) / half * 2 * half) : (unsigned)nblk;
   const Operands p0 = operands_of(a), p1 = b ? operands_of(*b) : p0;
   if (a.rev)  // the backward: no SiLU
     hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, true, false>), dim3(grid), dim3(D * 2), 0, st, p0, p1,
-                       a.decay, (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots,
-                       a.num_slots, a.warm_start ? 1 : 0, nblk, shift);
+                       a.decay, (const float*)a.tbl, (int)a.H, (int)a.N, Lm, ncm, a.tbl_stride, a.slots,
+                       a.num_slots, a.warm_start ? 1 : 0, nblk, shift, (int)a.L_warm, a.nc);
   else if (a.silu)
     hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, false, true>), dim3(grid), dim3(D * 2), 0, st, p0, p1,
-                       a.decay, (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots,
-                       a.num_slots, a.warm_start ? 1 : 0, nblk, shift);
+                       a.decay, (const float*)a.tbl, (int)a.H, (int)a.N, Lm, ncm, a.tbl_stride, a.slots,
+                       a.num_slots, a.warm_start ? 1 : 0, nblk, shift, (int)a.L_warm, a.nc);
   else
     hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, false, false>), dim3(grid), dim3(D * 2), 0, st, p0, p1,
-                       a.decay, (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc, a.tbl_stride, a.slots,
-                       a.num_slots, a.warm_start ? 1 : 0, nblk, shift);
+                       a.decay, (const float*)a.tbl, (int)a.H, (int)a.N, Lm, ncm, a.tbl_stride, a.slots,
+                       a.num_slots, a.warm_start ? 1 : 0, nblk, shift, (int)a.L_warm, a.nc);
 }
 
 template <typename TIn, typename TOut, int D, int BLK>
@@ -889,7 +898,7 @@ template <int MODE>
 static hipError_t launch_pair_mode(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st) {
   if (a.in_dtype != kBF16 || b.in_dtype != kBF16 || a.block != 64 || b.block != 64 || a.B != b.B || a.H != b.H ||
       a.N != b.N || a.nc != b.nc || a.d != b.d || a.out_dtype != b.out_dtype || a.rev != b.rev ||
-      a.warm_start != b.warm_start || a.silu != b.silu)
+      a.warm_start != b.warm_start || a.silu != b.silu || a.L != b.L || a.L_warm != b.L_warm)
     return hipErrorInvalidValue;
   if (MODE == kWarmStart && !a.warm_start) return hipErrorInvalidValue;
   if (a.out_dtype == kBF16) {

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
                                                              const float* __restrict__ decay,
                                                              const float* __restrict__ tbl_all, float* __restrict__ ws,
                                                              int H, int N, int L, int nc, int tbl_stride,
-                                                             int skip_decaying) {
+                                                             int skip_decaying, int Lw) {
   typedef Mfma<bf16> M;
   typedef M::op_t op_t;
   constexpr int NW = D / 32;
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
   const int hh = bh % H;
-  if (skip_decaying && decays_within_chunk(carry_span(decay[hh]), L)) return;
+  if (skip_decaying && decays_within_chunk(carry_span(decay[hh]), Lw)) return;  // judged by the warm chunk
   constexpr int RS = REV ? -D : D;  // elements from one token's row to the next
   const int64_t base = (int64_t)bh * N * D + (REV ? (int64_t)(N - 1) * D : 0);
   const bf16* kb = k + base;
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ d
                                                      const float* __restrict__ kv_in, float* __restrict__ kv_out,
                                                      int BH, int H, int N, int L, int nc, int D, int warm,
                                                      int undecayed, int scale_out, const int* __restrict__ slots,
-                                                     int64_t num_slots) {
+                                                     int64_t num_slots, int Lw) {
   const int per = D * D / 4;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)BH * per) return;
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ d
     kv_out = nullptr;
   }
   const float out_f = scale_out ? decay[bh % H] : 1.0f;
-  if (warm && decays_within_chunk(carry_span(decay[bh % H]), L)) {
+  if (warm && decays_within_chunk(carry_span(decay[bh % H]), Lw)) {  // judged by the warm chunk
     if (kv_out)
       reinterpret_cast<f32x4*>(kv_out)[srow * per + e4] =
           out_f * reinterpret_cast<const f32x4*>(ws)[((int64_t)bh * nc + nc - 1) * per + e4];
@@ -355,15 +355,15 @@ static hipError_t launch_aggregate_t(const PrefillArgs& a, hipStream_t st) {
     if (a.rev)  // the backward: no SiLU
       hipLaunchKernelGGL((la_chunk_state64<D, true, false>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                          (const bf16*)a.k, (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H,
-                         (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0);
+                         (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0, (int)a.L_warm);
     else if (a.silu)
       hipLaunchKernelGGL((la_chunk_state64<D, false, true>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                          (const bf16*)a.k, (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H,
-                         (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0);
+                         (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0, (int)a.L_warm);
     else
       hipLaunchKernelGGL((la_chunk_state64<D, false, false>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                          (const bf16*)a.k, (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H,
-                         (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0);
+                         (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0, (int)a.L_warm);
   } else if (a.silu) {
     return hipErrorInvalidValue;  // SiLU: bf16 inputs only
   } else if (a.rev)
@@ -389,7 +389,7 @@ hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st) {
   const int64_t threads = (int64_t)BH * D * D / 4;
   hipLaunchKernelGGL(la_chunk_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a.decay, a.states,
                      a.kv_in, a.kv_out, BH, (int)a.H, (int)a.N, (int)a.L, a.nc, D, a.warm_start ? 1 : 0,
-                     a.rev ? 1 : 0, a.scale_kv_out ? 1 : 0, a.slots, a.num_slots);
+                     a.rev ? 1 : 0, a.scale_kv_out ? 1 : 0, a.slots, a.num_slots, (int)a.L_warm);
   return hipGetLastError();
 }
 

@@ -54,9 +54,9 @@ def test_library_is_gfx950_only(lib):
 
 
 def _fwd(lib, q=FAKE[0], k=FAKE[1], v=FAKE[2], decay=FAKE[3], out=FAKE[4], kv_in=None, kv_out=None,
-         B=1, H=2, N=128, d=64, block=64, ind=0, outd=0, chunk=0, ws=None, wsb=0, flags=0):
+         B=1, H=2, N=128, d=64, block=64, ind=0, outd=0, chunk=0, ws=None, wsb=0, flags=0, warm_chunk=0):
     return lib.lightning_attn_fwd_ex(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, ind, outd, chunk,
-                                     flags, ws, wsb, None, None, None)
+                                     warm_chunk, flags, ws, wsb, None, None, None)
 
 
 def test_null_pointers_rejected(lib):
@@ -300,3 +300,22 @@ def test_partially_overlapping_states_rejected(lib):
     dec = lib.lightning_attn_decode_step
     assert dec(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], shifted["kv_in"], shifted["kv_out"], 1, 2, 64,
                None) == LA_ERR_INVALID
+
+
+def test_warm_chunk_rules(lib):
+    """The warm-start chunk: default up to four times the scan's default chunk
+    while at least 1024 workgroups remain; an explicit chunk sets both unless
+    warm_chunk is given; an explicit warm_chunk is a multiple of 64 and at
+    least the scan's chunk."""
+    wc = lib.lightning_attn_fwd_warm_chunk
+    assert lib.lightning_attn_fwd_chunk(1, 64, 1 << 20, 64, 0) == 16384
+    assert wc(1, 64, 1 << 20, 64, 0, 0) == 65536          # 16 chunks x 64 heads = 1024 workgroups
+    assert wc(1, 32, 1 << 20, 64, 0, 0) == 32768          # 32 x 32 = 1024
+    assert wc(4, 64, 1 << 16, 64, 0, 0) == 16384          # chunk 8192 for >= 2048; 4 x 64 x 4 = 1024
+    assert wc(1, 8, 3000, 64, 0, 0) == 256                # too few workgroups to grow
+    assert wc(1, 64, 1 << 20, 64, 4096, 0) == 4096        # an explicit chunk sets both
+    assert wc(1, 64, 1 << 20, 64, 4096, 32768) == 32768
+    assert wc(1, 64, 1 << 20, 64, 4096, 2048) == -1       # shorter than the scan's chunk
+    assert wc(1, 64, 1 << 20, 64, 4096, 4100) == -1       # not a multiple of 64
+    assert _fwd(lib, chunk=256, warm_chunk=128) == LA_ERR_INVALID
+    assert _fwd(lib, chunk=256, warm_chunk=320, ws=FAKE[5], wsb=1) == LA_ERR_WORKSPACE

@@ -379,3 +379,32 @@ def test_exact_flag_matches_oracle_on_mixed_decays(dev):
     for h in range(8):
         tol.assert_bf16_f32out(host(o)[:, h], o_ref[:, h], "O head %d" % h)
         tol.assert_state(host(kv)[:, h], s_ref[:, h], "kv_out head %d" % h)
+
+
+# decays whose carry spans (64, 128, 256, 448, 704, 1408, 4160 tokens, then none)
+# put heads on either path as the warm-start chunk grows
+SPAN_LAMS = np.array([0.3, 0.85, 0.9, 0.95, 0.97, 0.985, 0.995, 1.0], dtype=np.float32)
+
+
+@pytest.mark.parametrize("warm_chunk", [512, 1024, 4096])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_bf16_warm_chunk_longer_than_scan_chunk(dev, warm_chunk, in_place):
+    """The warm-start pass on chunks of warm_chunk tokens, the other heads'
+    scan and output passes on chunks of 256: every kernel must judge the heads
+    alike and the warm-start pass must leave its final states where the scan
+    looks for them (also with kv_in = kv_out)."""
+    B, H, n, d = 2, 8, 5000, 128
+    say("bf16 scan chunk 256, warm-start chunk", warm_chunk, "B2 H8 N5000 d128, in place", in_place)
+    q, k, v = qkv_device(B, H, n, d, seed=80, device=dev)
+    s0 = state_device(B, H, d, seed=80, device=dev)
+    s_host = host(s0).astype(np.float64)
+    kv = s0 if in_place else torch.empty_like(s0)
+    out = la.fwd(q, k, v, torch.from_numpy(SPAN_LAMS).to(dev), kv_in=s0, kv_out=kv, block=64,
+                 out_dtype=torch.float32, chunk=256, warm_chunk=warm_chunk)
+    torch.cuda.synchronize()
+    assert la.warm_chunk_for(B, H, n, 64, 256, warm_chunk) == warm_chunk
+    o_ref, s_ref = oracle(host(q), host(k), host(v), SPAN_LAMS, s_host)
+    o_h, s_h = host(out), host(kv)
+    for h in range(H):
+        tol.assert_bf16_f32out(o_h[:, h], o_ref[:, h], "O head %d (lam %g)" % (h, SPAN_LAMS[h]))
+        tol.assert_state(s_h[:, h], s_ref[:, h], "kv head %d (lam %g)" % (h, SPAN_LAMS[h]))
