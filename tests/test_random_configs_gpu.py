@@ -200,3 +200,40 @@ def test_random_decode(dev, i):
     assert np.all(host(o)[idle] == 0.0)
     untouched = [s for s in range(P) if s not in set(sl.tolist())]
     assert np.array_equal(pool1[untouched], pool0[untouched])
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_prefill_warm_chunk_and_silu(dev, i):
+    """bf16, block 64: random scan and warm-start chunk lengths, SiLU on the
+    tiles or not, against the oracle (fed the bf16-rounded fp64 SiLU when on)."""
+    import oracle as ora
+    rng = np.random.default_rng(11000 + i)
+    B, H, N, d = int(rng.integers(1, 3)), int(rng.integers(1, 7)), int(rng.integers(1, 4000)), int(rng.choice([64, 128]))
+    chunk = int(rng.choice([0, 64, 128, 256, 512]))
+    warm_chunk = 0 if chunk == 0 or rng.integers(0, 3) == 0 else chunk * int(rng.choice([1, 2, 4, 8]))
+    silu, state, exact = bool(rng.integers(0, 2)), bool(rng.integers(0, 2)), bool(rng.integers(0, 5) == 0)
+    odt = torch.float32 if rng.integers(0, 2) else torch.bfloat16
+    lam = _decays(rng, H)
+    say("random prefill, chunks and SiLU", i, dict(B=B, H=H, N=N, d=d, chunk=chunk, warm_chunk=warm_chunk, silu=silu,
+                                                   state=state, exact=exact, out=str(odt)),
+        "lam", np.round(lam, 5).tolist())
+    scale = 2.5 if silu else 1.0
+    q, k, v = (t * scale for t in qkv_device(B, H, N, d, seed=12000 + i, device=dev))
+    q, k, v = (t.contiguous() for t in (q, k, v))
+    s0 = state_device(B, H, d, seed=12000 + i, device=dev) if state else None
+    kv = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    o = la.fwd(q, k, v, torch.from_numpy(lam).to(dev), kv_in=s0, kv_out=kv, block=64, chunk=chunk,
+               warm_chunk=warm_chunk, out_dtype=odt, exact=exact, silu=silu)
+    torch.cuda.synchronize()
+    if silu:
+        ins = [torch.from_numpy(ora.silu(host(t))).to(torch.bfloat16).to(torch.float32).numpy() for t in (q, k, v)]
+    else:
+        ins = [host(t) for t in (q, k, v)]
+    o_ref, s_ref = oracle(*ins, lam, None if s0 is None else host(s0).astype(np.float64))
+    o_h, kv_h = host(o), host(kv)
+    for h in range(H):
+        if odt == torch.float32:
+            tol.assert_bf16_f32out(o_h[:, h], o_ref[:, h], "O head %d" % h)
+        else:
+            tol.assert_bf16_out(o_h[:, h], o_ref[:, h], "O head %d" % h)
+        tol.assert_state(kv_h[:, h], s_ref[:, h], "kv head %d" % h)
