@@ -150,7 +150,11 @@ struct Mfma<bf16> {
   }
   // x ~= hi + lo: hi = x truncated to bf16 (its top 16 bits), lo = RNE(x - hi).
   // x - hi is exact in fp32 and |x - hi| < 2^-7 |x|, so |x - hi - lo| < 2^-16 |x|.
+  // No contraction: were the product that forms x fused into x - hi, lo would
+  // depend on the compiler's choice per instantiation, and the fp32- and
+  // bf16-output kernels would no longer agree bit for bit.
   static __device__ __forceinline__ void split(const float* x, op_t& hi, op_t& lo) {
+#pragma clang fp contract(off)
     uint32_t h[4], l[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -41,11 +41,16 @@ hipError_t launch_aggregate_pass(const PrefillArgs& a, hipStream_t st);
 // final state); only with warm_start: la_output.hip.
 hipError_t launch_warm_start_pass(const PrefillArgs& a, hipStream_t st);
 // Pass B (chunk scan: start states, final state; with warm_start, the
-// decaying heads' final states are only copied out): la_state.hip.
-hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st);
+// decaying heads' final states are only copied out); part 0 every head, 1 the
+// scan of the other heads only, 2 the decaying heads' copy only: la_state.hip.
+hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st, int part = 0);
 // Pass C (outputs from the chunk start states; with warm_start, of the
 // heads that do not decay within their chunk only): la_output.hip.
 hipError_t launch_output_pass(const PrefillArgs& a, hipStream_t st);
+// The warm-start pass and pass C in one launch (warm_start, forward only):
+// every output row, and the decaying heads' final states; after pass B of the
+// other heads.  Timing events bracket it: la_output.hip.
+hipError_t launch_mixed_pass(const PrefillArgs& a, hipStream_t st);
 
 // Two problems of one shape (bf16 inputs, block 64) in one grid, the two
 // workgroups of each (bh, chunk) side by side, so that tensors both read

@@ -350,13 +350,26 @@ struct Operands {
   const float* kv_in;  // initial states, or null
 };
 
+// LDS of one block-64 workgroup (80 KiB at d = 128).
+template <int D>
+struct Lds64 {
+  __attribute__((aligned(16))) bf16 Qs[kSub * D];
+  __attribute__((aligned(16))) bf16 Ks[kSub * D];  // score operands (phase 1)
+  __attribute__((aligned(16))) bf16 Kt[kSub * D];  // update operands (phase 2)
+  __attribute__((aligned(16))) bf16 Vs[kSub * D];
+  __attribute__((aligned(16))) Mfma<bf16>::op_t Pbuf[3][2][2][64];  // [tile][g][hi/lo][lane]
+  __attribute__((aligned(16))) f32x4 Dtab[4][64];                    // diagonal-tile factors [jq][lane]
+};
+
+// The workgroup body: chunk blk of the (bh, chunk) grid of problem pi, on the
+// LDS sm of the calling kernel.
 template <typename TOut, int D, int MODE, bool REV, bool SILU>
-__global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Operands p1,
-                                                              const float* __restrict__ decay,
-                                                              const float* __restrict__ tbl_all, int H, int N, int L,
-                                                              int nc, int tbl_stride, const int* __restrict__ slots,
-                                                              int64_t num_slots, int warm, int nblk, int pair_shift,
-                                                              int Lw, int nc_ws) {
+__device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt, bf16* Vs,
+                                                    Mfma<bf16>::op_t (*Pbuf)[2][2][64], f32x4 (*Dtab)[64], int blk,
+                                                    int pi, Operands p0, Operands p1, const float* __restrict__ decay,
+                                                    const float* __restrict__ tbl_all, int H, int N, int L, int nc,
+                                                    int tbl_stride, const int* __restrict__ slots, int64_t num_slots,
+                                                    int warm, int Lw, int nc_ws) {
   typedef Mfma<bf16> M;
   typedef M::op_t op_t;
   constexpr int NW = D / 32;
@@ -365,21 +378,9 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
   constexpr int kStores = sizeof(TOut) == 2 ? 2 * 2 : 2 * 4;  // output store instructions per sub-tile
   constexpr bool kDefer = sizeof(TOut) == 2;  // bf16 rows are stored during the next sub-tile's phase 1
   constexpr int RS = REV ? -D : D;             // elements from one token's row to the next
-  __shared__ __attribute__((aligned(16))) bf16 Qs[kSub * D];
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kSub * D];  // score operands (phase 1)
-  __shared__ __attribute__((aligned(16))) bf16 Kt[kSub * D];  // update operands (phase 2)
-  __shared__ __attribute__((aligned(16))) bf16 Vs[kSub * D];
-  __shared__ __attribute__((aligned(16))) op_t Pbuf[3][2][2][64];  // [tile][g][hi/lo][lane]
-  __shared__ __attribute__((aligned(16))) f32x4 Dtab[4][64];        // diagonal-tile factors [jq][lane]
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  int blk = blockIdx.x, pi = 0;
-  if (pair_shift >= 0) {
-    pi = (blk >> pair_shift) & 1;
-    blk = ((blk >> (pair_shift + 1)) << pair_shift) | (blk & ((1 << pair_shift) - 1));
-    if (blk >= nblk) return;  // padding of the last group
-  }
   const bf16* __restrict__ q = pi ? p1.q : p0.q;
   const bf16* __restrict__ k = pi ? p1.k : p0.k;
   const bf16* __restrict__ v = pi ? p1.v : p0.v;
@@ -797,6 +798,58 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
   }
 }
 
+// One problem, or two in one grid (pair_shift >= 0, see above).
+template <typename TOut, int D, int MODE, bool REV, bool SILU>
+__global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Operands p1,
+                                                              const float* __restrict__ decay,
+                                                              const float* __restrict__ tbl_all, int H, int N, int L,
+                                                              int nc, int tbl_stride, const int* __restrict__ slots,
+                                                              int64_t num_slots, int warm, int nblk, int pair_shift,
+                                                              int Lw, int nc_ws) {
+  __shared__ __attribute__((aligned(16))) bf16 Qs[kSub * D];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kSub * D];  // score operands (phase 1)
+  __shared__ __attribute__((aligned(16))) bf16 Kt[kSub * D];  // update operands (phase 2)
+  __shared__ __attribute__((aligned(16))) bf16 Vs[kSub * D];
+  __shared__ __attribute__((aligned(16))) Mfma<bf16>::op_t Pbuf[3][2][2][64];  // [tile][g][hi/lo][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 Dtab[4][64];                    // diagonal-tile factors [jq][lane]
+  int blk = blockIdx.x, pi = 0;
+  if (pair_shift >= 0) {
+    pi = (blk >> pair_shift) & 1;
+    blk = ((blk >> (pair_shift + 1)) << pair_shift) | (blk & ((1 << pair_shift) - 1));
+    if (blk >= nblk) return;  // padding of the last group
+  }
+  chunk_output64_body<TOut, D, MODE, REV, SILU>(Qs, Ks, Kt, Vs, Pbuf, Dtab, blk, pi, p0, p1, decay, tbl_all, H, N, L, nc, tbl_stride, slots,
+                                                num_slots, warm, Lw, nc_ws);
+}
+
+// The warm-start pass and the other heads' output pass (pass C) in one grid:
+// workgroups [0, n_warm) take the warm-start pass's chunks (Lw tokens), the
+// rest pass C's (L tokens, from the scanned start states); each returns at
+// once for a head of the other kind.  One launch lets the few workgroups of a
+// layer's non-decaying heads fill the rounds the warm-start pass leaves
+// partly empty, and the other way round.
+template <typename TOut, int D, bool SILU>
+__global__ __launch_bounds__(D * 2, 2) void la_chunk_output64_mixed(Operands p0, const float* __restrict__ decay,
+                                                                    const float* __restrict__ tbl_all, int H, int N,
+                                                                    int L, int nc, int Lw, int ncw, int tbl_stride,
+                                                                    const int* __restrict__ slots, int64_t num_slots,
+                                                                    int n_warm) {
+  __shared__ __attribute__((aligned(16))) bf16 Qs[kSub * D];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kSub * D];
+  __shared__ __attribute__((aligned(16))) bf16 Kt[kSub * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[kSub * D];
+  __shared__ __attribute__((aligned(16))) Mfma<bf16>::op_t Pbuf[3][2][2][64];
+  __shared__ __attribute__((aligned(16))) f32x4 Dtab[4][64];
+  const int b = blockIdx.x;
+  if (b < n_warm)
+    chunk_output64_body<TOut, D, kWarmStart, false, SILU>(Qs, Ks, Kt, Vs, Pbuf, Dtab, b, 0, p0, p0, decay, tbl_all, H,
+                                                          N, Lw, ncw, tbl_stride, slots, num_slots, 1, Lw, nc);
+  else
+    chunk_output64_body<TOut, D, kFromStart, false, SILU>(Qs, Ks, Kt, Vs, Pbuf, Dtab, b - n_warm, 0, p0, p0, decay,
+                                                          tbl_all, H, N, L, nc, tbl_stride, slots, num_slots, 1, Lw,
+                                                          nc);
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launcher: the output pass on `st`, bracketed by the optional
 // timing events.
@@ -876,6 +929,36 @@ static hipError_t launch_warm_start_t(const PrefillArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   return hipGetLastError();
+}
+
+template <typename TOut, int D>
+static hipError_t launch_mixed_t(const PrefillArgs& a, hipStream_t st) {
+  if (a.evt_begin) {
+    hipError_t e = hipEventRecord((hipEvent_t)a.evt_begin, st);
+    if (e != hipSuccess) return e;
+  }
+  const int n_warm = (int)(a.B * a.H * a.nc_warm);
+  const unsigned grid = (unsigned)(n_warm + a.B * a.H * a.nc);
+  const Operands p0 = operands_of(a);
+  if (a.silu)
+    hipLaunchKernelGGL((la_chunk_output64_mixed<TOut, D, true>), dim3(grid), dim3(D * 2), 0, st, p0, a.decay,
+                       (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc, (int)a.L_warm, a.nc_warm,
+                       a.tbl_stride, a.slots, a.num_slots, n_warm);
+  else
+    hipLaunchKernelGGL((la_chunk_output64_mixed<TOut, D, false>), dim3(grid), dim3(D * 2), 0, st, p0, a.decay,
+                       (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc, (int)a.L_warm, a.nc_warm,
+                       a.tbl_stride, a.slots, a.num_slots, n_warm);
+  if (a.evt_end) {
+    hipError_t e = hipEventRecord((hipEvent_t)a.evt_end, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mixed_pass(const PrefillArgs& a, hipStream_t st) {
+  if (!a.warm_start || a.rev || a.in_dtype != kBF16 || a.block != 64) return hipErrorInvalidValue;
+  if (a.out_dtype == kBF16) return a.d == 128 ? launch_mixed_t<bf16, 128>(a, st) : launch_mixed_t<bf16, 64>(a, st);
+  return a.d == 128 ? launch_mixed_t<float, 128>(a, st) : launch_mixed_t<float, 64>(a, st);
 }
 
 hipError_t launch_warm_start_pass(const PrefillArgs& a, hipStream_t st) {

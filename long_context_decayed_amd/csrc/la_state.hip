@@ -273,11 +273,13 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
 // With undecayed set, kv_in enters the first token without decay (chunk 0
 // hands on lam^(L_0 - 1) kv_in + U_0); with scale_out, kv_out receives lam
 // times the final state (the backward's gradient of the initial state).
+// part: 0 every head; 1 only the heads that do not decay within their chunk
+// (the scan proper); 2 only the decaying heads' copy (after their pass).
 __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ decay, float* __restrict__ ws,
                                                      const float* __restrict__ kv_in, float* __restrict__ kv_out,
                                                      int BH, int H, int N, int L, int nc, int D, int warm,
                                                      int undecayed, int scale_out, const int* __restrict__ slots,
-                                                     int64_t num_slots, int Lw) {
+                                                     int64_t num_slots, int Lw, int part) {
   const int per = D * D / 4;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)BH * per) return;
@@ -289,11 +291,12 @@ __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ d
   }
   const float out_f = scale_out ? decay[bh % H] : 1.0f;
   if (warm && decays_within_chunk(carry_span(decay[bh % H]), Lw)) {  // judged by the warm chunk
-    if (kv_out)
+    if (kv_out && part != 1)
       reinterpret_cast<f32x4*>(kv_out)[srow * per + e4] =
           out_f * reinterpret_cast<const f32x4*>(ws)[((int64_t)bh * nc + nc - 1) * per + e4];
     return;
   }
+  if (part == 2) return;
   const double lam = (double)decay[bh % H];
   const float dl = (float)pow_int(lam, L);
   const float dlast = (float)pow_int(lam, N - (nc - 1) * L);
@@ -383,13 +386,13 @@ hipError_t launch_aggregate_pass(const PrefillArgs& a, hipStream_t st) {
   return a.d == 128 ? launch_aggregate_t<float, 128>(a, st) : launch_aggregate_t<float, 64>(a, st);
 }
 
-hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st) {
+hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st, int part) {
   const int BH = (int)(a.B * a.H);
   const int D = (int)a.d;
   const int64_t threads = (int64_t)BH * D * D / 4;
   hipLaunchKernelGGL(la_chunk_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a.decay, a.states,
                      a.kv_in, a.kv_out, BH, (int)a.H, (int)a.N, (int)a.L, a.nc, D, a.warm_start ? 1 : 0,
-                     a.rev ? 1 : 0, a.scale_kv_out ? 1 : 0, a.slots, a.num_slots, (int)a.L_warm);
+                     a.rev ? 1 : 0, a.scale_kv_out ? 1 : 0, a.slots, a.num_slots, (int)a.L_warm, part);
   return hipGetLastError();
 }
 
