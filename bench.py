@@ -4,17 +4,18 @@
 
 One step = one prefill of the million-token workload (B=1, H=64,
 N=1,048,576, d=128, bf16 inputs and output, block 64, fp32 state), i.e. all
-of its kernels: decay-power table, chunk aggregates of the heads that do not
-decay within a chunk, warm-start output pass of those that do, chunk scan,
-output pass from the chunk start states.  Inputs are synthetic (seeded,
+of its kernels: decay-power table, chunk aggregates and chunk scan of the
+heads that do not decay within a chunk, one output launch for every head
+(the warm-start pass of the decaying heads beside the other heads' pass from
+their chunk start states), and the decaying heads' final states copied out.  Inputs are synthetic (seeded,
 generated on the device) and resident in HBM before timing starts.  Prints
 ONE JSON line:
 
   value          whole-job prefill tokens/s (B*N / step time)
-  roofline       the kernel that writes every output row (the dominant one:
-                 the warm-start output pass here, all 64 heads decay within a
-                 chunk): algorithmic bytes per launch (1024 B per head-token of
-                 its heads: q, k, v read + o written, bf16) over its mean
+  roofline       the kernel that writes every output row (the dominant one;
+                 all 64 heads of this workload take its warm-start part):
+                 algorithmic bytes per launch (1024 B per head-token: q, k, v
+                 read + o written, bf16) over its mean
                  duration from HIP events recorded around it on its own
                  stream, against 8 TB/s
   cpu_baseline   the fp64 oracle (plain-C recurrence) on a bounded sample of
@@ -168,10 +169,7 @@ def bench_prefill(args, dev):
     kern_ms = sum(kern) / len(kern)
     ht = B * H * N
     fast = sum(decaying_heads(decay_lambdas(H), warm_chunk)) if block == 64 else H
-    if block == 64:  # warm-start pass: its heads' q, k, v read and o written
-        alg_bytes = BYTES_PER_HT * B * fast * N
-    else:            # output pass over every head
-        alg_bytes = BYTES_PER_HT * ht
+    alg_bytes = BYTES_PER_HT * ht  # the timed kernel reads q, k, v and writes o of every head
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     traffic = _traffic(alg_bytes) if block == 64 else None  # the counters were taken at block 64
     res = dict(
