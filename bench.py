@@ -76,7 +76,7 @@ def decaying_heads(lam, chunk):
     """Which heads the library puts through its warm-start pass (bf16 inputs,
     block 64): those whose chunk-start state weighs at most 2^-30 of itself
     (lam^(r+1)) from row r = carry span on, with the span rounded up to whole
-    64-token sub-tiles and at most a third of the chunk.  The kernels' rule,
+    64-token sub-tiles and at most half the chunk.  The kernels' rule,
     restated here for the byte count only."""
     out = []
     for x in lam:
@@ -88,7 +88,7 @@ def decaying_heads(lam, chunk):
         else:
             t = 20.79441541679836 / -math.log(x)  # 30 ln 2 / -ln lam
             span = None if not t < 1e9 else ((math.ceil(t) + 63) // 64) * 64
-        out.append(span is not None and 3 * span <= chunk)
+        out.append(span is not None and 2 * span <= chunk)
     return out
 
 

@@ -97,7 +97,7 @@ extern "C" {
  *               kernel that is several times slower.
  * Decays are meant to lie in [0, 1].  With bf16 inputs and block 64, a head
  * with span = ceil(30 ln 2 / -ln lam), rounded up to a multiple of 64, at
- * most a third of the warm-start chunk (lam^span <= 2^-30; the chunk is
+ * most half the warm-start chunk (lam^span <= 2^-30; the chunk is
  * lightning_attn_fwd_warm_chunk) is computed per chunk of that length from
  * the state that the span tokens before the chunk build from zero: at token
  * t of a chunk the state S_(c0-span-1) from before those tokens is left out

@@ -69,7 +69,7 @@ int64_t pick_chunk(int64_t B, int64_t H, int64_t N, int64_t block) {
 // Default warm-start chunk: the scan's chunk L doubled up to twice (4L) while
 // the warm-start pass keeps at least 1024 workgroups (two rounds at two per
 // CU) and the chunk stays within the sequence.  Longer chunks let more heads
-// take the warm start (a carry span up to a third of the chunk) and shorten
+// take the warm start (a carry span up to half the chunk) and shorten
 // its warm-up windows relative to the chunk, while the heads on the exact
 // path keep the shorter chunks and the workgroups they need.
 int64_t pick_warm_chunk(int64_t B, int64_t H, int64_t N, int64_t L) {

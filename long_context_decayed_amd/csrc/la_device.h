@@ -45,10 +45,11 @@ __device__ __forceinline__ int carry_span(float lam) {
   return (int)(((r + 63) / 64) * 64);
 }
 
-// A head decays within its chunk of L tokens when 3 carry_span <= L.  Each
+// A head decays within its chunk of L tokens when 2 carry_span <= L.  Each
 // chunk of such a head is then computed from the state that the carry_span
-// tokens before it build from zero, with no scan over chunks.
-__device__ __forceinline__ bool decays_within_chunk(int span, int L) { return 3ll * (long long)span <= (long long)L; }
+// tokens before it build from zero, with no scan over chunks (a warm-up of at
+// most half a chunk; the omission bound does not depend on the ratio).
+__device__ __forceinline__ bool decays_within_chunk(int span, int L) { return 2ll * (long long)span <= (long long)L; }
 
 // Row of the initial / final state array that (batch, head) pair bh uses:
 // bh itself, or, with a slot table, slot slots[b] of a pool of num_slots

@@ -189,7 +189,7 @@ def test_bf16_state_in_place(dev):
 
 # --- heads that decay within a chunk, next to heads that do not --------------
 # Chunk 1024, block 64, bf16 inputs.  A head whose start-state weight lam^(r+1)
-# falls below 2^-30 within a third of a chunk (here lam <= 0.9) is computed per
+# falls below 2^-30 within half a chunk (here lam <= 0.9) is computed per
 # chunk from the state that the preceding carry-span tokens build from zero;
 # the others take the three-pass path.  Each head is held to the tolerance on
 # its own RMS, so the fast-decaying heads are not hidden behind the large
@@ -323,14 +323,14 @@ def test_bf16_depth_scaled_decays(dev, layer, chunk):
 
 
 def test_bf16_classification_boundary(dev):
-    # At chunk 1536 a head takes the warm-start path when its carry span (30 ln 2
+    # At chunk 1024 a head takes the warm-start path when its carry span (30 ln 2
     # / -ln lam rounded up to 64) is at most 512: lam with 30 ln 2 / -ln lam =
     # 511.5 and 512 sit on the warm-start side, 512.5 just past it (span 576).
     lams = np.array([math.exp(-30 * math.log(2) / t) for t in (448.2, 511.5, 512.0, 512.5)], dtype=np.float32)
-    say("bf16 decays at the warm-start boundary, chunk 1536, B2 H4 N5000 d128, with state")
+    say("bf16 decays at the warm-start boundary, chunk 1024, B2 H4 N5000 d128, with state")
     q, k, v = qkv_device(2, 4, 5000, 128, seed=130, device=dev)
     s0 = state_device(2, 4, 128, seed=130, device=dev)
-    o32, kv = _run(q, k, v, lams, dev, 64, out_dtype=torch.float32, kv_in=s0, chunk=1536)
+    o32, kv = _run(q, k, v, lams, dev, 64, out_dtype=torch.float32, kv_in=s0, chunk=1024)
     o_ref, s_ref = oracle(host(q), host(k), host(v), lams, host(s0).astype(np.float64))
     o_h, kv_h = host(o32), host(kv)
     for h in range(4):
