@@ -22,9 +22,11 @@
 //   C  la_chunk_output: per chunk, the block loop above from Sstart_c (MFMA) [here]
 // With bf16 inputs and block 64, a head that decays within its chunk takes
 // none of the three: la_chunk_output64 in warm-start mode computes each of
-// its chunks from the state built by the carry_span tokens before the chunk
-// (from zero; older tokens weigh at most 2^-30 there), so Q, K and V of such
-// a head are read about once and nothing waits on a scan.
+// its chunks (of the longer warm-start chunk length) from the state built by
+// the carry_span tokens before the chunk (from zero; older tokens weigh at
+// most 2^-30 there), so Q, K and V of such a head are read about once and
+// nothing waits on a scan.  In the forward, that pass and pass C of the
+// other heads are one launch (la_chunk_output64_mixed).
 //
 // Precision recipe (bf16 inputs): products of two bf16 inputs are exact in the
 // fp32 MFMA accumulator.  Quantities formed in fp32 that feed an MFMA are
