@@ -117,7 +117,9 @@ def test_million_token_slices(dev, million, block):
     e1, e2, _, _ = _slice_checks(q, k, v, lam, dev, out, t0, t0 + 8192, block)
     # A slice across a chunk start: the rows whose outputs still depend on
     # the chunk's start state (up to about 5400 for the slowest head here).
-    L = la.chunk_for(1, 64, N, block)
+    # At block 64 every head here takes the warm start, whose chunks are the
+    # warm-start chunk length.
+    L = la.warm_chunk_for(1, 64, N, block) if block == 64 else la.chunk_for(1, 64, N, block)
     tb = 5 * L - 2048
     say("million-token layer block", block, "chunk", L, "slice across the chunk start", 5 * L)
     g1, g2, _, _ = _slice_checks(q, k, v, lam, dev, out, tb, tb + 8192, block)
