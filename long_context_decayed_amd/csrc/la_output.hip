@@ -843,9 +843,14 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64_mixed(Operands p0,
   __shared__ __attribute__((aligned(16))) Mfma<bf16>::op_t Pbuf[3][2][2][64];
   __shared__ __attribute__((aligned(16))) f32x4 Dtab[4][64];
   const int b = blockIdx.x;
+  // Warm-start chunks in reverse order, last head first: with ALiBi-style
+  // slopes, which shrink with the head index, the longest warm-ups come first
+  // and the short chunks fill the last round (measured 0.2-1% faster than in
+  // head order at 1024 warm-start workgroups).
   if (b < n_warm)
-    chunk_output64_body<TOut, D, kWarmStart, false, SILU>(Qs, Ks, Kt, Vs, Pbuf, Dtab, b, 0, p0, p0, decay, tbl_all, H,
-                                                          N, Lw, ncw, tbl_stride, slots, num_slots, 1, Lw, nc);
+    chunk_output64_body<TOut, D, kWarmStart, false, SILU>(Qs, Ks, Kt, Vs, Pbuf, Dtab, n_warm - 1 - b, 0, p0, p0, decay,
+                                                          tbl_all, H, N, Lw, ncw, tbl_stride, slots, num_slots, 1, Lw,
+                                                          nc);
   else
     chunk_output64_body<TOut, D, kFromStart, false, SILU>(Qs, Ks, Kt, Vs, Pbuf, Dtab, b - n_warm, 0, p0, p0, decay,
                                                           tbl_all, H, N, L, nc, tbl_stride, slots, num_slots, 1, Lw,
