@@ -319,3 +319,22 @@ def test_warm_chunk_rules(lib):
     assert wc(1, 64, 1 << 20, 64, 4096, 4100) == -1       # not a multiple of 64
     assert _fwd(lib, chunk=256, warm_chunk=128) == LA_ERR_INVALID
     assert _fwd(lib, chunk=256, warm_chunk=320, ws=FAKE[5], wsb=1) == LA_ERR_WORKSPACE
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/lightning_attn.h compiles as C99 on its own, and every declared
+    entry point can be referenced from C (a C caller needs no C++ at all)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc") or shutil.which("cc")
+    if gcc is None:
+        pytest.skip("no C compiler on this host")
+    names = declared_functions()
+    src = tmp_path / "use_header.c"
+    src.write_text('#include "lightning_attn.h"\n'
+                   "const void* entry_points[] = {\n" + "".join("    (const void*)&%s,\n" % n for n in names) +
+                   "};\n")
+    res = subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-pedantic", "-Wno-pedantic", "-c",
+                          "-I", os.path.join(ROOT, "include"), str(src), "-o", str(tmp_path / "use_header.o")],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
