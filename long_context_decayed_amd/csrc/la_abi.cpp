@@ -148,20 +148,22 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* d
   return LA_OK;
 }
 
-// The kernels of one prefill-shaped pass, in order, on `st`.  With the warm
-// start (forward): pass A and the scan of the heads that do not decay within
-// a chunk, then one launch for every output row (the decaying heads' warm-start
-// pass and the others' pass C side by side), then the decaying heads' final
-// states copied out (after every chunk has read kv_in, which may be kv_out).
+// The kernels of one prefill-shaped pass, in order, on `st`.  Without the
+// warm start: pass A, the scan, pass C.  With it (forward passes only; the
+// backward's reverse passes use the paired launches): pass A and the scan of
+// the heads that do not decay within a chunk, then one launch for every
+// output row (the decaying heads' warm-start pass and the others' pass C side
+// by side), then the decaying heads' final states copied out (after every
+// chunk has read kv_in, which may be kv_out).
 hipError_t run_passes(const la::PrefillArgs& a, hipStream_t st) {
+  if (a.warm_start && a.rev) return hipErrorInvalidValue;
   hipError_t e = la::launch_aggregate_pass(a, st);
-  if (a.warm_start && !a.rev) {
+  if (a.warm_start) {
     if (e == hipSuccess) e = la::launch_scan_pass(a, st, 1);
     if (e == hipSuccess) e = la::launch_mixed_pass(a, st);
     if (e == hipSuccess) e = la::launch_scan_pass(a, st, 2);
     return e;
   }
-  if (e == hipSuccess && a.warm_start) e = la::launch_warm_start_pass(a, st);
   if (e == hipSuccess) e = la::launch_scan_pass(a, st);
   if (e == hipSuccess) e = la::launch_output_pass(a, st);
   return e;

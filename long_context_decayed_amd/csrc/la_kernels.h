@@ -37,9 +37,6 @@ struct PrefillArgs {
 // Decay table and pass A (chunk aggregates; with warm_start, of the heads
 // that do not decay within their chunk only): la_state.hip.
 hipError_t launch_aggregate_pass(const PrefillArgs& a, hipStream_t st);
-// Warm-start output pass of the decaying heads (every output row and their
-// final state); only with warm_start: la_output.hip.
-hipError_t launch_warm_start_pass(const PrefillArgs& a, hipStream_t st);
 // Pass B (chunk scan: start states, final state; with warm_start, the
 // decaying heads' final states are only copied out); part 0 every head, 1 the
 // scan of the other heads only, 2 the decaying heads' copy only: la_state.hip.

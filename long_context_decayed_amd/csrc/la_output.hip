@@ -925,20 +925,6 @@ static hipError_t launch_output_t(const PrefillArgs& a, hipStream_t st) {
 }
 
 template <typename TOut, int D>
-static hipError_t launch_warm_start_t(const PrefillArgs& a, hipStream_t st) {
-  if (a.evt_begin) {
-    hipError_t e = hipEventRecord((hipEvent_t)a.evt_begin, st);
-    if (e != hipSuccess) return e;
-  }
-  launch_fast<TOut, D, kWarmStart>(a, st);
-  if (a.evt_end) {
-    hipError_t e = hipEventRecord((hipEvent_t)a.evt_end, st);
-    if (e != hipSuccess) return e;
-  }
-  return hipGetLastError();
-}
-
-template <typename TOut, int D>
 static hipError_t launch_mixed_t(const PrefillArgs& a, hipStream_t st) {
   if (a.evt_begin) {
     hipError_t e = hipEventRecord((hipEvent_t)a.evt_begin, st);
@@ -968,11 +954,6 @@ hipError_t launch_mixed_pass(const PrefillArgs& a, hipStream_t st) {
   return a.d == 128 ? launch_mixed_t<float, 128>(a, st) : launch_mixed_t<float, 64>(a, st);
 }
 
-hipError_t launch_warm_start_pass(const PrefillArgs& a, hipStream_t st) {
-  if (!a.warm_start) return hipErrorInvalidValue;
-  if (a.out_dtype == kBF16) return a.d == 128 ? launch_warm_start_t<bf16, 128>(a, st) : launch_warm_start_t<bf16, 64>(a, st);
-  return a.d == 128 ? launch_warm_start_t<float, 128>(a, st) : launch_warm_start_t<float, 64>(a, st);
-}
 
 template <typename TIn, typename TOut, int D>
 static hipError_t launch_output_d(const PrefillArgs& a, hipStream_t st) {
