@@ -455,10 +455,19 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
     // those tiles come from HBM about once.
     if (e == hipSuccess) e = la::launch_aggregate_pass(ak, st);
     if (e == hipSuccess) e = la::launch_aggregate_pass(av, st);
-    if (e == hipSuccess && a.warm_start) e = la::launch_warm_start_pair(ak, av, st);
-    if (e == hipSuccess) e = la::launch_scan_pass(ak, st);
-    if (e == hipSuccess) e = la::launch_scan_pass(av, st);
-    if (e == hipSuccess) e = la::launch_output_pair(ak, av, st);
+    if (a.warm_start) {
+      // as in the forward: the other heads' scans, one launch for every
+      // output row of both passes, then the decaying heads' final states
+      if (e == hipSuccess) e = la::launch_scan_pass(ak, st, 1);
+      if (e == hipSuccess) e = la::launch_scan_pass(av, st, 1);
+      if (e == hipSuccess) e = la::launch_mixed_pair(ak, av, st);
+      if (e == hipSuccess) e = la::launch_scan_pass(ak, st, 2);
+      if (e == hipSuccess) e = la::launch_scan_pass(av, st, 2);
+    } else {
+      if (e == hipSuccess) e = la::launch_scan_pass(ak, st);
+      if (e == hipSuccess) e = la::launch_scan_pass(av, st);
+      if (e == hipSuccess) e = la::launch_output_pair(ak, av, st);
+    }
   } else {
     if (e == hipSuccess) e = run_passes(ak, st);
     if (e == hipSuccess) e = run_passes(av, st);

@@ -48,13 +48,15 @@ hipError_t launch_output_pass(const PrefillArgs& a, hipStream_t st);
 // every output row, and the decaying heads' final states; after pass B of the
 // other heads.  Timing events bracket it: la_output.hip.
 hipError_t launch_mixed_pass(const PrefillArgs& a, hipStream_t st);
+// The same for two reverse-time problems of one shape paired as in
+// launch_output_pair (the backward's dK and dV passes): la_output.hip.
+hipError_t launch_mixed_pair(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st);
 
 // Two problems of one shape (bf16 inputs, block 64) in one grid, the two
 // workgroups of each (bh, chunk) side by side, so that tensors both read
-// are fetched from HBM about once: the warm-start pass and the output pass
-// (pass C) of a and b.  Each problem has its own tensors and chunk states;
-// flags, decays and the decay table are a's: la_output.hip.
-hipError_t launch_warm_start_pair(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st);
+// are fetched from HBM about once: pass C of a and b (without the warm
+// start; with it, launch_mixed_pair).  Each problem has its own tensors and
+// chunk states; flags, decays and the decay table are a's: la_output.hip.
 hipError_t launch_output_pair(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st);
 
 // dst[bh] = src[bh]^T for BH fp32 d x d states: la_state.hip.

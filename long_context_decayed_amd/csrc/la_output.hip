@@ -857,6 +857,33 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64_mixed(Operands p0,
                                                           nc);
 }
 
+// The same for the backward's reverse-time dK and dV passes, paired as above:
+// the grid's first n_warm_grid workgroups are the two problems' warm-start
+// chunks (paired, pair_shift = kPairShift, nblk_w per problem), the rest their
+// pass-C chunks (paired likewise, nblk_c per problem).
+template <typename TOut, int D>
+__global__ __launch_bounds__(D * 2, 2) void la_chunk_output64_mixed_pair(
+    Operands p0, Operands p1, const float* __restrict__ decay, const float* __restrict__ tbl_all, int H, int N, int L,
+    int nc, int Lw, int ncw, int tbl_stride, int nblk_w, int nblk_c, int n_warm_grid) {
+  __shared__ __attribute__((aligned(16))) bf16 Qs[kSub * D];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kSub * D];
+  __shared__ __attribute__((aligned(16))) bf16 Kt[kSub * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[kSub * D];
+  __shared__ __attribute__((aligned(16))) Mfma<bf16>::op_t Pbuf[3][2][2][64];
+  __shared__ __attribute__((aligned(16))) f32x4 Dtab[4][64];
+  const bool warm_part = (int)blockIdx.x < n_warm_grid;
+  const int b = warm_part ? (int)blockIdx.x : (int)blockIdx.x - n_warm_grid;
+  const int pi = (b >> kPairShift) & 1;
+  const int blk = ((b >> (kPairShift + 1)) << kPairShift) | (b & ((1 << kPairShift) - 1));
+  if (blk >= (warm_part ? nblk_w : nblk_c)) return;  // padding of a last group
+  if (warm_part)
+    chunk_output64_body<TOut, D, kWarmStart, true, false>(Qs, Ks, Kt, Vs, Pbuf, Dtab, blk, pi, p0, p1, decay, tbl_all,
+                                                          H, N, Lw, ncw, tbl_stride, nullptr, 0, 1, Lw, nc);
+  else
+    chunk_output64_body<TOut, D, kFromStart, true, false>(Qs, Ks, Kt, Vs, Pbuf, Dtab, blk, pi, p0, p1, decay, tbl_all,
+                                                          H, N, L, nc, tbl_stride, nullptr, 0, 1, Lw, nc);
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launcher: the output pass on `st`, bracketed by the optional
 // timing events.
@@ -948,6 +975,33 @@ static hipError_t launch_mixed_t(const PrefillArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <typename TOut, int D>
+static void launch_mixed_pair_t(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st) {
+  const int half = 1 << kPairShift;
+  const int nblk_w = (int)(a.B * a.H * a.nc_warm), nblk_c = (int)(a.B * a.H * a.nc);
+  const int n_warm_grid = (nblk_w + half - 1) / half * 2 * half;
+  const unsigned grid = (unsigned)(n_warm_grid + (nblk_c + half - 1) / half * 2 * half);
+  hipLaunchKernelGGL((la_chunk_output64_mixed_pair<TOut, D>), dim3(grid), dim3(D * 2), 0, st, operands_of(a),
+                     operands_of(b), a.decay, (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc,
+                     (int)a.L_warm, a.nc_warm, a.tbl_stride, nblk_w, nblk_c, n_warm_grid);
+}
+
+hipError_t launch_mixed_pair(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st) {
+  if (!a.warm_start || !a.rev || a.silu || a.in_dtype != kBF16 || a.block != 64 || b.in_dtype != kBF16 ||
+      b.block != 64 || a.B != b.B || a.H != b.H || a.N != b.N || a.nc != b.nc || a.d != b.d ||
+      a.out_dtype != b.out_dtype || a.rev != b.rev || a.warm_start != b.warm_start || a.silu != b.silu ||
+      a.L != b.L || a.L_warm != b.L_warm)
+    return hipErrorInvalidValue;
+  if (a.out_dtype == kBF16) {
+    if (a.d == 128) launch_mixed_pair_t<bf16, 128>(a, b, st);
+    else launch_mixed_pair_t<bf16, 64>(a, b, st);
+  } else {
+    if (a.d == 128) launch_mixed_pair_t<float, 128>(a, b, st);
+    else launch_mixed_pair_t<float, 64>(a, b, st);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_mixed_pass(const PrefillArgs& a, hipStream_t st) {
   if (!a.warm_start || a.rev || a.in_dtype != kBF16 || a.block != 64) return hipErrorInvalidValue;
   if (a.out_dtype == kBF16) return a.d == 128 ? launch_mixed_t<bf16, 128>(a, st) : launch_mixed_t<bf16, 64>(a, st);
@@ -980,10 +1034,6 @@ static hipError_t launch_pair_mode(const PrefillArgs& a, const PrefillArgs& b, h
     else launch_fast<float, 64, MODE>(a, st, &b);
   }
   return hipGetLastError();
-}
-
-hipError_t launch_warm_start_pair(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st) {
-  return launch_pair_mode<kWarmStart>(a, b, st);
 }
 
 hipError_t launch_output_pair(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st) {
