@@ -55,8 +55,15 @@ if _ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 BYTES_PER_HT = 1024            # q, k, v read + o written, bf16, d = 128
-FLOP_PER_HT = 131072           # causal half of 2*b*d (b = 256) + 4*d^2 (inter + state update)
-TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "chunk_output_traffic.json")
+FLOP_PER_MFMA = 32768          # one v_mfma_f32_32x32x16_bf16: 32 x 32 x 16 multiply-adds
+COUNTERS_FILE = os.path.join(_ROOT, "profiles", "prefill_counters.json")
+
+
+def flop_per_ht(block, d=128):
+    """Algorithmic flops per head-token of the blockwise form at this block
+    length: the causal half of the intra-block Q K^T and P V products (b d
+    each) plus the inter-block Q S and the state update (2 d^2 each)."""
+    return 2 * block * d + 4 * d * d
 
 
 def log(*a):
@@ -93,23 +100,26 @@ def decaying_heads(lam, chunk):
 
 
 def _src_hash():
+    """Hash of the prefill kernels' sources: the committed counter record is
+    used only while it matches."""
     h = hashlib.sha256()
-    for name in ("la_output.hip", "la_device.h"):
+    for name in ("la_output.hip", "la_state.hip", "la_device.h"):
         h.update(open(os.path.join(_ROOT, "long_context_decayed_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
 
-def _traffic(launch_alg_bytes):
-    """HBM bytes per launch of the output kernel from the committed rocprofv3
-    counter summary, or None when it is absent or the kernel source changed."""
+def _counters():
+    """The committed rocprofv3 counter record of the prefill kernels, or None
+    when it is absent or the kernel sources changed since it was taken."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(COUNTERS_FILE))
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256_16") != _src_hash():
-        log("traffic record is stale (kernel changed since the counters were taken): null")
+        log("counter record is stale (kernels changed since the counters were taken): traffic and "
+            "executed-MFMA figures are null")
         return None
-    return rec.get("bytes_per_launch")
+    return rec
 
 
 def _device_info(dev):
@@ -171,22 +181,50 @@ def bench_prefill(args, dev):
     fast = sum(decaying_heads(decay_lambdas(H), warm_chunk)) if block == 64 else H
     alg_bytes = BYTES_PER_HT * ht  # the timed kernel reads q, k, v and writes o of every head
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    traffic = _traffic(alg_bytes) if block == 64 else None  # the counters were taken at block 64
+    rec = _counters() if block == 64 else None  # the counters were taken at block 64
+    launch = (rec or {}).get("output_launch") or {}
+    fpt = flop_per_ht(block, d)
+    # Executed MFMA: the instructions the counter run saw per launch of the
+    # same kernel (SQ_INSTS_MFMA, summed over waves) times the flops of one
+    # 32x32x16 bf16 MFMA, over this run's own kernel time.
+    exec_flop = launch.get("sq_insts_mfma") * FLOP_PER_MFMA if launch.get("sq_insts_mfma") else None
+    mfma = dict(
+        alg_flop_per_head_token=fpt,
+        alg_flop_per_step=fpt * ht,
+        alg_frac_of_step=fpt * ht / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        alg_frac_of_output_launch=fpt * ht / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        exec_flop_per_output_launch=exec_flop,
+        exec_frac_of_output_launch=(exec_flop / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS) if exec_flop else None,
+        shader_clock_ghz_under_load=launch.get("shader_clock_ghz"),
+        peak_tflops=BF16_PEAK_TFLOPS,
+        source="algorithmic: 2*b*d + 4*d^2 flop per head-token at the block run; executed: SQ_INSTS_MFMA x "
+               "%d flop per launch from %s (null when stale)" % (FLOP_PER_MFMA, os.path.relpath(COUNTERS_FILE, _ROOT)),
+    )
     res = dict(
         B=B, H=H, N=N, d=d, block=block, chunk=chunk, warm_chunk=warm_chunk, warm_start_heads=fast,
         ms_per_step=ms_step,
         tokens_per_s=B * N / (ms_step * 1e-3),
         output_kernel_ms=kern_ms,
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=achieved / HBM_PEAK_GBS, traffic=traffic),
+                      frac=achieved / HBM_PEAK_GBS, traffic=launch.get("bytes_per_launch")),
         step_hbm_frac=BYTES_PER_HT * ht / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        mfma_alg_frac=FLOP_PER_HT * ht / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        mfma_alg_frac=mfma["alg_frac_of_step"],
+        mfma=mfma,
     )
     if args.exact:
-        # the same step with every head on the exact chunked path (LA_FLAG_EXACT)
+        # The same step with every head on the exact chunked path (LA_FLAG_EXACT:
+        # chunk aggregates, scan, outputs from the chunk start states).  Its
+        # roofline is taken over the whole step: the algorithmic bytes are the
+        # same 1024 B per head-token; the aggregate pass's second read of k and
+        # v shows up in `traffic` (all of the step's kernels, from the counters).
         ms_exact = _time_ms(lambda: la.fwd(q, k, v, lam, kv_out=kv_out, block=block, out=out, workspace=ws,
                                            exact=True), max(1, args.steps // 2))
-        res["exact"] = dict(ms_per_step=ms_exact, tokens_per_s=B * N / (ms_exact * 1e-3))
+        ach_x = alg_bytes / (ms_exact * 1e-3) / 1e9
+        ex = (rec or {}).get("exact_step") or {}
+        res["exact"] = dict(ms_per_step=ms_exact, tokens_per_s=B * N / (ms_exact * 1e-3),
+                            roofline=dict(bound="hbm", achieved=ach_x, peak=HBM_PEAK_GBS, unit="GB/s",
+                                          frac=ach_x / HBM_PEAK_GBS, traffic=ex.get("bytes_per_step"),
+                                          scope="whole step (aggregate pass, scan, output pass)"))
     if args.depth:
         rows = []
         for layer in (0, 23, 46, 69):
@@ -438,6 +476,7 @@ def main():
         "warm_start_heads": prefill["warm_start_heads"],
         "step_hbm_frac": prefill["step_hbm_frac"],
         "mfma_alg_frac": prefill["mfma_alg_frac"],
+        "mfma": prefill["mfma"],
         "exact_path": prefill.get("exact"),
         "depth_scaled": prefill.get("depth_scaled"),
         "backward": prefill.get("backward"),

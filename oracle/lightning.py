@@ -47,10 +47,11 @@ on the lightning output after that norm, before the output projection):
     silu(x)        = x * sigmoid(x),   sigmoid(x) = 1 / (1 + exp(-x))
     rmsnorm_heads  y = o / sqrt(mean_d(o^2) + eps) * gamma[h]   (per head, over
                    the d features of one token; eps = 1e-5 as the block norms)
-    gate           y * sigmoid(g)  The token
-form of the same gradients, an adjoint recurrence run from the last token
-back, is in recurrence.c (`crec.backward`); the two are checked against each
-other, against finite differences and against autograd.
+    gate           y * sigmoid(g)
+
+The token form of the same gradients, an adjoint recurrence run from the last
+token back, is in recurrence.c (`crec.backward`); the two are checked against
+each other and against central finite differences of the forward oracle.
 
 Every function works in float64 on whatever bits it is given: callers pass the
 exact values a GPU consumed (bf16 or fp32, upcast), and lambda as the fp32
