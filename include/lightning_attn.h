@@ -35,10 +35,12 @@
  *    not overlap.  out must not overlap q, k, v, kv_in or kv_out.
  *  - Arguments are validated before any HIP call, so validation errors are
  *    returned without touching the device.  Nothing is thrown across the ABI.
- *  - The library keeps no state between calls: calls on different streams
- *    may run at once.  Given a caller workspace (or none needed, as in the
- *    decode steps), a call allocates, frees, copies and synchronises nothing
- *    and issues no memset, so it can be captured in a HIP graph.
+ *  - The library keeps no state between calls (except the per-device array
+ *    of lightning_attn_fwd_noalloc): calls on different streams may run at
+ *    once.  Given a caller workspace (or none needed, as in the decode steps,
+ *    or the library's own array, as in lightning_attn_fwd_noalloc), a call
+ *    allocates, frees, copies and synchronises nothing and issues no memset,
+ *    so it can be captured in a HIP graph.
  *
  * Status codes: LA_OK, or one of the LA_ERR_* values below;
  * lightning_attn_strerror() names them.
@@ -303,6 +305,32 @@ int lightning_attn_norm_gate(const void* o, int o_dtype, const void* gate, const
  * (apply to Q, K and V before lightning_attn_fwd).  0 <= n <= 2^44; n = 0 is
  * a no-op. */
 int lightning_attn_silu(void* x, int64_t n, void* stream);
+
+/*
+ * Prefill that allocates nothing, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the computation of lightning_attn_fwd_ex at block 64,
+ * with its workspace (decay table and chunk states) in a device array of
+ * LA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  The caller passes inputs and outputs as for
+ * lightning_attn_fwd_ex; `stream` must belong to the current device.
+ *   chunk      : 0 = the default chunk (lightning_attn_fwd_chunk at block 64),
+ *                doubled until the chunk states fit the array; otherwise as in
+ *                lightning_attn_fwd_ex
+ *   warm_chunk : 0 = the default warm-start chunk of lightning_attn_fwd_ex
+ *                (chunk 0), but at least the chunk; otherwise as there
+ * Returns LA_ERR_WORKSPACE when the workspace for these sizes (see
+ * lightning_attn_fwd_workspace_bytes) exceeds LA_NOALLOC_SCRATCH_BYTES, with
+ * nothing enqueued.  The array is shared by every call on a GPU and keeps the
+ * last call's contents: calls that overlap in time on one GPU (two streams,
+ * two threads) race and give undefined results; calls ordered on one stream
+ * do not.  Every byte a call reads from the array it has written before.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
+int lightning_attn_fwd_noalloc(const void* q, const void* k, const void* v, const float* decay, void* out,
+                               const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d,
+                               int in_dtype, int out_dtype, int64_t chunk, int64_t warm_chunk, unsigned int flags,
+                               void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* lightning_attn_strerror(int status);

@@ -25,6 +25,8 @@ __all__ = [
     "LA_FLAG_EXACT",
     "LA_FLAG_SILU_QKV",
     "fwd",
+    "fwd_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
     "fwd_slots",
     "bwd",
     "decode_step",
@@ -45,6 +47,7 @@ LA_DTYPE_BF16 = 0
 LA_DTYPE_F32 = 1
 LA_FLAG_EXACT = 1
 LA_FLAG_SILU_QKV = 2
+NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024  # LA_NOALLOC_SCRATCH_BYTES
 _DT = {torch.bfloat16: LA_DTYPE_BF16, torch.float32: LA_DTYPE_F32}
 
 _lib = None
@@ -75,6 +78,8 @@ def load():
         fn.argtypes = fwd_args + [P]
     lib.lightning_attn_fwd_ex.restype = I
     lib.lightning_attn_fwd_ex.argtypes = fwd_args + [I, I, I64, I64, ctypes.c_uint, P, SZ, P, P, P]
+    lib.lightning_attn_fwd_noalloc.restype = I
+    lib.lightning_attn_fwd_noalloc.argtypes = [P] * 7 + [I64, I64, I64, I64, I, I, I64, I64, ctypes.c_uint, P]
     lib.lightning_attn_fwd_chunk.restype = I64
     lib.lightning_attn_fwd_chunk.argtypes = [I64, I64, I64, I64, I64]
     lib.lightning_attn_fwd_warm_chunk.restype = I64
@@ -201,6 +206,35 @@ def fwd(q, k, v, decay, kv_in=None, kv_out=None, block=64, out=None, out_dtype=N
     )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_fwd_ex")
+    return out
+
+
+def fwd_noalloc(q, k, v, decay, out, kv_in=None, kv_out=None, chunk=0, warm_chunk=0, exact=False, silu=False,
+                stream=None):
+    """Prefill at block 64 that allocates nothing: the library keeps its
+    workspace in a device array of NOALLOC_SCRATCH_BYTES per GPU (calls that
+    overlap on one GPU race).  out is the caller's [B, H, N, d] tensor (bf16 or
+    fp32); the rest as fwd.  chunk 0: the default chunk doubled until the chunk
+    states fit the array.  Returns out."""
+    lib = load()
+    if q.dtype not in _DT:
+        raise TypeError("q must be bfloat16 or float32")
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype, (B, H, N, d))
+    _check_dev("decay", decay, torch.float32, (H,))
+    for name, t in (("kv_in", kv_in), ("kv_out", kv_out)):
+        if t is not None:
+            _check_dev(name, t, torch.float32, (B, H, d, d))
+    if not isinstance(out, torch.Tensor) or out.dtype not in _DT:
+        raise TypeError("out must be a bfloat16 or float32 tensor")
+    _check_dev("out", out, out.dtype, (B, H, N, d))
+    rc = lib.lightning_attn_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(kv_in), _ptr(kv_out), B, H, N, d, _DT[q.dtype],
+        _DT[out.dtype], chunk, warm_chunk, _fwd_flags(exact, silu), _stream(stream),
+    )
+    if rc != 0:
+        raise LightningAttnError(rc, "lightning_attn_fwd_noalloc")
     return out
 
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/lightning_attn.h"
 #include "la_kernels.h"
 
@@ -607,3 +609,67 @@ int lightning_attn_runtime_version(int* version) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Prefill without allocation: the workspace of lightning_attn_fwd_ex lives in
+// a file-scope device array, one copy per GPU the library runs on, held until
+// the process ends.  Host code never passes the array's name to a kernel (in
+// host code it is a stand-in, not a device address): the device address is
+// fetched once per device with hipGetSymbolAddress and kept per device.
+
+static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (its device address).
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return LA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return LA_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LA_ERR_HIP;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);  // racing first calls store the same address
+  }
+  *out = p;
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" int lightning_attn_fwd_noalloc(const void* q, const void* k, const void* v, const float* decay, void* out,
+                                          const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t N,
+                                          int64_t d, int in_dtype, int out_dtype, int64_t chunk, int64_t warm_chunk,
+                                          unsigned int flags, void* stream) {
+  if (flags & ~kFwdFlags) return LA_ERR_INVALID;
+  const int64_t block = 64;
+  int64_t L = 0, Lw = 0;
+  int rc = validate_prefill(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, in_dtype, out_dtype, chunk, &L);
+  if (rc != LA_OK) return rc;
+  if (!flags_supported(flags, in_dtype, block)) return LA_ERR_UNSUPPORTED;
+  if (chunk == 0) {
+    // the default chunk, doubled until its chunk states fit the scratch array
+    while (workspace_layout(B, H, N, d, block, L, nullptr) > LA_NOALLOC_SCRATCH_BYTES && 2 * L <= kMaxTokens &&
+           L < ceil_div(N, block) * block)
+      L *= 2;
+    if (B * H * ceil_div(N, L) > kMaxGrid) return LA_ERR_UNSUPPORTED;
+  }
+  if (workspace_layout(B, H, N, d, block, L, nullptr) > LA_NOALLOC_SCRATCH_BYTES) return LA_ERR_WORKSPACE;
+  if (warm_chunk == 0) {
+    // the default warm-start chunk of lightning_attn_fwd_ex, at least L
+    const int64_t L0 = pick_chunk(B, H, N, block);
+    Lw = pick_warm_chunk(B, H, N, L0);
+    if (Lw < L) Lw = L;
+  } else {
+    rc = resolve_warm_chunk(B, H, N, L, warm_chunk, L, &Lw);
+    if (rc != LA_OK) return rc;
+  }
+  void* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc != LA_OK) return rc;
+  return prefill_run(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, in_dtype, out_dtype, L, Lw, ws,
+                     LA_NOALLOC_SCRATCH_BYTES, nullptr, nullptr, stream, nullptr, 0, flags);
+}

@@ -338,3 +338,29 @@ def test_header_is_plain_c(tmp_path):
                           "-I", os.path.join(ROOT, "include"), str(src), "-o", str(tmp_path / "use_header.o")],
                          capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
+
+
+def test_noalloc_scratch_size_matches_binding():
+    m = re.search(r"#define\s+LA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*\*\s*(\d+)u\s*\*\s*(\d+)u\)", open(HEADER).read())
+    assert m, "LA_NOALLOC_SCRATCH_BYTES not found in the header"
+    assert int(m.group(1)) * int(m.group(2)) * int(m.group(3)) == la.NOALLOC_SCRATCH_BYTES
+
+
+def _noalloc(lib, B=1, H=2, N=128, d=64, chunk=0, warm_chunk=0, flags=0, ind=0, outd=0, q=FAKE[0]):
+    return lib.lightning_attn_fwd_noalloc(q, FAKE[1], FAKE[2], FAKE[3], FAKE[4], None, None, B, H, N, d, ind, outd,
+                                          chunk, warm_chunk, flags, None)
+
+
+def test_noalloc_rejects_sizes_beyond_its_array(lib):
+    """Workspaces larger than the library's array are refused with
+    LA_ERR_WORKSPACE before any HIP call (fake pointers, no device)."""
+    # explicit chunk whose chunk states (16 x 64 heads x 256 chunks x 64 KiB) cannot fit
+    assert _noalloc(lib, B=16, H=64, N=1 << 16, d=128, chunk=256) == LA_ERR_WORKSPACE
+    # default chunk: doubled up to the whole sequence, the states of 4096 heads still need 256 MiB
+    assert _noalloc(lib, B=64, H=64, N=1 << 16, d=128) == LA_ERR_WORKSPACE
+    # the usual validation still comes first
+    assert _noalloc(lib, q=None) == LA_ERR_INVALID
+    assert _noalloc(lib, d=96) == LA_ERR_UNSUPPORTED
+    assert _noalloc(lib, chunk=100) == LA_ERR_INVALID
+    assert _noalloc(lib, flags=4) == LA_ERR_INVALID
+    assert _noalloc(lib, warm_chunk=96) == LA_ERR_INVALID
