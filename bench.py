@@ -35,7 +35,13 @@ ONE JSON line:
   decode         256 sequences x 64 heads x d=128 decode step, 1000 in-place
                  steps timed as a whole: GB/s of state + token traffic; and
                  the same rows through a slot table over a 512-slot pool, and
-                 those with SiLU, per-head RMSNorm and gate fused
+                 those with SiLU, per-head RMSNorm and gate fused; and one
+                 step of all 70 lightning layers of a model in one launch
+                 (each layer its own state pool) against 70 launches, at 256
+                 and 8 sequences per layer
+  mfma           algorithmic MFMA fraction (2*b*d + 4*d^2 flop per
+                 head-token at the block run) and the executed one (SQ_INSTS_MFMA
+                 from the committed counter run, over this run's kernel time)
 
 Only one GPU is used; --gpus > 1 exits with a message.
 """
@@ -47,6 +53,8 @@ import math
 import os
 import sys
 import time
+
+import numpy as np
 
 _ROOT = os.path.dirname(os.path.abspath(__file__))
 if _ROOT not in sys.path:
@@ -381,6 +389,47 @@ def bench_decode(args, dev):
     return res
 
 
+def bench_decode_layers(args, dev):
+    """Decode over the 70 lightning layers of a model in one launch
+    (lightning_attn_decode_layers: each layer its own state pool and the
+    decays of its depth) against 70 single-layer launches of the same rows,
+    at 256 and at 8 sequences per layer."""
+    import torch
+    import long_context_decayed_amd as la
+    from long_context_decayed_amd.inputs import decay_lambdas_depth, qkv_device
+
+    L, H, d = 70, 64, 128
+    lam = torch.from_numpy(np.stack([decay_lambdas_depth(H, l, L) for l in range(L)]).astype(np.float32)).to(dev)
+    rows = []
+    for B in (256, 8):
+        log("decode over %d layers x %d sequences x %d heads in one launch" % (L, B, H))
+        q, k, v = (t.reshape(L, B, H, d).contiguous() for t in qkv_device(L * B, H, 1, d, seed=7, device=dev))
+        states = torch.empty((L, B, H, d, d), device=dev, dtype=torch.float32)
+        g = torch.Generator(device=dev).manual_seed(7)
+        for l in range(L):  # N(0, 0.1^2) states, one layer at a time (a single draw would need 2x the memory)
+            states[l].normal_(0.0, 0.1, generator=g)
+        o = torch.empty_like(q)
+        reps = max(3, args.decode_steps // 50)
+        ms_one = _time_ms(lambda: la.decode_layers(q, k, v, lam, states, out=o), reps)
+        lam_l = [lam[l].contiguous() for l in range(L)]
+
+        def per_layer():
+            for l in range(L):
+                la.decode_fused(q[l], k[l], v[l], lam_l[l], states[l], silu=False, out=o[l])
+
+        ms_sep = _time_ms(per_layer, reps)
+        nbytes = L * (2 * B * H * d * d * 4 + 4 * B * H * d * 2)
+        rows.append(dict(sequences_per_layer=B, layers=L, steps=reps, bytes_per_step=nbytes,
+                         one_launch_us=ms_one * 1e3, one_launch_gb_per_s=nbytes / (ms_one * 1e-3) / 1e9,
+                         one_launch_frac_hbm=nbytes / (ms_one * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         per_layer_launches_us=ms_sep * 1e3,
+                         per_layer_launches_gb_per_s=nbytes / (ms_sep * 1e-3) / 1e9))
+        del q, k, v, states, o
+        torch.cuda.empty_cache()
+    return dict(workload="one decode step of every lightning layer of a 70-layer stack (64 heads, d=128, fp32 "
+                         "states, decays scaled down with depth), one launch vs 70 launches", rows=rows)
+
+
 def cpu_baseline(sample, args):
     """The fp64 oracle recurrence, untouched, on a bounded sample of the
     workload: the first `heads` heads x first `tokens` tokens."""
@@ -418,6 +467,8 @@ def main():
     ap.add_argument("--block", type=int, default=64, choices=[64, 128, 256])
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", dest="decode", action="store_false")
+    ap.add_argument("--no-decode-layers", dest="decode_layers", action="store_false",
+                    help="skip the 70-layer decode (one launch against one launch per layer)")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--no-backward", dest="backward", action="store_false")
     ap.add_argument("--no-exact", dest="exact", action="store_false",
@@ -452,6 +503,8 @@ def main():
         del src, dst
     prefill, sample = bench_prefill(args, dev)
     dec = bench_decode(args, dev) if args.decode else None
+    if dec is not None and args.decode_layers:
+        dec["layers"] = bench_decode_layers(args, dev)
     cpu = cpu_baseline(sample, args) if args.cpu_baseline else None
     line = {
         "metric": "lightning-attn fwd tokens/s + % bf16 MFMA peak at N=1M; decode GB/s % HBM peak",

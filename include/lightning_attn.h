@@ -291,6 +291,34 @@ int lightning_attn_decode_fused(const void* q, const void* k, const void* v, con
                                 void* stream);
 
 /*
+ * Decode over several layers' states in one launch (serving: the lightning
+ * layers of a model, each with its own state pool; the MiniMax-01 abstract on
+ * the aitopics.org "Zheng, Lin" page gives inference contexts of up to 4M
+ * tokens, for which the per-layer recurrent states are the whole decode-time
+ * working set).  Layer l steps its rows exactly as lightning_attn_decode_fused
+ * would with that layer's tensors:
+ *   q, k, v    : bf16 [num_layers][B][H][d]              (read)
+ *   decay      : float [num_layers][H]                   (read)
+ *   out        : bf16 [num_layers][B][H][d]              (written)
+ *   states     : float [num_layers][num_slots][H][d][d]  (read and written in place)
+ *   slots      : int32 [num_layers][B], device memory, or NULL: row b of
+ *                layer l uses slot slots[l][b] of layer l's pool (out of
+ *                range: idle row, zero output, no state touched; a layer
+ *                with no ready token for a row marks it idle), or row b
+ *                itself when NULL (then num_slots >= B)
+ *   silu, eps  : as lightning_attn_decode_fused
+ *   gamma      : float [num_layers][H][d] or NULL (no norm)
+ *   gate       : bf16 [num_layers][B][H][d] or NULL (no gate)
+ *   num_layers, B, H, num_slots >= 1; d in {64, 128}
+ * Rows of different layers never share a state.  Two rows of one layer
+ * naming the same slot race (undefined).
+ */
+int lightning_attn_decode_layers(const void* q, const void* k, const void* v, const float* decay, void* out,
+                                 float* states, const int32_t* slots, int64_t num_layers, int64_t B, int64_t H,
+                                 int64_t d, int64_t num_slots, int silu, const float* gamma, float eps,
+                                 const void* gate, void* stream);
+
+/*
  * Prefill epilogue as its own pass (the block-64 prefill kernel has no room
  * to take it in): out = RMSNorm_head(o) * gamma[h] * sigmoid(gate).
  *   o      : o_dtype (LA_DTYPE_BF16 or LA_DTYPE_F32) [B][H][N][d]   (read)

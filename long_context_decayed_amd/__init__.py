@@ -32,6 +32,7 @@ __all__ = [
     "decode_step",
     "decode_slots",
     "decode_fused",
+    "decode_layers",
     "norm_gate",
     "silu_",
     "workspace_bytes",
@@ -90,6 +91,8 @@ def load():
     lib.lightning_attn_decode_step.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, P]
     lib.lightning_attn_decode_fused.restype = I
     lib.lightning_attn_decode_fused.argtypes = [P] * 7 + [I64, I, P, ctypes.c_float, P, I64, I64, I64, P]
+    lib.lightning_attn_decode_layers.restype = I
+    lib.lightning_attn_decode_layers.argtypes = [P] * 7 + [I64, I64, I64, I64, I64, I, P, ctypes.c_float, P, P]
     lib.lightning_attn_norm_gate.restype = I
     lib.lightning_attn_norm_gate.argtypes = [P, I, P, P, ctypes.c_float, P, I64, I64, I64, I64, P]
     lib.lightning_attn_silu.restype = I
@@ -384,6 +387,39 @@ def decode_fused(q, k, v, decay, states, slots=None, silu=True, gamma=None, gate
     )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_decode_fused")
+    return out
+
+
+def decode_layers(q, k, v, decay, states, slots=None, silu=False, gamma=None, gate=None, eps=1e-5, out=None,
+                  stream=None):
+    """One decode step of several layers in one launch.  q, k, v: bf16
+    [L, B, H, d]; decay fp32 [L, H]; states fp32 [L, num_slots, H, d, d],
+    updated in place; slots int32 [L, B] on the device (out of range = idle
+    row) or None (row b uses slot b); silu / gamma fp32 [L, H, d] / gate bf16
+    [L, B, H, d] as decode_fused.  Returns o [L, B, H, d] bf16."""
+    lib = load()
+    L, B, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, torch.bfloat16, (L, B, H, d))
+    _check_dev("decay", decay, torch.float32, (L, H))
+    if states.dim() != 5:
+        raise ValueError("states must be [L, num_slots, H, d, d]")
+    _check_dev("states", states, torch.float32, (L, states.shape[1], H, d, d))
+    if slots is not None:
+        _check_dev("slots", slots, torch.int32, (L, B))
+    if gamma is not None:
+        _check_dev("gamma", gamma, torch.float32, (L, H, d))
+    if gate is not None:
+        _check_dev("gate", gate, torch.bfloat16, (L, B, H, d))
+    if out is None:
+        out = torch.empty((L, B, H, d), device=q.device, dtype=torch.bfloat16)
+    _check_dev("out", out, torch.bfloat16, (L, B, H, d))
+    rc = lib.lightning_attn_decode_layers(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(states), _ptr(slots), L, B, H, d, states.shape[1],
+        1 if silu else 0, _ptr(gamma), float(eps), _ptr(gate), _stream(stream)
+    )
+    if rc != 0:
+        raise LightningAttnError(rc, "lightning_attn_decode_layers")
     return out
 
 

@@ -564,6 +564,36 @@ int lightning_attn_decode_fused(const void* q, const void* k, const void* v, con
                                     (const int*)slots, num_slots, &fz));
 }
 
+int lightning_attn_decode_layers(const void* q, const void* k, const void* v, const float* decay, void* out,
+                                 float* states, const int32_t* slots, int64_t num_layers, int64_t B, int64_t H,
+                                 int64_t d, int64_t num_slots, int silu, const float* gamma, float eps,
+                                 const void* gate, void* stream) {
+  if (!q || !k || !v || !decay || !out || !states) return LA_ERR_INVALID;
+  if (num_layers < 1 || B < 1 || H < 1 || d < 1 || num_slots < 1) return LA_ERR_INVALID;
+  if (!slots && num_slots < B) return LA_ERR_INVALID;
+  if (!(eps >= 0.0f) || eps > 1.0f) return LA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(decay, 4) ||
+      !aligned(states, 16) || !aligned(slots, 4) || !aligned(gamma, 16) || !aligned(gate, 16))
+    return LA_ERR_INVALID;
+  if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+  // every layer's rows and pool as one of num_layers times the size
+  if (num_layers > kMaxGrid || !dims_fit(num_layers * B, H, 1, num_layers * num_slots)) return LA_ERR_UNSUPPORTED;
+  if (num_layers * B > kMaxGrid || num_layers * num_slots > kMaxGrid) return LA_ERR_UNSUPPORTED;
+  const int64_t vec_bytes = num_layers * B * H * d * 2, pool_bytes = num_layers * num_slots * H * d * d * 4;
+  const int64_t slot_bytes = num_layers * B * 4, gamma_bytes = num_layers * H * d * 4;
+  if (overlap(out, vec_bytes, q, vec_bytes) || overlap(out, vec_bytes, k, vec_bytes) ||
+      overlap(out, vec_bytes, v, vec_bytes) || overlap(out, vec_bytes, states, pool_bytes) ||
+      overlap(out, vec_bytes, slots, slot_bytes) || overlap(states, pool_bytes, slots, slot_bytes) ||
+      overlap(out, vec_bytes, gate, vec_bytes) || overlap(out, vec_bytes, gamma, gamma_bytes) ||
+      overlap(states, pool_bytes, gate, vec_bytes) || overlap(states, pool_bytes, gamma, gamma_bytes) ||
+      overlap(states, pool_bytes, q, vec_bytes) || overlap(states, pool_bytes, k, vec_bytes) ||
+      overlap(states, pool_bytes, v, vec_bytes) || overlap(states, pool_bytes, decay, num_layers * H * 4))
+    return LA_ERR_INVALID;
+  la::DecodeFusion fz{silu ? 1 : 0, gamma, eps, gate};
+  return from_hip(la::launch_decode(q, k, v, decay, out, states, states, B, H, d, (hipStream_t)stream,
+                                    (const int*)slots, num_slots, &fz, num_layers));
+}
+
 int lightning_attn_norm_gate(const void* o, int o_dtype, const void* gate, const float* gamma, float eps, void* out,
                              int64_t B, int64_t H, int64_t N, int64_t d, void* stream) {
   if (!o || !out) return LA_ERR_INVALID;

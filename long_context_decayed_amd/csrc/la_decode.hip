@@ -19,6 +19,13 @@
 // slot lies outside [0, num_slots) is idle: its output is zero and no state
 // is touched.
 //
+// Several layers in one launch: rows are grouped by layer (rows_per_layer
+// rows each, layer-major), and each layer has its own decays ([layer][H]),
+// state pool ([layer][num_slots][H][d][d]), slot table rows and norm weights,
+// so a serving loop can step every lightning layer's ready tokens at once
+// (for example requests pipelined across layers).  A single-layer call is
+// the case rows_per_layer = B.
+//
 // Fused form (the layer's elementwise steps either side of the core; the
 // MiniMax-M1 fact sheet, "linear / SSM layer configuration" and "output gate"
 // fields): SiLU on q, k, v as they are read; per-head RMSNorm of o over its d
@@ -41,7 +48,7 @@ __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ decay, bf16* __restrict__ o, const float* kv_in, float* kv_out, int H, int64_t pairs,
     const int* __restrict__ slots, int64_t num_slots, int silu, const float* __restrict__ gamma, float eps,
-    const bf16* __restrict__ gate) {
+    const bf16* __restrict__ gate, int64_t rows_per_layer) {
   constexpr int TPR = D / 4;              // threads per row
   constexpr int RG = kDecThreads / TPR;   // row groups
   constexpr int RPT = D / RG;             // rows per thread
@@ -53,14 +60,18 @@ __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
   bool valid = pair < pairs;  // no early return: every thread reaches the barriers
   const int cg = tid % TPR, rg = tid / TPR;
   const int64_t b = pair / H, hh = pair - (pair / H) * H;
-  int64_t srow = b;  // state row of this pair: the batch row, or its slot
+  const int64_t layer = b / rows_per_layer;  // 0 for a single-layer call
+  const int64_t lh = layer * H + hh;         // this pair's (layer, head): decay and norm weights
+  // state row of this pair within the layer's pool: the row itself, or its slot
+  int64_t srow = b - layer * rows_per_layer;
   bool idle = false;
   if (slots && valid) {
     srow = slots[b];
     idle = srow < 0 || srow >= num_slots;
     valid = !idle;
   }
-  const float lam = valid ? decay[hh] : 0.0f;
+  srow += layer * num_slots;  // the layer's pool (num_slots rows each)
+  const float lam = valid ? decay[lh] : 0.0f;
   if (valid && tid < D) {
     const float qf = (float)q[pair * D + tid], kf = (float)k[pair * D + tid];
     qs[sub][tid] = silu ? silu_hw(qf) : qf;
@@ -108,7 +119,7 @@ __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
 #pragma unroll
       for (int m = TPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, TPR);
       const float inv = 1.0f / sqrtf(ss / (float)D + eps);
-      const f32x4 gm = *reinterpret_cast<const f32x4*>(gamma + hh * D + 4 * tid);
+      const f32x4 gm = *reinterpret_cast<const f32x4*>(gamma + lh * D + 4 * tid);
       r = r * inv * gm;
     }
     if (gate) {
@@ -125,21 +136,23 @@ __global__ __launch_bounds__(kDecThreads * kDecPairs) void la_decode_kernel(
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* decay, void* out,
                          const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t d, hipStream_t st,
-                         const int* slots, int64_t num_slots, const DecodeFusion* fz) {
+                         const int* slots, int64_t num_slots, const DecodeFusion* fz, int64_t num_layers) {
   const int silu = fz ? fz->silu : 0;
   const float* gamma = fz ? fz->gamma : nullptr;
   const float eps = fz ? fz->eps : 0.0f;
   const bf16* gate = fz ? (const bf16*)fz->gate : nullptr;
-  const int64_t pairs = B * H;
+  const int64_t pairs = num_layers * B * H;
+  // without a slot table a layer's rows use its first B pool rows
+  const int64_t pool = (slots || num_layers > 1) ? num_slots : 0;
   const unsigned grid = (unsigned)((pairs + kDecPairs - 1) / kDecPairs);
   if (d == 128)
     hipLaunchKernelGGL(la_decode_kernel<128>, dim3(grid), dim3(kDecThreads * kDecPairs), 0, st, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, decay, (bf16*)out, kv_in, kv_out, (int)H, pairs, slots,
-                       num_slots, silu, gamma, eps, gate);
+                       pool, silu, gamma, eps, gate, B);
   else
     hipLaunchKernelGGL(la_decode_kernel<64>, dim3(grid), dim3(kDecThreads * kDecPairs), 0, st, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, decay, (bf16*)out, kv_in, kv_out, (int)H, pairs, slots,
-                       num_slots, silu, gamma, eps, gate);
+                       pool, silu, gamma, eps, gate, B);
   return hipGetLastError();
 }
 

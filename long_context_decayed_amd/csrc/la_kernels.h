@@ -73,10 +73,14 @@ struct DecodeFusion {
 
 // Decode step (la_decode.hip); with `slots` (device int32[B]) batch row b uses
 // state row slots[b] of kv_in / kv_out ([num_slots][H][d][d]); rows whose slot
-// is out of range are idle.
+// is out of range are idle.  num_layers > 1: q, k, v, out are
+// [num_layers][B][H][d], decay [num_layers][H], gamma [num_layers][H][d],
+// slots [num_layers][B] and the states [num_layers][num_slots][H][d][d] (row b
+// of a layer without a slot table uses its pool row b).
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* decay, void* out,
                          const float* kv_in, float* kv_out, int64_t B, int64_t H, int64_t d, hipStream_t st,
-                         const int* slots = nullptr, int64_t num_slots = 0, const DecodeFusion* fz = nullptr);
+                         const int* slots = nullptr, int64_t num_slots = 0, const DecodeFusion* fz = nullptr,
+                         int64_t num_layers = 1);
 
 // Per-head RMSNorm of o (bf16 or fp32 [rows][d], rows = B*H*N, head of a row =
 // (row / N) % H) times gamma [H][d] when given, times sigmoid(gate) when given

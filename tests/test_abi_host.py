@@ -364,3 +364,21 @@ def test_noalloc_rejects_sizes_beyond_its_array(lib):
     assert _noalloc(lib, chunk=100) == LA_ERR_INVALID
     assert _noalloc(lib, flags=4) == LA_ERR_INVALID
     assert _noalloc(lib, warm_chunk=96) == LA_ERR_INVALID
+
+
+def test_decode_layers_validation(lib):
+    P = FAKE
+
+    def call(q=P[0], states=P[5], slots=None, L=2, B=3, H=4, d=64, num_slots=3, eps=1e-5, gamma=None, gate=None):
+        return lib.lightning_attn_decode_layers(q, P[1], P[2], P[3], P[4], states, slots, L, B, H, d, num_slots, 0,
+                                                gamma, ctypes.c_float(eps), gate, None)
+
+    assert call(q=None) == LA_ERR_INVALID
+    assert call(states=None) == LA_ERR_INVALID
+    for kw in (dict(L=0), dict(B=0), dict(H=0), dict(num_slots=0), dict(d=0)):
+        assert call(**kw) == LA_ERR_INVALID, kw
+    assert call(num_slots=2) == LA_ERR_INVALID          # no slot table: the pool must hold the batch
+    assert call(eps=-1.0) == LA_ERR_INVALID
+    assert call(d=96) == LA_ERR_UNSUPPORTED
+    assert call(states=ctypes.c_void_p(P[5].value + 4)) == LA_ERR_INVALID  # misaligned
+    assert call(states=P[4]) == LA_ERR_INVALID           # the pool overlapping the output
