@@ -69,8 +69,7 @@ extern "C" {
 /* Flags of lightning_attn_fwd_ex, lightning_attn_fwd_slots, lightning_attn_bwd.
  * LA_FLAG_EXACT: every head by the exact chunked path (chunk aggregates, scan,
  * outputs from the chunk start states), never the warm start described at
- * lightning_attn_fwd; for inputs whose magnitudes vary so much over time that
- * 2^-30 of a state older than the carry span still matters. */
+ * lightning_attn_fwd (nor its check). */
 #define LA_FLAG_EXACT 1u
 /* LA_FLAG_SILU_QKV (lightning_attn_fwd_ex and lightning_attn_fwd_slots only):
  * q, k, v are the pre-activation projections; the kernels apply
@@ -94,23 +93,30 @@ extern "C" {
  *   B, H, N   : >= 1;  d in {64, 128}
  *   block     : intra-block length of the blockwise algorithm, one of
  *               {64, 128, 256}.  The result does not depend on it beyond
- *               rounding.  64 is the tuned path (the 64-token kernels with
- *               LDS DMA and the warm start); 128 and 256 run a general
- *               kernel that is several times slower.
+ *               rounding (at 64 with the warm start and its check described
+ *               below).  64 is the tuned path (the 64-token kernels with LDS
+ *               DMA and the warm start); 128 and 256 run a general kernel
+ *               that is several times slower.
  * Decays are meant to lie in [0, 1].  With bf16 inputs and block 64, a head
  * with span = ceil(30 ln 2 / -ln lam), rounded up to a multiple of 64, at
  * most half the warm-start chunk (lam^span <= 2^-30; the chunk is
- * lightning_attn_fwd_warm_chunk) is computed per chunk of that length from
- * the state that the span tokens before the chunk build from zero: at token
- * t of a chunk the state S_(c0-span-1) from before those tokens is left out
- * of its term lam^(t-c0+span+1) S_(c0-span-1), at most 2^-30 of that state
- * (c0 = the chunk's first token; the first chunk starts from kv_in exactly).
- * Every other head, and every other dtype and block, is computed without
- * omission.  The bound is relative to the omitted term, not to the output:
- * a token whose k^T v is ~10^8 times the typical one, just before a chunk's
- * warm-up window, can move outputs of the chunk by ~10% of their size.  The
+ * lightning_attn_fwd_warm_chunk) is first computed per chunk of that length
+ * from the state W_c that the span tokens before the chunk build from zero
+ * (the warm start; c0 = the chunk's first token, the first chunk starts from
+ * kv_in): the state X_c = S_(c0-span-1) from before those tokens is left
+ * out, and it would enter token t of the chunk as lam^(t-c0+span+1) X_c,
+ * beside the carried lam^(t-c0+1) W_c.  A check on the device then compares,
+ * for every chunk, lam^span max|X_c| with 2^-24 max|W_c| (largest entries):
+ * if any chunk exceeds it (a burst of large keys and values just before a
+ * window, a window of zeros, NaN or inf), the head is computed again on the
+ * exact path, so what is left out never exceeds the fp32 rounding bound of
+ * the carried term.  On Gaussian inputs the ratio is about 2^-30 and no head
+ * is recomputed; the check and the (then empty) recomputation launches add
+ * a few microseconds.  Heads that do not decay within a warm-start chunk,
+ * and every other dtype and block, take the exact path from the start.  The
  * _ex entry point with LA_FLAG_EXACT takes the exact path for every head.
- * Scratch (decay-power table and per-chunk states, see
+ * The result does not depend on the path beyond rounding.
+ * Scratch (decay-power table, per-chunk states and the check's slots, see
  * lightning_attn_fwd_workspace_bytes) is allocated stream-ordered with
  * hipMallocAsync/hipFreeAsync on `stream`.
  */
@@ -186,10 +192,14 @@ int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const 
  * G_t = dL/dS_t = lam G_{t+1} + q_t^T dout_t, G_{N-1} = dkv_out + q_{N-1}^T dout_{N-1}:
  *     dq_t = dout_t S_t^T,  dk_t = v_t G_t^T,  dv_t = k_t G_t,  dkv_in = lam G_0.
  * Each of dq, dk, dv is computed as a prefill-shaped pass (dk and dv run the
- * tokens last first) with the kernels of lightning_attn_fwd_ex at block 64,
- * so with bf16 inputs the same omission below 2^-30 applies to heads that
- * decay within a chunk.  With bf16 inputs the dk and dv passes share their
- * kernel launches (each keeps its own chunk states in the workspace).
+ * tokens last first) with the kernels of lightning_attn_fwd_ex at block 64.
+ * With bf16 inputs the heads that decay within a chunk take the warm start:
+ * the dq pass with its check, as in lightning_attn_fwd; the reverse dk and dv
+ * passes without it (their warm starts leave out at most 2^-30 of the
+ * adjoint state from before each window, relative to that state; use
+ * LA_FLAG_EXACT where gradients can burst).  With bf16 inputs the dk and dv
+ * passes share their kernel launches (each keeps its own chunk states in the
+ * workspace).
  *   q, k, v, dout : in_dtype [B][H][N][d]          (read)
  *   decay         : float [H]                      (read)
  *   kv_in         : float [B][H][d][d] or NULL     (read: the forward's initial state; NULL = zero)
@@ -230,8 +240,12 @@ int64_t lightning_attn_fwd_warm_chunk(int64_t B, int64_t H, int64_t N, int64_t b
                                       int64_t warm_chunk);
 
 /* Bytes of scratch lightning_attn_fwd_ex needs for these sizes (0 on invalid
- * arguments).  Layout: the decay-power table, then B*H*ceil(N/chunk) float32
- * d x d chunk states. */
+ * arguments).  Layout, each part starting 256-byte aligned: the decay-power
+ * table; B*H*ceil(N/chunk) float32 d x d chunk states; the warm-start check's
+ * slots (8 floats per (b, h) and chunk); and, as the last B*H*4 bytes, one
+ * int32 per (b, h), row-major: 1 when the check sent that head to the exact
+ * path in the call, else 0 (written by every bf16 block-64 call without
+ * LA_FLAG_EXACT). */
 size_t lightning_attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
                                           int64_t chunk);
 

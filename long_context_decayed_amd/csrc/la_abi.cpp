@@ -108,12 +108,22 @@ int resolve_warm_chunk(int64_t B, int64_t H, int64_t N, int64_t chunk, int64_t w
 
 int64_t tbl_stride_for(int64_t block) { return ((block + 1 + 63) / 64) * 64; }
 
-size_t workspace_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, int64_t L, size_t* tbl_bytes) {
+// Workspace: the decay-power table, the chunk states [B*H][nc][d][d], the
+// warm-start check's slots (kGuardSlots floats per (bh, chunk); the
+// warm-start chunks are never more than the scan's) and its flags (one int
+// per bh), each part 256-byte aligned.
+size_t workspace_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, int64_t L, size_t* tbl_bytes,
+                        size_t* guard_off = nullptr, size_t* flags_off = nullptr) {
   const size_t tb = (size_t)H * (size_t)tbl_stride_for(block) * sizeof(float);
   const size_t tb_al = (tb + 255) / 256 * 256;
   const size_t nc = (size_t)ceil_div(N, L);
+  const size_t bh = (size_t)B * (size_t)H;
   if (tbl_bytes) *tbl_bytes = tb_al;
-  return tb_al + (size_t)B * (size_t)H * nc * (size_t)d * (size_t)d * sizeof(float);
+  const size_t g = (tb_al + bh * nc * (size_t)d * (size_t)d * sizeof(float) + 255) / 256 * 256;
+  const size_t f = (g + bh * nc * la::kGuardSlots * sizeof(float) + 255) / 256 * 256;
+  if (guard_off) *guard_off = g;
+  if (flags_off) *flags_off = f;
+  return f + bh * sizeof(int);
 }
 
 int from_hip(hipError_t e) {
@@ -157,13 +167,30 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* d
 // output row (the decaying heads' warm-start pass and the others' pass C side
 // by side), then the decaying heads' final states copied out (after every
 // chunk has read kv_in, which may be kv_out).
+// With the warm-start check (a.guard and a.flags set), after the output
+// launch the check flags the decaying heads whose warm start left out a
+// state that is not negligible; the copy skips them, and they are run again
+// on the exact path (pass A, scan, pass C of the flagged heads only: three
+// launches whose workgroups return at once when no head is flagged).
 hipError_t run_passes(const la::PrefillArgs& a, hipStream_t st) {
   if (a.warm_start && a.rev) return hipErrorInvalidValue;
   hipError_t e = la::launch_aggregate_pass(a, st);
   if (a.warm_start) {
     if (e == hipSuccess) e = la::launch_scan_pass(a, st, 1);
     if (e == hipSuccess) e = la::launch_mixed_pass(a, st);
+    const bool check = a.guard && a.flags;
+    if (e == hipSuccess && check) e = la::launch_warm_guard(a, st);
     if (e == hipSuccess) e = la::launch_scan_pass(a, st, 2);
+    if (check) {
+      la::PrefillArgs r = a;
+      r.warm_start = false;
+      r.rerun = true;
+      r.evt_begin = nullptr;
+      r.evt_end = nullptr;
+      if (e == hipSuccess) e = la::launch_aggregate_pass(r, st);
+      if (e == hipSuccess) e = la::launch_scan_pass(r, st, 3);
+      if (e == hipSuccess) e = la::launch_output_pass(r, st);
+    }
     return e;
   }
   if (e == hipSuccess) e = la::launch_scan_pass(a, st);
@@ -239,8 +266,8 @@ int prefill_run(const void* q, const void* k, const void* v, const float* decay,
                 int out_dtype, int64_t L, int64_t Lw, void* workspace, size_t workspace_bytes, void* evt_begin,
                 void* evt_end, void* stream, const int* slots, int64_t num_slots, unsigned int flags) {
   const bool exact = (flags & LA_FLAG_EXACT) != 0;
-  size_t tbl_bytes = 0;
-  const size_t need = workspace_layout(B, H, N, d, block, L, &tbl_bytes);
+  size_t tbl_bytes = 0, guard_off = 0, flags_off = 0;
+  const size_t need = workspace_layout(B, H, N, d, block, L, &tbl_bytes, &guard_off, &flags_off);
   if (workspace) {
     if (workspace_bytes < need) return LA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return LA_ERR_INVALID;
@@ -282,6 +309,9 @@ int prefill_run(const void* q, const void* k, const void* v, const float* decay,
   a.num_slots = num_slots;
   a.evt_begin = evt_begin;
   a.evt_end = evt_end;
+  a.guard = a.warm_start ? (float*)((char*)ws + guard_off) : nullptr;
+  a.flags = a.warm_start ? (int*)((char*)ws + flags_off) : nullptr;
+  a.rerun = false;
   hipError_t e = run_passes(a, st);
   if (!workspace) {
     hipError_t f = hipFreeAsync(ws, st);
@@ -389,8 +419,8 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
     hipError_t e = hipMallocAsync(&ws, need, st);
     if (e != hipSuccess) return e == hipErrorOutOfMemory ? LA_ERR_NOMEM : LA_ERR_HIP;
   }
-  size_t tbl_bytes = 0;
-  workspace_layout(B, H, N, d, 64, L, &tbl_bytes);
+  size_t tbl_bytes = 0, guard_off = 0, flags_off = 0;
+  workspace_layout(B, H, N, d, 64, L, &tbl_bytes, &guard_off, &flags_off);
   float* s0t = (float*)((char*)ws + s0t_off);
   float* dsnt = (float*)((char*)ws + dsnt_off);
 
@@ -415,6 +445,11 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
   a.num_slots = 0;
   a.evt_begin = nullptr;
   a.evt_end = nullptr;
+  // the dQ pass runs forward and takes the warm-start check; the reverse
+  // passes of dK and dV below do not
+  a.guard = a.warm_start ? (float*)((char*)ws + guard_off) : nullptr;
+  a.flags = a.warm_start ? (int*)((char*)ws + flags_off) : nullptr;
+  a.rerun = false;
 
   hipError_t e = hipSuccess;
   if (kv_in) e = la::launch_transpose_states(kv_in, s0t, B * H, d, st);
@@ -433,6 +468,8 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
   }
   // dK: dk_t = v_t G_t^T, G^T run last token first over (V, dO, Q) from dSN^T.
   la::PrefillArgs ak = a;
+  ak.guard = nullptr;
+  ak.flags = nullptr;
   ak.q = v;
   ak.k = dout;
   ak.v = q;

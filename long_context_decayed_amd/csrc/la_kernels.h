@@ -8,6 +8,11 @@ namespace la {
 
 enum { kBF16 = 0, kF32 = 1 };
 
+// Floats per (bh, warm-start chunk) slot of the warm-start check: the
+// per-wave largest |S| of the state just before the next chunk's warm-up
+// window ([0, 4)) and of the state the chunk's own warm-up builds ([4, 8)).
+constexpr int kGuardSlots = 8;
+
 struct PrefillArgs {
   const void* q;
   const void* k;
@@ -32,6 +37,13 @@ struct PrefillArgs {
   int64_t num_slots;
   void* evt_begin; // optional hipEvent_t pair around the kernel that writes every output row
   void* evt_end;
+  // Warm-start check (forward passes with warm_start): guard, kGuardSlots
+  // floats per (bh, warm-start chunk), written by the warm-start chunks;
+  // flags, one int per bh, set by the check for the heads whose warm start
+  // left out a state that is not negligible.  Null: no check.
+  float* guard;
+  int* flags;
+  bool rerun;      // run only the heads whose flag is set, on the exact path
 };
 
 // Decay table and pass A (chunk aggregates; with warm_start, of the heads
@@ -39,8 +51,13 @@ struct PrefillArgs {
 hipError_t launch_aggregate_pass(const PrefillArgs& a, hipStream_t st);
 // Pass B (chunk scan: start states, final state; with warm_start, the
 // decaying heads' final states are only copied out); part 0 every head, 1 the
-// scan of the other heads only, 2 the decaying heads' copy only: la_state.hip.
+// scan of the other heads only, 2 the decaying heads' copy only (those whose
+// flag is set excepted), 3 the scan of the flagged heads only: la_state.hip.
 hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st, int part = 0);
+// The warm-start check: flags[bh] = 1 for a decaying head when some chunk's
+// warm-up window left out a state above 2^-24 of the state it starts from
+// (la_state.hip).
+hipError_t launch_warm_guard(const PrefillArgs& a, hipStream_t st);
 // Pass C (outputs from the chunk start states; with warm_start, of the
 // heads that do not decay within their chunk only): la_output.hip.
 hipError_t launch_output_pass(const PrefillArgs& a, hipStream_t st);

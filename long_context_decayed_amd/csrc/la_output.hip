@@ -350,7 +350,30 @@ struct Operands {
   void* o;
   float* states;       // chunk states of this problem
   const float* kv_in;  // initial states, or null
+  // Warm-start check (forward, or null): per (bh, warm-start chunk) slot of
+  // kGuardSlots floats, [0, NW) the largest |S| per wave of the state just
+  // before the next chunk's warm-up window, [4, 4 + NW) that of the state
+  // the chunk's own warm-up builds (see la_warm_guard in la_state.hip).
+  float* guard;
+  // Heads to run (pass C of the heads whose warm start failed the check), or
+  // null: every head of the launch's kind.
+  const int* only;
 };
+
+// Largest |x| over this wave's share of the state (each lane's 16 NRT
+// accumulators), taken on the bit patterns of |x| so that a NaN (above +inf)
+// is not lost; lane 0 stores it to dst.
+template <int NRT>
+__device__ __forceinline__ void store_wave_absmax(const f32x16 (&S)[NRT], float* dst, int lane) {
+  uint32_t m = 0u;
+#pragma unroll
+  for (int kt = 0; kt < NRT; ++kt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m = max(m, __float_as_uint(S[kt][j]) & 0x7fffffffu);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if (lane == 0) *dst = __uint_as_float(m);
+}
 
 // LDS of one block-64 workgroup (80 KiB at d = 128).
 template <int D>
@@ -394,6 +417,9 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
   const int span = carry_span(decay[hh]);
   const bool decaying = warm && decays_within_chunk(span, Lw);  // warm = 0: every head from its start state
   if (decaying != (MODE == kWarmStart)) return;
+  const int* __restrict__ only = pi ? p1.only : p0.only;
+  if (only && !only[bh]) return;
+  float* __restrict__ guard = pi ? p1.guard : p0.guard;
   const int t_begin = c * L;
   const int t_end = min(N, t_begin + L);
   const int64_t base = (int64_t)bh * N * D + (REV ? (int64_t)(N - 1) * D : 0);
@@ -515,8 +541,12 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
         update_full(odd ? Ks : Kt, odd ? Qs : Vs);
       }
       __syncthreads();  // every wave is done with the warm-up tiles
+      if (guard) store_wave_absmax<NRT>(S, guard + ((int64_t)bh * nc + c) * kGuardSlots + 4 + w, lane);
     }
   }
+  // Warm start: the token before the next chunk's warm-up window, where the
+  // state that window leaves out is this chunk's (none for the last chunk).
+  const int t_mark = (MODE == kWarmStart && guard && c + 1 < nc && span > 0) ? t_end - span : -1;
 
   {
     const int nv = min(kSub, t_end - t_begin);
@@ -545,6 +575,8 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
     const bool first = REV && c == 0 && t0 == t_begin;
     const int nv_next = min(kSub, t_end - t0 - kSub);
     const int64_t off_next = (int64_t)(t0 + kSub) * RS;
+    if (MODE == kWarmStart && t0 == t_mark)  // S is the state after token t0 - 1
+      store_wave_absmax<NRT>(S, guard + ((int64_t)bh * nc + c) * kGuardSlots + w, lane);
 
     // Phase 1.  Inter term acc[rt] = S_b^T Q^T for tokens 32rt + l (S split
     // into bf16 hi + lo on the fly) and this wave's score tiles P^T = K Q^T,
@@ -891,7 +923,8 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64_mixed_pair(
 // The events bracket the kernel that writes every output row: the
 // warm-start pass when there is one (bf16 inputs, block 64), else this one.
 static Operands operands_of(const PrefillArgs& a) {
-  return Operands{(const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.out, a.states, a.kv_in};
+  return Operands{(const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.out, a.states, a.kv_in,
+                  a.warm_start ? a.guard : nullptr, a.rerun ? a.flags : nullptr};
 }
 
 // One problem (b == nullptr), or two of one shape in one grid (the pair's
@@ -925,7 +958,7 @@ static hipError_t launch_output_t(const PrefillArgs& a, hipStream_t st) {
   if (a.silu && !(BLK == 64 && sizeof(TIn) == 2)) return hipErrorInvalidValue;  // SiLU: block-64 bf16 kernels only
   const int BH = (int)(a.B * a.H);
   const int nc = a.nc;
-  const bool timed = !a.warm_start;
+  const bool timed = !a.warm_start && !a.rerun;
   if (timed && a.evt_begin) {
     hipError_t e = hipEventRecord((hipEvent_t)a.evt_begin, st);
     if (e != hipSuccess) return e;

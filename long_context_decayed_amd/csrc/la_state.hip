@@ -134,7 +134,8 @@ __global__ __launch_bounds__(D * 2, sizeof(TIn) == 2 ? 3 : 1) void la_chunk_stat
 // transpose-read operands): lam^(63-s) u = ul[i] * (lam^(48-16kk) u) with the
 // per-lane ul[i] = lam^(15 - crow(i, h)).
 //   With skip_decaying set, heads that decay within their chunk return at
-// once: the warm-start output pass needs no aggregates.  REV reads the
+// once: the warm-start output pass needs no aggregates.  With `only`, just
+// the heads whose flag is set run (their warm start failed its check).  REV reads the
 // tokens last first (token t of the pass is row N-1-t), for the reverse-time
 // passes of the backward; the aggregates start from zero either way.  SILU:
 // k and v are pre-activations, given SiLU in LDS as each tile arrives (as in
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
                                                              const float* __restrict__ decay,
                                                              const float* __restrict__ tbl_all, float* __restrict__ ws,
                                                              int H, int N, int L, int nc, int tbl_stride,
-                                                             int skip_decaying, int Lw) {
+                                                             int skip_decaying, int Lw, const int* __restrict__ only) {
   typedef Mfma<bf16> M;
   typedef M::op_t op_t;
   constexpr int NW = D / 32;
@@ -156,7 +157,11 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
   const int hh = bh % H;
-  if (skip_decaying && decays_within_chunk(carry_span(decay[hh]), Lw)) return;  // judged by the warm chunk
+  if (only) {
+    if (!only[bh]) return;  // the exact path for the heads whose warm start failed its check
+  } else if (skip_decaying && decays_within_chunk(carry_span(decay[hh]), Lw)) {
+    return;  // judged by the warm chunk
+  }
   constexpr int RS = REV ? -D : D;  // elements from one token's row to the next
   const int64_t base = (int64_t)bh * N * D + (REV ? (int64_t)(N - 1) * D : 0);
   const bf16* kb = k + base;
@@ -274,12 +279,15 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
 // hands on lam^(L_0 - 1) kv_in + U_0); with scale_out, kv_out receives lam
 // times the final state (the backward's gradient of the initial state).
 // part: 0 every head; 1 only the heads that do not decay within their chunk
-// (the scan proper); 2 only the decaying heads' copy (after their pass).
+// (the scan proper); 2 only the decaying heads' copy (after their pass),
+// except those whose flag is set; 3 the scan proper of the flagged heads
+// only (their warm start failed its check: the exact path).
 __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ decay, float* __restrict__ ws,
                                                      const float* __restrict__ kv_in, float* __restrict__ kv_out,
                                                      int BH, int H, int N, int L, int nc, int D, int warm,
                                                      int undecayed, int scale_out, const int* __restrict__ slots,
-                                                     int64_t num_slots, int Lw, int part) {
+                                                     int64_t num_slots, int Lw, int part,
+                                                     const int* __restrict__ flags) {
   const int per = D * D / 4;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)BH * per) return;
@@ -290,8 +298,10 @@ __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ d
     kv_out = nullptr;
   }
   const float out_f = scale_out ? decay[bh % H] : 1.0f;
-  if (warm && decays_within_chunk(carry_span(decay[bh % H]), Lw)) {  // judged by the warm chunk
-    if (kv_out && part != 1)
+  const bool flagged = flags && flags[bh];
+  if (part == 3 && !flagged) return;
+  if (part != 3 && warm && decays_within_chunk(carry_span(decay[bh % H]), Lw)) {  // judged by the warm chunk
+    if (kv_out && part != 1 && !flagged)
       reinterpret_cast<f32x4*>(kv_out)[srow * per + e4] =
           out_f * reinterpret_cast<const f32x4*>(ws)[((int64_t)bh * nc + nc - 1) * per + e4];
     return;
@@ -327,6 +337,50 @@ __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ d
 }
 
 // ---------------------------------------------------------------------------
+// The warm-start check.  Chunk c > 0 of a decaying head starts from W_c, the
+// state its warm-up window of span tokens builds from zero, and leaves out
+// lam^span X_c, X_c the state just before that window (computed by chunk
+// c - 1, which passes that token).  Both enter every row t of the chunk
+// with the same factor lam^(t - c0 + 1), so the omission is below the
+// rounding of the carried term when lam^span max|X_c| <= 2^-24 max|W_c| (the
+// largest entries; each row's error then stays under 2^-24 sum_j |q_j| max|W|,
+// the fp32 rounding bound of q W itself).  On the workloads' inputs the ratio
+// is about lam^span <= 2^-30; a state 2^6 times larger than the window's own
+// (a burst of large keys and values just before a window, or a window of
+// zeros) fails it, and the head is then run on the exact path.  lam = 0 has
+// span 0 and omits nothing.  NaN or inf in either fails the check.  One wave
+// per bh; every flag is written.
+__global__ __launch_bounds__(64) void la_warm_guard(const float* __restrict__ decay, const float* __restrict__ guard,
+                                                    int* __restrict__ flags, int H, int ncw, int Lw, int nw) {
+  const int bh = blockIdx.x, lane = threadIdx.x;
+  const float lam = decay[bh % H];
+  const int span = carry_span(lam);
+  bool bad = false;
+  if (span > 0 && decays_within_chunk(span, Lw)) {
+    const double f = pow_int((double)lam, span);
+    for (int c = 1 + lane; c < ncw; c += 64) {
+      const float* xs = guard + ((int64_t)bh * ncw + c - 1) * kGuardSlots;
+      const float* ws = guard + ((int64_t)bh * ncw + c) * kGuardSlots + 4;
+      float x = 0.0f, wv = 0.0f;
+      for (int w = 0; w < nw; ++w) {  // as bit patterns: a NaN stays the largest
+        x = __uint_as_float(max(__float_as_uint(x), __float_as_uint(xs[w])));
+        wv = __uint_as_float(max(__float_as_uint(wv), __float_as_uint(ws[w])));
+      }
+      if (!((double)x * f <= 0x1p-24 * (double)wv)) bad = true;
+    }
+  }
+  bad = __any(bad);
+  if (lane == 0) flags[bh] = bad ? 1 : 0;
+}
+
+hipError_t launch_warm_guard(const PrefillArgs& a, hipStream_t st) {
+  if (!a.guard || !a.flags || !a.warm_start) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(la_warm_guard, dim3((unsigned)(a.B * a.H)), dim3(64), 0, st, a.decay, (const float*)a.guard,
+                     a.flags, (int)a.H, a.nc_warm, (int)a.L_warm, (int)(a.d / 32));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // dst[bh] = src[bh]^T for BH fp32 d x d states (the backward passes take the
 // transposed initial state and final-state gradient).  One thread per
 // element; writes are contiguous.
@@ -353,22 +407,25 @@ template <typename TIn, int D>
 static hipError_t launch_aggregate_t(const PrefillArgs& a, hipStream_t st) {
   const int BH = (int)(a.B * a.H);
   const int nc = a.nc;
-  hipLaunchKernelGGL(la_decay_table, dim3((unsigned)a.H), dim3(256), 0, st, a.decay, a.tbl, a.tbl_stride);
+  // the exact path of heads whose warm start failed its check reuses the table
+  if (!a.rerun)
+    hipLaunchKernelGGL(la_decay_table, dim3((unsigned)a.H), dim3(256), 0, st, a.decay, a.tbl, a.tbl_stride);
+  const int* only = a.rerun ? a.flags : nullptr;
   if constexpr (sizeof(TIn) == 2) {
     if (a.rev)  // the backward: no SiLU
       hipLaunchKernelGGL((la_chunk_state64<D, true, false>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                          (const bf16*)a.k, (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H,
-                         (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0, (int)a.L_warm);
+                         (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0, (int)a.L_warm, only);
     else if (a.silu)
       hipLaunchKernelGGL((la_chunk_state64<D, false, true>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                          (const bf16*)a.k, (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H,
-                         (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0, (int)a.L_warm);
+                         (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0, (int)a.L_warm, only);
     else
       hipLaunchKernelGGL((la_chunk_state64<D, false, false>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st,
                          (const bf16*)a.k, (const bf16*)a.v, a.decay, (const float*)a.tbl, a.states, (int)a.H,
-                         (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0, (int)a.L_warm);
-  } else if (a.silu) {
-    return hipErrorInvalidValue;  // SiLU: bf16 inputs only
+                         (int)a.N, (int)a.L, nc, a.tbl_stride, a.warm_start ? 1 : 0, (int)a.L_warm, only);
+  } else if (a.silu || a.rerun) {
+    return hipErrorInvalidValue;  // SiLU and the warm-start check: bf16 inputs only
   } else if (a.rev)
     hipLaunchKernelGGL((la_chunk_state<TIn, D, true>), dim3((unsigned)(BH * nc)), dim3(D * 2), 0, st, (const TIn*)a.k,
                        (const TIn*)a.v, (const float*)a.tbl, a.states, (int)a.H, (int)a.N, (int)a.L, nc,
@@ -392,7 +449,8 @@ hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st, int part) {
   const int64_t threads = (int64_t)BH * D * D / 4;
   hipLaunchKernelGGL(la_chunk_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a.decay, a.states,
                      a.kv_in, a.kv_out, BH, (int)a.H, (int)a.N, (int)a.L, a.nc, D, a.warm_start ? 1 : 0,
-                     a.rev ? 1 : 0, a.scale_kv_out ? 1 : 0, a.slots, a.num_slots, (int)a.L_warm, part);
+                     a.rev ? 1 : 0, a.scale_kv_out ? 1 : 0, a.slots, a.num_slots, (int)a.L_warm, part,
+                     (const int*)a.flags);
   return hipGetLastError();
 }
 

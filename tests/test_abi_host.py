@@ -112,7 +112,9 @@ def test_workspace_and_chunk_values(lib):
     # million-token prefill: 64 heads, d=128, block 256 -> 16384-token chunks, 64 per head (4096 workgroups)
     assert lib.lightning_attn_fwd_chunk(1, 64, 1 << 20, 256, 0) == 16384
     tbl = 64 * 320 * 4
-    assert lib.lightning_attn_fwd_workspace_bytes(1, 64, 1 << 20, 128, 256, 0) == tbl + 64 * 64 * 128 * 128 * 4
+    states = 64 * 64 * 128 * 128 * 4
+    guard = 64 * 64 * 8 * 4  # the warm-start check: 8 floats per (b, h, chunk), then one int per (b, h)
+    assert lib.lightning_attn_fwd_workspace_bytes(1, 64, 1 << 20, 128, 256, 0) == tbl + states + guard + 64 * 4
     # batched: 4 x 64 heads x 65536 tokens -> halve once to reach 2048 workgroups
     assert lib.lightning_attn_fwd_chunk(4, 64, 65536, 64, 0) == 8192
     # 8192 tokens x 64 heads: chunks halve until >= 2048 workgroups (floor 256)

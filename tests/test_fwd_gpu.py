@@ -340,31 +340,79 @@ def test_bf16_classification_boundary(dev):
 
 # --- the exact path on demand --------------------------------------------------
 
-def test_exact_flag_with_a_spike_before_the_warm_up_window(dev):
+def _warm_flags(ws, B, H):
+    """The warm-start check's per-(b, h) flags: the last B*H int32 of the
+    workspace (its documented layout)."""
+    return ws[ws.numel() - 4 * B * H:].view(torch.int32).cpu().numpy()
+
+
+def test_spike_before_the_warm_up_window_is_caught(dev):
     # lam = 0.7 at chunk 256 takes the warm start (carry span 64): chunk 1
     # starts from zero at token 192.  A token at 190 whose k and v are 1e5
     # times the others still weighs lam^66 * 1e10 ~ 0.6 of a typical term on
-    # the first rows of chunk 1: the warm start leaves it out (it bounds the
-    # omission by 2^-30 of that term, not of the output), the exact path not.
-    say("exact flag: spike before the warm-up window, B1 H1 N512 d128 chunk 256")
+    # the first rows of chunk 1.  The warm-start check sees the left-out state
+    # far above 2^-24 of the window's own, flags the head and runs it on the
+    # exact path: the default entry point matches the oracle there, as the
+    # exact flag does.
+    say("spike before the warm-up window, B1 H1 N512 d128 chunk 256: default and exact flag")
     q, k, v = qkv_device(1, 1, 512, 128, seed=140, device=dev)
     k[:, :, 190] *= 1e5
     v[:, :, 190] *= 1e5
     lam = np.array([0.7], dtype=np.float32)
-    o_ref, _ = oracle(host(q), host(k), host(v), lam)
-    rows = slice(256, 320)
-    r = tol.rms(o_ref[:, :, rows])
-    warm = la.fwd(q, k, v, torch.from_numpy(lam).to(dev), block=64, chunk=256, out_dtype=torch.float32)
-    exact = la.fwd(q, k, v, torch.from_numpy(lam).to(dev), block=64, chunk=256, out_dtype=torch.float32, exact=True)
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lam)
+    lam_d = torch.from_numpy(lam).to(dev)
+    ws = torch.empty(la.workspace_bytes(1, 1, 512, 128, 64, 256), device=dev, dtype=torch.uint8)
+    kv = torch.empty((1, 1, 128, 128), device=dev, dtype=torch.float32)
+    default = la.fwd(q, k, v, lam_d, kv_out=kv, block=64, chunk=256, out_dtype=torch.float32, workspace=ws)
     torch.cuda.synchronize()
-    e_exact = tol.assert_bf16_f32out(host(exact)[:, :, rows], o_ref[:, :, rows], "exact, rows 256-319")
-    e_warm = tol.bf16_rms_error(host(warm)[:, :, rows], o_ref[:, :, rows], r)
-    print("rows 256-319: exact %.3e, warm start %.3e (max|err| / RMS of those rows)" % (e_exact, e_warm))
-    assert e_warm > 0.1, "the spike should be visible to the exact path only"
-    # away from the spike's reach both agree with the oracle
-    far = slice(400, 512)
-    for o in (warm, exact):
-        tol.assert_bf16_f32out(host(o)[:, :, far], o_ref[:, :, far], "rows 400-511")
+    flags = _warm_flags(ws, 1, 1)
+    exact = la.fwd(q, k, v, lam_d, block=64, chunk=256, out_dtype=torch.float32, exact=True)
+    torch.cuda.synchronize()
+    assert flags.tolist() == [1], flags
+    rows = slice(256, 320)
+    for name, o in (("default", default), ("exact", exact)):
+        tol.assert_bf16_f32out(host(o)[:, :, rows], o_ref[:, :, rows], "%s, rows 256-319" % name)
+        tol.assert_bf16_f32out(host(o), o_ref, name)
+    tol.assert_state(host(kv), s_ref, "kv_out")
+    # the flagged head ran the exact path: the same kernels as the exact flag
+    assert torch.equal(default, exact)
+
+
+def test_warm_up_window_of_zeros_is_caught(dev):
+    # Keys of zero over chunk 1's whole warm-up window [192, 256): the window
+    # builds no state at all, so any earlier state is not negligible against
+    # it and the head runs on the exact path.
+    say("zero keys over the warm-up window, B1 H2 N700 d64 chunk 256, with state")
+    q, k, v = qkv_device(1, 2, 700, 64, seed=141, device=dev)
+    k[:, :, 192:256] = 0
+    lam = np.array([0.7, 0.3], dtype=np.float32)
+    s0 = state_device(1, 2, 64, seed=141, device=dev)
+    ws = torch.empty(la.workspace_bytes(1, 2, 700, 64, 64, 256), device=dev, dtype=torch.uint8)
+    kv = torch.empty_like(s0)
+    o = la.fwd(q, k, v, torch.from_numpy(lam).to(dev), kv_in=s0, kv_out=kv, block=64, chunk=256,
+               out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    flags = _warm_flags(ws, 1, 2)
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lam, host(s0).astype(np.float64))
+    assert flags.tolist() == [1, 1], flags
+    for h in range(2):
+        tol.assert_bf16_f32out(host(o)[:, h], o_ref[:, h], "O head %d" % h)
+        tol.assert_state(host(kv)[:, h], s_ref[:, h], "kv_out head %d" % h)
+
+
+def test_warm_start_check_passes_the_workloads(dev):
+    """On the workloads' Gaussian inputs no head is flagged (the left-out
+    state is about lam^span <= 2^-30 of the window's), at the 64-head
+    8192-token layer and with the decays of deeper layers."""
+    B, H, N, d = 1, 64, 8192, 128
+    q, k, v = qkv_device(B, H, N, d, seed=1, device=dev)
+    ws = torch.empty(la.workspace_bytes(B, H, N, d, 64), device=dev, dtype=torch.uint8)
+    for layer in (0, 23, 46, 60):
+        say("warm-start check on the B1 H64 N8192 d128 layer, decays of layer", layer, "of 70")
+        lam = torch.from_numpy(decay_lambdas_depth(H, layer, 70)).to(dev)
+        la.fwd(q, k, v, lam, block=64, workspace=ws)
+        torch.cuda.synchronize()
+        assert not _warm_flags(ws, B, H).any(), layer
 
 
 def test_exact_flag_matches_oracle_on_mixed_decays(dev):
