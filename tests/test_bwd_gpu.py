@@ -175,3 +175,36 @@ def test_bwd_exact_flag(dev):
     _check_heads(dv, rv, "dV", H)
     for h in range(H):
         tol.assert_state(host(ds0)[:, h], rs[:, h], "dS0 head %d" % h)
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_bwd_warm_chunk_longer_than_scan_chunk(dev, in_place):
+    """At B16 H4 N16384 the backward's scan chunk is 512 tokens and its
+    warm-start chunk 1024, so the paired dK / dV launch runs warm-start chunks
+    of one length beside pass-C chunks of another, and hands the reverse-time
+    warm start's final state on as dS0.  Decays: 0, one with a carry span of
+    512 (warm start only at the longer chunk), one just below 1, and 1; initial
+    state and final-state gradient given, dS0 written over dS_N (in place) or
+    apart."""
+    B, H, n, d = 16, 4, 16384, 64
+    assert la.chunk_for(B, H, n, 64) == 512 and la.warm_chunk_for(B, H, n, 64) == 1024
+    lams = np.array([0.0, 0.96, 0.9995, 1.0], dtype=np.float32)
+    say("bwd warm chunk 1024 > scan chunk 512, B16 H4 N16384 d64, in place", in_place)
+    q, k, v = qkv_device(B, H, n, d, seed=170, device=dev)
+    g = qkv_device(B, H, n, d, seed=171, device=dev)[0]
+    s0 = state_device(B, H, d, seed=172, device=dev)
+    dsn = state_device(B, H, d, seed=173, device=dev)
+    dsn_host = dsn.clone()
+    ds_out = dsn if in_place else True
+    dq, dk, dv, ds0 = la.bwd(q, k, v, torch.from_numpy(lams).to(dev), g, kv_in=s0, dkv_out=dsn,
+                             out_dtype=torch.float32, dkv_in=ds_out)
+    torch.cuda.synchronize()
+    if in_place:
+        assert ds0.data_ptr() == dsn.data_ptr()
+    rq, rk, rv, rs = _grad_oracle(q, k, v, lams, g, s0, dsn_host)
+    _check_heads(dq, rq, "dQ", H)
+    _check_heads(dk, rk, "dK", H)
+    _check_heads(dv, rv, "dV", H)
+    ds_h = host(ds0)
+    for h in range(H):
+        tol.assert_state(ds_h[:, h], rs[:, h], "dS0 head %d" % h)
