@@ -28,10 +28,12 @@ ONE JSON line:
                  warm start
   backward       the backward pass of the same layer (dq, dk, dv from dout)
   epilogue_prologue  per-head RMSNorm + sigmoid gate of the output and SiLU
-                 on one input, as their own passes over the same layer; and
-                 the prefill step with SiLU on q, k, v fused into its tile
-                 loads (LA_FLAG_SILU_QKV) beside the step plus three SiLU
-                 passes
+                 on one input, as their own passes over the same layer; the
+                 prefill step with SiLU on q, k, v fused into its tile loads
+                 (LA_FLAG_SILU_QKV) beside the step plus three SiLU passes;
+                 and the step with the norm and gate fused into its output
+                 kernels (lightning_attn_fwd_fused), with and without SiLU,
+                 beside the same work as separate passes
   decode         256 sequences x 64 heads x d=128 decode step, 1000 in-place
                  steps timed as a whole: GB/s of state + token traffic; and
                  the same rows through a slot table over a 512-slot pool, and
@@ -244,17 +246,32 @@ def bench_prefill(args, dev):
                              ms_per_step=ms_l, tokens_per_s=B * N / (ms_l * 1e-3)))
         res["depth_scaled"] = dict(n_layers=70, layers=rows,
                                    mean_ms_over_sampled_layers=sum(r["ms_per_step"] for r in rows) / len(rows))
-    ms_silu = None
+    ms_silu = ms_norm_gate_fused = ms_layer_fused = None
     if args.fused and block == 64:
         # the same step on pre-activations, SiLU applied to the tiles as they load
         ms_silu = _time_ms(lambda: la.fwd(q, k, v, lam, kv_out=kv_out, block=block, out=out, workspace=ws,
                                           silu=True), max(1, args.steps // 2))
+        # the output's per-head RMSNorm and sigmoid gate in the kernels that write
+        # the output rows: core -> norm -> gate, and SiLU -> core -> norm -> gate
+        gate = qkv_device(B, H, N, d, seed=6, device=dev, slice_tokens=65536)[0]
+        gamma = torch.ones((H, d), device=dev, dtype=torch.float32)
+        reps = max(1, args.steps // 2)
+        ms_norm_gate_fused = _time_ms(lambda: la.fwd_fused(q, k, v, lam, gamma=gamma, gate=gate, kv_out=kv_out,
+                                                           out=out, workspace=ws), reps)
+        ms_layer_fused = _time_ms(lambda: la.fwd_fused(q, k, v, lam, gamma=gamma, gate=gate, kv_out=kv_out, out=out,
+                                                       workspace=ws, silu=True), reps)
+        del gate
     del ws
     if args.fused:
         ep = bench_norm_gate_silu(args, dev, out)
         if ms_silu is not None:
             ep["prefill_silu_fused_ms"] = ms_silu
             ep["prefill_plus_silu_passes_ms"] = ms_step + 3 * ep["silu_ms_per_tensor"]
+            ep["prefill_norm_gate_fused_ms"] = ms_norm_gate_fused
+            ep["prefill_plus_norm_gate_pass_ms"] = ms_step + ep["norm_gate_ms"]
+            ep["layer_silu_core_norm_gate_fused_ms"] = ms_layer_fused
+            ep["layer_silu_fused_core_plus_norm_gate_pass_ms"] = ms_silu + ep["norm_gate_ms"]
+            ep["layer_all_separate_passes_ms"] = ms_step + 3 * ep["silu_ms_per_tensor"] + ep["norm_gate_ms"]
         res["epilogue_prologue"] = ep
     del out
     if args.backward:

@@ -169,6 +169,31 @@ int lightning_attn_fwd_ex(const void* q, const void* k, const void* v, const flo
                           void* stream);
 
 /*
+ * Prefill with the lightning layer's output steps fused into the kernels
+ * that write the output rows (no extra pass over HBM): the MiniMax-M1 fact
+ * sheet puts an RMSNorm on the output (its "linear / SSM layer
+ * configuration" field) and a sigmoid gate after that norm, before the
+ * output projection (its "output gate" field).  Per token t and head h:
+ *     o   = the prefill output of lightning_attn_fwd_ex (same arguments)
+ *     out = o / sqrt(mean_j(o_j^2) + eps) * gamma[h] * sigmoid(gate_t)
+ * the mean over the d features of the token's head row, every factor
+ * optional; fp32 until the one rounding of out.
+ *   q, k, v   : bf16 [B][H][N][d] (with LA_FLAG_SILU_QKV: pre-activations)
+ *   gamma     : float [H][d] or NULL (no norm)
+ *   eps       : in [0, 1] (the block norms use 1e-5)
+ *   gate      : bf16 [B][H][N][d] or NULL (no gate); sigmoid(x) = 1 / (1 + e^-x)
+ *   out       : out_dtype [B][H][N][d] (written; apart from every input)
+ *   other arguments as lightning_attn_fwd_ex at block 64 (bf16 inputs)
+ * kv_out is the recurrence's final state, as in lightning_attn_fwd_ex (the
+ * epilogue touches the outputs only).
+ */
+int lightning_attn_fwd_fused(const void* q, const void* k, const void* v, const float* decay, const float* gamma,
+                             float eps, const void* gate, void* out, const float* kv_in, float* kv_out, int64_t B,
+                             int64_t H, int64_t N, int64_t d, int out_dtype, int64_t chunk, int64_t warm_chunk,
+                             unsigned int flags, void* workspace, size_t workspace_bytes, void* evt_begin,
+                             void* evt_end, void* stream);
+
+/*
  * Prefill into a pool of states (serving: chunked prefill of several
  * requests into their existing states).  The same computation as
  * lightning_attn_fwd_ex with kv_in = kv_out, except that batch row b starts

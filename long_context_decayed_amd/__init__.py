@@ -26,6 +26,7 @@ __all__ = [
     "LA_FLAG_SILU_QKV",
     "fwd",
     "fwd_noalloc",
+    "fwd_fused",
     "NOALLOC_SCRATCH_BYTES",
     "fwd_slots",
     "bwd",
@@ -79,6 +80,9 @@ def load():
         fn.argtypes = fwd_args + [P]
     lib.lightning_attn_fwd_ex.restype = I
     lib.lightning_attn_fwd_ex.argtypes = fwd_args + [I, I, I64, I64, ctypes.c_uint, P, SZ, P, P, P]
+    lib.lightning_attn_fwd_fused.restype = I
+    lib.lightning_attn_fwd_fused.argtypes = [P] * 5 + [ctypes.c_float, P, P, P, P, I64, I64, I64, I64, I, I64, I64,
+                                                       ctypes.c_uint, P, SZ, P, P, P]
     lib.lightning_attn_fwd_noalloc.restype = I
     lib.lightning_attn_fwd_noalloc.argtypes = [P] * 7 + [I64, I64, I64, I64, I, I, I64, I64, ctypes.c_uint, P]
     lib.lightning_attn_fwd_chunk.restype = I64
@@ -209,6 +213,46 @@ def fwd(q, k, v, decay, kv_in=None, kv_out=None, block=64, out=None, out_dtype=N
     )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_fwd_ex")
+    return out
+
+
+def fwd_fused(q, k, v, decay, gamma=None, gate=None, eps=1e-5, kv_in=None, kv_out=None, out=None,
+              out_dtype=torch.bfloat16, chunk=0, warm_chunk=0, workspace=None, events=None, exact=False, silu=False,
+              stream=None):
+    """Prefill with the per-head RMSNorm (gamma fp32 [H, d]) and the sigmoid
+    gate (gate bf16 [B, H, N, d]) applied in the kernels that write the output
+    rows: out = o / sqrt(mean(o^2) + eps) * gamma[h] * sigmoid(gate).  q, k, v
+    bf16 [B, H, N, d] (pre-activations with silu=True); block 64; the rest as
+    fwd.  Returns out [B, H, N, d] in out_dtype."""
+    lib = load()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, torch.bfloat16, (B, H, N, d))
+    _check_dev("decay", decay, torch.float32, (H,))
+    if gamma is not None:
+        _check_dev("gamma", gamma, torch.float32, (H, d))
+    if gate is not None:
+        _check_dev("gate", gate, torch.bfloat16, (B, H, N, d))
+    for name, t in (("kv_in", kv_in), ("kv_out", kv_out)):
+        if t is not None:
+            _check_dev(name, t, torch.float32, (B, H, d, d))
+    if out is None:
+        out = torch.empty((B, H, N, d), device=q.device, dtype=out_dtype)
+    _check_dev("out", out, out_dtype, (B, H, N, d))
+    need = int(lib.lightning_attn_fwd_workspace_bytes(B, H, N, d, 64, chunk))
+    if need == 0:
+        raise LightningAttnError(1, "lightning_attn_fwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    _check_dev("workspace", workspace, torch.uint8)
+    e0, e1 = (None, None) if events is None else (ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
+    rc = lib.lightning_attn_fwd_fused(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(gamma), float(eps), _ptr(gate), _ptr(out), _ptr(kv_in),
+        _ptr(kv_out), B, H, N, d, _DT[out_dtype], chunk, warm_chunk, _fwd_flags(exact, silu), _ptr(workspace),
+        workspace.numel(), e0, e1, _stream(stream),
+    )
+    if rc != 0:
+        raise LightningAttnError(rc, "lightning_attn_fwd_fused")
     return out
 
 

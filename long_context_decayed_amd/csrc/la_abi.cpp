@@ -200,10 +200,18 @@ hipError_t run_passes(const la::PrefillArgs& a, hipStream_t st) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// The epilogue of lightning_attn_fwd_fused (null: none).
+struct Epilogue {
+  const float* gamma;
+  float eps;
+  const void* gate;
+};
+
 int prefill_run(const void* q, const void* k, const void* v, const float* decay, void* out, const float* kv_in,
                 float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, int in_dtype,
                 int out_dtype, int64_t L, int64_t Lw, void* workspace, size_t workspace_bytes, void* evt_begin,
-                void* evt_end, void* stream, const int* slots, int64_t num_slots, unsigned int flags);
+                void* evt_end, void* stream, const int* slots, int64_t num_slots, unsigned int flags,
+                const Epilogue* epi = nullptr);
 
 constexpr unsigned int kFwdFlags = LA_FLAG_EXACT | LA_FLAG_SILU_QKV;
 
@@ -257,6 +265,26 @@ int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const 
                      flags);
 }
 
+int lightning_attn_fwd_fused(const void* q, const void* k, const void* v, const float* decay, const float* gamma,
+                             float eps, const void* gate, void* out, const float* kv_in, float* kv_out, int64_t B,
+                             int64_t H, int64_t N, int64_t d, int out_dtype, int64_t chunk, int64_t warm_chunk,
+                             unsigned int flags, void* workspace, size_t workspace_bytes, void* evt_begin,
+                             void* evt_end, void* stream) {
+  if (flags & ~kFwdFlags) return LA_ERR_INVALID;
+  if (!(eps >= 0.0f) || eps > 1.0f) return LA_ERR_INVALID;
+  if (!aligned(gamma, 16) || !aligned(gate, 16)) return LA_ERR_INVALID;
+  int64_t L = 0, Lw = 0;
+  int rc = validate_prefill(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, 64, LA_DTYPE_BF16, out_dtype, chunk, &L);
+  if (rc != LA_OK) return rc;
+  rc = resolve_warm_chunk(B, H, N, chunk, warm_chunk, L, &Lw);
+  if (rc != LA_OK) return rc;
+  const int64_t out_bytes = B * H * N * d * (out_dtype == LA_DTYPE_BF16 ? 2 : 4), gate_bytes = B * H * N * d * 2;
+  if (overlap(out, out_bytes, gate, gate_bytes) || overlap(out, out_bytes, gamma, H * d * 4)) return LA_ERR_INVALID;
+  const Epilogue epi{gamma, eps, gate};
+  return prefill_run(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, 64, LA_DTYPE_BF16, out_dtype, L, Lw, workspace,
+                     workspace_bytes, evt_begin, evt_end, stream, nullptr, 0, flags, &epi);
+}
+
 }  // extern "C"
 
 namespace {
@@ -264,7 +292,8 @@ namespace {
 int prefill_run(const void* q, const void* k, const void* v, const float* decay, void* out, const float* kv_in,
                 float* kv_out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, int in_dtype,
                 int out_dtype, int64_t L, int64_t Lw, void* workspace, size_t workspace_bytes, void* evt_begin,
-                void* evt_end, void* stream, const int* slots, int64_t num_slots, unsigned int flags) {
+                void* evt_end, void* stream, const int* slots, int64_t num_slots, unsigned int flags,
+                const Epilogue* epi) {
   const bool exact = (flags & LA_FLAG_EXACT) != 0;
   size_t tbl_bytes = 0, guard_off = 0, flags_off = 0;
   const size_t need = workspace_layout(B, H, N, d, block, L, &tbl_bytes, &guard_off, &flags_off);
@@ -312,6 +341,10 @@ int prefill_run(const void* q, const void* k, const void* v, const float* decay,
   a.guard = a.warm_start ? (float*)((char*)ws + guard_off) : nullptr;
   a.flags = a.warm_start ? (int*)((char*)ws + flags_off) : nullptr;
   a.rerun = false;
+  a.epi = epi != nullptr;
+  a.gamma = epi ? epi->gamma : nullptr;
+  a.eps = epi ? epi->eps : 0.0f;
+  a.gate = epi ? epi->gate : nullptr;
   hipError_t e = run_passes(a, st);
   if (!workspace) {
     hipError_t f = hipFreeAsync(ws, st);
@@ -450,6 +483,10 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
   a.guard = a.warm_start ? (float*)((char*)ws + guard_off) : nullptr;
   a.flags = a.warm_start ? (int*)((char*)ws + flags_off) : nullptr;
   a.rerun = false;
+  a.epi = false;
+  a.gamma = nullptr;
+  a.eps = 0.0f;
+  a.gate = nullptr;
 
   hipError_t e = hipSuccess;
   if (kv_in) e = la::launch_transpose_states(kv_in, s0t, B * H, d, st);

@@ -44,6 +44,13 @@ struct PrefillArgs {
   float* guard;
   int* flags;
   bool rerun;      // run only the heads whose flag is set, on the exact path
+  // Epilogue (forward, bf16 inputs, block 64): out = RMSNorm_head(o) *
+  // gamma[h] * sigmoid(gate) in the kernels that write the output rows;
+  // gamma [H][d] or null (no norm), gate [B][H][N][d] bf16 or null (no gate).
+  bool epi;
+  const float* gamma;
+  float eps;
+  const void* gate;
 };
 
 // Decay table and pass A (chunk aggregates; with warm_start, of the heads

@@ -342,6 +342,7 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 // same time, the second often from L2.  The backward's dK and dV passes run
 // this way: both read Q and dO.
 enum { kWarmStart = 0, kFromStart = 1 };
+constexpr int kEtab = 64;  // entries of the diagonal-tile factor table (60 used)
 
 struct Operands {
   const bf16* q;
@@ -358,6 +359,11 @@ struct Operands {
   // Heads to run (pass C of the heads whose warm start failed the check), or
   // null: every head of the launch's kind.
   const int* only;
+  // Epilogue (EPI kernels): per-head RMSNorm weights [H][D] (null: no norm),
+  // its eps, and the gate's pre-activation [B][H][N][D] (null: no gate).
+  const float* gamma;
+  float eps;
+  const bf16* gate;
 };
 
 // Largest |x| over this wave's share of the state (each lane's 16 NRT
@@ -375,22 +381,12 @@ __device__ __forceinline__ void store_wave_absmax(const f32x16 (&S)[NRT], float*
   if (lane == 0) *dst = __uint_as_float(m);
 }
 
-// LDS of one block-64 workgroup (80 KiB at d = 128).
-template <int D>
-struct Lds64 {
-  __attribute__((aligned(16))) bf16 Qs[kSub * D];
-  __attribute__((aligned(16))) bf16 Ks[kSub * D];  // score operands (phase 1)
-  __attribute__((aligned(16))) bf16 Kt[kSub * D];  // update operands (phase 2)
-  __attribute__((aligned(16))) bf16 Vs[kSub * D];
-  __attribute__((aligned(16))) Mfma<bf16>::op_t Pbuf[3][2][2][64];  // [tile][g][hi/lo][lane]
-  __attribute__((aligned(16))) f32x4 Dtab[4][64];                    // diagonal-tile factors [jq][lane]
-};
-
 // The workgroup body: chunk blk of the (bh, chunk) grid of problem pi, on the
 // LDS sm of the calling kernel.
-template <typename TOut, int D, int MODE, bool REV, bool SILU>
+template <typename TOut, int D, int MODE, bool REV, bool SILU, bool EPI>
 __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt, bf16* Vs,
-                                                    Mfma<bf16>::op_t (*Pbuf)[2][2][64], f32x4 (*Dtab)[64], int blk,
+                                                    Mfma<bf16>::op_t (*Pbuf)[2][2][64], f32x4* Etab,
+                                                    f32x4 (*Nbuf)[32], float* Gam, int blk,
                                                     int pi, Operands p0, Operands p1, const float* __restrict__ decay,
                                                     const float* __restrict__ tbl_all, int H, int N, int L, int nc,
                                                     int tbl_stride, const int* __restrict__ slots, int64_t num_slots,
@@ -401,6 +397,9 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
   constexpr int NRT = D / 32;
   constexpr int MAXT = (3 + NW - 1) / NW;  // score tiles per wave
   constexpr int kStores = sizeof(TOut) == 2 ? 2 * 2 : 2 * 4;  // output store instructions per sub-tile
+  // EPI: out = RMSNorm_head(o) * gamma[h] * sigmoid(gate) instead of o (the
+  // MiniMax-M1 fact sheet's "linear / SSM layer configuration" field puts an
+  // RMSNorm on the output, its "output gate" field a sigmoid gate after it).
   constexpr bool kDefer = sizeof(TOut) == 2;  // bf16 rows are stored during the next sub-tile's phase 1
   constexpr int RS = REV ? -D : D;             // elements from one token's row to the next
 
@@ -420,6 +419,9 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
   const int* __restrict__ only = pi ? p1.only : p0.only;
   if (only && !only[bh]) return;
   float* __restrict__ guard = pi ? p1.guard : p0.guard;
+  static_assert(!(EPI && REV), "the epilogue is a forward step");
+  const float* __restrict__ gamma = p0.gamma;  // forward launches carry one problem
+  const bf16* __restrict__ gate = p0.gate;
   const int t_begin = c * L;
   const int t_end = min(N, t_begin + L);
   const int64_t base = (int64_t)bh * N * D + (REV ? (int64_t)(N - 1) * D : 0);
@@ -435,8 +437,12 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
   //   inter,  token p = 32rt + l:      lam^(p+1)  = rf[rt]
   //   off-diagonal score tile (r = 32 + l, s = crow(j, h)):
   //           lam^(r-s) = lam^(24-8jq) * ol[jj],  ol[jj] = lam^(l+4-4h+4-jj)
-  //   diagonal tile (r = l, s = crow(j, h)), d = r - s: lam^d for d >= 0,
-  //           0 (masked) for d < 0, kept in Dtab[jq][lane][jj].
+  //   diagonal tile (r = l, s = crow(j, h)), d = r - s = l - 4h - 8jq - jj:
+  //           lam^d for d >= 0, 0 (masked) for d < 0.  The four factors of
+  //           one jq depend on l - 4h - 8jq alone (in [-28, 31]), so they are
+  //           kept once per value in an LDS table, Etab[l - 4h - 8jq + 28][jj]
+  //           (64 entries of 16 bytes; consecutive lanes read consecutive
+  //           entries).
   // They are loaded here, before the tile loop, so that the loop issues no
   // vector-memory loads of its own.
   float ol[4], ul[8], rf[2], wl[4][8];
@@ -467,11 +473,15 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
   // last, partial one).
   float d_first = 0.0f;
   if constexpr (REV) d_first = (t_end - t_begin <= kSub) ? tb[n_last - 1] : tb[63];
-  for (int e = tid; e < 4 * 64; e += NW * 64) {
-    const int jq = e >> 6, ln = e & 63;
-    const int dd = (ln & 31) - 4 * (ln >> 5) - 8 * jq;
-    Dtab[jq][ln] = f32x4{dd >= 0 ? tb[dd] : 0.0f, dd >= 1 ? tb[dd - 1] : 0.0f, dd >= 2 ? tb[dd - 2] : 0.0f,
-                         dd >= 3 ? tb[dd - 3] : 0.0f};
+  for (int e = tid; e < kEtab; e += NW * 64) {
+    const int dd = e - 28;
+    Etab[e] = f32x4{dd >= 0 ? tb[dd] : 0.0f, dd >= 1 ? tb[dd - 1] : 0.0f, dd >= 2 ? tb[dd - 2] : 0.0f,
+                    dd >= 3 ? tb[dd - 3] : 0.0f};
+  }
+  const f32x4* etab_lane = Etab + (l32 - 4 * hf + 28);  // this lane's entry for jq = 0
+  if constexpr (EPI) {
+    // the head's norm weights, made visible by the barrier after the first tiles
+    for (int e = tid; e < D; e += NW * 64) Gam[e] = gamma ? gamma[(int64_t)hh * D + e] : 1.0f;
   }
 
   // State tile kt, register j of lane (h, n): feature 32kt + pf(crow(j, h)),
@@ -666,7 +676,7 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
         } else {
 #pragma unroll
           for (int jq = 0; jq < 4; ++jq) {
-            const f32x4 f = Dtab[jq][lane];
+            const f32x4 f = etab_lane[-8 * jq];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) pt[m][4 * jq + jj] *= f[jj];
           }
@@ -715,6 +725,21 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
       dma_tile<D, NW, RS>(qb + off_next, Qs, nv_next, w, lane);
       dma_tile<D, NW, RS>(kb + off_next, Ks, nv_next, w, lane);
     }
+    // EPI: this sub-tile's gate values, 8 bf16 per (token tile, column pair)
+    // at the columns this lane owns after the lane-half swap below; they
+    // arrive during phase 2 and are waited for at its closing barrier.
+    uint4 gq[2][2];
+    if constexpr (EPI) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int t = t0 + 32 * rt + l32;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+          gq[rt][pp] = (gate && t < t_end) ? *reinterpret_cast<const uint4*>(
+                                                 gate + base + (int64_t)t * D + 32 * w + 16 * pp + 8 * hf)
+                                           : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
 
     // Phase 2.  Intra-block term acc[rt] += V^T P^T over the shared score tiles.
 #pragma unroll
@@ -731,6 +756,27 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
     // State update.  A partial last sub-tile of warm-start mode is added
     // after the loop.
     if (!(MODE == kWarmStart && !more && t_end - t0 < kSub)) update_full(Kt, Vs);
+
+    // EPI: each token's sum of squares over this wave's 32 columns (the lane
+    // and its partner in the other half hold 16 each), published in Nbuf for
+    // the other waves by the barrier below (Nbuf is read after it and not
+    // written again before the next sub-tile's first barrier).
+    if constexpr (EPI) {
+      if (gamma) {
+        float ss[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          float a = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) a = __builtin_fmaf(acc[rt][j], acc[rt][j], a);
+          ss[rt] = a + __shfl_xor(a, 32);
+        }
+        if (hf == 0) {
+          reinterpret_cast<float*>(&Nbuf[0][l32])[w] = ss[0];
+          reinterpret_cast<float*>(&Nbuf[1][l32])[w] = ss[1];
+        }
+      }
+    }
 
     // The next sub-tile's Q and K (and this wave's older stores) are done
     // and visible; V, K^T and the score tiles are free from here on.
@@ -752,7 +798,60 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
     // column pair p, stored as 16 bytes (the two halves then write 32
     // contiguous bytes of each row) during the next sub-tile, or below after
     // the last one.  fp32: four 16-byte stores per token tile, here.
-    if constexpr (kDefer) {
+    if constexpr (EPI) {
+      // Lane halves trade fp32 quads first, so that each lane holds the 8
+      // consecutive columns 32w + 16pp + 8h .. + 7 of its token, then
+      // y = ((o * inv) * gamma) * sigmoid(gate) per element (inv = 1 /
+      // sqrt(mean(o^2) + eps) over the token's d columns, the four waves'
+      // partial sums added in wave order), rounded once.
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        float inv = 1.0f;
+        if (gamma) {
+          const f32x4 p = Nbuf[rt][l32];
+          float sum = p[0];
+#pragma unroll
+          for (int i = 1; i < NW; ++i) sum += p[i];
+          inv = 1.0f / sqrtf(sum * (1.0f / D) + p0.eps);
+        }
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int ja = 8 * pp, jb = 8 * pp + 4;  // quads jq = 2pp (kept by h = 0), 2pp + 1 (kept by h = 1)
+          float y[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[rt][ja + i]),
+                                                             __float_as_uint(acc[rt][jb + i]), false, false);
+            y[i] = __uint_as_float(sw[0]);      // column 8h + i of the pair
+            y[4 + i] = __uint_as_float(sw[1]);  // column 8h + 4 + i
+          }
+          const int c0 = 32 * w + 16 * pp + 8 * hf;
+          const f32x4 ga = *reinterpret_cast<const f32x4*>(Gam + c0);
+          const f32x4 gb = *reinterpret_cast<const f32x4*>(Gam + c0 + 4);
+          const bf16x8 gv = __builtin_bit_cast(bf16x8, gq[rt][pp]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float sg = gate ? sigmoid_hw((float)gv[i]) : 1.0f;
+            y[i] = ((y[i] * inv) * (i < 4 ? ga[i] : gb[i - 4])) * sg;
+          }
+          if constexpr (kDefer) {
+            pend[rt][pp] = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                                      pack_bf16x2(y[6], y[7]));
+          } else {
+            const int t = t0 + 32 * rt + l32;
+            if (t < t_end) {
+              float* orow = reinterpret_cast<float*>(ob) + (int64_t)t * RS + c0;
+              *reinterpret_cast<f32x4*>(orow) = f32x4{y[0], y[1], y[2], y[3]};
+              *reinterpret_cast<f32x4*>(orow + 4) = f32x4{y[4], y[5], y[6], y[7]};
+            }
+          }
+        }
+      }
+      if constexpr (kDefer) {
+        have_pend = true;
+        t_pend = t0;
+      }
+    } else if constexpr (kDefer) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -833,7 +932,7 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
 }
 
 // One problem, or two in one grid (pair_shift >= 0, see above).
-template <typename TOut, int D, int MODE, bool REV, bool SILU>
+template <typename TOut, int D, int MODE, bool REV, bool SILU, bool EPI>
 __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Operands p1,
                                                               const float* __restrict__ decay,
                                                               const float* __restrict__ tbl_all, int H, int N, int L,
@@ -845,14 +944,16 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
   __shared__ __attribute__((aligned(16))) bf16 Kt[kSub * D];  // update operands (phase 2)
   __shared__ __attribute__((aligned(16))) bf16 Vs[kSub * D];
   __shared__ __attribute__((aligned(16))) Mfma<bf16>::op_t Pbuf[3][2][2][64];  // [tile][g][hi/lo][lane]
-  __shared__ __attribute__((aligned(16))) f32x4 Dtab[4][64];                    // diagonal-tile factors [jq][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 Etab[kEtab];                    // diagonal-tile factors
+  __shared__ __attribute__((aligned(16))) f32x4 Nbuf[2][32];  // epilogue: per-wave sums of squares [tile][token]
+  __shared__ __attribute__((aligned(16))) float Gam[D];        // epilogue: the head's norm weights
   int blk = blockIdx.x, pi = 0;
   if (pair_shift >= 0) {
     pi = (blk >> pair_shift) & 1;
     blk = ((blk >> (pair_shift + 1)) << pair_shift) | (blk & ((1 << pair_shift) - 1));
     if (blk >= nblk) return;  // padding of the last group
   }
-  chunk_output64_body<TOut, D, MODE, REV, SILU>(Qs, Ks, Kt, Vs, Pbuf, Dtab, blk, pi, p0, p1, decay, tbl_all, H, N, L, nc, tbl_stride, slots,
+  chunk_output64_body<TOut, D, MODE, REV, SILU, EPI>(Qs, Ks, Kt, Vs, Pbuf, Etab, Nbuf, Gam, blk, pi, p0, p1, decay, tbl_all, H, N, L, nc, tbl_stride, slots,
                                                 num_slots, warm, Lw, nc_ws);
 }
 
@@ -862,7 +963,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
 // once for a head of the other kind.  One launch lets the few workgroups of a
 // layer's non-decaying heads fill the rounds the warm-start pass leaves
 // partly empty, and the other way round.
-template <typename TOut, int D, bool SILU>
+template <typename TOut, int D, bool SILU, bool EPI>
 __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64_mixed(Operands p0, const float* __restrict__ decay,
                                                                     const float* __restrict__ tbl_all, int H, int N,
                                                                     int L, int nc, int Lw, int ncw, int tbl_stride,
@@ -873,18 +974,20 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64_mixed(Operands p0,
   __shared__ __attribute__((aligned(16))) bf16 Kt[kSub * D];
   __shared__ __attribute__((aligned(16))) bf16 Vs[kSub * D];
   __shared__ __attribute__((aligned(16))) Mfma<bf16>::op_t Pbuf[3][2][2][64];
-  __shared__ __attribute__((aligned(16))) f32x4 Dtab[4][64];
+  __shared__ __attribute__((aligned(16))) f32x4 Etab[kEtab];
+  __shared__ __attribute__((aligned(16))) f32x4 Nbuf[2][32];
+  __shared__ __attribute__((aligned(16))) float Gam[D];
   const int b = blockIdx.x;
   // Warm-start chunks in reverse order, last head first: with ALiBi-style
   // slopes, which shrink with the head index, the longest warm-ups come first
   // and the short chunks fill the last round (measured 0.2-1% faster than in
   // head order at 1024 warm-start workgroups).
   if (b < n_warm)
-    chunk_output64_body<TOut, D, kWarmStart, false, SILU>(Qs, Ks, Kt, Vs, Pbuf, Dtab, n_warm - 1 - b, 0, p0, p0, decay,
+    chunk_output64_body<TOut, D, kWarmStart, false, SILU, EPI>(Qs, Ks, Kt, Vs, Pbuf, Etab, Nbuf, Gam, n_warm - 1 - b, 0, p0, p0, decay,
                                                           tbl_all, H, N, Lw, ncw, tbl_stride, slots, num_slots, 1, Lw,
                                                           nc);
   else
-    chunk_output64_body<TOut, D, kFromStart, false, SILU>(Qs, Ks, Kt, Vs, Pbuf, Dtab, b - n_warm, 0, p0, p0, decay,
+    chunk_output64_body<TOut, D, kFromStart, false, SILU, EPI>(Qs, Ks, Kt, Vs, Pbuf, Etab, Nbuf, Gam, b - n_warm, 0, p0, p0, decay,
                                                           tbl_all, H, N, L, nc, tbl_stride, slots, num_slots, 1, Lw,
                                                           nc);
 }
@@ -902,17 +1005,19 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64_mixed_pair(
   __shared__ __attribute__((aligned(16))) bf16 Kt[kSub * D];
   __shared__ __attribute__((aligned(16))) bf16 Vs[kSub * D];
   __shared__ __attribute__((aligned(16))) Mfma<bf16>::op_t Pbuf[3][2][2][64];
-  __shared__ __attribute__((aligned(16))) f32x4 Dtab[4][64];
+  __shared__ __attribute__((aligned(16))) f32x4 Etab[kEtab];
+  __shared__ __attribute__((aligned(16))) f32x4 Nbuf[2][32];
+  __shared__ __attribute__((aligned(16))) float Gam[D];
   const bool warm_part = (int)blockIdx.x < n_warm_grid;
   const int b = warm_part ? (int)blockIdx.x : (int)blockIdx.x - n_warm_grid;
   const int pi = (b >> kPairShift) & 1;
   const int blk = ((b >> (kPairShift + 1)) << kPairShift) | (b & ((1 << kPairShift) - 1));
   if (blk >= (warm_part ? nblk_w : nblk_c)) return;  // padding of a last group
   if (warm_part)
-    chunk_output64_body<TOut, D, kWarmStart, true, false>(Qs, Ks, Kt, Vs, Pbuf, Dtab, blk, pi, p0, p1, decay, tbl_all,
+    chunk_output64_body<TOut, D, kWarmStart, true, false, false>(Qs, Ks, Kt, Vs, Pbuf, Etab, Nbuf, Gam, blk, pi, p0, p1, decay, tbl_all,
                                                           H, N, Lw, ncw, tbl_stride, nullptr, 0, 1, Lw, nc);
   else
-    chunk_output64_body<TOut, D, kFromStart, true, false>(Qs, Ks, Kt, Vs, Pbuf, Dtab, blk, pi, p0, p1, decay, tbl_all,
+    chunk_output64_body<TOut, D, kFromStart, true, false, false>(Qs, Ks, Kt, Vs, Pbuf, Etab, Nbuf, Gam, blk, pi, p0, p1, decay, tbl_all,
                                                           H, N, L, nc, tbl_stride, nullptr, 0, 1, Lw, nc);
 }
 
@@ -924,7 +1029,8 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64_mixed_pair(
 // warm-start pass when there is one (bf16 inputs, block 64), else this one.
 static Operands operands_of(const PrefillArgs& a) {
   return Operands{(const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.out, a.states, a.kv_in,
-                  a.warm_start ? a.guard : nullptr, a.rerun ? a.flags : nullptr};
+                  a.warm_start ? a.guard : nullptr, a.rerun ? a.flags : nullptr, a.gamma, a.eps,
+                  (const bf16*)a.gate};
 }
 
 // One problem (b == nullptr), or two of one shape in one grid (the pair's
@@ -939,23 +1045,28 @@ static void launch_fast(const PrefillArgs& a, hipStream_t st, const PrefillArgs*
   const int64_t half = int64_t(1) << kPairShift;  // workgroups of one problem per group of the pair
   const unsigned grid = b ? (unsigned)((nblk + half - 1) / half * 2 * half) : (unsigned)nblk;
   const Operands p0 = operands_of(a), p1 = b ? operands_of(*b) : p0;
-  if (a.rev)  // the backward: no SiLU
-    hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, true, false>), dim3(grid), dim3(D * 2), 0, st, p0, p1,
-                       a.decay, (const float*)a.tbl, (int)a.H, (int)a.N, Lm, ncm, a.tbl_stride, a.slots,
-                       a.num_slots, a.warm_start ? 1 : 0, nblk, shift, (int)a.L_warm, a.nc);
+#define LA_FAST(REV, SILU, EPI)                                                                               \
+  hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, REV, SILU, EPI>), dim3(grid), dim3(D * 2), 0, st, p0, p1, \
+                     a.decay, (const float*)a.tbl, (int)a.H, (int)a.N, Lm, ncm, a.tbl_stride, a.slots,            \
+                     a.num_slots, a.warm_start ? 1 : 0, nblk, shift, (int)a.L_warm, a.nc)
+  if (a.rev)  // the backward: no SiLU, no epilogue
+    LA_FAST(true, false, false);
+  else if (a.epi && a.silu)
+    LA_FAST(false, true, true);
+  else if (a.epi)
+    LA_FAST(false, false, true);
   else if (a.silu)
-    hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, false, true>), dim3(grid), dim3(D * 2), 0, st, p0, p1,
-                       a.decay, (const float*)a.tbl, (int)a.H, (int)a.N, Lm, ncm, a.tbl_stride, a.slots,
-                       a.num_slots, a.warm_start ? 1 : 0, nblk, shift, (int)a.L_warm, a.nc);
+    LA_FAST(false, true, false);
   else
-    hipLaunchKernelGGL((la_chunk_output64<TOut, D, MODE, false, false>), dim3(grid), dim3(D * 2), 0, st, p0, p1,
-                       a.decay, (const float*)a.tbl, (int)a.H, (int)a.N, Lm, ncm, a.tbl_stride, a.slots,
-                       a.num_slots, a.warm_start ? 1 : 0, nblk, shift, (int)a.L_warm, a.nc);
+    LA_FAST(false, false, false);
+#undef LA_FAST
 }
 
 template <typename TIn, typename TOut, int D, int BLK>
 static hipError_t launch_output_t(const PrefillArgs& a, hipStream_t st) {
-  if (a.silu && !(BLK == 64 && sizeof(TIn) == 2)) return hipErrorInvalidValue;  // SiLU: block-64 bf16 kernels only
+  // SiLU and the epilogue: block-64 bf16 kernels only, the epilogue forward only
+  if ((a.silu || a.epi) && !(BLK == 64 && sizeof(TIn) == 2)) return hipErrorInvalidValue;
+  if (a.epi && a.rev) return hipErrorInvalidValue;
   const int BH = (int)(a.B * a.H);
   const int nc = a.nc;
   const bool timed = !a.warm_start && !a.rerun;
@@ -993,14 +1104,19 @@ static hipError_t launch_mixed_t(const PrefillArgs& a, hipStream_t st) {
   const int n_warm = (int)(a.B * a.H * a.nc_warm);
   const unsigned grid = (unsigned)(n_warm + a.B * a.H * a.nc);
   const Operands p0 = operands_of(a);
-  if (a.silu)
-    hipLaunchKernelGGL((la_chunk_output64_mixed<TOut, D, true>), dim3(grid), dim3(D * 2), 0, st, p0, a.decay,
-                       (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc, (int)a.L_warm, a.nc_warm,
-                       a.tbl_stride, a.slots, a.num_slots, n_warm);
+#define LA_MIXED(SILU, EPI)                                                                                   \
+  hipLaunchKernelGGL((la_chunk_output64_mixed<TOut, D, SILU, EPI>), dim3(grid), dim3(D * 2), 0, st, p0, a.decay, \
+                     (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc, (int)a.L_warm, a.nc_warm,        \
+                     a.tbl_stride, a.slots, a.num_slots, n_warm)
+  if (a.epi && a.silu)
+    LA_MIXED(true, true);
+  else if (a.epi)
+    LA_MIXED(false, true);
+  else if (a.silu)
+    LA_MIXED(true, false);
   else
-    hipLaunchKernelGGL((la_chunk_output64_mixed<TOut, D, false>), dim3(grid), dim3(D * 2), 0, st, p0, a.decay,
-                       (const float*)a.tbl, (int)a.H, (int)a.N, (int)a.L, a.nc, (int)a.L_warm, a.nc_warm,
-                       a.tbl_stride, a.slots, a.num_slots, n_warm);
+    LA_MIXED(false, false);
+#undef LA_MIXED
   if (a.evt_end) {
     hipError_t e = hipEventRecord((hipEvent_t)a.evt_end, st);
     if (e != hipSuccess) return e;
@@ -1020,7 +1136,7 @@ static void launch_mixed_pair_t(const PrefillArgs& a, const PrefillArgs& b, hipS
 }
 
 hipError_t launch_mixed_pair(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st) {
-  if (!a.warm_start || !a.rev || a.silu || a.in_dtype != kBF16 || a.block != 64 || b.in_dtype != kBF16 ||
+  if (!a.warm_start || !a.rev || a.silu || a.epi || b.epi || a.in_dtype != kBF16 || a.block != 64 || b.in_dtype != kBF16 ||
       b.block != 64 || a.B != b.B || a.H != b.H || a.N != b.N || a.nc != b.nc || a.d != b.d ||
       a.out_dtype != b.out_dtype || a.rev != b.rev || a.warm_start != b.warm_start || a.silu != b.silu ||
       a.L != b.L || a.L_warm != b.L_warm)
@@ -1054,6 +1170,7 @@ static hipError_t launch_output_d(const PrefillArgs& a, hipStream_t st) {
 
 template <int MODE>
 static hipError_t launch_pair_mode(const PrefillArgs& a, const PrefillArgs& b, hipStream_t st) {
+  if (a.epi || b.epi) return hipErrorInvalidValue;
   if (a.in_dtype != kBF16 || b.in_dtype != kBF16 || a.block != 64 || b.block != 64 || a.B != b.B || a.H != b.H ||
       a.N != b.N || a.nc != b.nc || a.d != b.d || a.out_dtype != b.out_dtype || a.rev != b.rev ||
       a.warm_start != b.warm_start || a.silu != b.silu || a.L != b.L || a.L_warm != b.L_warm)

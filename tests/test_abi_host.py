@@ -384,3 +384,21 @@ def test_decode_layers_validation(lib):
     assert call(d=96) == LA_ERR_UNSUPPORTED
     assert call(states=ctypes.c_void_p(P[5].value + 4)) == LA_ERR_INVALID  # misaligned
     assert call(states=P[4]) == LA_ERR_INVALID           # the pool overlapping the output
+
+
+def test_fwd_fused_validation(lib):
+    P = FAKE
+
+    def call(q=P[0], gamma=None, gate=None, eps=1e-5, out=P[4], d=64, outd=0, flags=0, B=1, H=2, N=128):
+        return lib.lightning_attn_fwd_fused(q, P[1], P[2], P[3], gamma, ctypes.c_float(eps), gate, out, None, None,
+                                            B, H, N, d, outd, 0, 0, flags, None, 0, None, None, None)
+
+    assert call(q=None) == LA_ERR_INVALID
+    assert call(eps=-1.0) == LA_ERR_INVALID
+    assert call(eps=2.0) == LA_ERR_INVALID
+    assert call(flags=8) == LA_ERR_INVALID
+    assert call(gamma=ctypes.c_void_p(P[5].value + 4)) == LA_ERR_INVALID   # misaligned
+    assert call(gate=P[4]) == LA_ERR_INVALID                               # gate overlapping the output
+    assert call(gamma=ctypes.c_void_p(P[4].value + 64)) == LA_ERR_INVALID  # gamma inside the output
+    assert call(d=96) == LA_ERR_UNSUPPORTED
+    assert call(outd=7) == LA_ERR_INVALID

@@ -195,3 +195,108 @@ def test_pooled_prefill_silu_fused(dev):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
     assert torch.equal(pool1, pool2)
+
+
+# --- the per-head RMSNorm and sigmoid gate fused into the prefill ----------------
+
+def _epilogue_ref(o_ref, gamma, gate, eps=1e-5):
+    y = o_ref if gamma is None else ora.rmsnorm_heads(o_ref, host(gamma), eps=eps)
+    return y if gate is None else ora.sigmoid_gate(y, host(gate))
+
+
+@pytest.mark.parametrize("d,N,silu,exact", [(128, 1500, False, False), (128, 1500, True, False),
+                                            (64, 1037, True, False), (128, 700, False, True),
+                                            (64, 63, False, False)])
+def test_prefill_norm_gate_fused_against_oracle(dev, d, N, silu, exact):
+    """out = RMSNorm_head(o) * gamma * sigmoid(gate) from the output kernels,
+    against the oracle chain (SiLU in fp64 rounded to bf16 when asked, the
+    fp64 recurrence, the fp64 norm and gate), per head, on decays that take
+    both the warm-start and the chunked paths, with an initial state and a
+    ragged last tile; fp32 out at the RMS rule, bf16 out = RNE(fp32 out)."""
+    B, H = 2, 8
+    say("prefill + fused norm/gate vs oracle: B2 H8 N", N, "d", d, "silu", silu, "exact", exact)
+    q, k, v = _preact(B, H, N, d, 400 + d + N, dev) if silu else qkv_device(B, H, N, d, seed=400 + d + N, device=dev)
+    gate = qkv_device(B, H, N, d, seed=401 + N, device=dev)[0] * 8.0
+    gamma = _gamma(H, d, 402, dev)
+    s0 = state_device(B, H, d, seed=403, device=dev)
+    lam = torch.from_numpy(LAMS8).to(dev)
+    kv = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    kw = dict(kv_in=s0, chunk=256, silu=silu, exact=exact)
+    y32 = la.fwd_fused(q, k, v, lam, gamma=gamma, gate=gate, kv_out=kv, out_dtype=torch.float32, **kw)
+    y16 = la.fwd_fused(q, k, v, lam, gamma=gamma, gate=gate, out_dtype=torch.bfloat16, **kw)
+    kv_plain = torch.empty_like(kv)
+    la.fwd(q, k, v, lam, kv_out=kv_plain, block=64, out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y32.to(torch.bfloat16), y16), "bf16 out must be RNE(fp32 out)"
+    assert torch.equal(kv, kv_plain), "the epilogue must leave the final state alone"
+    if silu:
+        act = [torch.from_numpy(ora.silu(host(t))).to(torch.bfloat16).to(torch.float32).numpy() for t in (q, k, v)]
+    else:
+        act = [host(t) for t in (q, k, v)]
+    o_ref, s_ref = oracle(*act, LAMS8, host(s0).astype(np.float64))
+    y_ref = _epilogue_ref(o_ref, gamma, gate)
+    for h in range(H):
+        tol.assert_bf16_f32out(host(y32)[:, h], y_ref[:, h], "y head %d" % h)
+        tol.assert_bf16_out(host(y16)[:, h], y_ref[:, h], "y bf16 head %d" % h)
+        tol.assert_state(host(kv)[:, h], s_ref[:, h], "state head %d" % h)
+
+
+@pytest.mark.parametrize("which", ["norm", "gate", "neither"])
+def test_prefill_fused_optional_steps(dev, which):
+    """Either factor alone, or neither (then the plain prefill, bit for bit)."""
+    B, H, N, d = 1, 8, 900, 128
+    say("prefill + fused", which, "B1 H8 N900 d128")
+    q, k, v = qkv_device(B, H, N, d, seed=410, device=dev)
+    gate = qkv_device(B, H, N, d, seed=411, device=dev)[0] * 8.0 if which == "gate" else None
+    gamma = _gamma(H, d, 412, dev) if which == "norm" else None
+    lam = torch.from_numpy(LAMS8).to(dev)
+    y = la.fwd_fused(q, k, v, lam, gamma=gamma, gate=gate, out_dtype=torch.float32, chunk=256)
+    o = la.fwd(q, k, v, lam, block=64, out_dtype=torch.float32, chunk=256)
+    torch.cuda.synchronize()
+    if which == "neither":
+        assert torch.equal(y, o)
+        return
+    o_ref, _ = oracle(host(q), host(k), host(v), LAMS8)
+    y_ref = _epilogue_ref(o_ref, gamma, gate)
+    for h in range(H):
+        tol.assert_bf16_f32out(host(y)[:, h], y_ref[:, h], "y head %d" % h)
+
+
+def test_prefill_fused_matches_the_separate_pass(dev):
+    """The fused epilogue against the prefill followed by the norm/gate pass
+    on its fp32 output: the same function, differing only in the order the
+    sums of squares are added (a few ulps)."""
+    B, H, N, d = 1, 8, 2000, 128
+    say("prefill + fused norm/gate vs prefill then norm_gate pass: B1 H8 N2000 d128")
+    q, k, v = qkv_device(B, H, N, d, seed=420, device=dev)
+    gate = qkv_device(B, H, N, d, seed=421, device=dev)[0] * 8.0
+    gamma = _gamma(H, d, 422, dev)
+    lam = torch.from_numpy(LAMS8).to(dev)
+    y = la.fwd_fused(q, k, v, lam, gamma=gamma, gate=gate, out_dtype=torch.float32)
+    o = la.fwd(q, k, v, lam, block=64, out_dtype=torch.float32)
+    y2 = la.norm_gate(o, gamma=gamma, gate=gate, eps=1e-5, out=torch.empty_like(o, dtype=torch.bfloat16))
+    torch.cuda.synchronize()
+    yf, y2f = host(y), host(y2)
+    # the pass stores bf16: agreement to within its rounding plus a few fp32 ulps
+    assert np.all(np.abs(yf - y2f) <= 2.0 ** -8 * np.abs(yf) + 1e-6 * np.abs(yf).max())
+
+
+def test_prefill_fused_with_a_flagged_head(dev):
+    """A head that fails the warm-start check is run again on the exact path
+    with the epilogue: the result still matches the oracle chain."""
+    say("prefill + fused norm/gate with a spike before a warm-up window, B1 H2 N512 d128 chunk 256")
+    q, k, v = qkv_device(1, 2, 512, 128, seed=430, device=dev)
+    k[:, 0, 190] *= 1e5
+    v[:, 0, 190] *= 1e5
+    lam = np.array([0.7, 0.3], dtype=np.float32)
+    gate = qkv_device(1, 2, 512, 128, seed=431, device=dev)[0] * 8.0
+    gamma = _gamma(2, 128, 432, dev)
+    ws = torch.empty(la.workspace_bytes(1, 2, 512, 128, 64, 256), device=dev, dtype=torch.uint8)
+    y = la.fwd_fused(q, k, v, torch.from_numpy(lam).to(dev), gamma=gamma, gate=gate, out_dtype=torch.float32,
+                     chunk=256, workspace=ws)
+    torch.cuda.synchronize()
+    assert ws[ws.numel() - 8:].view(torch.int32).cpu().tolist() == [1, 0]
+    o_ref, _ = oracle(host(q), host(k), host(v), lam)
+    y_ref = _epilogue_ref(o_ref, gamma, gate)
+    for h in range(2):
+        tol.assert_bf16_f32out(host(y)[:, h], y_ref[:, h], "y head %d" % h)
