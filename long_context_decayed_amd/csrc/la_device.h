@@ -122,29 +122,6 @@ struct Mfma<bf16> {
     const bf16x4 lo = ds_tr4(p), hi = ds_tr4(p + 8 * ld);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
-  // Transpose reads from an unpadded D-column tile swizzled as in
-  // RowTile::store_swz (chunk c of row r stored at chunk c ^ 2(r & 3)).  The
-  // 16 lanes of a read touch 4 rows r0..r0+3 (r0 % 4 == 0) x 2 adjacent
-  // chunks; the swizzle sends them to 8 distinct bank groups.
-  template <int D>
-  static __device__ __forceinline__ const bf16* tr_swz_addr(const bf16* X, int row, int col, int j) {
-    return X + row * D + ((((col >> 3) ^ (2 * j)) << 3) | (col & 7));
-  }
-  template <int D>
-  static __device__ __forceinline__ op_t ld_tr_nat_swz(const bf16* X, int row0, int col0, int lane) {
-    const int h = lane >> 5, j = (lane & 15) >> 2;
-    const bf16* p = tr_swz_addr<D>(X, row0 + 8 * h + j, col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3), j);
-    const bf16x4 lo = ds_tr4(p), hi = ds_tr4(p + 4 * D);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  }
-  template <int D>
-  static __device__ __forceinline__ op_t ld_tr_cperm_swz(const bf16* X, int row0, int g, int col0, int lane) {
-    const int h = lane >> 5, j = (lane & 15) >> 2;
-    const bf16* p =
-        tr_swz_addr<D>(X, row0 + 16 * g + 4 * h + j, col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3), j);
-    const bf16x4 lo = ds_tr4(p), hi = ds_tr4(p + 8 * D);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  }
   static __device__ __forceinline__ op_t cvt(const float* x) {
     return __builtin_bit_cast(op_t, uint4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
                                           pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])});
@@ -291,18 +268,28 @@ struct RowTile {
 
 // ---------------------------------------------------------------------------
 // Swizzled LDS tiles of the bf16 fast paths: 64 rows x D bf16, unpadded,
-// 16-byte chunk c of row r stored at chunk c ^ swz(r), swz(r) = 2(r & 3) |
-// ((r >> 2) & 1).
-//   * 16-byte row reads (8 lanes = 8 consecutive rows at one chunk) see swz
-//     take all 8 values on r % 8, so the 8 lanes cover all 32 banks;
-//   * transpose reads (16 lanes = rows r0..r0+3, r0 % 4 == 0, x two adjacent
-//     chunks) see 2(r & 3) move the chunk pair to 4 distinct pairs while bit
-//     (r >> 2) & 1, equal for the 4 rows, only swaps within a pair.
-__device__ __forceinline__ int swz(int r) { return (2 * (r & 3)) | ((r >> 2) & 1); }
+// 16-byte chunk c of row r stored at chunk c ^ swz<D>(r).  At D = 128 a row is
+// 256 bytes, one pass over all 64 banks, and
+//   swz(r) = ((r & 3) << 2) | ((r >> 2) & 3):
+//   * 16-byte row reads (16 lanes = 16 consecutive rows at one chunk) see swz
+//     take all 16 values on r % 16, so the 16 lanes cover all 64 banks;
+//   * transpose reads (32 lanes = rows r0..r0+3, r0 % 4 == 0, x four
+//     adjacent chunks c0..c0+3, c0 % 4 == 0) see (r & 3) << 2 send each row's
+//     four chunks to a different aligned group of four, while (r >> 2) & 3,
+//     equal for the 4 rows, only permutes within a group: 16 distinct chunks.
+// At D = 64 (8 chunks per row) swz(r) = 2(r & 3) | ((r >> 2) & 1) does the
+// same over half as many banks per row.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D >= 128)
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  else
+    return (2 * (r & 3)) | ((r >> 2) & 1);
+}
 // Element offset of (row, col) within the tile (row stride D).
 template <int D>
 __device__ __forceinline__ int swz_at(int row, int col) {
-  return row * D + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
+  return row * D + ((((col >> 3) ^ swz<D>(row)) << 3) | (col & 7));
 }
 
 // LDS DMA.  The tiles reach LDS without passing through registers: with
@@ -381,12 +368,12 @@ __device__ __forceinline__ void dma_tile(const bf16* __restrict__ src, bf16* dst
     for (int m = 0; m < NI / NW; ++m) {
       const int qi = w + NW * m;
       const int row = RPI * qi + rr;
-      dma_dwordx4(src + row * RS + ((pc ^ swz(row)) << 3), t0 + 1024 * qi);
+      dma_dwordx4(src + row * RS + ((pc ^ swz<D>(row)) << 3), t0 + 1024 * qi);
     }
   } else if (lane < D / 2) {
     for (int r = w; r < kSub; r += NW) {
       if (r < nvalid)
-        dma_dword(src + r * RS + (((lane >> 2) ^ swz(r)) << 3) + 2 * (lane & 3), t0 + 2 * r * D);
+        dma_dword(src + r * RS + (((lane >> 2) ^ swz<D>(r)) << 3) + 2 * (lane & 3), t0 + 2 * r * D);
       else
         *reinterpret_cast<uint32_t*>(dst + r * D + 2 * lane) = 0u;
     }
@@ -429,19 +416,30 @@ __device__ __forceinline__ bf16x8 ld_row8(const bf16* X, int row, int col) {
   return *reinterpret_cast<const bf16x8*>(X + swz_at<D>(row, col));
 }
 
+// Row order of the transpose-read operands: element i of lane L = 32h + n
+// holds row row0 + trow(i, h), trow(i, h) = 16(i >> 2) + 4h + (i & 3), so one
+// MFMA step contracts rows row0 + {0..7, 16..23}, and the steps at row0 =
+// trbase(kk) = 8(kk & 1) + 32(kk >> 1), kk < 4, cover a 64-row sub-tile.  (Any
+// fixed order of the contraction index works when both operands and the
+// decay factors follow it; this one keeps the two halves of a read 16 rows
+// apart, where the swizzle repeats.)
+__device__ __forceinline__ int trow(int i, int h) { return 16 * (i >> 2) + 4 * h + (i & 3); }
+__device__ __forceinline__ int trbase(int kk) { return 8 * (kk & 1) + 32 * (kk >> 1); }
+
 // Transpose-read operand: lane L = 32h + n gets, as element i < 8, X[row0 +
-// crow(i, h)][col0 + cn(n)] with cn(n) = n, or, with PI, n with bits 2 and 3
-// swapped (the feature order of the state's accumulator rows).  Within a
-// group of 16 lanes, lane 4j + q points at row row0 + 4h + j and the 4
-// columns of piece q (piece ((q & 1) << 1 | q >> 1) with PI); the second read
-// is 8 rows further down (same swizzle).
+// trow(i, h)][col0 + cn(n)] with cn(n) = n, or, with PI, n with bits 2 and 3
+// swapped (the feature order of the state's accumulator rows); row0 % 4 == 0.
+// Within a group of 16 lanes, lane 4j + q points at row row0 + 4h + j and the
+// 4 columns of piece q (piece ((q & 1) << 1 | q >> 1) with PI); the second
+// read is 16 rows further down, at the same swizzle (swz depends on r % 16),
+// so its address is the first one's plus an immediate offset.
 template <int D, bool PI>
 __device__ __forceinline__ bf16x8 ld_tr8(const bf16* X, int row0, int col0, int lane) {
   const int h = lane >> 5, j = (lane & 15) >> 2, q = lane & 3;
   const int qq = PI ? (((q & 1) << 1) | (q >> 1)) : q;
   const int row = row0 + 4 * h + j;
   const bf16* p = X + swz_at<D>(row, col0 + 16 * ((lane >> 4) & 1) + 4 * qq);
-  const bf16x4 lo = ds_tr4(p), hi = ds_tr4(p + 8 * D);
+  const bf16x4 lo = ds_tr4(p), hi = ds_tr4(p + 16 * D);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 

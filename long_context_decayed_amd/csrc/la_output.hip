@@ -433,7 +433,8 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
   const float* tb = tbl_all + (int64_t)hh * tbl_stride;  // lam^e, e <= 64
 
   // Decay factors (all exponents non-negative), j = 4jq + jj:
-  //   update, s = 16kk + crow(i, h):   lam^(63-s) = wl[kk][i] = lam^(48-16kk) * ul[i],  ul[i] = lam^(15-crow(i,h))
+  //   update, s = trbase(kk) + trow(i, h):
+  //           lam^(63-s) = wl[kk][i] = lam^(56-trbase(kk)-16(i>>2)) * ul[i],  ul[i] = lam^(7-4h-(i&3))
   //   inter,  token p = 32rt + l:      lam^(p+1)  = rf[rt]
   //   off-diagonal score tile (r = 32 + l, s = crow(j, h)):
   //           lam^(r-s) = lam^(24-8jq) * ol[jj],  ol[jj] = lam^(l+4-4h+4-jj)
@@ -449,11 +450,11 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) ol[jj] = tb[l32 + 8 - 4 * hf - jj];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ul[i] = tb[15 - crow(i, hf)];
+  for (int i = 0; i < 8; ++i) ul[i] = tb[7 - 4 * hf - (i & 3)];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wl[kk][i] = ul[i] * tb[48 - 16 * kk];
+    for (int i = 0; i < 8; ++i) wl[kk][i] = ul[i] * tb[56 - trbase(kk) - 16 * (i >> 2)];
   rf[0] = tb[l32 + 1];
   rf[1] = tb[l32 + 33];
   const float d64 = tb[64];
@@ -504,11 +505,11 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the state and the factors are in registers
 
   // State update over one full sub-tile in (Kx, Vx): S += sum_s lam^(63-s)
-  // k_s^T v_s, tokens s = 16kk + crow(i, h).
+  // k_s^T v_s, tokens s = trbase(kk) + trow(i, h).
   auto update_full = [&](const bf16* Kx, const bf16* Vx) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const op_t vraw = ld_tr8<D, false>(Vx, 16 * kk, 32 * w, lane);
+      const op_t vraw = ld_tr8<D, false>(Vx, trbase(kk), 32 * w, lane);
       float x[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * wl[kk][i];
@@ -516,7 +517,7 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
       M::split(x, bhi, blo);
 #pragma unroll
       for (int kt = 0; kt < NRT; ++kt) {
-        const op_t a = ld_tr8<D, true>(Kx, 16 * kk, 32 * kt, lane);
+        const op_t a = ld_tr8<D, true>(Kx, trbase(kk), 32 * kt, lane);
         S[kt] = M::mma(a, bhi, S[kt]);
         S[kt] = M::mma(a, blo, S[kt]);
       }
@@ -681,11 +682,13 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
             for (int jj = 0; jj < 4; ++jj) pt[m][4 * jq + jj] *= f[jj];
           }
         }
+        // operand g, element i: register 4g + 8(i >> 2) + (i & 3), the score of
+        // token 8g + trow(i, h) of the tile, to match the V rows of phase 2
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
           float x[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) x[i] = pt[m][8 * g + i];
+          for (int i = 0; i < 8; ++i) x[i] = pt[m][4 * g + 8 * (i >> 2) + (i & 3)];
           op_t hi, lo;
           M::split(x, hi, lo);
           Pbuf[ti][g][0][lane] = hi;
@@ -747,7 +750,7 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
       const int st = ti == 2 ? 1 : 0, rt = ti == 0 ? 0 : 1;
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const op_t vop = ld_tr8<D, false>(Vs, 32 * st + 16 * g, 32 * w, lane);
+        const op_t vop = ld_tr8<D, false>(Vs, 32 * st + 8 * g, 32 * w, lane);
         acc[rt] = M::mma(vop, Pbuf[ti][g][0][lane], acc[rt]);
         acc[rt] = M::mma(vop, Pbuf[ti][g][1][lane], acc[rt]);
       }
@@ -900,11 +903,11 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
     if (n < kSub) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const op_t vraw = ld_tr8<D, false>(Vs, 16 * kk, 32 * w, lane);
+        const op_t vraw = ld_tr8<D, false>(Vs, trbase(kk), 32 * w, lane);
         float x[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const int e = n - 1 - (16 * kk + crow(i, hf));
+          const int e = n - 1 - (trbase(kk) + trow(i, hf));
           const float f = __shfl(tlane, e < 0 ? 0 : e);
           x[i] = e >= 0 ? (float)vraw[i] * f : 0.0f;
         }
@@ -912,7 +915,7 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
         M::split(x, bhi, blo);
 #pragma unroll
         for (int kt = 0; kt < NRT; ++kt) {
-          const op_t a = ld_tr8<D, true>(Kt, 16 * kk, 32 * kt, lane);
+          const op_t a = ld_tr8<D, true>(Kt, trbase(kk), 32 * kt, lane);
           S[kt] = M::mma(a, bhi, S[kt]);
           S[kt] = M::mma(a, blo, S[kt]);
         }

@@ -130,9 +130,9 @@ __global__ __launch_bounds__(D * 2, sizeof(TIn) == 2 ? 3 : 1) void la_chunk_stat
 // per-token power, so U is never rescaled.  Only the last sub-tile of the
 // sequence can be partial (n < 64 tokens, factors lam^(n-1-s)); it comes
 // first and then sets u to lam^n.
-//   Token s = 16kk + crow(i, h) of a full sub-tile (the row order of the
-// transpose-read operands): lam^(63-s) u = ul[i] * (lam^(48-16kk) u) with the
-// per-lane ul[i] = lam^(15 - crow(i, h)).
+//   Token s = trbase(kk) + trow(i, h) of a full sub-tile (the row order of
+// the transpose-read operands): lam^(63-s) u = ul[i] * (lam^(56-trbase(kk)-
+// 16(i>>2)) u) with the per-lane ul[i] = lam^(7 - 4h - (i & 3)).
 //   With skip_decaying set, heads that decay within their chunk return at
 // once: the warm-start output pass needs no aggregates.  With `only`, just
 // the heads whose flag is set run (their warm start failed its check).  REV reads the
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
 
   float ul[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ul[i] = tb[15 - crow(i, hf)];
+  for (int i = 0; i < 8; ++i) ul[i] = tb[7 - 4 * hf - (i & 3)];
   const double lam = (double)decay[hh];
   const double lam64 = pow_int(lam, kSub);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the factors are in registers before any transfer
@@ -206,18 +206,18 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const op_t vraw = ld_tr8<D, false>(Vs[0], 16 * kk, 32 * w, lane);
+      const op_t vraw = ld_tr8<D, false>(Vs[0], trbase(kk), 32 * w, lane);
       float x[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int s = 16 * kk + crow(i, hf);
+        const int s = trbase(kk) + trow(i, hf);
         x[i] = s < n_last ? (float)vraw[i] * tb[max(n_last - 1 - s, 0)] : 0.0f;
       }
       op_t bhi, blo;
       M::split(x, bhi, blo);
 #pragma unroll
       for (int kt = 0; kt < NRT; ++kt) {
-        const op_t a = ld_tr8<D, false>(Ks[0], 16 * kk, 32 * kt, lane);
+        const op_t a = ld_tr8<D, false>(Ks[0], trbase(kk), 32 * kt, lane);
         U[kt] = M::mma(a, bhi, U[kt]);
         U[kt] = M::mma(a, blo, U[kt]);
       }
@@ -245,16 +245,16 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
     const float u = (float)ud;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const op_t vraw = ld_tr8<D, false>(Vc, 16 * kk, 32 * w, lane);
-      const float wk = tb[48 - 16 * kk] * u;
+      const op_t vraw = ld_tr8<D, false>(Vc, trbase(kk), 32 * w, lane);
+      const float wk0 = tb[56 - trbase(kk)] * u, wk1 = tb[40 - trbase(kk)] * u;
       float x[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * ul[i] * wk;
+      for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * ul[i] * (i < 4 ? wk0 : wk1);
       op_t bhi, blo;
       M::split(x, bhi, blo);
 #pragma unroll
       for (int kt = 0; kt < NRT; ++kt) {
-        const op_t a = ld_tr8<D, false>(Kc, 16 * kk, 32 * kt, lane);
+        const op_t a = ld_tr8<D, false>(Kc, trbase(kk), 32 * kt, lane);
         U[kt] = M::mma(a, bhi, U[kt]);
         U[kt] = M::mma(a, blo, U[kt]);
       }
