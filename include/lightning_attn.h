@@ -218,13 +218,12 @@ int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const 
  *     dq_t = dout_t S_t^T,  dk_t = v_t G_t^T,  dv_t = k_t G_t,  dkv_in = lam G_0.
  * Each of dq, dk, dv is computed as a prefill-shaped pass (dk and dv run the
  * tokens last first) with the kernels of lightning_attn_fwd_ex at block 64.
- * With bf16 inputs the heads that decay within a chunk take the warm start:
- * the dq pass with its check, as in lightning_attn_fwd; the reverse dk and dv
- * passes without it (their warm starts leave out at most 2^-30 of the
- * adjoint state from before each window, relative to that state; use
- * LA_FLAG_EXACT where gradients can burst).  With bf16 inputs the dk and dv
- * passes share their kernel launches (each keeps its own chunk states in the
- * workspace).
+ * With bf16 inputs the heads that decay within a chunk take the warm start
+ * and its check, as in lightning_attn_fwd, in every pass (for dk and dv on
+ * the adjoint state); a head that fails the check in a pass is computed
+ * again on the exact path for that pass.  With bf16 inputs the dk and dv
+ * passes share their kernel launches (each keeps its own chunk states and
+ * check slots in the workspace).
  *   q, k, v, dout : in_dtype [B][H][N][d]          (read)
  *   decay         : float [H]                      (read)
  *   kv_in         : float [B][H][d][d] or NULL     (read: the forward's initial state; NULL = zero)

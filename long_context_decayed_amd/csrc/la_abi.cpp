@@ -478,8 +478,8 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
   a.num_slots = 0;
   a.evt_begin = nullptr;
   a.evt_end = nullptr;
-  // the dQ pass runs forward and takes the warm-start check; the reverse
-  // passes of dK and dV below do not
+  // every pass takes the warm-start check (the dQ pass through run_passes,
+  // the paired dK and dV passes below)
   a.guard = a.warm_start ? (float*)((char*)ws + guard_off) : nullptr;
   a.flags = a.warm_start ? (int*)((char*)ws + flags_off) : nullptr;
   a.rerun = false;
@@ -504,9 +504,7 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
     e = run_passes(a, st);
   }
   // dK: dk_t = v_t G_t^T, G^T run last token first over (V, dO, Q) from dSN^T.
-  la::PrefillArgs ak = a;
-  ak.guard = nullptr;
-  ak.flags = nullptr;
+  la::PrefillArgs ak = a;  // reuses a's check slots and flags once the dQ pass is done with them
   ak.q = v;
   ak.k = dout;
   ak.v = q;
@@ -526,6 +524,11 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
   av.kv_out = dkv_in;
   av.scale_kv_out = true;
   av.states = (float*)((char*)ws + states2_off);
+  // the second region has the forward layout's room after its chunk states
+  if (a.warm_start) {
+    av.guard = (float*)((char*)ws + states2_off + (guard_off - tbl_bytes));
+    av.flags = (int*)((char*)ws + states2_off + (flags_off - tbl_bytes));
+  }
   if (a.in_dtype == la::kBF16) {
     // Both read Q and dO: their workgroups for one chunk run side by side, so
     // those tiles come from HBM about once.
@@ -533,12 +536,24 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
     if (e == hipSuccess) e = la::launch_aggregate_pass(av, st);
     if (a.warm_start) {
       // as in the forward: the other heads' scans, one launch for every
-      // output row of both passes, then the decaying heads' final states
+      // output row of both passes, the warm-start check of each pass, the
+      // decaying heads' final states, and the exact path for the flagged
+      // heads of either pass (paired as well)
       if (e == hipSuccess) e = la::launch_scan_pass(ak, st, 1);
       if (e == hipSuccess) e = la::launch_scan_pass(av, st, 1);
       if (e == hipSuccess) e = la::launch_mixed_pair(ak, av, st);
+      if (e == hipSuccess) e = la::launch_warm_guard(ak, st);
+      if (e == hipSuccess) e = la::launch_warm_guard(av, st);
       if (e == hipSuccess) e = la::launch_scan_pass(ak, st, 2);
       if (e == hipSuccess) e = la::launch_scan_pass(av, st, 2);
+      la::PrefillArgs rk = ak, rv = av;
+      rk.warm_start = rv.warm_start = false;
+      rk.rerun = rv.rerun = true;
+      if (e == hipSuccess) e = la::launch_aggregate_pass(rk, st);
+      if (e == hipSuccess) e = la::launch_aggregate_pass(rv, st);
+      if (e == hipSuccess) e = la::launch_scan_pass(rk, st, 3);
+      if (e == hipSuccess) e = la::launch_scan_pass(rv, st, 3);
+      if (e == hipSuccess) e = la::launch_output_pair(rk, rv, st);
     } else {
       if (e == hipSuccess) e = la::launch_scan_pass(ak, st);
       if (e == hipSuccess) e = la::launch_scan_pass(av, st);

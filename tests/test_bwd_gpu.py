@@ -208,3 +208,34 @@ def test_bwd_warm_chunk_longer_than_scan_chunk(dev, in_place):
     ds_h = host(ds0)
     for h in range(H):
         tol.assert_state(ds_h[:, h], rs[:, h], "dS0 head %d" % h)
+
+
+def test_bwd_gradient_burst_before_a_reverse_warm_up_window(dev):
+    """The dK and dV passes run the tokens last first; with lam = 0.7 at
+    chunk 256 (carry span 64) the reverse pass's second chunk starts at row
+    255 and its warm-up window covers rows 256-319.  A burst in dO (and q) at
+    row 321, just past that window in reverse order, makes the adjoint state
+    the window leaves out ~1e10 times the window's own: the check flags the
+    head in both passes and they are computed on the exact path, so dk, dv
+    and dS0 match the oracle (as with LA_FLAG_EXACT)."""
+    say("bwd: burst in dO and q at row 321, B1 H2 N512 d128 chunk 256, lam 0.7 / 0.3")
+    B, H, n, d = 1, 2, 512, 128
+    q, k, v = qkv_device(B, H, n, d, seed=180, device=dev)
+    g = qkv_device(B, H, n, d, seed=181, device=dev)[0]
+    g[:, :, 321] *= 1e5
+    q[:, :, 321] *= 1e5
+    lams = np.array([0.7, 0.3], dtype=np.float32)
+    assert la.chunk_for(B, H, n, 64) == 256
+    lam_t = torch.from_numpy(lams).to(dev)
+    dq, dk, dv, ds0 = la.bwd(q, k, v, lam_t, g, out_dtype=torch.float32, dkv_in=True)
+    xq, xk, xv, xs = la.bwd(q, k, v, lam_t, g, out_dtype=torch.float32, dkv_in=True, exact=True)
+    torch.cuda.synchronize()
+    rq, rk, rv, rs = _grad_oracle(q, k, v, lams, g, None, None)
+    _check_heads(dq, rq, "dQ", H)
+    _check_heads(dk, rk, "dK", H)
+    _check_heads(dv, rv, "dV", H)
+    for h in range(H):
+        tol.assert_state(host(ds0)[:, h], rs[:, h], "dS0 head %d" % h)
+    # head 0 was flagged in both reverse passes and ran the exact path's
+    # kernels; head 1 (lam^64 ~ 3e-34) left out nothing that mattered
+    assert torch.equal(dk[:, 0], xk[:, 0]) and torch.equal(dv[:, 0], xv[:, 0]) and torch.equal(ds0[:, 0], xs[:, 0])
