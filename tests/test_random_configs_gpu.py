@@ -237,3 +237,103 @@ def test_random_prefill_warm_chunk_and_silu(dev, i):
         else:
             tol.assert_bf16_out(o_h[:, h], o_ref[:, h], "O head %d" % h)
         tol.assert_state(kv_h[:, h], s_ref[:, h], "kv head %d" % h)
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_random_prefill_fused_norm_gate(dev, i):
+    """The prefill with the per-head RMSNorm and the gate in its output
+    kernels: random sizes, chunks, SiLU, exact flag, either factor or both,
+    against the oracle chain; bf16 out = RNE(fp32 out)."""
+    import oracle as ora
+    rng = np.random.default_rng(13000 + i)
+    B, H, N, d = int(rng.integers(1, 3)), int(rng.integers(1, 7)), int(rng.integers(1, 3000)), int(rng.choice([64, 128]))
+    chunk = int(rng.choice([0, 64, 256, 512]))
+    warm_chunk = 0 if chunk == 0 or rng.integers(0, 2) else chunk * int(rng.choice([1, 2, 4]))
+    silu, state, exact = bool(rng.integers(0, 2)), bool(rng.integers(0, 2)), bool(rng.integers(0, 5) == 0)
+    use_gamma, use_gate = [(True, True), (True, False), (False, True)][int(rng.integers(0, 3))]
+    eps = float(rng.choice([1e-5, 1e-3]))
+    lam = _decays(rng, H)
+    say("random fused prefill", i, dict(B=B, H=H, N=N, d=d, chunk=chunk, warm_chunk=warm_chunk, silu=silu,
+                                        state=state, exact=exact, gamma=use_gamma, gate=use_gate, eps=eps),
+        "lam", np.round(lam, 5).tolist())
+    scale = 2.5 if silu else 1.0
+    q, k, v = (t * scale for t in qkv_device(B, H, N, d, seed=14000 + i, device=dev))
+    q, k, v = (t.contiguous() for t in (q, k, v))
+    gate = (qkv_device(B, H, N, d, seed=14100 + i, device=dev)[0] * 8.0).contiguous() if use_gate else None
+    gen = torch.Generator().manual_seed(14200 + i)
+    gamma = (1.0 + 0.3 * torch.randn((H, d), generator=gen)).to(dev) if use_gamma else None
+    s0 = state_device(B, H, d, seed=14300 + i, device=dev) if state else None
+    lam_d = torch.from_numpy(lam).to(dev)
+    kw = dict(gamma=gamma, gate=gate, eps=eps, kv_in=s0, chunk=chunk, warm_chunk=warm_chunk, exact=exact, silu=silu)
+    y32 = la.fwd_fused(q, k, v, lam_d, out_dtype=torch.float32, **kw)
+    y16 = la.fwd_fused(q, k, v, lam_d, out_dtype=torch.bfloat16, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y32.to(torch.bfloat16), y16)
+    if silu:
+        ins = [torch.from_numpy(ora.silu(host(t))).to(torch.bfloat16).to(torch.float32).numpy() for t in (q, k, v)]
+    else:
+        ins = [host(t) for t in (q, k, v)]
+    o_ref, _ = oracle(*ins, lam, None if s0 is None else host(s0).astype(np.float64), want_state=False)
+    y_ref = o_ref if gamma is None else ora.rmsnorm_heads(o_ref, host(gamma), eps=eps)
+    y_ref = y_ref if gate is None else ora.sigmoid_gate(y_ref, host(gate))
+    for h in range(H):
+        tol.assert_bf16_f32out(host(y32)[:, h], y_ref[:, h], "y head %d" % h)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_decode_layers(dev, i):
+    """One launch over several layers' pools: random layer counts, sizes,
+    slot tables (idle rows included) and fusion flags, per layer against the
+    oracle."""
+    import oracle as ora
+    rng = np.random.default_rng(15000 + i)
+    L, H, d, P = int(rng.integers(1, 6)), int(rng.integers(1, 9)), int(rng.choice([64, 128])), int(rng.integers(1, 12))
+    pooled, silu = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    use_gamma, use_gate = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    B = int(rng.integers(1, P + 3)) if pooled else P
+    tables = np.empty((L, B), dtype=np.int32)
+    for l in range(L):
+        if pooled:
+            t = rng.integers(-2, P + 2, size=B)
+            seen = set()
+            for b in range(B):  # no two rows of a layer on one slot
+                if 0 <= t[b] < P and t[b] in seen:
+                    t[b] = -1
+                seen.add(int(t[b]))
+            tables[l] = t
+        else:
+            tables[l] = np.arange(B)
+    lam = np.stack([_decays(rng, H) for _ in range(L)])
+    say("random decode layers", i, dict(L=L, B=B, H=H, d=d, P=P, pooled=pooled, silu=silu, gamma=use_gamma,
+                                        gate=use_gate))
+    q, k, v = (t.reshape(L, B, H, d).mul(float(rng.uniform(1, 6))).contiguous()
+               for t in qkv_device(L * B, H, 1, d, seed=15100 + i, device=dev))
+    gate = (qkv_device(L * B, H, 1, d, seed=15200 + i, device=dev)[0].reshape(L, B, H, d) * 8.0).contiguous() \
+        if use_gate else None
+    gen = torch.Generator().manual_seed(15300 + i)
+    gamma = (1.0 + 0.3 * torch.randn((L, H, d), generator=gen)).to(dev) if use_gamma else None
+    pool = torch.stack([state_device(P, H, d, seed=15400 + 10 * i + l, device=dev) for l in range(L)]).contiguous()
+    pool0 = host(pool).astype(np.float64)
+    o = la.decode_layers(q, k, v, torch.from_numpy(lam).to(dev), pool,
+                         torch.from_numpy(tables).to(dev) if pooled else None, silu=silu, gamma=gamma, gate=gate)
+    torch.cuda.synchronize()
+    o_h, pool1 = host(o), host(pool).astype(np.float64)
+    for l in range(L):
+        rows = np.array([b for b in range(B) if 0 <= tables[l, b] < P], dtype=np.int64)
+        sl = tables[l, rows].astype(np.int64)
+        if len(rows):
+            qs, ks, vs = (host(t)[l, rows] for t in (q, k, v))
+            if silu:
+                qs, ks, vs = ora.silu(qs), ora.silu(ks), ora.silu(vs)
+            y, s_ref = ora.decode_step(qs, ks, vs, lam[l].astype(np.float64), pool0[l, sl])
+            if use_gamma:
+                y = ora.rmsnorm_heads(y[:, :, None, :], host(gamma)[l], eps=1e-5)[:, :, 0, :]
+            if use_gate:
+                y = ora.sigmoid_gate(y, host(gate)[l, rows])
+            for h in range(H):
+                tol.assert_bf16_out(o_h[l, rows][:, h], y[:, h], "layer %d o head %d" % (l, h))
+                tol.assert_state(pool1[l, sl][:, h], s_ref[:, h], "layer %d state head %d" % (l, h))
+        idle = [b for b in range(B) if b not in set(rows.tolist())]
+        assert np.all(o_h[l, idle] == 0.0)
+        untouched = [s for s in range(P) if s not in set(sl.tolist())]
+        assert np.array_equal(pool1[l, untouched], pool0[l, untouched])
