@@ -320,13 +320,18 @@ __device__ __forceinline__ void dma_dword(const void* g, uint32_t m0) {
       : "v"(g), "s"(m0)
       : "memory");
 }
-__device__ __forceinline__ void dma_dwordx4(const void* g, uint32_t m0) {
-  uint32_t keep;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "v"(g), "s"(m0)
-      : "memory");
+// Full-tile form: wave-uniform base in SGPRs plus a per-lane 32-bit byte
+// offset (the scalar-base addressing of global instructions), so the
+// instruction needs no 64-bit address arithmetic of its own; m0 is written
+// and not restored.  The compiler emits no m0 use of its own in these
+// kernels (no LDS-DMA builtins, no indexed register access, no messages),
+// which a host test checks on the built code objects, so nothing it holds in
+// m0 can be lost.  One wait state separates the m0 write from the transfer.
+__device__ __forceinline__ void dma_dwordx4_sbase(const void* base, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(m0)
+               : "memory");
 }
 
 // Wait until at most N of this wave's vector-memory instructions are in
@@ -363,12 +368,17 @@ __device__ __forceinline__ void dma_tile(const bf16* __restrict__ src, bf16* dst
   const uint32_t t0 = lds_addr(dst);
   if (nvalid >= kSub) {
     constexpr int CPR = D / 8, RPI = 64 / CPR, NI = kSub / RPI;
+    // Row r sits at src + r * RS; the lowest address of the tile is row 0
+    // (RS > 0) or row 63 (RS < 0), and every lane's offset from it is >= 0.
+    constexpr int kLow = RS < 0 ? (kSub - 1) * RS : 0;
+    const bf16* low = src + kLow;
     const int rr = lane / CPR, pc = lane % CPR;
 #pragma unroll
     for (int m = 0; m < NI / NW; ++m) {
       const int qi = w + NW * m;
       const int row = RPI * qi + rr;
-      dma_dwordx4(src + row * RS + ((pc ^ swz<D>(row)) << 3), t0 + 1024 * qi);
+      const uint32_t off = (uint32_t)(row * RS - kLow + ((pc ^ swz<D>(row)) << 3)) * (uint32_t)sizeof(bf16);
+      dma_dwordx4_sbase(low, off, t0 + 1024 * qi);
     }
   } else if (lane < D / 2) {
     for (int r = w; r < kSub; r += NW) {
