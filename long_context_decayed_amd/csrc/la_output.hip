@@ -619,10 +619,7 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
           if (ti < 3) {
             const int st = ti == 2 ? 1 : 0, rt = ti == 0 ? 0 : 1;
             const op_t ka = ld_row8<D>(Ks, 32 * st + l32, f0);
-            // the tile's Q operand read again by row (one LDS read) rather
-            // than selected from qa0 / qa1 (four VALU selects per step)
-            const op_t qs = ld_row8<D>(Qs, 32 * rt + l32, f0);
-            pt[m] = M::mma(ka, qs, pt[m]);
+            pt[m] = M::mma(ka, rt ? qa1 : qa0, pt[m]);
           }
         }
       }
