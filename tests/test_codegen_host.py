@@ -7,6 +7,9 @@ disassembled on the host; no GPU).
   messages, no LDS-DMA builtins): no other instruction may name m0.
 * No packed fp32 VALU instructions: the library is built with them turned
   off, and nothing may bring them back.
+* No kernel uses scratch memory: the prefill kernels run at 256 VGPRs, and a
+  register spill to memory would add a memory round trip per spilled value
+  inside their loops.
 """
 import os
 import re
@@ -39,7 +42,8 @@ def disassembly(tmp_path_factory):
     data = fat.read_bytes()
     starts = [m.start() for m in re.finditer(re.escape(MAGIC), data)]
     assert starts, "no offload bundle in .hip_fatbin"
-    text = []
+    text, notes = [], []
+    readelf = _tool("llvm-readelf")
     for i, a in enumerate(starts):
         b = starts[i + 1] if i + 1 < len(starts) else len(data)
         part, co = d / ("b%d.bin" % i), d / ("b%d.co" % i)
@@ -48,11 +52,14 @@ def disassembly(tmp_path_factory):
                         "--output=%s" % co], check=True)
         out = subprocess.run([objdump, "-d", "--mcpu=gfx950", str(co)], check=True, capture_output=True, text=True)
         text.append(out.stdout)
+        if readelf:
+            notes.append(subprocess.run([readelf, "--notes", str(co)], check=True, capture_output=True,
+                                        text=True).stdout)
     lines = [l.split("//")[0].strip() for l in "\n".join(text).splitlines()]
     ins = [l for l in lines if l and not l.endswith(":") and not l.startswith("Disassembly")
            and "file format" not in l]
     assert sum(1 for l in ins if l.startswith("v_mfma")) > 100, "disassembly looks empty"
-    return ins
+    return {"ins": ins, "notes": "\n".join(notes)}
 
 
 def _names_m0(ins):
@@ -60,7 +67,7 @@ def _names_m0(ins):
 
 
 def test_m0_only_feeds_lds_dma(disassembly):
-    ins = disassembly
+    ins = disassembly["ins"]
     writes = 0
     for i, l in enumerate(ins):
         if not _names_m0(l):
@@ -80,5 +87,17 @@ def test_m0_only_feeds_lds_dma(disassembly):
 
 
 def test_no_packed_fp32(disassembly):
-    bad = [l for l in disassembly if re.match(r"v_pk_(add|mul|fma)_f32\b", l)]
+    bad = [l for l in disassembly["ins"] if re.match(r"v_pk_(add|mul|fma)_f32\b", l)]
     assert not bad, bad[:5]
+
+
+def test_no_scratch(disassembly):
+    notes = disassembly["notes"]
+    if not notes:
+        pytest.skip("llvm-readelf not found")
+    names = re.findall(r"\.name:\s+(\S+)", notes)
+    sizes = [int(x) for x in re.findall(r"\.private_segment_fixed_size:\s+(\d+)", notes)]
+    assert len(sizes) >= 20 and len(sizes) == len([n for n in names if n.startswith("_Z")]), (len(sizes), len(names))
+    kernels = [n for n in names if n.startswith("_Z")]
+    bad = [(k, z) for k, z in zip(kernels, sizes) if z != 0]
+    assert not bad, bad
