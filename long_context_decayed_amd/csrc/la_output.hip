@@ -383,7 +383,7 @@ __device__ __forceinline__ void store_wave_absmax(const f32x16 (&S)[NRT], float*
 
 // The workgroup body: chunk blk of the (bh, chunk) grid of problem pi, on the
 // LDS sm of the calling kernel.
-template <typename TOut, int D, int MODE, bool REV, bool SILU, bool EPI>
+template <typename TOut, int D, int MODE, bool REV, bool SILU, bool EPI, bool UNIT = false>
 __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt, bf16* Vs,
                                                     Mfma<bf16>::op_t (*Pbuf)[2][2][64], f32x4* Etab,
                                                     f32x4 (*Nbuf)[32], float* Gam, int blk,
@@ -420,6 +420,13 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
   if (only && !only[bh]) return;
   float* __restrict__ guard = pi ? p1.guard : p0.guard;
   static_assert(!(EPI && REV), "the epilogue is a forward step");
+  // UNIT: lam = 1 (no decay; the head is plain causal linear attention).
+  // Every factor is then 1, so V enters the state update as the bf16 input
+  // itself (one MFMA per step instead of the hi + lo pair) and the decays of
+  // S, of the inter term and of the off-diagonal score tile are skipped: the
+  // same values as the general path, whose factors and lo parts are exactly
+  // 1 and 0 there.  Only heads that do not decay within a chunk (kFromStart).
+  static_assert(!(UNIT && MODE == kWarmStart), "lam = 1 never takes the warm start");
   const float* __restrict__ gamma = p0.gamma;  // forward launches carry one problem
   const bf16* __restrict__ gate = p0.gate;
   const int t_begin = c * L;
@@ -510,6 +517,11 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const op_t vraw = ld_tr8<D, false>(Vx, trbase(kk), 32 * w, lane);
+      if constexpr (UNIT) {
+#pragma unroll
+        for (int kt = 0; kt < NRT; ++kt) S[kt] = M::mma(ld_tr8<D, true>(Kx, trbase(kk), 32 * kt, lane), vraw, S[kt]);
+        continue;
+      }
       float x[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = (float)vraw[i] * wl[kk][i];
@@ -623,7 +635,8 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
           }
         }
       }
-      if (REV && first)
+      if constexpr (UNIT) {
+      } else if (REV && first)
         S[kt] *= d_first;
       else if constexpr (MODE == kWarmStart)
         S[kt] *= more ? d64 : d_last;
@@ -668,11 +681,13 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
       const int ti = w + m * NW;
       if (ti < 3) {
         if (ti == 1) {
+          if constexpr (!UNIT) {
 #pragma unroll
-          for (int jq = 0; jq < 4; ++jq) {
-            const float u = tb[24 - 8 * jq];
+            for (int jq = 0; jq < 4; ++jq) {
+              const float u = tb[24 - 8 * jq];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) pt[m][4 * jq + jj] *= ol[jj] * u;
+              for (int jj = 0; jj < 4; ++jj) pt[m][4 * jq + jj] *= ol[jj] * u;
+            }
           }
         } else {
 #pragma unroll
@@ -700,18 +715,20 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
     // element by element: as a vector-by-scalar product the compiler hoists a
     // 16-wide copy of each factor out of the loop (30 registers).
     float r_tile[2] = {rf[0], rf[1]};
-    if (REV && first) {
+    if (!UNIT && REV && first) {
       // lam^p = rf of row p - 1: lane l - 1 of the same tile, or for l = 0,
       // lam^0 = 1 (tile 0) and lam^32 = rf[0] of lane 31 (tile 1).
       const float up0 = __shfl(rf[0], lane - 1), up1 = __shfl(rf[1], lane - 1), top = __shfl(rf[0], lane + 31);
       r_tile[0] = l32 == 0 ? 1.0f : up0;
       r_tile[1] = l32 == 0 ? top : up1;
     }
+    if constexpr (!UNIT) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const float r = r_tile[rt];
+      for (int rt = 0; rt < 2; ++rt) {
+        const float r = r_tile[rt];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[rt][j] *= r;
+        for (int j = 0; j < 16; ++j) acc[rt][j] *= r;
+      }
     }
 
     // This sub-tile's V and K^T copy (requested before the previous
@@ -934,6 +951,28 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
   }
 }
 
+// kFromStart body with the head's decay looked at once: lam = 1 takes the
+// UNIT instantiation (not with SiLU and the epilogue together, where the
+// two bodies in one kernel would spill registers; the general body is
+// exact at lam = 1 too).
+template <typename TOut, int D, bool REV, bool SILU, bool EPI>
+__device__ __forceinline__ void chunk_output64_from_start(bf16* Qs, bf16* Ks, bf16* Kt, bf16* Vs,
+                                                          Mfma<bf16>::op_t (*Pbuf)[2][2][64], f32x4* Etab,
+                                                          f32x4 (*Nbuf)[32], float* Gam, int blk, int pi, Operands p0,
+                                                          Operands p1, const float* __restrict__ decay,
+                                                          const float* __restrict__ tbl_all, int H, int N, int L,
+                                                          int nc, int tbl_stride, const int* __restrict__ slots,
+                                                          int64_t num_slots, int warm, int Lw, int nc_ws) {
+  if (!(SILU && EPI) && decay[(blk / nc) % H] == 1.0f)
+    chunk_output64_body<TOut, D, kFromStart, REV, SILU, EPI, !(SILU && EPI)>(Qs, Ks, Kt, Vs, Pbuf, Etab, Nbuf, Gam, blk, pi, p0,
+                                                                   p1, decay, tbl_all, H, N, L, nc, tbl_stride, slots,
+                                                                   num_slots, warm, Lw, nc_ws);
+  else
+    chunk_output64_body<TOut, D, kFromStart, REV, SILU, EPI, false>(Qs, Ks, Kt, Vs, Pbuf, Etab, Nbuf, Gam, blk, pi, p0,
+                                                                    p1, decay, tbl_all, H, N, L, nc, tbl_stride, slots,
+                                                                    num_slots, warm, Lw, nc_ws);
+}
+
 // One problem, or two in one grid (pair_shift >= 0, see above).
 template <typename TOut, int D, int MODE, bool REV, bool SILU, bool EPI>
 __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Operands p1,
@@ -956,8 +995,14 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64(Operands p0, Opera
     blk = ((blk >> (pair_shift + 1)) << pair_shift) | (blk & ((1 << pair_shift) - 1));
     if (blk >= nblk) return;  // padding of the last group
   }
-  chunk_output64_body<TOut, D, MODE, REV, SILU, EPI>(Qs, Ks, Kt, Vs, Pbuf, Etab, Nbuf, Gam, blk, pi, p0, p1, decay, tbl_all, H, N, L, nc, tbl_stride, slots,
-                                                num_slots, warm, Lw, nc_ws);
+  if constexpr (MODE == kFromStart)
+    chunk_output64_from_start<TOut, D, REV, SILU, EPI>(Qs, Ks, Kt, Vs, Pbuf, Etab, Nbuf, Gam, blk, pi, p0, p1, decay,
+                                                       tbl_all, H, N, L, nc, tbl_stride, slots, num_slots, warm, Lw,
+                                                       nc_ws);
+  else
+    chunk_output64_body<TOut, D, MODE, REV, SILU, EPI>(Qs, Ks, Kt, Vs, Pbuf, Etab, Nbuf, Gam, blk, pi, p0, p1, decay,
+                                                       tbl_all, H, N, L, nc, tbl_stride, slots, num_slots, warm, Lw,
+                                                       nc_ws);
 }
 
 // The warm-start pass and the other heads' output pass (pass C) in one grid:
@@ -990,7 +1035,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64_mixed(Operands p0,
                                                           tbl_all, H, N, Lw, ncw, tbl_stride, slots, num_slots, 1, Lw,
                                                           nc);
   else
-    chunk_output64_body<TOut, D, kFromStart, false, SILU, EPI>(Qs, Ks, Kt, Vs, Pbuf, Etab, Nbuf, Gam, b - n_warm, 0, p0, p0, decay,
+    chunk_output64_from_start<TOut, D, false, SILU, EPI>(Qs, Ks, Kt, Vs, Pbuf, Etab, Nbuf, Gam, b - n_warm, 0, p0, p0, decay,
                                                           tbl_all, H, N, L, nc, tbl_stride, slots, num_slots, 1, Lw,
                                                           nc);
 }
@@ -1020,7 +1065,7 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_output64_mixed_pair(
     chunk_output64_body<TOut, D, kWarmStart, true, false, false>(Qs, Ks, Kt, Vs, Pbuf, Etab, Nbuf, Gam, blk, pi, p0, p1, decay, tbl_all,
                                                           H, N, Lw, ncw, tbl_stride, nullptr, 0, 1, Lw, nc);
   else
-    chunk_output64_body<TOut, D, kFromStart, true, false, false>(Qs, Ks, Kt, Vs, Pbuf, Etab, Nbuf, Gam, blk, pi, p0, p1, decay, tbl_all,
+    chunk_output64_from_start<TOut, D, true, false, false>(Qs, Ks, Kt, Vs, Pbuf, Etab, Nbuf, Gam, blk, pi, p0, p1, decay, tbl_all,
                                                           H, N, L, nc, tbl_stride, nullptr, 0, 1, Lw, nc);
 }
 

@@ -140,28 +140,24 @@ __global__ __launch_bounds__(D * 2, sizeof(TIn) == 2 ? 3 : 1) void la_chunk_stat
 // passes of the backward; the aggregates start from zero either way.  SILU:
 // k and v are pre-activations, given SiLU in LDS as each tile arrives (as in
 // the output pass).
-template <int D, bool REV, bool SILU>
-__global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restrict__ k, const bf16* __restrict__ v,
-                                                             const float* __restrict__ decay,
-                                                             const float* __restrict__ tbl_all, float* __restrict__ ws,
-                                                             int H, int N, int L, int nc, int tbl_stride,
-                                                             int skip_decaying, int Lw, const int* __restrict__ only) {
+//   UNIT: lam = 1 (plain causal linear attention): every factor is 1, so V
+// enters the MFMA as the bf16 input itself (one MFMA per step instead of the
+// hi + lo pair), the same values as the general path gives there.
+template <int D, bool REV, bool SILU, bool UNIT>
+__device__ __forceinline__ void chunk_state64_body(bf16 (*Ks)[kSub * D], bf16 (*Vs)[kSub * D],
+                                                   const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                                   const float* __restrict__ decay, const float* __restrict__ tbl_all,
+                                                   float* __restrict__ ws, int H, int N, int L, int nc,
+                                                   int tbl_stride) {
   typedef Mfma<bf16> M;
   typedef M::op_t op_t;
   constexpr int NW = D / 32;
   constexpr int NRT = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kSub * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][kSub * D];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int bh = blockIdx.x / nc, c = blockIdx.x - (blockIdx.x / nc) * nc;
   const int hh = bh % H;
-  if (only) {
-    if (!only[bh]) return;  // the exact path for the heads whose warm start failed its check
-  } else if (skip_decaying && decays_within_chunk(carry_span(decay[hh]), Lw)) {
-    return;  // judged by the warm chunk
-  }
   constexpr int RS = REV ? -D : D;  // elements from one token's row to the next
   const int64_t base = (int64_t)bh * N * D + (REV ? (int64_t)(N - 1) * D : 0);
   const bf16* kb = k + base;
@@ -242,6 +238,15 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
     }
     const bf16* Kc = Ks[cur];
     const bf16* Vc = Vs[cur];
+    if constexpr (UNIT) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const op_t vraw = ld_tr8<D, false>(Vc, trbase(kk), 32 * w, lane);
+#pragma unroll
+        for (int kt = 0; kt < NRT; ++kt) U[kt] = M::mma(ld_tr8<D, false>(Kc, trbase(kk), 32 * kt, lane), vraw, U[kt]);
+      }
+      continue;
+    }
     const float u = (float)ud;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -268,6 +273,27 @@ __global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restr
   for (int kt = 0; kt < NRT; ++kt)
 #pragma unroll
     for (int j = 0; j < 16; ++j) dst[(32 * kt + crow(j, hf)) * D] = U[kt][j];
+}
+
+template <int D, bool REV, bool SILU>
+__global__ __launch_bounds__(D * 2, 2) void la_chunk_state64(const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                                             const float* __restrict__ decay,
+                                                             const float* __restrict__ tbl_all, float* __restrict__ ws,
+                                                             int H, int N, int L, int nc, int tbl_stride,
+                                                             int skip_decaying, int Lw, const int* __restrict__ only) {
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kSub * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][kSub * D];
+  const int bh = blockIdx.x / nc;
+  const float lam = decay[bh % H];
+  if (only) {
+    if (!only[bh]) return;  // the exact path for the heads whose warm start failed its check
+  } else if (skip_decaying && decays_within_chunk(carry_span(lam), Lw)) {
+    return;  // judged by the warm chunk
+  }
+  if (lam == 1.0f)
+    chunk_state64_body<D, REV, SILU, true>(Ks, Vs, k, v, decay, tbl_all, ws, H, N, L, nc, tbl_stride);
+  else
+    chunk_state64_body<D, REV, SILU, false>(Ks, Vs, k, v, decay, tbl_all, ws, H, N, L, nc, tbl_stride);
 }
 
 // ---------------------------------------------------------------------------
