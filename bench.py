@@ -221,6 +221,16 @@ def bench_prefill(args, dev):
         mfma_alg_frac=mfma["alg_frac_of_step"],
         mfma=mfma,
     )
+    # What this GPU streams for the same traffic mix (3 reads + 1 write of
+    # the layer's bf16 tensors, 1024 B per head-token) with a plain
+    # elementwise kernel: torch.addcmul(q, k, v, out=o).  The 8 TB/s
+    # datasheet figure is not reached by such a mix; this is the practical
+    # ceiling the output launch is compared with beside the datasheet one.
+    ms_mix = _time_ms(lambda: torch.addcmul(q, k, v, out=out), 3)
+    mix_gbs = alg_bytes / (ms_mix * 1e-3) / 1e9
+    res["stream_ceiling"] = dict(probe="torch.addcmul(q, k, v, out=o) over the layer's bf16 tensors",
+                                 ms=ms_mix, achieved=mix_gbs, unit="GB/s",
+                                 output_launch_frac_of_it=achieved / mix_gbs)
     if args.exact:
         # The same step with every head on the exact chunked path (LA_FLAG_EXACT:
         # chunk aggregates, scan, outputs from the chunk start states).  Its
@@ -542,6 +552,7 @@ def main():
                    "batch": prefill["B"], "heads": prefill["H"], "seq_len": prefill["N"], "head_dim": 128,
                    "block": prefill["block"], "chunk": prefill["chunk"], "warm_chunk": prefill["warm_chunk"]},
         "roofline": prefill["roofline"],
+        "stream_ceiling": prefill["stream_ceiling"],
         "output_kernel_ms": prefill["output_kernel_ms"],
         "warm_start_heads": prefill["warm_start_heads"],
         "step_hbm_frac": prefill["step_hbm_frac"],

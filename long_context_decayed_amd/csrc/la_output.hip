@@ -807,6 +807,14 @@ __device__ __forceinline__ void chunk_output64_body(bf16* Qs, bf16* Ks, bf16* Kt
         silu_own<D, NW>(Ks, nv_next, w, lane);
       }
     }
+    if constexpr (EPI) {
+      // The gate values count as used here, where every load of this wave
+      // is waited for anyway: the compiler, which cannot see the transfers
+      // issued from inline assembly, would otherwise wait for the gate
+      // loads in the epilogue below with a count that also covers the next
+      // V tile requested right after this barrier.
+      asm volatile("" : : "v"(gq[0][0].x), "v"(gq[0][1].x), "v"(gq[1][0].x), "v"(gq[1][1].x));
+    }
     sync_lds_after_vmem<0>();
     if (more) {
       dma_tile<D, NW, RS>(vb + off_next, Vs, nv_next, w, lane);
