@@ -6,11 +6,11 @@
 // (a sigmoid gate after that norm, before the output projection).
 //
 // The block-64 prefill kernels can also apply SiLU to the tiles as they load
-// them (la_output.hip, la_state.hip; same silu_hw, so the results agree bit
-// for bit); the epilogue has no room there (the output pass uses all 80 KiB
-// of LDS per workgroup and nearly all of its registers, and the per-head
-// norm would need a cross-wave reduction).  The decode step fuses all of
-// them (la_decode.hip).  Both passes here are bound by HBM: 16-byte
+// them and the norm and gate in the path that stores the output rows
+// (la_output.hip, la_state.hip; the same silu_hw and sigmoid_hw, so the
+// results agree bit for bit with these passes); these passes serve the other
+// prefill forms (blocks 128 and 256, fp32 inputs) and callers that want the
+// steps on their own.  The decode step fuses all of them (la_decode.hip).  Both passes here are bound by HBM: 16-byte
 // non-temporal loads and stores (the data is touched once), one row of d
 // features per d/8 lanes, the row's sum of squares reduced across those lanes.
 

@@ -277,7 +277,9 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 // ---------------------------------------------------------------------------
 // Pass C, block = 64, bf16 inputs: the fast path.  Same arithmetic as
 // la_chunk_output with BLK = 64, organised around what binds it on MI355X:
-// VALU + MFMA issue per SIMD, vector-memory instruction issue, HBM, LDS.
+// streaming the tiles from HBM (the kernel with its arithmetic taken out runs
+// within 10% of it), then VALU + MFMA issue per SIMD, vector-memory
+// instruction issue, LDS.
 //   * the output is computed transposed, O^T = S^T diag Q^T + V^T P^T: with
 //     the accumulator holding O^T, each lane owns one token row and 4
 //     consecutive columns per register quad, so after a lane-half swap a
@@ -304,7 +306,8 @@ __global__ __launch_bounds__(D * 2, (BLK == 64 && sizeof(TIn) == 2) ? 2 : 1) voi
 //     next V is requested, ahead of this sub-tile's output stores, and waited
 //     for at the end of the next phase 1, during which the K copy is made
 //     (with 4 waves by the one that computes no score tile).
-// Two workgroups per CU (80 KiB of LDS each).
+// Two workgroups per CU (77 KiB of LDS each, 78.5 KiB with the fused
+// epilogue's buffers).
 //
 // Two modes, by where the chunk's start state comes from:
 //   kWarmStart  heads that decay within their chunk (decays_within_chunk),
