@@ -53,6 +53,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -109,12 +110,20 @@ def decaying_heads(lam, chunk):
     return out
 
 
+def _code_text(path):
+    """A source file without its comments, trailing blanks and empty lines."""
+    s = open(path).read()
+    s = re.sub(r"/\*.*?\*/", "", s, flags=re.S)
+    s = re.sub(r"//[^\n]*", "", s)
+    return "\n".join(l.rstrip() for l in s.splitlines() if l.strip())
+
+
 def _src_hash():
-    """Hash of the prefill kernels' sources: the committed counter record is
-    used only while it matches."""
+    """Hash of the prefill kernels' code (comments left out): the committed
+    counter record is used only while it matches."""
     h = hashlib.sha256()
     for name in ("la_output.hip", "la_state.hip", "la_device.h"):
-        h.update(open(os.path.join(_ROOT, "long_context_decayed_amd", "csrc", name), "rb").read())
+        h.update(_code_text(os.path.join(_ROOT, "long_context_decayed_amd", "csrc", name)).encode())
     return h.hexdigest()[:16]
 
 
