@@ -379,7 +379,8 @@ int lightning_attn_silu(void* x, int64_t n, void* stream);
  * with its workspace (decay table and chunk states) in a device array of
  * LA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
  * until the process ends.  The caller passes inputs and outputs as for
- * lightning_attn_fwd_ex; `stream` must belong to the current device.
+ * lightning_attn_fwd_ex; `stream` must belong to the current device
+ * (LA_ERR_INVALID otherwise).
  *   chunk      : 0 = the default chunk (lightning_attn_fwd_chunk at block 64),
  *                doubled until the chunk states fit the array; otherwise as in
  *                lightning_attn_fwd_ex

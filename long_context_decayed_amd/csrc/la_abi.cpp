@@ -789,6 +789,15 @@ extern "C" int lightning_attn_fwd_noalloc(const void* q, const void* k, const vo
   void* ws = nullptr;
   rc = scratch_of_current_device(&ws);
   if (rc != LA_OK) return rc;
+  if (stream) {
+    // the array's address is the current device's copy: a stream of another
+    // device would run the kernels against it
+    int cur = -1;
+    hipDevice_t sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess)
+      return LA_ERR_HIP;
+    if (sdev != cur) return LA_ERR_INVALID;
+  }
   return prefill_run(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, block, in_dtype, out_dtype, L, Lw, ws,
                      LA_NOALLOC_SCRATCH_BYTES, nullptr, nullptr, stream, nullptr, 0, flags);
 }
