@@ -11,6 +11,9 @@
   truncation error is at most lam_max^8193 = e^-32 of the state.
 * Long-range carries: lam = 1 over 2^20 tokens (nothing decays, so every
   chunk's contribution reaches the end).
+* The longest sequence the library takes, N = 2^24 (N * d = 2^31 at d = 128):
+  a warm-start head and a lam = 1 head, final slice and state from the GPU's
+  own prefix state.
 * Backward of the million-token layer: the interior and the final slice of
   dq, dk, dv against the gradient oracle (prefix state from the GPU forward,
   a future window for the adjoint).
@@ -151,6 +154,31 @@ def test_lambda_one_million_tokens(dev):
     kh, vh = host(k).astype(np.float64), host(v).astype(np.float64)
     st = np.matmul(np.swapaxes(kh, -1, -2), vh)
     tol.assert_state(host(kv), st, "kv_out vs K^T V")
+
+
+def test_max_sequence_length(dev):
+    B, H, N, d = 1, 2, 1 << 24, 128
+    say("longest sequence: B1 H2 N2^24 d128 (warm-start head and lam = 1 head)")
+    q, k, v = qkv_device(B, H, N, d, seed=44, device=dev, slice_tokens=1 << 20)
+    # head 0 (lam = 0.99610, carry span 5376 tokens) takes the warm start at
+    # the 32768-token warm-start chunk of this shape; head 1 (lam = 1) the
+    # exact path's lam = 1 kernels
+    lam = np.array([decay_lambdas(64)[63], 1.0], dtype=np.float32)
+    lam_t = torch.from_numpy(lam).to(dev)
+    assert la.warm_chunk_for(B, H, N, 64) == 32768
+    kv = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    out = la.fwd(q, k, v, lam_t, kv_out=kv, block=64, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    t0 = N - 8192
+    kv_pre = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    la.fwd(q[:, :, :t0].contiguous(), k[:, :, :t0].contiguous(), v[:, :, :t0].contiguous(), lam_t, kv_out=kv_pre,
+           block=64)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle(host(q[:, :, t0:]), host(k[:, :, t0:]), host(v[:, :, t0:]), lam,
+                          host(kv_pre).astype(np.float64))
+    e = tol.assert_bf16_f32out(host(out[:, :, t0:]), o_ref, "last 8192 rows vs oracle from GPU prefix state")
+    es = tol.assert_state(host(kv), s_ref, "kv_out")
+    print("N = 2^24: last rows max|err|/RMS %.3e, state %.3e" % (e, es))
 
 
 def test_million_token_backward_slices(dev, million):
