@@ -22,6 +22,26 @@ def _tokens(b, h, d, seed, dev):
     return q[:, :, 0].contiguous(), k[:, :, 0].contiguous(), v[:, :, 0].contiguous()
 
 
+def test_decode_large_batch(dev):
+    """4096 sequences x 64 heads (16 GiB of fp32 state, 262,144 pairs) in one
+    in-place step: 64 seeded (sequence, head) pairs against the oracle."""
+    B, H, d = 4096, 64, 128
+    say("decode large batch B4096 H64 d128")
+    q, k, v = _tokens(B, H, d, 91, dev)
+    lam = decay_lambdas(H)
+    s = state_device(B, H, d, seed=91, device=dev)
+    rng = np.random.default_rng(91)
+    pick = rng.choice(B * H, size=64, replace=False)
+    bs, hs = pick // H, pick % H
+    s0 = np.stack([host(s[b, h]) for b, h in zip(bs, hs)]).astype(np.float64)
+    o = la.decode_step(q, k, v, torch.from_numpy(lam).to(dev), s, s)
+    torch.cuda.synchronize()
+    sel = lambda x: np.stack([host(x[b, h]) for b, h in zip(bs, hs)])
+    o_ref, s_ref = ora.decode_step(sel(q), sel(k), sel(v), lam[hs].astype(np.float64), s0)
+    tol.assert_bf16_out(sel(o), o_ref)
+    tol.assert_state(sel(s), s_ref)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_one_step(dev, d):
     say("decode one step B256 H64 d", d)

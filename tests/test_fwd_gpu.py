@@ -154,6 +154,26 @@ def test_bf16_tails_with_state(dev, n, block, d):
     assert torch.equal(kv, kv16)
 
 
+def test_bf16_many_heads_short_sequences(dev):
+    """32,768 (batch, head) pairs of 200 tokens in one call (one chunk each;
+    the decays of the 64-head workload, so fast heads take the warm start and
+    the slowest the exact path), with initial and final states: 64 seeded
+    pairs against the oracle."""
+    B, H, n, d = 512, 64, 200, 128
+    say("many heads: B512 H64 N200 d128 with states")
+    q, k, v = qkv_device(B, H, n, d, seed=77, device=dev)
+    lam = decay_lambdas(H)
+    s0 = state_device(B, H, d, seed=77, device=dev)
+    o32, kv = _run(q, k, v, lam, dev, 64, out_dtype=torch.float32, kv_in=s0)
+    rng = np.random.default_rng(77)
+    pick = rng.choice(B * H, size=64, replace=False)
+    bs, hs = pick // H, pick % H
+    sel = lambda x: np.stack([host(x[b, h]) for b, h in zip(bs, hs)])
+    o_ref, s_ref = oracle(sel(q), sel(k), sel(v), lam[hs], sel(s0).astype(np.float64))
+    tol.assert_bf16_f32out(sel(o32), o_ref)
+    tol.assert_state(sel(kv), s_ref, "kv_out")
+
+
 @pytest.mark.parametrize("t0", [512, 700])
 def test_bf16_state_carry(dev, t0):
     say("bf16 state carry B1 H4 N2048 split", t0)
