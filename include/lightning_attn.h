@@ -116,6 +116,11 @@ extern "C" {
  * and every other dtype and block, take the exact path from the start.  The
  * _ex entry point with LA_FLAG_EXACT takes the exact path for every head.
  * The result does not depend on the path beyond rounding.
+ * Non-finite inputs: a NaN or inf in token t of a head makes that head's
+ * later state and output rows non-finite, as in the exact function (the check
+ * above never lets the warm start drop such a state); rows of the same block
+ * before t may come out non-finite too, as the blocked products meet the
+ * value there (0 * NaN).
  * Scratch (decay-power table, per-chunk states and the check's slots, see
  * lightning_attn_fwd_workspace_bytes) is allocated stream-ordered with
  * hipMallocAsync/hipFreeAsync on `stream`.

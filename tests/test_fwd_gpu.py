@@ -420,6 +420,43 @@ def test_warm_up_window_of_zeros_is_caught(dev):
         tol.assert_state(host(kv)[:, h], s_ref[:, h], "kv_out head %d" % h)
 
 
+def test_nan_input_reaches_every_later_row(dev):
+    # A NaN in one key entry of head 0 at token 100: in the exact function
+    # the state's row for that feature is NaN from then on (lam^n NaN = NaN),
+    # so every later output row of the head is NaN.  The warm start of the
+    # chunks after it would start from finite windows; the check sees the
+    # NaN in the state those windows leave out and sends the head to the
+    # exact path, so no later row comes out finite.  Rows of the NaN's own
+    # 64-token sub-tile before it are not specified: the blocked products
+    # meet the NaN there (0 * NaN), as any blocked attention kernel does.
+    # Head 1 has no NaN and stays on the warm start.
+    say("NaN key at token 100 of head 0, B1 H2 N700 d64 chunk 256")
+    q, k, v = qkv_device(1, 2, 700, 64, seed=151, device=dev)
+    k[0, 0, 100, 5] = float("nan")
+    lam = np.array([0.7, 0.7], dtype=np.float32)
+    lam_d = torch.from_numpy(lam).to(dev)
+    ws = torch.empty(la.workspace_bytes(1, 2, 700, 64, 64, 256), device=dev, dtype=torch.uint8)
+    kv = torch.empty((1, 2, 64, 64), device=dev, dtype=torch.float32)
+    o = la.fwd(q, k, v, lam_d, kv_out=kv, block=64, chunk=256, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    flags = _warm_flags(ws, 1, 2)
+    kvx = torch.empty_like(kv)
+    exact = la.fwd(q, k, v, lam_d, kv_out=kvx, block=64, chunk=256, out_dtype=torch.float32, exact=True)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle(host(q), host(k), host(v), lam)
+    assert flags.tolist() == [1, 0], flags
+    og, kg = host(o), host(kv)
+    assert np.isnan(o_ref[0, 0, 100:]).all() and np.isnan(og[0, 0, 100:]).all()
+    tol.assert_bf16_f32out(og[0, 0, :64], o_ref[0, 0, :64], "head 0 before the NaN's sub-tile")
+    tol.assert_bf16_f32out(og[0, 1], o_ref[0, 1], "head 1")
+    assert np.array_equal(np.isnan(kg), np.isnan(s_ref)) and np.isnan(kg[0, 0, 5]).all()
+    fin = ~np.isnan(s_ref)
+    tol.assert_state(kg[fin], s_ref[fin], "finite state entries")
+    # the flagged head ran the exact path: bit for bit the exact flag's result
+    assert torch.equal(o[:, 0].view(torch.int32), exact[:, 0].view(torch.int32))
+    assert torch.equal(kv[:, 0].view(torch.int32), kvx[:, 0].view(torch.int32))
+
+
 def test_warm_start_check_passes_the_workloads(dev):
     """On the workloads' Gaussian inputs no head is flagged (the left-out
     state is about lam^span <= 2^-30 of the window's), at the 64-head
