@@ -13,6 +13,7 @@ no CPU fallback.
 block 64 is the tuned path; 128 and 256 give the same result up to rounding
 through a general, slower kernel.
 """
+import contextlib
 import ctypes
 import os
 
@@ -128,17 +129,39 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
-
-
-def _check_dev(name, t, dtype=None, shape=None):
+def _device_of(name, t):
+    """The device of the tensor that anchors a call (every other tensor of the
+    call must be on it)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
     if t.device.type != "cuda":
         raise ValueError("%s must be a device tensor" % name)
+    return t.device
+
+
+def _current(device):
+    """Makes the call's device the current one for the library call (a no-op
+    when it already is)."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    elif stream.device != device:
+        raise ValueError("stream is on %s, the tensors on %s" % (stream.device, device))
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_dev(name, t, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, the call's tensors on %s" % (name, t.device, device))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     if dtype is not None and t.dtype != dtype:
@@ -184,33 +207,35 @@ def fwd(q, k, v, decay, kv_in=None, kv_out=None, block=64, out=None, out_dtype=N
     warm_chunk: chunk of the warm-start pass (0: the library's default,
     warm_chunk_for)."""
     lib = load()
+    dev = _device_of("q", q)
     if q.dtype not in _DT:
         raise TypeError("q must be bfloat16 or float32")
     B, H, N, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, q.dtype, (B, H, N, d))
-    _check_dev("decay", decay, torch.float32, (H,))
+        _check_dev(name, t, q.dtype, (B, H, N, d), device=dev)
+    _check_dev("decay", decay, torch.float32, (H,), device=dev)
     for name, t in (("kv_in", kv_in), ("kv_out", kv_out)):
         if t is not None:
-            _check_dev(name, t, torch.float32, (B, H, d, d))
+            _check_dev(name, t, torch.float32, (B, H, d, d), device=dev)
     odt = out_dtype if out_dtype is not None else (out.dtype if out is not None else q.dtype)
     if odt not in _DT:
         raise TypeError("out dtype must be bfloat16 or float32")
     if out is None:
         out = torch.empty((B, H, N, d), device=q.device, dtype=odt)
-    _check_dev("out", out, odt, (B, H, N, d))
+    _check_dev("out", out, odt, (B, H, N, d), device=dev)
     need = int(lib.lightning_attn_fwd_workspace_bytes(B, H, N, d, block, chunk))
     if need == 0:
         raise LightningAttnError(1, "lightning_attn_fwd_workspace_bytes")
     if workspace is None:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
-    _check_dev("workspace", workspace, torch.uint8)
+    _check_dev("workspace", workspace, torch.uint8, device=dev)
     e0, e1 = (None, None) if events is None else (ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
-    rc = lib.lightning_attn_fwd_ex(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(kv_in), _ptr(kv_out),
-        B, H, N, d, block, _DT[q.dtype], _DT[odt], chunk, warm_chunk, _fwd_flags(exact, silu),
-        _ptr(workspace), workspace.numel(), e0, e1, _stream(stream),
-    )
+    with _current(dev):
+        rc = lib.lightning_attn_fwd_ex(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(kv_in), _ptr(kv_out),
+            B, H, N, d, block, _DT[q.dtype], _DT[odt], chunk, warm_chunk, _fwd_flags(exact, silu),
+            _ptr(workspace), workspace.numel(), e0, e1, _stream(stream, dev),
+        )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_fwd_ex")
     return out
@@ -225,32 +250,34 @@ def fwd_fused(q, k, v, decay, gamma=None, gate=None, eps=1e-5, kv_in=None, kv_ou
     bf16 [B, H, N, d] (pre-activations with silu=True); block 64; the rest as
     fwd.  Returns out [B, H, N, d] in out_dtype."""
     lib = load()
+    dev = _device_of("q", q)
     B, H, N, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, torch.bfloat16, (B, H, N, d))
-    _check_dev("decay", decay, torch.float32, (H,))
+        _check_dev(name, t, torch.bfloat16, (B, H, N, d), device=dev)
+    _check_dev("decay", decay, torch.float32, (H,), device=dev)
     if gamma is not None:
-        _check_dev("gamma", gamma, torch.float32, (H, d))
+        _check_dev("gamma", gamma, torch.float32, (H, d), device=dev)
     if gate is not None:
-        _check_dev("gate", gate, torch.bfloat16, (B, H, N, d))
+        _check_dev("gate", gate, torch.bfloat16, (B, H, N, d), device=dev)
     for name, t in (("kv_in", kv_in), ("kv_out", kv_out)):
         if t is not None:
-            _check_dev(name, t, torch.float32, (B, H, d, d))
+            _check_dev(name, t, torch.float32, (B, H, d, d), device=dev)
     if out is None:
         out = torch.empty((B, H, N, d), device=q.device, dtype=out_dtype)
-    _check_dev("out", out, out_dtype, (B, H, N, d))
+    _check_dev("out", out, out_dtype, (B, H, N, d), device=dev)
     need = int(lib.lightning_attn_fwd_workspace_bytes(B, H, N, d, 64, chunk))
     if need == 0:
         raise LightningAttnError(1, "lightning_attn_fwd_workspace_bytes")
     if workspace is None:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
-    _check_dev("workspace", workspace, torch.uint8)
+    _check_dev("workspace", workspace, torch.uint8, device=dev)
     e0, e1 = (None, None) if events is None else (ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
-    rc = lib.lightning_attn_fwd_fused(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(gamma), float(eps), _ptr(gate), _ptr(out), _ptr(kv_in),
-        _ptr(kv_out), B, H, N, d, _DT[out_dtype], chunk, warm_chunk, _fwd_flags(exact, silu), _ptr(workspace),
-        workspace.numel(), e0, e1, _stream(stream),
-    )
+    with _current(dev):
+        rc = lib.lightning_attn_fwd_fused(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(gamma), float(eps), _ptr(gate), _ptr(out), _ptr(kv_in),
+            _ptr(kv_out), B, H, N, d, _DT[out_dtype], chunk, warm_chunk, _fwd_flags(exact, silu), _ptr(workspace),
+            workspace.numel(), e0, e1, _stream(stream, dev),
+        )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_fwd_fused")
     return out
@@ -264,22 +291,24 @@ def fwd_noalloc(q, k, v, decay, out, kv_in=None, kv_out=None, chunk=0, warm_chun
     fp32); the rest as fwd.  chunk 0: the default chunk doubled until the chunk
     states fit the array.  Returns out."""
     lib = load()
+    dev = _device_of("q", q)
     if q.dtype not in _DT:
         raise TypeError("q must be bfloat16 or float32")
     B, H, N, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, q.dtype, (B, H, N, d))
-    _check_dev("decay", decay, torch.float32, (H,))
+        _check_dev(name, t, q.dtype, (B, H, N, d), device=dev)
+    _check_dev("decay", decay, torch.float32, (H,), device=dev)
     for name, t in (("kv_in", kv_in), ("kv_out", kv_out)):
         if t is not None:
-            _check_dev(name, t, torch.float32, (B, H, d, d))
+            _check_dev(name, t, torch.float32, (B, H, d, d), device=dev)
     if not isinstance(out, torch.Tensor) or out.dtype not in _DT:
         raise TypeError("out must be a bfloat16 or float32 tensor")
-    _check_dev("out", out, out.dtype, (B, H, N, d))
-    rc = lib.lightning_attn_fwd_noalloc(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(kv_in), _ptr(kv_out), B, H, N, d, _DT[q.dtype],
-        _DT[out.dtype], chunk, warm_chunk, _fwd_flags(exact, silu), _stream(stream),
-    )
+    _check_dev("out", out, out.dtype, (B, H, N, d), device=dev)
+    with _current(dev):
+        rc = lib.lightning_attn_fwd_noalloc(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(kv_in), _ptr(kv_out), B, H, N, d, _DT[q.dtype],
+            _DT[out.dtype], chunk, warm_chunk, _fwd_flags(exact, silu), _stream(stream, dev),
+        )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_fwd_noalloc")
     return out
@@ -289,19 +318,21 @@ def decode_step(q, k, v, decay, kv_in=None, kv_out=None, out=None, stream=None):
     """One decode step.  q, k, v: [B, H, d] bf16; decay fp32 [H]; kv_in / kv_out:
     fp32 [B, H, d, d] (may be the same tensor).  Returns o [B, H, d] bf16."""
     lib = load()
+    dev = _device_of("q", q)
     B, H, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, torch.bfloat16, (B, H, d))
-    _check_dev("decay", decay, torch.float32, (H,))
+        _check_dev(name, t, torch.bfloat16, (B, H, d), device=dev)
+    _check_dev("decay", decay, torch.float32, (H,), device=dev)
     for name, t in (("kv_in", kv_in), ("kv_out", kv_out)):
         if t is not None:
-            _check_dev(name, t, torch.float32, (B, H, d, d))
+            _check_dev(name, t, torch.float32, (B, H, d, d), device=dev)
     if out is None:
         out = torch.empty((B, H, d), device=q.device, dtype=torch.bfloat16)
-    _check_dev("out", out, torch.bfloat16, (B, H, d))
-    rc = lib.lightning_attn_decode_step(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(kv_in), _ptr(kv_out), B, H, d, _stream(stream)
-    )
+    _check_dev("out", out, torch.bfloat16, (B, H, d), device=dev)
+    with _current(dev):
+        rc = lib.lightning_attn_decode_step(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(kv_in), _ptr(kv_out), B, H, d, _stream(stream, dev)
+        )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_decode_step")
     return out
@@ -314,24 +345,26 @@ def fwd_slots(q, k, v, decay, states, slots, block=64, out=None, out_dtype=None,
     slots: int32 [B] on the device (out of range: zero start, no write-back).
     Returns out [B, H, N, d] in out_dtype (default: the input dtype)."""
     lib = load()
+    dev = _device_of("q", q)
     B, H, N, d = q.shape
     if q.dtype not in _DT:
         raise TypeError("q must be bfloat16 or float32")
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, q.dtype, (B, H, N, d))
-    _check_dev("decay", decay, torch.float32, (H,))
+        _check_dev(name, t, q.dtype, (B, H, N, d), device=dev)
+    _check_dev("decay", decay, torch.float32, (H,), device=dev)
     if states.dim() != 4:
         raise ValueError("states must be [num_slots, H, d, d]")
-    _check_dev("states", states, torch.float32, (states.shape[0], H, d, d))
-    _check_dev("slots", slots, torch.int32, (B,))
+    _check_dev("states", states, torch.float32, (states.shape[0], H, d, d), device=dev)
+    _check_dev("slots", slots, torch.int32, (B,), device=dev)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((B, H, N, d), device=q.device, dtype=out_dtype)
-    _check_dev("out", out, out_dtype, (B, H, N, d))
-    rc = lib.lightning_attn_fwd_slots(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(states), _ptr(slots), B, H, N, d,
-        states.shape[0], block, _DT[q.dtype], _DT[out_dtype], _fwd_flags(exact, silu), _stream(stream)
-    )
+    _check_dev("out", out, out_dtype, (B, H, N, d), device=dev)
+    with _current(dev):
+        rc = lib.lightning_attn_fwd_slots(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(states), _ptr(slots), B, H, N, d,
+            states.shape[0], block, _DT[q.dtype], _DT[out_dtype], _fwd_flags(exact, silu), _stream(stream, dev)
+        )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_fwd_slots")
     return out
@@ -345,15 +378,16 @@ def bwd(q, k, v, decay, dout, kv_in=None, dkv_out=None, out_dtype=None, dkv_in=F
     dq, dk, dv in out_dtype (default: the input dtype); dkv_in is an fp32
     tensor when asked for (True, or a tensor to write into), else None."""
     lib = load()
+    dev = _device_of("q", q)
     B, H, N, d = q.shape
     if q.dtype not in _DT:
         raise TypeError("q must be bfloat16 or float32")
     for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
-        _check_dev(name, t, q.dtype, (B, H, N, d))
-    _check_dev("decay", decay, torch.float32, (H,))
+        _check_dev(name, t, q.dtype, (B, H, N, d), device=dev)
+    _check_dev("decay", decay, torch.float32, (H,), device=dev)
     for name, t in (("kv_in", kv_in), ("dkv_out", dkv_out)):
         if t is not None:
-            _check_dev(name, t, torch.float32, (B, H, d, d))
+            _check_dev(name, t, torch.float32, (B, H, d, d), device=dev)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     code = _DT[out_dtype]
     dq, dk, dv = (torch.empty((B, H, N, d), device=q.device, dtype=out_dtype) for _ in range(3))
@@ -362,15 +396,17 @@ def bwd(q, k, v, decay, dout, kv_in=None, dkv_out=None, out_dtype=None, dkv_in=F
     elif dkv_in is False:
         dkv_in = None
     if dkv_in is not None:
-        _check_dev("dkv_in", dkv_in, torch.float32, (B, H, d, d))
+        _check_dev("dkv_in", dkv_in, torch.float32, (B, H, d, d), device=dev)
     need = lib_bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
-    rc = lib.lightning_attn_bwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(dout), _ptr(kv_in), _ptr(dkv_out), _ptr(dq), _ptr(dk),
-        _ptr(dv), _ptr(dkv_in), B, H, N, d, _DT[q.dtype], code, LA_FLAG_EXACT if exact else 0, _ptr(workspace),
-        workspace.numel(), _stream(stream)
-    )
+    _check_dev("workspace", workspace, torch.uint8, device=dev)
+    with _current(dev):
+        rc = lib.lightning_attn_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(dout), _ptr(kv_in), _ptr(dkv_out), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(dkv_in), B, H, N, d, _DT[q.dtype], code, LA_FLAG_EXACT if exact else 0, _ptr(workspace),
+            workspace.numel(), _stream(stream, dev)
+        )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_bwd")
     return dq, dk, dv, dkv_in
@@ -382,21 +418,23 @@ def decode_slots(q, k, v, decay, states, slots, out=None, stream=None):
     slots: int32 [B] on the device (out of range = idle row, zero output).
     Returns o [B, H, d] bf16."""
     lib = load()
+    dev = _device_of("q", q)
     B, H, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, torch.bfloat16, (B, H, d))
-    _check_dev("decay", decay, torch.float32, (H,))
+        _check_dev(name, t, torch.bfloat16, (B, H, d), device=dev)
+    _check_dev("decay", decay, torch.float32, (H,), device=dev)
     if states.dim() != 4:
         raise ValueError("states must be [num_slots, H, d, d]")
-    _check_dev("states", states, torch.float32, (states.shape[0], H, d, d))
-    _check_dev("slots", slots, torch.int32, (B,))
+    _check_dev("states", states, torch.float32, (states.shape[0], H, d, d), device=dev)
+    _check_dev("slots", slots, torch.int32, (B,), device=dev)
     if out is None:
         out = torch.empty((B, H, d), device=q.device, dtype=torch.bfloat16)
-    _check_dev("out", out, torch.bfloat16, (B, H, d))
-    rc = lib.lightning_attn_decode_slots(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(states), _ptr(slots), B, H, d, states.shape[0],
-        _stream(stream)
-    )
+    _check_dev("out", out, torch.bfloat16, (B, H, d), device=dev)
+    with _current(dev):
+        rc = lib.lightning_attn_decode_slots(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(states), _ptr(slots), B, H, d, states.shape[0],
+            _stream(stream, dev)
+        )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_decode_slots")
     return out
@@ -409,26 +447,28 @@ def decode_fused(q, k, v, decay, states, slots=None, silu=True, gamma=None, gate
     states: fp32 [num_slots, H, d, d] in place; slots: int32 [B] or None
     (row b uses state row b).  Returns o [B, H, d] bf16."""
     lib = load()
+    dev = _device_of("q", q)
     B, H, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, torch.bfloat16, (B, H, d))
-    _check_dev("decay", decay, torch.float32, (H,))
+        _check_dev(name, t, torch.bfloat16, (B, H, d), device=dev)
+    _check_dev("decay", decay, torch.float32, (H,), device=dev)
     if states.dim() != 4:
         raise ValueError("states must be [num_slots, H, d, d]")
-    _check_dev("states", states, torch.float32, (states.shape[0], H, d, d))
+    _check_dev("states", states, torch.float32, (states.shape[0], H, d, d), device=dev)
     if slots is not None:
-        _check_dev("slots", slots, torch.int32, (B,))
+        _check_dev("slots", slots, torch.int32, (B,), device=dev)
     if gamma is not None:
-        _check_dev("gamma", gamma, torch.float32, (H, d))
+        _check_dev("gamma", gamma, torch.float32, (H, d), device=dev)
     if gate is not None:
-        _check_dev("gate", gate, torch.bfloat16, (B, H, d))
+        _check_dev("gate", gate, torch.bfloat16, (B, H, d), device=dev)
     if out is None:
         out = torch.empty((B, H, d), device=q.device, dtype=torch.bfloat16)
-    _check_dev("out", out, torch.bfloat16, (B, H, d))
-    rc = lib.lightning_attn_decode_fused(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(states), _ptr(slots), states.shape[0],
-        1 if silu else 0, _ptr(gamma), float(eps), _ptr(gate), B, H, d, _stream(stream)
-    )
+    _check_dev("out", out, torch.bfloat16, (B, H, d), device=dev)
+    with _current(dev):
+        rc = lib.lightning_attn_decode_fused(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(states), _ptr(slots), states.shape[0],
+            1 if silu else 0, _ptr(gamma), float(eps), _ptr(gate), B, H, d, _stream(stream, dev)
+        )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_decode_fused")
     return out
@@ -442,26 +482,28 @@ def decode_layers(q, k, v, decay, states, slots=None, silu=False, gamma=None, ga
     row) or None (row b uses slot b); silu / gamma fp32 [L, H, d] / gate bf16
     [L, B, H, d] as decode_fused.  Returns o [L, B, H, d] bf16."""
     lib = load()
+    dev = _device_of("q", q)
     L, B, H, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, torch.bfloat16, (L, B, H, d))
-    _check_dev("decay", decay, torch.float32, (L, H))
+        _check_dev(name, t, torch.bfloat16, (L, B, H, d), device=dev)
+    _check_dev("decay", decay, torch.float32, (L, H), device=dev)
     if states.dim() != 5:
         raise ValueError("states must be [L, num_slots, H, d, d]")
-    _check_dev("states", states, torch.float32, (L, states.shape[1], H, d, d))
+    _check_dev("states", states, torch.float32, (L, states.shape[1], H, d, d), device=dev)
     if slots is not None:
-        _check_dev("slots", slots, torch.int32, (L, B))
+        _check_dev("slots", slots, torch.int32, (L, B), device=dev)
     if gamma is not None:
-        _check_dev("gamma", gamma, torch.float32, (L, H, d))
+        _check_dev("gamma", gamma, torch.float32, (L, H, d), device=dev)
     if gate is not None:
-        _check_dev("gate", gate, torch.bfloat16, (L, B, H, d))
+        _check_dev("gate", gate, torch.bfloat16, (L, B, H, d), device=dev)
     if out is None:
         out = torch.empty((L, B, H, d), device=q.device, dtype=torch.bfloat16)
-    _check_dev("out", out, torch.bfloat16, (L, B, H, d))
-    rc = lib.lightning_attn_decode_layers(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(states), _ptr(slots), L, B, H, d, states.shape[1],
-        1 if silu else 0, _ptr(gamma), float(eps), _ptr(gate), _stream(stream)
-    )
+    _check_dev("out", out, torch.bfloat16, (L, B, H, d), device=dev)
+    with _current(dev):
+        rc = lib.lightning_attn_decode_layers(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(states), _ptr(slots), L, B, H, d, states.shape[1],
+            1 if silu else 0, _ptr(gamma), float(eps), _ptr(gate), _stream(stream, dev)
+        )
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_decode_layers")
     return out
@@ -472,17 +514,21 @@ def norm_gate(o, gamma=None, gate=None, eps=1e-5, out=None, stream=None):
     shape) of a prefill output o [B, H, N, d] (bf16 or fp32), into bf16 out
     (o itself allowed when o is bf16)."""
     lib = load()
+    dev = _device_of("o", o)
+    if o.dtype not in _DT:
+        raise TypeError("o must be bfloat16 or float32")
     B, H, N, d = o.shape
-    _check_dev("o", o, None, (B, H, N, d))
+    _check_dev("o", o, None, (B, H, N, d), device=dev)
     if gamma is not None:
-        _check_dev("gamma", gamma, torch.float32, (H, d))
+        _check_dev("gamma", gamma, torch.float32, (H, d), device=dev)
     if gate is not None:
-        _check_dev("gate", gate, torch.bfloat16, (B, H, N, d))
+        _check_dev("gate", gate, torch.bfloat16, (B, H, N, d), device=dev)
     if out is None:
         out = torch.empty((B, H, N, d), device=o.device, dtype=torch.bfloat16)
-    _check_dev("out", out, torch.bfloat16, (B, H, N, d))
-    rc = lib.lightning_attn_norm_gate(_ptr(o), _DT[o.dtype], _ptr(gate), _ptr(gamma), float(eps), _ptr(out),
-                                      B, H, N, d, _stream(stream))
+    _check_dev("out", out, torch.bfloat16, (B, H, N, d), device=dev)
+    with _current(dev):
+        rc = lib.lightning_attn_norm_gate(_ptr(o), _DT[o.dtype], _ptr(gate), _ptr(gamma), float(eps), _ptr(out),
+                                          B, H, N, d, _stream(stream, dev))
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_norm_gate")
     return out
@@ -491,8 +537,10 @@ def norm_gate(o, gamma=None, gate=None, eps=1e-5, out=None, stream=None):
 def silu_(x, stream=None):
     """x <- SiLU(x) in place (bf16 device tensor); returns x."""
     lib = load()
-    _check_dev("x", x, torch.bfloat16)
-    rc = lib.lightning_attn_silu(_ptr(x), x.numel(), _stream(stream))
+    dev = _device_of("x", x)
+    _check_dev("x", x, torch.bfloat16, device=dev)
+    with _current(dev):
+        rc = lib.lightning_attn_silu(_ptr(x), x.numel(), _stream(stream, dev))
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_silu")
     return x

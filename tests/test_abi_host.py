@@ -402,3 +402,17 @@ def test_fwd_fused_validation(lib):
     assert call(gamma=ctypes.c_void_p(P[4].value + 64)) == LA_ERR_INVALID  # gamma inside the output
     assert call(d=96) == LA_ERR_UNSUPPORTED
     assert call(outd=7) == LA_ERR_INVALID
+
+
+def test_binding_rejects_a_stream_of_another_device():
+    """The binding launches on the tensors' device: a caller's stream on
+    another device is refused before the library is called."""
+    import torch
+
+    class _Stream:
+        device = torch.device("cuda", 1)
+        cuda_stream = 0
+
+    with pytest.raises(ValueError, match="stream is on"):
+        la._stream(_Stream(), torch.device("cuda", 0))
+    assert la._stream(_Stream(), torch.device("cuda", 1)).value is None  # same device: passed through
