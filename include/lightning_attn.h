@@ -32,7 +32,10 @@
  *  - The caller owns every buffer.  The library never frees or retains
  *    caller memory.
  *  - kv_in may equal kv_out (in-place state update); otherwise the two must
- *    not overlap.  out must not overlap q, k, v, kv_in or kv_out.
+ *    not overlap.  Every buffer a call writes (out, kv_out, a state pool, a
+ *    caller's workspace) must not overlap any other argument; the one
+ *    exception is the in-place state.  Overlaps are reported as
+ *    LA_ERR_INVALID.
  *  - Arguments are validated before any HIP call, so validation errors are
  *    returned without touching the device.  Nothing is thrown across the ABI.
  *  - The library keeps no state between calls (except the per-device array

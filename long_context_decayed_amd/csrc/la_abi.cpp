@@ -153,9 +153,14 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* d
   const int64_t in_es = in_dtype == LA_DTYPE_BF16 ? 2 : 4, out_es = out_dtype == LA_DTYPE_BF16 ? 2 : 4;
   const int64_t in_bytes = B * H * N * d * in_es, out_bytes = B * H * N * d * out_es;
   const int64_t st_bytes = B * H * d * d * 4;
+  const int64_t dec_bytes = H * 4;
   if (overlap(out, out_bytes, q, in_bytes) || overlap(out, out_bytes, k, in_bytes) ||
       overlap(out, out_bytes, v, in_bytes) || overlap(out, out_bytes, kv_in, st_bytes) ||
-      overlap(out, out_bytes, kv_out, st_bytes) || !states_apart_or_same(kv_in, kv_out, st_bytes))
+      overlap(out, out_bytes, kv_out, st_bytes) || overlap(out, out_bytes, decay, dec_bytes) ||
+      !states_apart_or_same(kv_in, kv_out, st_bytes))
+    return LA_ERR_INVALID;
+  if (overlap(kv_out, st_bytes, q, in_bytes) || overlap(kv_out, st_bytes, k, in_bytes) ||
+      overlap(kv_out, st_bytes, v, in_bytes) || overlap(kv_out, st_bytes, decay, dec_bytes))
     return LA_ERR_INVALID;
   return LA_OK;
 }
@@ -258,7 +263,8 @@ int lightning_attn_fwd_slots(const void* q, const void* k, const void* v, const 
   const int64_t pool_bytes = num_slots * H * d * d * 4;
   if (overlap(states, pool_bytes, q, in_bytes) || overlap(states, pool_bytes, k, in_bytes) ||
       overlap(states, pool_bytes, v, in_bytes) || overlap(states, pool_bytes, out, out_bytes) ||
-      overlap(states, pool_bytes, slots, B * 4) || overlap(out, out_bytes, slots, B * 4))
+      overlap(states, pool_bytes, slots, B * 4) || overlap(out, out_bytes, slots, B * 4) ||
+      overlap(states, pool_bytes, decay, H * 4))
     return LA_ERR_INVALID;
   return prefill_run(q, k, v, decay, out, states, states, B, H, N, d, block, in_dtype, out_dtype, L,
                      pick_warm_chunk(B, H, N, L), nullptr, 0, nullptr, nullptr, stream, (const int*)slots, num_slots,
@@ -279,7 +285,10 @@ int lightning_attn_fwd_fused(const void* q, const void* k, const void* v, const 
   rc = resolve_warm_chunk(B, H, N, chunk, warm_chunk, L, &Lw);
   if (rc != LA_OK) return rc;
   const int64_t out_bytes = B * H * N * d * (out_dtype == LA_DTYPE_BF16 ? 2 : 4), gate_bytes = B * H * N * d * 2;
-  if (overlap(out, out_bytes, gate, gate_bytes) || overlap(out, out_bytes, gamma, H * d * 4)) return LA_ERR_INVALID;
+  const int64_t st_bytes = B * H * d * d * 4;
+  if (overlap(out, out_bytes, gate, gate_bytes) || overlap(out, out_bytes, gamma, H * d * 4) ||
+      overlap(kv_out, st_bytes, gate, gate_bytes) || overlap(kv_out, st_bytes, gamma, H * d * 4))
+    return LA_ERR_INVALID;
   const Epilogue epi{gamma, eps, gate};
   return prefill_run(q, k, v, decay, out, kv_in, kv_out, B, H, N, d, 64, LA_DTYPE_BF16, out_dtype, L, Lw, workspace,
                      workspace_bytes, evt_begin, evt_end, stream, nullptr, 0, flags, &epi);
@@ -300,6 +309,17 @@ int prefill_run(const void* q, const void* k, const void* v, const float* decay,
   if (workspace) {
     if (workspace_bytes < need) return LA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return LA_ERR_INVALID;
+    // the passes write the workspace: it may overlap none of the arguments
+    const int64_t in_bytes = B * H * N * d * (in_dtype == LA_DTYPE_BF16 ? 2 : 4);
+    const int64_t out_bytes = B * H * N * d * (out_dtype == LA_DTYPE_BF16 ? 2 : 4);
+    const int64_t st_bytes = B * H * d * d * 4, wsb = (int64_t)need;
+    if (overlap(workspace, wsb, q, in_bytes) || overlap(workspace, wsb, k, in_bytes) ||
+        overlap(workspace, wsb, v, in_bytes) || overlap(workspace, wsb, out, out_bytes) ||
+        overlap(workspace, wsb, kv_in, st_bytes) || overlap(workspace, wsb, kv_out, st_bytes) ||
+        overlap(workspace, wsb, decay, H * 4))
+      return LA_ERR_INVALID;
+    if (epi && (overlap(workspace, wsb, epi->gamma, H * d * 4) || overlap(workspace, wsb, epi->gate, B * H * N * d * 2)))
+      return LA_ERR_INVALID;
   }
 
   hipStream_t st = (hipStream_t)stream;
@@ -433,6 +453,9 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
   if (overlap(dq, out_bytes, dk, out_bytes) || overlap(dq, out_bytes, dv, out_bytes) ||
       overlap(dk, out_bytes, dv, out_bytes))
     return LA_ERR_INVALID;
+  for (const void* o : outs)
+    if (overlap(o, out_bytes, decay, H * 4)) return LA_ERR_INVALID;
+  if (overlap(dkv_in, st_bytes, decay, H * 4)) return LA_ERR_INVALID;
   if (dkv_in && dkv_in != dkv_out) {
     for (const void* i : ins)
       if (overlap(dkv_in, st_bytes, i, in_bytes)) return LA_ERR_INVALID;
@@ -444,6 +467,14 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
   if (workspace) {
     if (workspace_bytes < need) return LA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return LA_ERR_INVALID;
+    const int64_t wsb = (int64_t)need;
+    for (const void* i : ins)
+      if (overlap(workspace, wsb, i, in_bytes)) return LA_ERR_INVALID;
+    for (const void* o : outs)
+      if (overlap(workspace, wsb, o, out_bytes)) return LA_ERR_INVALID;
+    if (overlap(workspace, wsb, kv_in, st_bytes) || overlap(workspace, wsb, dkv_out, st_bytes) ||
+        overlap(workspace, wsb, dkv_in, st_bytes) || overlap(workspace, wsb, decay, H * 4))
+      return LA_ERR_INVALID;
   }
 
   hipStream_t st = (hipStream_t)stream;
@@ -604,7 +635,11 @@ int lightning_attn_decode_step(const void* q, const void* k, const void* v, cons
   const int64_t vec_bytes = B * H * d * 2, st_bytes = B * H * d * d * 4;
   if (overlap(out, vec_bytes, q, vec_bytes) || overlap(out, vec_bytes, k, vec_bytes) ||
       overlap(out, vec_bytes, v, vec_bytes) || overlap(out, vec_bytes, kv_in, st_bytes) ||
-      overlap(out, vec_bytes, kv_out, st_bytes) || !states_apart_or_same(kv_in, kv_out, st_bytes))
+      overlap(out, vec_bytes, kv_out, st_bytes) || overlap(out, vec_bytes, decay, H * 4) ||
+      !states_apart_or_same(kv_in, kv_out, st_bytes))
+    return LA_ERR_INVALID;
+  if (overlap(kv_out, st_bytes, q, vec_bytes) || overlap(kv_out, st_bytes, k, vec_bytes) ||
+      overlap(kv_out, st_bytes, v, vec_bytes) || overlap(kv_out, st_bytes, decay, H * 4))
     return LA_ERR_INVALID;
   return from_hip(la::launch_decode(q, k, v, decay, out, kv_in, kv_out, B, H, d, (hipStream_t)stream));
 }
@@ -622,7 +657,10 @@ int lightning_attn_decode_slots(const void* q, const void* k, const void* v, con
   const int64_t vec_bytes = B * H * d * 2, pool_bytes = num_slots * H * d * d * 4;
   if (overlap(out, vec_bytes, q, vec_bytes) || overlap(out, vec_bytes, k, vec_bytes) ||
       overlap(out, vec_bytes, v, vec_bytes) || overlap(out, vec_bytes, states, pool_bytes) ||
-      overlap(out, vec_bytes, slots, B * 4) || overlap(states, pool_bytes, slots, B * 4))
+      overlap(out, vec_bytes, slots, B * 4) || overlap(states, pool_bytes, slots, B * 4) ||
+      overlap(out, vec_bytes, decay, H * 4) || overlap(states, pool_bytes, q, vec_bytes) ||
+      overlap(states, pool_bytes, k, vec_bytes) || overlap(states, pool_bytes, v, vec_bytes) ||
+      overlap(states, pool_bytes, decay, H * 4))
     return LA_ERR_INVALID;
   return from_hip(la::launch_decode(q, k, v, decay, out, states, states, B, H, d, (hipStream_t)stream,
                                     (const int*)slots, num_slots));
@@ -646,7 +684,10 @@ int lightning_attn_decode_fused(const void* q, const void* k, const void* v, con
       overlap(out, vec_bytes, v, vec_bytes) || overlap(out, vec_bytes, states, pool_bytes) ||
       overlap(out, vec_bytes, slots, B * 4) || overlap(states, pool_bytes, slots, B * 4) ||
       overlap(out, vec_bytes, gate, vec_bytes) || overlap(out, vec_bytes, gamma, H * d * 4) ||
-      overlap(states, pool_bytes, gate, vec_bytes) || overlap(states, pool_bytes, gamma, H * d * 4))
+      overlap(states, pool_bytes, gate, vec_bytes) || overlap(states, pool_bytes, gamma, H * d * 4) ||
+      overlap(out, vec_bytes, decay, H * 4) || overlap(states, pool_bytes, q, vec_bytes) ||
+      overlap(states, pool_bytes, k, vec_bytes) || overlap(states, pool_bytes, v, vec_bytes) ||
+      overlap(states, pool_bytes, decay, H * 4))
     return LA_ERR_INVALID;
   la::DecodeFusion fz{silu ? 1 : 0, gamma, eps, gate};
   return from_hip(la::launch_decode(q, k, v, decay, out, states, states, B, H, d, (hipStream_t)stream,
@@ -676,7 +717,8 @@ int lightning_attn_decode_layers(const void* q, const void* k, const void* v, co
       overlap(out, vec_bytes, gate, vec_bytes) || overlap(out, vec_bytes, gamma, gamma_bytes) ||
       overlap(states, pool_bytes, gate, vec_bytes) || overlap(states, pool_bytes, gamma, gamma_bytes) ||
       overlap(states, pool_bytes, q, vec_bytes) || overlap(states, pool_bytes, k, vec_bytes) ||
-      overlap(states, pool_bytes, v, vec_bytes) || overlap(states, pool_bytes, decay, num_layers * H * 4))
+      overlap(states, pool_bytes, v, vec_bytes) || overlap(states, pool_bytes, decay, num_layers * H * 4) ||
+      overlap(out, vec_bytes, decay, num_layers * H * 4))
     return LA_ERR_INVALID;
   la::DecodeFusion fz{silu ? 1 : 0, gamma, eps, gate};
   return from_hip(la::launch_decode(q, k, v, decay, out, states, states, B, H, d, (hipStream_t)stream,

@@ -416,3 +416,36 @@ def test_binding_rejects_a_stream_of_another_device():
     with pytest.raises(ValueError, match="stream is on"):
         la._stream(_Stream(), torch.device("cuda", 0))
     assert la._stream(_Stream(), torch.device("cuda", 1)).value is None  # same device: passed through
+
+
+def test_written_buffers_apart_from_every_input(lib):
+    """A buffer a call writes may overlap no other argument (bar the in-place
+    state): each case is refused before any HIP call."""
+    inside = lambda p, off=64: ctypes.c_void_p(p.value + off)
+    # prefill: the final state inside q, k or v or on the decays; the output on the decays
+    assert _fwd(lib, kv_out=inside(FAKE[0])) == LA_ERR_INVALID
+    assert _fwd(lib, kv_out=inside(FAKE[2])) == LA_ERR_INVALID
+    assert _fwd(lib, kv_out=FAKE[3]) == LA_ERR_INVALID
+    assert _fwd(lib, out=FAKE[3]) == LA_ERR_INVALID
+    # a caller's workspace over q, over the output, over the decays
+    need = lib.lightning_attn_fwd_workspace_bytes(1, 2, 128, 64, 64, 0)
+    for target in (FAKE[0], FAKE[4], FAKE[3]):
+        assert _fwd(lib, ws=target, wsb=need) == LA_ERR_INVALID
+    # decode: the written state over q, the output over the decays
+    dec = lib.lightning_attn_decode_step
+    assert dec(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], None, inside(FAKE[0]), 1, 2, 64, None) == LA_ERR_INVALID
+    assert dec(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[3], None, FAKE[5], 1, 2, 64, None) == LA_ERR_INVALID
+    # a state pool over k
+    slots = lib.lightning_attn_decode_slots
+    assert slots(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], inside(FAKE[1]), FAKE[6], 1, 2, 64, 4, None) \
+        == LA_ERR_INVALID
+    # backward: a caller's workspace over dq, dk over the decays
+    f = lib.lightning_attn_bwd
+    base = [FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], None, None, FAKE[5], FAKE[6], FAKE[7], None,
+            1, 1, 128, 128, 0, 0, 0, None, 0, None]
+    a = list(base)
+    a[18], a[19] = FAKE[5], lib.lightning_attn_bwd_workspace_bytes(1, 1, 128, 128)
+    assert f(*a) == LA_ERR_INVALID
+    a = list(base)
+    a[8] = FAKE[3]
+    assert f(*a) == LA_ERR_INVALID
