@@ -69,15 +69,19 @@ int64_t pick_chunk(int64_t B, int64_t H, int64_t N, int64_t block) {
 }
 
 // Default warm-start chunk: the scan's chunk L doubled up to twice (4L) while
-// the warm-start pass keeps at least 1024 workgroups (two rounds at two per
-// CU) and the chunk stays within the sequence.  Longer chunks let more heads
-// take the warm start (a carry span up to half the chunk) and shorten
-// its warm-up windows relative to the chunk, while the heads on the exact
-// path keep the shorter chunks and the workgroups they need.
+// the warm-start pass keeps at least kResidentGroups workgroups (one full
+// round at two per CU) and the chunk stays within the sequence.  Longer
+// chunks let more heads take the warm start (a carry span up to half the
+// chunk) and shorten its warm-up windows relative to the chunk, while the
+// heads on the exact path keep the shorter chunks and the workgroups they
+// need; fewer workgroups than one round would leave CUs idle.
+constexpr int64_t kResidentGroups = 512;  // 256 CUs x 2 workgroups of the block-64 kernels
+
 int64_t pick_warm_chunk(int64_t B, int64_t H, int64_t N, int64_t L) {
   int64_t Lw = L;
   const int64_t cap = ceil_div(N, L) * L;
-  while (Lw < 4 * L && 2 * Lw <= kMaxTokens && 2 * Lw <= cap && B * H * ceil_div(N, 2 * Lw) >= 1024) Lw *= 2;
+  while (Lw < 4 * L && 2 * Lw <= kMaxTokens && 2 * Lw <= cap && B * H * ceil_div(N, 2 * Lw) >= kResidentGroups)
+    Lw *= 2;
   return Lw;
 }
 

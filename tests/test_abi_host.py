@@ -306,14 +306,16 @@ def test_partially_overlapping_states_rejected(lib):
 
 def test_warm_chunk_rules(lib):
     """The warm-start chunk: default up to four times the scan's default chunk
-    while at least 1024 workgroups remain; an explicit chunk sets both unless
-    warm_chunk is given; an explicit warm_chunk is a multiple of 64 and at
-    least the scan's chunk."""
+    while at least 512 workgroups (one round at two per CU) remain; an
+    explicit chunk sets both unless warm_chunk is given; an explicit
+    warm_chunk is a multiple of 64 and at least the scan's chunk."""
     wc = lib.lightning_attn_fwd_warm_chunk
     assert lib.lightning_attn_fwd_chunk(1, 64, 1 << 20, 64, 0) == 16384
-    assert wc(1, 64, 1 << 20, 64, 0, 0) == 65536          # 16 chunks x 64 heads = 1024 workgroups
-    assert wc(1, 32, 1 << 20, 64, 0, 0) == 32768          # 32 x 32 = 1024
-    assert wc(4, 64, 1 << 16, 64, 0, 0) == 16384          # chunk 8192 for >= 2048; 4 x 64 x 4 = 1024
+    assert wc(1, 64, 1 << 20, 64, 0, 0) == 65536          # four times the chunk: 16 chunks x 64 heads
+    assert wc(1, 32, 1 << 20, 64, 0, 0) == 65536          # 16 x 32 = 512
+    assert wc(1, 8, 1 << 20, 64, 0, 0) == 16384           # chunk 4096; 64 x 8 = 512
+    assert wc(4, 64, 1 << 16, 64, 0, 0) == 32768          # chunk 8192 for >= 2048; 4 x 64 x 2 = 512
+    assert wc(1, 64, 8192, 64, 0, 0) == 1024              # chunk 256; 8 x 64 = 512
     assert wc(1, 8, 3000, 64, 0, 0) == 256                # too few workgroups to grow
     assert wc(1, 64, 1 << 20, 64, 4096, 0) == 4096        # an explicit chunk sets both
     assert wc(1, 64, 1 << 20, 64, 4096, 32768) == 32768

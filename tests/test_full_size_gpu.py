@@ -161,11 +161,11 @@ def test_max_sequence_length(dev):
     say("longest sequence: B1 H2 N2^24 d128 (warm-start head and lam = 1 head)")
     q, k, v = qkv_device(B, H, N, d, seed=44, device=dev, slice_tokens=1 << 20)
     # head 0 (lam = 0.99610, carry span 5376 tokens) takes the warm start at
-    # the 32768-token warm-start chunk of this shape; head 1 (lam = 1) the
+    # the 65536-token warm-start chunk of this shape; head 1 (lam = 1) the
     # exact path's lam = 1 kernels
     lam = np.array([decay_lambdas(64)[63], 1.0], dtype=np.float32)
     lam_t = torch.from_numpy(lam).to(dev)
-    assert la.warm_chunk_for(B, H, N, 64) == 32768
+    assert la.warm_chunk_for(B, H, N, 64) == 65536
     kv = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
     out = la.fwd(q, k, v, lam_t, kv_out=kv, block=64, out_dtype=torch.float32)
     torch.cuda.synchronize()
