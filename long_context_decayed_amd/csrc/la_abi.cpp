@@ -54,14 +54,19 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 bool valid_block(int64_t block) { return block == 64 || block == 128 || block == 256; }
 
 // Default chunk: 16384 tokens, halved while the chunk-parallel passes would
-// launch fewer than 2048 workgroups, never below max(block, 256), and never
-// longer than the sequence rounded up to a whole block.
+// launch fewer than 2048 workgroups, never below a floor of N/8 (a power of
+// two, clamped to [256, 1024], and at least the block), and never longer
+// than the sequence rounded up to a whole block.
 int64_t pick_chunk(int64_t B, int64_t H, int64_t N, int64_t block) {
-  // Long chunks keep the chunk-state traffic small (each chunk moves four
-  // d x d fp32 states through HBM across the three passes); enough of them
-  // keep four rounds of resident workgroups (2 per CU) busy.
+  // Long chunks keep the chunk-state traffic small: each chunk moves four
+  // d x d fp32 states through HBM across the three passes (at d = 128 and
+  // 256 tokens as many bytes as q, k, v and o); enough of them keep four
+  // rounds of resident workgroups (2 per CU) busy.  On short sequences the
+  // state traffic weighs more than the extra rounds, hence the floor.
   int64_t L = 16384;
-  const int64_t floor_l = block > 256 ? block : 256;
+  int64_t floor_l = 256;
+  while (floor_l < 1024 && 16 * floor_l <= N) floor_l *= 2;
+  if (floor_l < block) floor_l = block;
   while (L > floor_l && B * H * ceil_div(N, L) < 2048) L /= 2;
   const int64_t cap = ceil_div(N, block) * block;
   if (L > cap) L = cap;

@@ -117,8 +117,12 @@ def test_workspace_and_chunk_values(lib):
     assert lib.lightning_attn_fwd_workspace_bytes(1, 64, 1 << 20, 128, 256, 0) == tbl + states + guard + 64 * 4
     # batched: 4 x 64 heads x 65536 tokens -> halve once to reach 2048 workgroups
     assert lib.lightning_attn_fwd_chunk(4, 64, 65536, 64, 0) == 8192
-    # 8192 tokens x 64 heads: chunks halve until >= 2048 workgroups (floor 256)
-    assert lib.lightning_attn_fwd_chunk(1, 64, 8192, 256, 0) == 256
+    # 8192 tokens x 64 heads: chunks would halve until >= 2048 workgroups, but
+    # stop at the floor N/8 = 1024 (chunk states as large as the data below it)
+    assert lib.lightning_attn_fwd_chunk(1, 64, 8192, 256, 0) == 1024
+    assert lib.lightning_attn_fwd_chunk(1, 64, 4096, 64, 0) == 512
+    assert lib.lightning_attn_fwd_chunk(1, 64, 16384, 64, 0) == 1024
+    assert lib.lightning_attn_fwd_chunk(1, 64, 65536, 64, 0) == 2048   # 2048 workgroups above the floor
     # tiny: floor at 256 tokens, capped by the block-rounded length
     assert lib.lightning_attn_fwd_chunk(1, 2, 1024, 64, 0) == 256
     assert lib.lightning_attn_fwd_chunk(1, 1, 100, 64, 0) == 128
@@ -315,7 +319,8 @@ def test_warm_chunk_rules(lib):
     assert wc(1, 32, 1 << 20, 64, 0, 0) == 65536          # 16 x 32 = 512
     assert wc(1, 8, 1 << 20, 64, 0, 0) == 16384           # chunk 4096; 64 x 8 = 512
     assert wc(4, 64, 1 << 16, 64, 0, 0) == 32768          # chunk 8192 for >= 2048; 4 x 64 x 2 = 512
-    assert wc(1, 64, 8192, 64, 0, 0) == 1024              # chunk 256; 8 x 64 = 512
+    assert wc(1, 64, 8192, 64, 0, 0) == 1024              # the chunk itself (1024: 8 x 64 = 512 already)
+    assert wc(1, 64, 16384, 64, 0, 0) == 2048             # chunk 1024; 8 x 64 = 512
     assert wc(1, 8, 3000, 64, 0, 0) == 256                # too few workgroups to grow
     assert wc(1, 64, 1 << 20, 64, 4096, 0) == 4096        # an explicit chunk sets both
     assert wc(1, 64, 1 << 20, 64, 4096, 32768) == 32768

@@ -6,6 +6,8 @@ block 64 (dK and dV with the tokens last first), so the cases mix heads that
 take the warm-start path with heads that take the three-pass path, ragged
 tails, initial states and final-state gradients.  Each head is held to the
 tolerance on its own RMS."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -179,17 +181,20 @@ def test_bwd_exact_flag(dev):
 
 @pytest.mark.parametrize("in_place", [False, True])
 def test_bwd_warm_chunk_longer_than_scan_chunk(dev, in_place):
-    """At B16 H4 N16384 the backward's scan chunk is 512 tokens and its
+    """At B16 H4 N16384 the backward's scan chunk is 1024 tokens and its
     warm-start chunk 2048, so the paired dK / dV launch runs warm-start chunks
     of one length beside pass-C chunks of another, and hands the reverse-time
     warm start's final state on as dS0.  Decays: 0, one with a carry span of
-    512 (warm start only at the longer chunk), one just below 1, and 1; initial
+    832 (warm start only at the longer chunk), one just below 1, and 1; initial
     state and final-state gradient given, dS0 written over dS_N (in place) or
     apart."""
     B, H, n, d = 16, 4, 16384, 64
-    assert la.chunk_for(B, H, n, 64) == 512 and la.warm_chunk_for(B, H, n, 64) == 2048
-    lams = np.array([0.0, 0.96, 0.9995, 1.0], dtype=np.float32)
-    say("bwd warm chunk 2048 > scan chunk 512, B16 H4 N16384 d64, in place", in_place)
+    assert la.chunk_for(B, H, n, 64) == 1024 and la.warm_chunk_for(B, H, n, 64) == 2048
+    lams = np.array([0.0, 0.975, 0.9995, 1.0], dtype=np.float32)
+    span = int(math.ceil(30 * math.log(2) / -math.log(float(lams[1]))))
+    span = (span + 63) // 64 * 64
+    assert 1024 < 2 * span <= 2048, span
+    say("bwd warm chunk 2048 > scan chunk 1024, B16 H4 N16384 d64, in place", in_place)
     q, k, v = qkv_device(B, H, n, d, seed=170, device=dev)
     g = qkv_device(B, H, n, d, seed=171, device=dev)[0]
     s0 = state_device(B, H, d, seed=172, device=dev)

@@ -71,12 +71,12 @@ def test_noalloc_default_chunk(dev):
     """chunk 0: a workload whose default workspace (128 MiB of chunk states)
     exceeds the array, so the chunk is doubled; equal to the workspace entry
     point at that chunk and its default warm-start chunk."""
-    B, H, N, d = 1, 64, 8192, 128
+    B, H, N, d = 2, 64, 16384, 128
     L = _noalloc_chunk(B, H, N, d)
     assert la.workspace_bytes(B, H, N, d, 64) > la.NOALLOC_SCRATCH_BYTES
     assert L > la.chunk_for(B, H, N, 64)
     Lw = max(la.warm_chunk_for(B, H, N, 64), L)
-    say("noalloc default chunk B1 H64 N8192 d128 (chunk %d, warm %d)" % (L, Lw))
+    say("noalloc default chunk B2 H64 N16384 d128 (chunk %d, warm %d)" % (L, Lw))
     from long_context_decayed_amd.inputs import decay_lambdas
     q, k, v = qkv_device(B, H, N, d, seed=23, device=dev)
     lam = torch.from_numpy(decay_lambdas(H)).to(dev)
