@@ -183,9 +183,10 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* d
 // chunk has read kv_in, which may be kv_out).
 // With the warm-start check (a.guard and a.flags set), after the output
 // launch the check flags the decaying heads whose warm start left out a
-// state that is not negligible; the copy skips them, and they are run again
-// on the exact path (pass A, scan, pass C of the flagged heads only: three
-// launches whose workgroups return at once when no head is flagged).
+// state that is not negligible and copies out the others' final states (in
+// place of that copy); the flagged heads are run again on the exact path
+// (pass A, scan, pass C of the flagged heads only: three launches whose
+// workgroups return at once when no head is flagged).
 hipError_t run_passes(const la::PrefillArgs& a, hipStream_t st) {
   if (a.warm_start && a.rev) return hipErrorInvalidValue;
   hipError_t e = la::launch_aggregate_pass(a, st);
@@ -193,8 +194,8 @@ hipError_t run_passes(const la::PrefillArgs& a, hipStream_t st) {
     if (e == hipSuccess) e = la::launch_scan_pass(a, st, 1);
     if (e == hipSuccess) e = la::launch_mixed_pass(a, st);
     const bool check = a.guard && a.flags;
-    if (e == hipSuccess && check) e = la::launch_warm_guard(a, st);
-    if (e == hipSuccess) e = la::launch_scan_pass(a, st, 2);
+    // the check also hands on the final states of the decaying heads that pass it
+    if (e == hipSuccess) e = check ? la::launch_warm_guard(a, st) : la::launch_scan_pass(a, st, 2);
     if (check) {
       la::PrefillArgs r = a;
       r.warm_start = false;
@@ -584,8 +585,6 @@ int lightning_attn_bwd(const void* q, const void* k, const void* v, const float*
       if (e == hipSuccess) e = la::launch_mixed_pair(ak, av, st);
       if (e == hipSuccess) e = la::launch_warm_guard(ak, st);
       if (e == hipSuccess) e = la::launch_warm_guard(av, st);
-      if (e == hipSuccess) e = la::launch_scan_pass(ak, st, 2);
-      if (e == hipSuccess) e = la::launch_scan_pass(av, st, 2);
       la::PrefillArgs rk = ak, rv = av;
       rk.warm_start = rv.warm_start = false;
       rk.rerun = rv.rerun = true;

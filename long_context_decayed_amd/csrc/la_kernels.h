@@ -62,8 +62,9 @@ hipError_t launch_aggregate_pass(const PrefillArgs& a, hipStream_t st);
 // flag is set excepted), 3 the scan of the flagged heads only: la_state.hip.
 hipError_t launch_scan_pass(const PrefillArgs& a, hipStream_t st, int part = 0);
 // The warm-start check: flags[bh] = 1 for a decaying head when some chunk's
-// warm-up window left out a state above 2^-24 of the state it starts from
-// (la_state.hip).
+// warm-up window left out a state above 2^-24 of the state it starts from;
+// the decaying heads that pass it have their final states copied to kv_out
+// (the work of scan part 2 for them) (la_state.hip).
 hipError_t launch_warm_guard(const PrefillArgs& a, hipStream_t st);
 // Pass C (outputs from the chunk start states; with warm_start, of the
 // heads that do not decay within their chunk only): la_output.hip.

@@ -376,33 +376,58 @@ __global__ __launch_bounds__(256) void la_chunk_scan(const float* __restrict__ d
 // zeros) fails it, and the head is then run on the exact path.  lam = 0 has
 // span 0 and omits nothing.  NaN or inf in either fails the check.  One wave
 // per bh; every flag is written.
-__global__ __launch_bounds__(64) void la_warm_guard(const float* __restrict__ decay, const float* __restrict__ guard,
-                                                    int* __restrict__ flags, int H, int ncw, int Lw, int nw) {
-  const int bh = blockIdx.x, lane = threadIdx.x;
+//   The same workgroup then hands on the head's final state, which the
+// warm-start pass left in the head's last chunk slot of ws: copied to kv_out
+// (times lam with scale_out, the backward's initial-state gradient) for a
+// decaying head that passed the check.  A flagged head's final state comes
+// from its exact re-run; the other heads' from the scan.
+__global__ __launch_bounds__(256) void la_warm_guard(const float* __restrict__ decay, const float* __restrict__ guard,
+                                                     int* __restrict__ flags, int H, int ncw, int Lw, int nw,
+                                                     const float* __restrict__ ws, float* __restrict__ kv_out, int nc,
+                                                     int D, int scale_out, const int* __restrict__ slots,
+                                                     int64_t num_slots) {
+  __shared__ int bad_s;
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const float lam = decay[bh % H];
   const int span = carry_span(lam);
-  bool bad = false;
-  if (span > 0 && decays_within_chunk(span, Lw)) {
-    const double f = pow_int((double)lam, span);
-    for (int c = 1 + lane; c < ncw; c += 64) {
-      const float* xs = guard + ((int64_t)bh * ncw + c - 1) * kGuardSlots;
-      const float* ws = guard + ((int64_t)bh * ncw + c) * kGuardSlots + 4;
-      float x = 0.0f, wv = 0.0f;
-      for (int w = 0; w < nw; ++w) {  // as bit patterns: a NaN stays the largest
-        x = __uint_as_float(max(__float_as_uint(x), __float_as_uint(xs[w])));
-        wv = __uint_as_float(max(__float_as_uint(wv), __float_as_uint(ws[w])));
+  const bool warm = decays_within_chunk(span, Lw);
+  if (tid < 64) {
+    bool bad = false;
+    if (span > 0 && warm) {
+      const double f = pow_int((double)lam, span);
+      for (int c = 1 + lane; c < ncw; c += 64) {
+        const float* xs = guard + ((int64_t)bh * ncw + c - 1) * kGuardSlots;
+        const float* wsl = guard + ((int64_t)bh * ncw + c) * kGuardSlots + 4;
+        float x = 0.0f, wv = 0.0f;
+        for (int w = 0; w < nw; ++w) {  // as bit patterns: a NaN stays the largest
+          x = __uint_as_float(max(__float_as_uint(x), __float_as_uint(xs[w])));
+          wv = __uint_as_float(max(__float_as_uint(wv), __float_as_uint(wsl[w])));
+        }
+        if (!((double)x * f <= 0x1p-24 * (double)wv)) bad = true;
       }
-      if (!((double)x * f <= 0x1p-24 * (double)wv)) bad = true;
+    }
+    bad = __any(bad);
+    if (lane == 0) {
+      flags[bh] = bad ? 1 : 0;
+      bad_s = bad ? 1 : 0;
     }
   }
-  bad = __any(bad);
-  if (lane == 0) flags[bh] = bad ? 1 : 0;
+  __syncthreads();
+  if (!warm || bad_s || !kv_out) return;
+  const int64_t srow = state_row(bh, H, slots, num_slots);
+  if (srow < 0) return;  // a slot out of range keeps no final state
+  const float out_f = scale_out ? lam : 1.0f;
+  const int per = D * D / 4;
+  const f32x4* src = reinterpret_cast<const f32x4*>(ws) + ((int64_t)bh * nc + nc - 1) * per;
+  f32x4* dst = reinterpret_cast<f32x4*>(kv_out) + srow * per;
+  for (int e = tid; e < per; e += 256) dst[e] = out_f * src[e];
 }
 
 hipError_t launch_warm_guard(const PrefillArgs& a, hipStream_t st) {
   if (!a.guard || !a.flags || !a.warm_start) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(la_warm_guard, dim3((unsigned)(a.B * a.H)), dim3(64), 0, st, a.decay, (const float*)a.guard,
-                     a.flags, (int)a.H, a.nc_warm, (int)a.L_warm, (int)(a.d / 32));
+  hipLaunchKernelGGL(la_warm_guard, dim3((unsigned)(a.B * a.H)), dim3(256), 0, st, a.decay, (const float*)a.guard,
+                     a.flags, (int)a.H, a.nc_warm, (int)a.L_warm, (int)(a.d / 32), (const float*)a.states, a.kv_out,
+                     a.nc, (int)a.d, a.scale_kv_out ? 1 : 0, a.slots, a.num_slots);
   return hipGetLastError();
 }
 
