@@ -160,7 +160,7 @@ int lightning_attn_fwd_bf16_f32out(const void* q, const void* k, const void* v, 
  *               explicit chunk, that chunk); otherwise a multiple of 64, at
  *               least the scan's chunk.  Ignored by the other paths.
  *   flags     : 0, or LA_FLAG_EXACT and/or LA_FLAG_SILU_QKV
- *   workspace : device scratch of at least lightning_attn_fwd_workspace_bytes()
+ *   workspace : device scratch of at least lightning_attn_fwd_workspace_bytes_ex()
  *               bytes, 256-byte aligned, owned by the caller and not used
  *               after the enqueued work completes; NULL = allocate
  *               stream-ordered as lightning_attn_fwd does.
@@ -271,15 +271,20 @@ int64_t lightning_attn_fwd_chunk(int64_t B, int64_t H, int64_t N, int64_t block,
 int64_t lightning_attn_fwd_warm_chunk(int64_t B, int64_t H, int64_t N, int64_t block, int64_t chunk,
                                       int64_t warm_chunk);
 
-/* Bytes of scratch lightning_attn_fwd_ex needs for these sizes (0 on invalid
- * arguments).  Layout, each part starting 256-byte aligned: the decay-power
+/* Bytes of scratch the prefill needs for these sizes at the default chunk
+ * (lightning_attn_fwd, or lightning_attn_fwd_ex with chunk 0); 0 on invalid
+ * arguments.  Layout, each part starting 256-byte aligned: the decay-power
  * table; B*H*ceil(N/chunk) float32 d x d chunk states; the warm-start check's
  * slots (8 floats per (b, h) and chunk); and, as the last B*H*4 bytes, one
  * int32 per (b, h), row-major: 1 when the check sent that head to the exact
  * path in the call, else 0 (written by every bf16 block-64 call without
  * LA_FLAG_EXACT). */
-size_t lightning_attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
-                                          int64_t chunk);
+size_t lightning_attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block);
+
+/* The same for lightning_attn_fwd_ex with an explicit chunk (0 = the
+ * default, as above). */
+size_t lightning_attn_fwd_workspace_bytes_ex(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                                             int64_t chunk);
 
 /*
  * One decode step for B sequences (N = 1 of the recurrence above):
@@ -395,7 +400,7 @@ int lightning_attn_silu(void* x, int64_t n, void* stream);
  *   warm_chunk : 0 = the default warm-start chunk of lightning_attn_fwd_ex
  *                (chunk 0), but at least the chunk; otherwise as there
  * Returns LA_ERR_WORKSPACE when the workspace for these sizes (see
- * lightning_attn_fwd_workspace_bytes) exceeds LA_NOALLOC_SCRATCH_BYTES, with
+ * lightning_attn_fwd_workspace_bytes_ex) exceeds LA_NOALLOC_SCRATCH_BYTES, with
  * nothing enqueued.  The array is shared by every call on a GPU and keeps the
  * last call's contents: calls that overlap in time on one GPU (two streams,
  * two threads) race and give undefined results; calls ordered on one stream

@@ -91,7 +91,9 @@ def load():
     lib.lightning_attn_fwd_warm_chunk.restype = I64
     lib.lightning_attn_fwd_warm_chunk.argtypes = [I64, I64, I64, I64, I64, I64]
     lib.lightning_attn_fwd_workspace_bytes.restype = SZ
-    lib.lightning_attn_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64]
+    lib.lightning_attn_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64]
+    lib.lightning_attn_fwd_workspace_bytes_ex.restype = SZ
+    lib.lightning_attn_fwd_workspace_bytes_ex.argtypes = [I64, I64, I64, I64, I64, I64]
     lib.lightning_attn_decode_step.restype = I
     lib.lightning_attn_decode_step.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, P]
     lib.lightning_attn_decode_fused.restype = I
@@ -185,7 +187,7 @@ def lib_bwd_workspace_bytes(B, H, N, d):
 
 
 def workspace_bytes(B, H, N, d, block=64, chunk=0):
-    return int(load().lightning_attn_fwd_workspace_bytes(B, H, N, d, block, chunk))
+    return int(load().lightning_attn_fwd_workspace_bytes_ex(B, H, N, d, block, chunk))
 
 
 def _fwd_flags(exact, silu):
@@ -223,9 +225,9 @@ def fwd(q, k, v, decay, kv_in=None, kv_out=None, block=64, out=None, out_dtype=N
     if out is None:
         out = torch.empty((B, H, N, d), device=q.device, dtype=odt)
     _check_dev("out", out, odt, (B, H, N, d), device=dev)
-    need = int(lib.lightning_attn_fwd_workspace_bytes(B, H, N, d, block, chunk))
+    need = int(lib.lightning_attn_fwd_workspace_bytes_ex(B, H, N, d, block, chunk))
     if need == 0:
-        raise LightningAttnError(1, "lightning_attn_fwd_workspace_bytes")
+        raise LightningAttnError(1, "lightning_attn_fwd_workspace_bytes_ex")
     if workspace is None:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
     _check_dev("workspace", workspace, torch.uint8, device=dev)
@@ -265,9 +267,9 @@ def fwd_fused(q, k, v, decay, gamma=None, gate=None, eps=1e-5, kv_in=None, kv_ou
     if out is None:
         out = torch.empty((B, H, N, d), device=q.device, dtype=out_dtype)
     _check_dev("out", out, out_dtype, (B, H, N, d), device=dev)
-    need = int(lib.lightning_attn_fwd_workspace_bytes(B, H, N, d, 64, chunk))
+    need = int(lib.lightning_attn_fwd_workspace_bytes_ex(B, H, N, d, 64, chunk))
     if need == 0:
-        raise LightningAttnError(1, "lightning_attn_fwd_workspace_bytes")
+        raise LightningAttnError(1, "lightning_attn_fwd_workspace_bytes_ex")
     if workspace is None:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
     _check_dev("workspace", workspace, torch.uint8, device=dev)

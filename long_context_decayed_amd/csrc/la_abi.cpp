@@ -623,11 +623,15 @@ int64_t lightning_attn_fwd_warm_chunk(int64_t B, int64_t H, int64_t N, int64_t b
   return Lw;
 }
 
-size_t lightning_attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
-                                          int64_t chunk) {
+size_t lightning_attn_fwd_workspace_bytes_ex(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                                             int64_t chunk) {
   int64_t L = 0;
   if (d < 1 || resolve_chunk(B, H, N, block, chunk, &L) != LA_OK) return 0;
   return workspace_layout(B, H, N, d, block, L, nullptr);
+}
+
+size_t lightning_attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block) {
+  return lightning_attn_fwd_workspace_bytes_ex(B, H, N, d, block, 0);
 }
 
 int lightning_attn_decode_step(const void* q, const void* k, const void* v, const float* decay, void* out,

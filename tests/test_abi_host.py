@@ -35,6 +35,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ("lightning_attn_fwd", "lightning_attn_fwd_f32", "lightning_attn_fwd_bf16_f32out",
                      "lightning_attn_fwd_ex", "lightning_attn_decode_step", "lightning_attn_fwd_workspace_bytes",
+                     "lightning_attn_fwd_workspace_bytes_ex",
                      "lightning_attn_fwd_chunk", "lightning_attn_strerror", "lightning_attn_runtime_version"):
         assert required in names
 
@@ -102,7 +103,7 @@ def test_alignment_and_overlap(lib):
 
 
 def test_workspace_checks(lib):
-    need = lib.lightning_attn_fwd_workspace_bytes(1, 2, 128, 64, 64, 0)
+    need = lib.lightning_attn_fwd_workspace_bytes(1, 2, 128, 64, 64)
     assert need > 0
     assert _fwd(lib, ws=FAKE[6], wsb=need - 1) == LA_ERR_WORKSPACE
     assert _fwd(lib, ws=ctypes.c_void_p(FAKE[6].value + 16), wsb=need) == LA_ERR_INVALID
@@ -114,7 +115,12 @@ def test_workspace_and_chunk_values(lib):
     tbl = 64 * 320 * 4
     states = 64 * 64 * 128 * 128 * 4
     guard = 64 * 64 * 8 * 4  # the warm-start check: 8 floats per (b, h, chunk), then one int per (b, h)
-    assert lib.lightning_attn_fwd_workspace_bytes(1, 64, 1 << 20, 128, 256, 0) == tbl + states + guard + 64 * 4
+    assert lib.lightning_attn_fwd_workspace_bytes(1, 64, 1 << 20, 128, 256) == tbl + states + guard + 64 * 4
+    assert lib.lightning_attn_fwd_workspace_bytes_ex(1, 64, 1 << 20, 128, 256, 0) == tbl + states + guard + 64 * 4
+    # an explicit chunk: 4096 tokens -> 256 chunk states per head
+    assert lib.lightning_attn_fwd_workspace_bytes_ex(1, 64, 1 << 20, 128, 256, 4096) == (
+        tbl + 4 * states + 4 * guard + 64 * 4)
+    assert lib.lightning_attn_fwd_workspace_bytes_ex(1, 64, 1 << 20, 128, 256, 100) == 0  # not a multiple of block
     # batched: 4 x 64 heads x 65536 tokens -> halve once to reach 2048 workgroups
     assert lib.lightning_attn_fwd_chunk(4, 64, 65536, 64, 0) == 8192
     # 8192 tokens x 64 heads: chunks would halve until >= 2048 workgroups, but
@@ -128,7 +134,8 @@ def test_workspace_and_chunk_values(lib):
     assert lib.lightning_attn_fwd_chunk(1, 1, 100, 64, 0) == 128
     assert lib.lightning_attn_fwd_chunk(1, 1, 100, 64, 192) == 192
     assert lib.lightning_attn_fwd_chunk(1, 1, 100, 64, 100) == -1
-    assert lib.lightning_attn_fwd_workspace_bytes(1, 1, 0, 64, 64, 0) == 0
+    assert lib.lightning_attn_fwd_workspace_bytes(1, 1, 0, 64, 64) == 0
+    assert lib.lightning_attn_fwd_workspace_bytes_ex(1, 1, 0, 64, 64, 0) == 0
 
 
 def test_decode_validation(lib):
@@ -245,7 +252,7 @@ def test_bwd_validation(lib):
     a[18], a[19] = FAKE[5], 16                                 # workspace too small
     assert f(*a) == LA_ERR_WORKSPACE
     need = lib.lightning_attn_bwd_workspace_bytes(1, 64, 1 << 20, 128)
-    fwd = lib.lightning_attn_fwd_workspace_bytes(1, 64, 1 << 20, 128, 64, 0)
+    fwd = lib.lightning_attn_fwd_workspace_bytes(1, 64, 1 << 20, 128, 64)
     tbl = 64 * 128 * 4  # decay table: H rows of 128 floats (block + 1 rounded up to 64)
     assert need == fwd + (fwd - tbl) + 2 * 64 * 128 * 128 * 4  # second chunk-state area, S0^T, dS_N^T
     assert lib.lightning_attn_bwd_workspace_bytes(1, 1, 0, 128) == 0
@@ -435,7 +442,7 @@ def test_written_buffers_apart_from_every_input(lib):
     assert _fwd(lib, kv_out=FAKE[3]) == LA_ERR_INVALID
     assert _fwd(lib, out=FAKE[3]) == LA_ERR_INVALID
     # a caller's workspace over q, over the output, over the decays
-    need = lib.lightning_attn_fwd_workspace_bytes(1, 2, 128, 64, 64, 0)
+    need = lib.lightning_attn_fwd_workspace_bytes(1, 2, 128, 64, 64)
     for target in (FAKE[0], FAKE[4], FAKE[3]):
         assert _fwd(lib, ws=target, wsb=need) == LA_ERR_INVALID
     # decode: the written state over q, the output over the decays
