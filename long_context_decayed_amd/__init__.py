@@ -9,6 +9,7 @@ no CPU fallback.
     out = fwd(q, k, v, decay, kv_in=None, kv_out=None, block=64)
     o   = decode_step(q, k, v, decay, kv_in, kv_out)
     dq, dk, dv, dkv_in = bwd(q, k, v, decay, dout)
+    out, kv_out = lightning_attn(q, k, v, decay, kv_in)   # differentiable (autograd)
 
 block 64 is the tuned path; 128 and 256 give the same result up to rounding
 through a general, slower kernel.
@@ -31,6 +32,7 @@ __all__ = [
     "NOALLOC_SCRATCH_BYTES",
     "fwd_slots",
     "bwd",
+    "lightning_attn",
     "decode_step",
     "decode_slots",
     "decode_fused",
@@ -412,6 +414,35 @@ def bwd(q, k, v, decay, dout, kv_in=None, dkv_out=None, out_dtype=None, dkv_in=F
     if rc != 0:
         raise LightningAttnError(rc, "lightning_attn_bwd")
     return dq, dk, dv, dkv_in
+
+
+class _LightningAttnFunction(torch.autograd.Function):
+    """fwd in the forward, bwd in the backward: the same library calls, with
+    the tensors autograd hands over."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, decay, kv_in, block):
+        B, H, N, d = q.shape
+        kv_out = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32)
+        out = fwd(q, k, v, decay, kv_in=kv_in, kv_out=kv_out, block=block)
+        ctx.save_for_backward(q, k, v, decay, kv_in)
+        return out, kv_out
+
+    @staticmethod
+    def backward(ctx, dout, dkv_out):
+        q, k, v, decay, kv_in = ctx.saved_tensors
+        want_dkv_in = kv_in is not None and ctx.needs_input_grad[4]
+        dq, dk, dv, dkv_in = bwd(q, k, v, decay, dout.contiguous(), kv_in=kv_in,
+                                 dkv_out=None if dkv_out is None else dkv_out.contiguous(), dkv_in=want_dkv_in)
+        return dq, dk, dv, None, dkv_in, None
+
+
+def lightning_attn(q, k, v, decay, kv_in=None, block=64):
+    """The prefill as a differentiable op: returns (out, kv_out) like fwd with
+    kv_out given, and gradients for q, k, v and kv_in through bwd (out's and
+    kv_out's gradients both enter).  decay gets no gradient.  q, k, v: bf16 or
+    fp32 [B, H, N, d] on one device; kv_in fp32 [B, H, d, d] or None."""
+    return _LightningAttnFunction.apply(q, k, v, decay, kv_in, block)
 
 
 def decode_slots(q, k, v, decay, states, slots, out=None, stream=None):
