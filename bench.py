@@ -395,6 +395,13 @@ def bench_decode(args, dev):
     res = dict(workload="decode 256 seq x H=64 x d=128, fp32 state, bf16 q/k/v/o", steps=steps,
                us_per_step=ms * 1e3 / steps, bytes_per_step=per_step_bytes, gb_per_s=gbs,
                frac_hbm=gbs / HBM_PEAK_GBS)
+    # The same 1 GiB state swept in place by a plain elementwise kernel (read
+    # and written once, as the decode step does): what this GPU streams for
+    # that traffic, beside the datasheet's 8 TB/s.
+    us_mix = _time_ms(lambda: s.mul_(1.0), 50) * 1e3
+    mix_gbs = 2 * B * H * d * d * 4 / (us_mix * 1e-6) / 1e9
+    res["stream_ceiling"] = dict(probe="torch: state.mul_(1.0) in place over the same fp32 state", us=us_mix,
+                                 achieved=mix_gbs, unit="GB/s", decode_frac_of_it=gbs / mix_gbs)
     del s
     # Serving form: the same 256 rows over a pool of 512 state slots, through a
     # seeded random slot table (each row its own slot).
